@@ -1,0 +1,341 @@
+/*
+ * fp4kv_oracle.c -- plain, slow CPU oracle for the FP4 KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the CPU baseline leg of
+ * the benchmark do.  It shares no code, header, table or constant with the
+ * HIP path: every table below is built from the number-format definitions.
+ *
+ * What it computes, and where the pages state it:
+ *
+ *   Quantiser -- "Quantising the KV cache" (numerics-explained), Code section,
+ *   the FP4 block quantiser excerpt, and Concept section, paragraph "FP4 with
+ *   a fine-grained scale": a row is cut into blocks of 16 consecutive
+ *   channels; the block's scale is its largest magnitude divided by 6, rounded
+ *   to FP8 E4M3 (round to nearest, ties to even, saturating); a scale that
+ *   rounds to zero is replaced by the smallest positive E4M3 subnormal; each
+ *   element divided by the scale is rounded to FP4 E2M1 (same rounding) and the
+ *   stored value is that E2M1 number times the scale.
+ *
+ *   Attention -- same page, Code section (the quantised K and V replace the
+ *   real ones between the projections and an unchanged attention; Q is not
+ *   quantised) and Concept section (every new token reads every cached key
+ *   and value).  Attention is written out from its definition in fp64:
+ *   z_t = scale * <q, k_t>,  w_t = exp(z_t - max z),  o = sum w_t v_t / sum w_t.
+ *
+ * Readings where the pages are silent are listed with the functions that
+ * make them.  Every arithmetic step here is exact except the exp/sum/divide
+ * of the attention, which runs in fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- formats */
+
+/* FP4 E2M1 magnitude of a 3-bit code: 2 exponent bits with bias 1, one
+ * mantissa bit, a subnormal at exponent 0, no infinity or NaN.
+ * Codes 0..7 give 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double fp4kv_oracle_e2m1_value(int code)
+{
+    int e = (code >> 1) & 3, m = code & 1;
+    if (e == 0)
+        return 0.5 * m;                         /* subnormal: m * 2^(1-1) * 0.5 */
+    return ldexp(1.0 + 0.5 * m, e - 1);
+}
+
+/* FP8 E4M3 magnitude of a 7-bit code, OCP "FN" variant (reading: the pages
+ * name E4M3 and its smallest subnormal, which fixes bias 7).  4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals at exponent 0; code 0x7F is NaN,
+ * so the finite codes are 0..126 and the largest is 0x7E = 448. */
+double fp4kv_oracle_e4m3_value(int code)
+{
+    int e = (code >> 3) & 15, m = code & 7;
+    if (e == 0)
+        return ldexp((double)m, -9);            /* m/8 * 2^(1-7) */
+    return ldexp(1.0 + m / 8.0, e - 7);
+}
+
+#define E2M1_MAX_CODE 7
+#define E4M3_MAX_CODE 126
+
+/* Round the exact quotient num/den (num >= 0, den > 0) to the nearest finite
+ * magnitude of a format, ties to the even code, and saturate anything at or
+ * beyond the largest finite magnitude to that magnitude.
+ *
+ * Reading: the pages call their encoder with mode "rne" and a flag set to
+ * true; the flag is read as saturation, as E2M1 has no infinity to overflow
+ * into.  The pages divide in double precision before rounding; rounding the
+ * exact quotient instead gives the same code for every bf16 input (the
+ * quotient is never within a double ulp of a rounding boundary it is not
+ * equal to), and keeps this function exact by construction.
+ *
+ * No division is done: num is compared with value*den, and 2*num with the
+ * sum of two neighbouring values times den.  For the operands used here
+ * (num a bf16 magnitude, den = 6 or an E4M3 value, values with at most 4
+ * significant bits) every product and sum is exact in double. */
+static int round_ratio_rne_sat(double num, double den, double (*value)(int), int max_code)
+{
+    if (num >= value(max_code) * den)
+        return max_code;
+    int lo = 0;
+    while (value(lo + 1) * den <= num)          /* value(lo)*den <= num < value(lo+1)*den */
+        lo++;
+    double twice = 2.0 * num;
+    double mid2 = (value(lo) + value(lo + 1)) * den;
+    if (twice < mid2)
+        return lo;
+    if (twice > mid2)
+        return lo + 1;
+    return (lo % 2 == 0) ? lo : lo + 1;         /* exactly halfway: the even code */
+}
+
+/* bf16 bit pattern -> its exact value. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------- quantiser */
+
+/* Quantise one block of n (1..16) bf16 values, following the block loop of
+ * the page's quantiser excerpt in its order:
+ *   amax -> scale code = RNE_sat_E4M3(amax / 6) -> zero scale replaced by the
+ *   smallest subnormal -> per element code = RNE_sat_E2M1(|x| / s).
+ * Outputs: nib[c] = sign << 3 | magnitude code (reading: the sign of the input
+ * is kept, also when the magnitude rounds to zero, as an IEEE conversion
+ * does); *scale_code = E4M3 code of s; xhat[c] = +-E2M1(code) * s (may be
+ * NULL).  Returns -1 if an input is not finite (inputs must be finite). */
+int fp4kv_oracle_quantize_block(const uint16_t *x, int n, uint8_t *nib,
+                                uint8_t *scale_code, double *xhat)
+{
+    double amax = 0.0;
+    for (int c = 0; c < n; c++) {
+        double v = bf16_value(x[c]);
+        if (!isfinite(v))
+            return -1;
+        if (fabs(v) > amax)
+            amax = fabs(v);
+    }
+    int sc = round_ratio_rne_sat(amax, 6.0, fp4kv_oracle_e4m3_value, E4M3_MAX_CODE);
+    if (sc == 0)
+        sc = 1;                                  /* the smallest positive E4M3 subnormal, 2^-9 */
+    double s = fp4kv_oracle_e4m3_value(sc);
+    *scale_code = (uint8_t)sc;
+    for (int c = 0; c < n; c++) {
+        double v = bf16_value(x[c]);
+        int neg = signbit(v) ? 1 : 0;
+        int e = round_ratio_rne_sat(fabs(v), s, fp4kv_oracle_e2m1_value, E2M1_MAX_CODE);
+        nib[c] = (uint8_t)((neg << 3) | e);
+        if (xhat)
+            xhat[c] = (neg ? -1.0 : 1.0) * fp4kv_oracle_e2m1_value(e) * s;
+    }
+    return 0;
+}
+
+/* Quantise rows [r0, r1) of a row-major [n_rows][row_len] bf16 array.
+ * A row is cut into blocks of 16 consecutive channels; a row length that is
+ * not a multiple of 16 leaves a shorter last block (as slicing does).
+ * nib: [n_rows][row_len], one code per byte.  scales: [n_rows][n_blocks].
+ * xhat: [n_rows][row_len] or NULL. */
+static int quantize_row_range(const uint16_t *x, int64_t r0, int64_t r1, int row_len,
+                              uint8_t *nib, uint8_t *scales, double *xhat)
+{
+    int n_blocks = (row_len + 15) / 16;
+    for (int64_t r = r0; r < r1; r++) {
+        for (int b = 0; b < n_blocks; b++) {
+            int c0 = 16 * b;
+            int n = row_len - c0 < 16 ? row_len - c0 : 16;
+            int rc = fp4kv_oracle_quantize_block(x + r * row_len + c0, n,
+                                                 nib + r * row_len + c0,
+                                                 scales + r * n_blocks + b,
+                                                 xhat ? xhat + r * row_len + c0 : NULL);
+            if (rc)
+                return rc;
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    const uint16_t *x;
+    int64_t r0, r1;
+    int row_len;
+    uint8_t *nib, *scales;
+    double *xhat;
+    int rc;
+} quant_job;
+
+static void *quant_worker(void *arg)
+{
+    quant_job *j = (quant_job *)arg;
+    j->rc = quantize_row_range(j->x, j->r0, j->r1, j->row_len, j->nib, j->scales, j->xhat);
+    return NULL;
+}
+
+/* Threaded over rows only; each row is quantised exactly as above. */
+int fp4kv_oracle_quantize_rows(const uint16_t *x, int64_t n_rows, int row_len,
+                               uint8_t *nib, uint8_t *scales, double *xhat, int n_threads)
+{
+    if (row_len <= 0 || n_rows < 0)
+        return -2;
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if ((int64_t)n_threads > n_rows)
+        n_threads = n_rows > 0 ? (int)n_rows : 1;
+    if (n_threads == 1)
+        return quantize_row_range(x, 0, n_rows, row_len, nib, scales, xhat);
+    pthread_t tid[256];
+    quant_job job[256];
+    int64_t per = (n_rows + n_threads - 1) / n_threads;
+    for (int i = 0; i < n_threads; i++) {
+        int64_t r0 = i * per, r1 = r0 + per > n_rows ? n_rows : r0 + per;
+        if (r0 > r1)
+            r0 = r1;
+        job[i] = (quant_job){x, r0, r1, row_len, nib, scales, xhat, 0};
+        pthread_create(&tid[i], NULL, quant_worker, &job[i]);
+    }
+    int rc = 0;
+    for (int i = 0; i < n_threads; i++) {
+        pthread_join(tid[i], NULL);
+        if (job[i].rc)
+            rc = job[i].rc;
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------- attention */
+
+/* Dequantised cache value: E2M1(code) * scale, signed by the nibble's sign
+ * bit (the page's encoder returns the rounded element times the scale). */
+static double fp4_value(uint8_t nib, uint8_t scale_code)
+{
+    double v = fp4kv_oracle_e2m1_value(nib & 7) * fp4kv_oracle_e4m3_value(scale_code & 0x7F);
+    return (nib & 8) ? -v : v;
+}
+
+/* Decode attention for the G query heads that share one KV head, over T
+ * cached tokens, straight from the definition in fp64.
+ *   q:      [G][D] bf16 (not quantised)
+ *   k_nib:  token t's codes at k_nib + t*nib_stride, D bytes (one code each)
+ *   k_sc:   token t's scale codes at k_sc + t*sc_stride, D/16 bytes
+ *   v_nib, v_sc: the same for V
+ *   out:    [G][D] fp64.  T == 0 gives zeros (reading: an empty context
+ *           attends to nothing).
+ * D must be a multiple of 16 here. Returns -1 on bad arguments. */
+int fp4kv_oracle_attention(const uint16_t *q, int G, int D, int64_t T,
+                           const uint8_t *k_nib, const uint8_t *k_sc,
+                           const uint8_t *v_nib, const uint8_t *v_sc,
+                           int64_t nib_stride, int64_t sc_stride,
+                           double scale, double *out)
+{
+    if (G < 1 || D < 16 || D % 16 || T < 0)
+        return -1;
+    for (int i = 0; i < G * D; i++)
+        out[i] = 0.0;
+    if (T == 0)
+        return 0;
+    double *z = (double *)malloc(sizeof(double) * (size_t)T);
+    double *kv = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!z || !kv) {
+        free(z);
+        free(kv);
+        return -3;
+    }
+    for (int g = 0; g < G; g++) {
+        const uint16_t *qg = q + (int64_t)g * D;
+        double zmax = -INFINITY;
+        for (int64_t t = 0; t < T; t++) {
+            double dot = 0.0;
+            for (int c = 0; c < D; c++)
+                dot += bf16_value(qg[c]) * fp4_value(k_nib[t * nib_stride + c], k_sc[t * sc_stride + c / 16]);
+            z[t] = scale * dot;
+            if (z[t] > zmax)
+                zmax = z[t];
+        }
+        double wsum = 0.0;
+        double *og = out + (int64_t)g * D;
+        for (int64_t t = 0; t < T; t++) {
+            double w = exp(z[t] - zmax);
+            wsum += w;
+            for (int c = 0; c < D; c++)
+                kv[c] = fp4_value(v_nib[t * nib_stride + c], v_sc[t * sc_stride + c / 16]);
+            for (int c = 0; c < D; c++)
+                og[c] += w * kv[c];
+        }
+        for (int c = 0; c < D; c++)
+            og[c] /= wsum;
+    }
+    free(z);
+    free(kv);
+    return 0;
+}
+
+/* A batch of independent (sequence, KV head) attention problems, run on
+ * n_threads threads.  Problem i reads q_ptrs[i] ([G][D]), the code/scale
+ * pointers of index i (token stride nib_stride / sc_stride), T[i] tokens,
+ * and writes out_ptrs[i] ([G][D]). */
+typedef struct {
+    int64_t i0, i1;
+    int G, D;
+    const uint16_t *const *q;
+    const int64_t *T;
+    const uint8_t *const *kn, *const *ks, *const *vn, *const *vs;
+    int64_t nib_stride, sc_stride;
+    double scale;
+    double *const *out;
+    int rc;
+} attn_job;
+
+static void *attn_worker(void *arg)
+{
+    attn_job *j = (attn_job *)arg;
+    for (int64_t i = j->i0; i < j->i1; i++) {
+        int rc = fp4kv_oracle_attention(j->q[i], j->G, j->D, j->T[i], j->kn[i], j->ks[i],
+                                        j->vn[i], j->vs[i], j->nib_stride, j->sc_stride,
+                                        j->scale, j->out[i]);
+        if (rc)
+            j->rc = rc;
+    }
+    return NULL;
+}
+
+int fp4kv_oracle_attention_batch(int64_t n_problems, int G, int D,
+                                 const uint16_t *const *q, const int64_t *T,
+                                 const uint8_t *const *k_nib, const uint8_t *const *k_sc,
+                                 const uint8_t *const *v_nib, const uint8_t *const *v_sc,
+                                 int64_t nib_stride, int64_t sc_stride, double scale,
+                                 double *const *out, int n_threads)
+{
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if ((int64_t)n_threads > n_problems)
+        n_threads = n_problems > 0 ? (int)n_problems : 1;
+    pthread_t tid[256];
+    attn_job job[256];
+    int64_t per = (n_problems + n_threads - 1) / n_threads;
+    for (int i = 0; i < n_threads; i++) {
+        int64_t i0 = i * per, i1 = i0 + per > n_problems ? n_problems : i0 + per;
+        if (i0 > i1)
+            i0 = i1;
+        job[i] = (attn_job){i0, i1, G, D, q, T, k_nib, k_sc, v_nib, v_sc,
+                            nib_stride, sc_stride, scale, out, 0};
+        pthread_create(&tid[i], NULL, attn_worker, &job[i]);
+    }
+    int rc = 0;
+    for (int i = 0; i < n_threads; i++) {
+        pthread_join(tid[i], NULL);
+        if (job[i].rc)
+            rc = job[i].rc;
+    }
+    return rc;
+}
