@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 KV-cache decode path on one MI355X.
+
+Default workload: 32 sequences of 32768 tokens, 64 query heads over 8 KV heads
+(group 8), head dim 128, 64 context splits -- 1.2 GB of packed cache, larger
+than the GPU's last-level cache, so every step streams it from HBM.  A step
+is one decode-attention call (split kernel + combine kernel); for the paged
+workload a step also appends one token per sequence first.  The cache, the
+queries and every argument are resident on the device before timing starts.
+
+Prints one JSON line: achieved HBM GB/s over the step's algorithmic bytes
+(packed K/V read, queries read, outputs written, page-table and length
+entries read), decode steps/s, the split kernel's roofline figures, and the
+CPU oracle's rate on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--splits S]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4-KV decode attention: achieved HBM GB/s (% of peak) and decode steps/s"
+PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E peak, GB/s
+KERNEL_SOURCE = os.path.join(ROOT, "fp4_quantised_kv_amd", "csrc", "fp4kv_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Per-launch HBM bytes of the split kernel from the committed counter
+    summary, if it was taken from the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"decode_split_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seed, threads):
+    """The oracle (fp64 decode attention from its own codes) on a bounded
+    sample: whole sequences of the workload, all their KV heads."""
+    import numpy as np
+    import fp4kv_workloads as wl
+    import oracle
+    lens = wl.seq_lengths(w, seed)
+    n_seq = min(w.batch, max(1, threads // 2))
+    seqs = list(range(n_seq))
+    q = wl.queries(w, seed)
+    kc, ks, vc, vs = [], [], [], []
+    budget_tokens = 1 << 17                    # cap the sample at 131072 tokens per sequence
+    sample_lens = [min(int(lens[b]), budget_tokens) for b in range(w.batch)]
+    for b in range(w.batch):
+        if b in seqs:
+            k = wl.kv_tokens(w, seed, b, "k", 0, sample_lens[b])
+            v = wl.kv_tokens(w, seed, b, "v", 0, sample_lens[b])
+            a, sa, _ = oracle.quantize(wl.bf16_bits(k), want_xhat=False, n_threads=threads)
+            c, sc, _ = oracle.quantize(wl.bf16_bits(v), want_xhat=False, n_threads=threads)
+        else:
+            a = c = np.zeros((0, w.kv_heads, w.head_dim), np.uint8)
+            sa = sc = np.zeros((0, w.kv_heads, w.head_dim // 16), np.uint8)
+        kc.append(a); ks.append(sa); vc.append(c); vs.append(sc)
+    heads = [(b, h) for b in seqs for h in range(w.kv_heads)]
+    t0 = time.perf_counter()
+    oracle.decode_attention(wl.bf16_bits(q), kc, ks, vc, vs, sample_lens, w.head_dim ** -0.5,
+                            heads=heads, n_threads=threads)
+    dt = time.perf_counter() - t0
+    tokens = sum(sample_lens[b] for b in seqs)
+    bytes_ = tokens * 2 * w.kv_heads * w.head_dim * 9 // 16 + n_seq * w.q_heads * w.head_dim * 6
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {w.batch} sequences, {tokens} tokens, all {w.kv_heads} KV heads; "
+                      f"decode attention from the oracle's own codes in fp64, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa8_b32_ctx32k")
+    ap.add_argument("--splits", type=int, default=None, help="context splits (default: the workload's)")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode path shards by sequence and KV head with no "
+              "exchange, so a multi-GPU figure is N independent copies of this one; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_quantised_kv_amd as fk
+    import fp4kv_harness as hx
+    import fp4kv_workloads as wl
+
+    if not os.path.exists(fk.LIBRARY_PATH):
+        from fp4_quantised_kv_amd import build as hip_build
+        hip_build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = wl.WORKLOADS[args.workload]
+    if w.kind == "prefill":
+        raise SystemExit("the prefill workload is timed by its own test, not as a decode step")
+    splits_req = w.splits if args.splits is None else args.splits
+    paged = w.kind == "paged"
+    total_steps = args.warmup + args.steps
+    t_setup = time.perf_counter()
+    print(f"# building cache for {w.name}: {w.description}", file=sys.stderr, flush=True)
+    gc = hx.build_cache(w, args.seed, extra_tokens=total_steps if paged else 0, zero=False)
+    print(f"# cache built in {time.perf_counter() - t_setup:.1f} s "
+          f"({gc.layout.cache_bytes / 1e9:.3f} GB)", file=sys.stderr, flush=True)
+    L = gc.layout
+    B, Hq, D = w.batch, w.q_heads, w.head_dim
+    max_pages = gc.page_table.shape[1]
+    splits, ws_bytes = fk.decode_plan(L, B, Hq, max_pages, splits_req)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    lens0 = gc.lens_cpu.clone()
+
+    # per-step inputs, all on the device before timing
+    qs = [wl.queries(w, args.seed, step=s if paged else 0).to(dev) for s in range(total_steps if paged else 1)]
+    if paged:
+        news, slots, lens_dev = [], [], []
+        for s in range(total_steps):
+            kn, vn = wl.new_tokens(w, args.seed, s)
+            sl = torch.stack([wl.slots_for(gc.pt_cpu.table, b, int(lens0[b]) + s, int(lens0[b]) + s + 1)[0]
+                              for b in range(B)])
+            news.append((kn.to(dev), vn.to(dev)))
+            slots.append(sl.to(dev))
+            lens_dev.append((lens0 + s + 1).to(torch.int32).to(dev))
+    else:
+        lens_dev = [gc.seq_lens]
+    scale = D ** -0.5
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total_steps)]
+
+    def step(s):
+        e = ev[s]
+        e[0].record(stream)
+        if paged:
+            fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
+        e[1].record(stream)
+        fk.decode_split(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
+                        softmax_scale=scale, num_splits=splits_req, workspace=ws)
+        e[2].record(stream)
+        fk.decode_combine(ws, B, Hq, D, splits, out=out)
+        e[3].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.warmup, total_steps):
+        step(s)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    timed = ev[args.warmup:]
+    t_append = sum(e[0].elapsed_time(e[1]) for e in timed) / args.steps
+    t_split = sum(e[1].elapsed_time(e[2]) for e in timed) / args.steps
+    t_comb = sum(e[2].elapsed_time(e[3]) for e in timed) / args.steps
+    ms_per_step = total_ms / args.steps
+
+    # algorithmic bytes
+    if paged:
+        ctx = [int(lens0[b]) + args.warmup + 1 for b in range(B)]   # mid-run lengths, +1 per step
+        ctx_tokens = sum(ctx) + B * (args.steps - 1) / 2.0
+    else:
+        ctx = [int(x) for x in lens0]
+        ctx_tokens = float(sum(ctx))
+    pages_read = sum(-(-c // 64) for c in ctx)
+    cache_read = ctx_tokens * L.bytes_per_token
+    split_bytes = cache_read + B * Hq * D * 2 + pages_read * 4 + B * 4
+    step_bytes = split_bytes + B * Hq * D * 4
+    if paged:
+        step_bytes += B * w.kv_heads * D * 2 * 2 + B * L.bytes_per_token + B * 8
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    split_gbs = split_bytes / (t_split * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": w.kv_heads,
+                   "head_dim": D, "context": w.context if not paged else f"{w.min_len}..{w.max_len}",
+                   "splits": splits, "page_size": 64, "cache_bytes": L.cache_bytes},
+        "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
+                      "decode_combine": round(t_comb, 5)},
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(split_gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

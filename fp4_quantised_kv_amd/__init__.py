@@ -1,0 +1,244 @@
+"""Python binding of the FP4 KV-cache C ABI (include/fp4kv.h).
+
+Argument marshalling only: torch tensors are checked for dtype, device and
+contiguity and handed to the HIP library as raw pointers on the current
+stream; every step of the computation runs in the library's kernels.  If the
+library has not been built this module raises instead of computing anything
+another way.
+
+    layout = cache_layout(num_kv_heads=8, head_dim=128, num_pages=n)
+    cache = torch.empty(layout.cache_bytes, dtype=torch.uint8, device="cuda")
+    quantize_append(layout, k, v, slot_mapping, cache)
+    out = decode_attention(layout, cache, q, seq_lens, page_table)
+"""
+import ctypes
+import math
+import os
+
+__all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "library", "cache_layout", "decode_plan",
+           "quantize_append", "decode_attention", "decode_split", "decode_combine",
+           "status_string", "PAGE_SIZE", "MAX_GROUP"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(HERE, "libfp4kv.so")
+PAGE_SIZE = 64
+MAX_GROUP = 16
+
+OK = 0
+ERR_INVALID_ARGUMENT = -1
+ERR_UNSUPPORTED = -2
+ERR_MISALIGNED = -3
+ERR_WORKSPACE_TOO_SMALL = -4
+ERR_HIP = -5
+
+
+class Fp4KVError(RuntimeError):
+    def __init__(self, call, status):
+        super().__init__(f"{call}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class CacheParams(ctypes.Structure):
+    _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64)]
+
+
+class CacheLayout(ctypes.Structure):
+    _fields_ = [("params", CacheParams), ("block_bytes", ctypes.c_int64),
+                ("k_codes_offset", ctypes.c_int64), ("k_scales_offset", ctypes.c_int64),
+                ("v_codes_offset", ctypes.c_int64), ("v_scales_offset", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64), ("page_stride", ctypes.c_int64),
+                ("cache_bytes", ctypes.c_int64), ("bytes_per_token", ctypes.c_int64)]
+
+    @property
+    def num_kv_heads(self):
+        return self.params.num_kv_heads
+
+    @property
+    def head_dim(self):
+        return self.params.head_dim
+
+    @property
+    def num_pages(self):
+        return self.params.num_pages
+
+
+_LIB = None
+_P = ctypes.c_void_p
+
+
+def library():
+    """The loaded libfp4kv.so.  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY_PATH):
+            raise RuntimeError(f"{LIBRARY_PATH} is missing: build it with "
+                               "`python -m fp4_quantised_kv_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIBRARY_PATH)
+        L.fp4kv_cache_layout.argtypes = [ctypes.POINTER(CacheParams), ctypes.POINTER(CacheLayout)]
+        L.fp4kv_cache_layout.restype = ctypes.c_int
+        L.fp4kv_quantize_append.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int64,
+                                            _P, _P, _P]
+        L.fp4kv_quantize_append.restype = ctypes.c_int
+        L.fp4kv_decode_plan.argtypes = [ctypes.POINTER(CacheLayout), ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
+        L.fp4kv_decode_plan.restype = ctypes.c_int
+        L.fp4kv_decode_attention.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int32,
+                                             ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_float,
+                                             ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
+        L.fp4kv_decode_attention.restype = ctypes.c_int
+        L.fp4kv_decode_split.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int32,
+                                         ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_float,
+                                         ctypes.c_int32, _P, ctypes.c_int64, _P]
+        L.fp4kv_decode_split.restype = ctypes.c_int
+        L.fp4kv_decode_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
+        L.fp4kv_decode_combine.restype = ctypes.c_int
+        L.fp4kv_status_string.argtypes = [ctypes.c_int]
+        L.fp4kv_status_string.restype = ctypes.c_char_p
+        L.fp4kv_version.argtypes = []
+        L.fp4kv_version.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return library().fp4kv_status_string(int(status)).decode()
+
+
+def _check(call, rc):
+    if rc != OK:
+        raise Fp4KVError(call, rc)
+
+
+def cache_layout(num_kv_heads: int, head_dim: int, num_pages: int,
+                 page_size: int = PAGE_SIZE) -> CacheLayout:
+    p = CacheParams(num_kv_heads, head_dim, page_size, 0, num_pages)
+    out = CacheLayout()
+    _check("fp4kv_cache_layout", library().fp4kv_cache_layout(ctypes.byref(p), ctypes.byref(out)))
+    return out
+
+
+def decode_plan(layout: CacheLayout, batch: int, num_q_heads: int, max_pages_per_seq: int,
+                num_splits: int = 0):
+    """(splits, workspace bytes) that decode_attention uses for these arguments."""
+    s = ctypes.c_int32()
+    ws = ctypes.c_int64()
+    _check("fp4kv_decode_plan", library().fp4kv_decode_plan(
+        ctypes.byref(layout), batch, num_q_heads, max_pages_per_seq, num_splits,
+        ctypes.byref(s), ctypes.byref(ws)))
+    return s.value, ws.value
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _need(t, name, dtype, device_type="cuda"):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != device_type:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_append(layout: CacheLayout, k, v, slot_mapping, cache, stream=None):
+    """Quantise k, v (bf16 [n_tokens][H_kv][D]) into `cache` at `slot_mapping`
+    (int64 [n_tokens]; negative slots are skipped)."""
+    import torch
+    for t, n, d in ((k, "k", torch.bfloat16), (v, "v", torch.bfloat16),
+                    (slot_mapping, "slot_mapping", torch.int64), (cache, "cache", torch.uint8)):
+        _need(t, n, d)
+    n = k.shape[0] if k.dim() else 0
+    want = (n, layout.num_kv_heads, layout.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want:
+        raise ValueError(f"k and v must have shape {want}")
+    if tuple(slot_mapping.shape) != (n,):
+        raise ValueError("slot_mapping must have one entry per token")
+    if cache.numel() < layout.cache_bytes:
+        raise ValueError("cache is smaller than layout.cache_bytes")
+    _check("fp4kv_quantize_append", library().fp4kv_quantize_append(
+        ctypes.byref(layout), k.data_ptr(), v.data_ptr(), n, slot_mapping.data_ptr(),
+        cache.data_ptr(), _stream(stream)))
+
+
+def _decode_inputs(layout, cache, q, seq_lens, page_table, num_splits, workspace):
+    import torch
+    _need(cache, "cache", torch.uint8)
+    _need(q, "q", torch.bfloat16)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_table, "page_table", torch.int32)
+    B, Hq, D = q.shape
+    if D != layout.head_dim:
+        raise ValueError("q's last dimension must equal the cache head_dim")
+    if tuple(seq_lens.shape) != (B,) or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("seq_lens must be [B] and page_table [B][max_pages]")
+    if cache.numel() < layout.cache_bytes:
+        raise ValueError("cache is smaller than layout.cache_bytes")
+    max_pages = page_table.shape[1]
+    splits, ws_bytes = decode_plan(layout, B, Hq, max_pages, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    return B, Hq, D, max_pages, splits, workspace
+
+
+def _out_tensor(out, B, Hq, D, device):
+    import torch
+    if out is None:
+        return torch.empty(B, Hq, D, dtype=torch.float32, device=device)
+    _need(out, "out", torch.float32)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    return out
+
+
+def decode_attention(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_scale=None,
+                     num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Decode attention of q (bf16 [B][Hq][D]) over the cache; returns fp32
+    [B][Hq][D].  seq_lens int32 [B]; page_table int32 [B][max_pages]."""
+    B, Hq, D, max_pages, splits, workspace = _decode_inputs(
+        layout, cache, q, seq_lens, page_table, num_splits, workspace)
+    out = _out_tensor(out, B, Hq, D, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _check("fp4kv_decode_attention", library().fp4kv_decode_attention(
+        ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, Hq, seq_lens.data_ptr(),
+        page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
+        workspace.data_ptr(), workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def decode_split(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_scale=None,
+                 num_splits: int = 0, workspace=None, stream=None):
+    """First half of decode_attention: per-split partials in the workspace.
+    Returns (workspace, splits)."""
+    B, Hq, D, max_pages, splits, workspace = _decode_inputs(
+        layout, cache, q, seq_lens, page_table, num_splits, workspace)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _check("fp4kv_decode_split", library().fp4kv_decode_split(
+        ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, Hq, seq_lens.data_ptr(),
+        page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return workspace, splits
+
+
+def decode_combine(workspace, batch: int, num_q_heads: int, head_dim: int, splits: int,
+                   out=None, stream=None):
+    """Second half of decode_attention: merge `splits` partials into fp32
+    [batch][num_q_heads][head_dim]."""
+    import torch
+    _need(workspace, "workspace", torch.uint8)
+    out = _out_tensor(out, batch, num_q_heads, head_dim, workspace.device)
+    _check("fp4kv_decode_combine", library().fp4kv_decode_combine(
+        batch, num_q_heads, head_dim, splits, workspace.data_ptr(), workspace.numel(),
+        out.data_ptr(), _stream(stream)))
+    return out

@@ -1,0 +1,318 @@
+// Host side of the FP4 KV-cache C ABI: layout arithmetic, argument checks,
+// split planning and kernel launches.  Every check runs before the first HIP
+// call, so a rejected call has no effect on the device.
+#include "fp4kv.h"
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include <hip/hip_runtime.h>
+
+#include "fp4kv_internal.h"
+
+namespace {
+
+constexpr int32_t kPage = FP4KV_PAGE_SIZE;
+constexpr int32_t kTargetWaves = 2048;    // ~8 resident waves per CU on 256 CUs
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Layout of one (page, KV head) block: K codes, K scales, V codes, V scales.
+int fill_layout(const fp4kv_cache_params &p, fp4kv_cache_layout_t *out)
+{
+    if (p.num_kv_heads < 1 || p.num_pages < 1 || p.reserved != 0)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (p.head_dim != 64 && p.head_dim != 128)
+        return FP4KV_ERR_UNSUPPORTED;
+    if (p.page_size != kPage)
+        return FP4KV_ERR_UNSUPPORTED;
+    const int64_t D = p.head_dim;
+    const int64_t codes = static_cast<int64_t>(kPage) * D / 2;
+    const int64_t scales = static_cast<int64_t>(kPage) * D / 16;
+    const int64_t block = 2 * (codes + scales);               // = 64 * D * 9 / 8
+    const int64_t page_stride = block * p.num_kv_heads;
+    if (p.num_pages > std::numeric_limits<int64_t>::max() / page_stride)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    fp4kv_cache_layout_t L{};
+    L.params = p;
+    L.block_bytes = block;
+    L.k_codes_offset = 0;
+    L.k_scales_offset = codes;
+    L.v_codes_offset = codes + scales;
+    L.v_scales_offset = 2 * codes + scales;
+    L.head_stride = block;
+    L.page_stride = page_stride;
+    L.cache_bytes = page_stride * p.num_pages;
+    L.bytes_per_token = 2 * static_cast<int64_t>(p.num_kv_heads) * D * 9 / 16;
+    *out = L;
+    return FP4KV_OK;
+}
+
+// A layout passed back in must be exactly what fp4kv_cache_layout produces.
+int check_layout(const fp4kv_cache_layout_t *L)
+{
+    if (!L)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    fp4kv_cache_layout_t ref;
+    const int rc = fill_layout(L->params, &ref);
+    if (rc != FP4KV_OK)
+        return rc;
+    if (ref.block_bytes != L->block_bytes || ref.k_codes_offset != L->k_codes_offset ||
+        ref.k_scales_offset != L->k_scales_offset || ref.v_codes_offset != L->v_codes_offset ||
+        ref.v_scales_offset != L->v_scales_offset || ref.head_stride != L->head_stride ||
+        ref.page_stride != L->page_stride || ref.cache_bytes != L->cache_bytes ||
+        ref.bytes_per_token != L->bytes_per_token)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    return FP4KV_OK;
+}
+
+fp4kv::CacheGeom geom_of(const fp4kv_cache_layout_t &L)
+{
+    fp4kv::CacheGeom g;
+    g.num_kv_heads = L.params.num_kv_heads;
+    g.head_dim = L.params.head_dim;
+    g.num_pages = L.params.num_pages;
+    g.k_codes_off = L.k_codes_offset;
+    g.k_scales_off = L.k_scales_offset;
+    g.v_codes_off = L.v_codes_offset;
+    g.v_scales_off = L.v_scales_offset;
+    g.head_stride = L.head_stride;
+    g.page_stride = L.page_stride;
+    return g;
+}
+
+struct Plan {
+    int32_t splits;
+    int32_t pages_per_split;
+    int64_t ws_o_bytes;        // fp32 partial outputs
+    int64_t ws_bytes;          // total, including the (max, sum) pairs
+};
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
+              int32_t max_pages, int32_t requested, Plan *plan)
+{
+    if (batch < 0 || num_q_heads < 1 || max_pages < 1 || requested < 0)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    const int32_t hkv = L.params.num_kv_heads;
+    if (num_q_heads % hkv != 0)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (num_q_heads / hkv > FP4KV_MAX_GROUP)
+        return FP4KV_ERR_UNSUPPORTED;
+    int64_t s = requested;
+    if (s == 0) {
+        const int64_t units = static_cast<int64_t>(batch > 0 ? batch : 1) * hkv;
+        s = (kTargetWaves + units - 1) / units;
+    }
+    if (s > max_pages)
+        s = max_pages;
+    if (s < 1)
+        s = 1;
+    const int64_t pps = (max_pages + s - 1) / s;
+    s = (max_pages + pps - 1) / pps;                          // no split starts past the last page
+    plan->splits = static_cast<int32_t>(s);
+    plan->pages_per_split = static_cast<int32_t>(pps);
+    const int64_t rows = static_cast<int64_t>(batch) * num_q_heads * s;
+    plan->ws_o_bytes = round_up(rows * L.params.head_dim * 4, 256);
+    plan->ws_bytes = plan->ws_o_bytes + round_up(rows * 2 * 4, 256);
+    return FP4KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4kv_cache_layout(const fp4kv_cache_params *params, fp4kv_cache_layout_t *out)
+{
+    if (!params || !out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    return fill_layout(*params, out);
+}
+
+int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout, const void *k, const void *v,
+                          int64_t n_tokens, const int64_t *slot_mapping, void *cache, void *stream)
+{
+    int rc = check_layout(layout);
+    if (rc != FP4KV_OK)
+        return rc;
+    if (n_tokens < 0)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (n_tokens == 0)
+        return FP4KV_OK;
+    if (!k || !v || !slot_mapping || !cache)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    const int64_t per_token = static_cast<int64_t>(layout->params.num_kv_heads) * (layout->params.head_dim / 16);
+    if (n_tokens > static_cast<int64_t>(std::numeric_limits<int32_t>::max()) * 256 / per_token)
+        return FP4KV_ERR_UNSUPPORTED;                        // the launch grid would not fit
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8) || !aligned(cache, 256))
+        return FP4KV_ERR_MISALIGNED;
+    const hipError_t e = fp4kv::launch_quantize_append(
+        geom_of(*layout), static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
+        n_tokens, slot_mapping, static_cast<uint8_t *>(cache), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t num_q_heads,
+                      int32_t max_pages_per_seq, int32_t num_splits, int32_t *splits_out,
+                      int64_t *workspace_bytes_out)
+{
+    int rc = check_layout(layout);
+    if (rc != FP4KV_OK)
+        return rc;
+    if (!splits_out || !workspace_bytes_out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    Plan plan;
+    rc = make_plan(*layout, batch, num_q_heads, max_pages_per_seq, num_splits, &plan);
+    if (rc != FP4KV_OK)
+        return rc;
+    *splits_out = plan.splits;
+    *workspace_bytes_out = plan.ws_bytes;
+    return FP4KV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by fp4kv_decode_split and fp4kv_decode_attention; fills the
+// kernel arguments (out is left null).
+int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
+                  int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
+                  const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
+                  int32_t num_splits, void *workspace, int64_t workspace_bytes,
+                  fp4kv::DecodeArgs *a)
+{
+    int rc = check_layout(layout);
+    if (rc != FP4KV_OK)
+        return rc;
+    Plan plan;
+    rc = make_plan(*layout, batch, num_q_heads, max_pages_per_seq, num_splits, &plan);
+    if (rc != FP4KV_OK)
+        return rc;
+    if (!std::isfinite(softmax_scale) || softmax_scale == 0.0f)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (static_cast<int64_t>(max_pages_per_seq) * kPage > std::numeric_limits<int32_t>::max())
+        return FP4KV_ERR_UNSUPPORTED;
+    if (batch > 65535 || layout->params.num_kv_heads > 65535)
+        return FP4KV_ERR_UNSUPPORTED;                        // grid y/z limits
+    if (batch == 0)
+        return FP4KV_OK;
+    if (!cache || !q || !seq_lens || !page_table || !workspace)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(cache, 256) || !aligned(q, 16) || !aligned(seq_lens, 4) ||
+        !aligned(page_table, 4) || !aligned(workspace, 256))
+        return FP4KV_ERR_MISALIGNED;
+    if (workspace_bytes < plan.ws_bytes)
+        return FP4KV_ERR_WORKSPACE_TOO_SMALL;
+
+    a->geom = geom_of(*layout);
+    a->cache = static_cast<const uint8_t *>(cache);
+    a->q = static_cast<const uint16_t *>(q);
+    a->seq_lens = seq_lens;
+    a->page_table = page_table;
+    a->batch = batch;
+    a->num_q_heads = num_q_heads;
+    a->group = num_q_heads / layout->params.num_kv_heads;
+    a->max_pages = max_pages_per_seq;
+    a->splits = plan.splits;
+    a->pages_per_split = plan.pages_per_split;
+    a->scale_log2e = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+    a->ws_o = static_cast<float *>(workspace);
+    a->ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + plan.ws_o_bytes);
+    a->out = nullptr;
+    return FP4KV_OK;
+}
+
+int64_t partial_o_bytes(int32_t batch, int32_t num_q_heads, int32_t splits, int32_t head_dim)
+{
+    return round_up(static_cast<int64_t>(batch) * num_q_heads * splits * head_dim * 4, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
+                       int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
+                       const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
+                       int32_t num_splits, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    fp4kv::DecodeArgs a;
+    const int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table,
+                                 max_pages_per_seq, softmax_scale, num_splits, workspace,
+                                 workspace_bytes, &a);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    const hipError_t e = fp4kv::launch_decode_split(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t splits,
+                         const void *workspace, int64_t workspace_bytes, float *out, void *stream)
+{
+    if (batch < 0 || num_q_heads < 1 || splits < 1)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (head_dim != 64 && head_dim != 128)
+        return FP4KV_ERR_UNSUPPORTED;
+    if (batch == 0)
+        return FP4KV_OK;
+    if (!workspace || !out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 256) || !aligned(out, 16))
+        return FP4KV_ERR_MISALIGNED;
+    const int64_t rows = static_cast<int64_t>(batch) * num_q_heads;
+    if (rows > std::numeric_limits<int32_t>::max())
+        return FP4KV_ERR_UNSUPPORTED;
+    const int64_t o_bytes = partial_o_bytes(batch, num_q_heads, splits, head_dim);
+    if (workspace_bytes < o_bytes + round_up(rows * splits * 2 * 4, 256))
+        return FP4KV_ERR_WORKSPACE_TOO_SMALL;
+    const float *ws_o = static_cast<const float *>(workspace);
+    const float *ws_ml = reinterpret_cast<const float *>(static_cast<const uint8_t *>(workspace) + o_bytes);
+    const hipError_t e = fp4kv::launch_decode_combine(ws_o, ws_ml, rows, splits, head_dim, out,
+                                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
+                           int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
+                           const int32_t *page_table, int32_t max_pages_per_seq,
+                           float softmax_scale, int32_t num_splits, void *workspace,
+                           int64_t workspace_bytes, float *out, void *stream)
+{
+    fp4kv::DecodeArgs a;
+    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table,
+                           max_pages_per_seq, softmax_scale, num_splits, workspace,
+                           workspace_bytes, &a);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    if (!out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(out, 16))
+        return FP4KV_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = fp4kv::launch_decode_split(a, st);
+    if (e != hipSuccess)
+        return FP4KV_ERR_HIP;
+    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, static_cast<int64_t>(batch) * num_q_heads,
+                                     a.splits, layout->params.head_dim, out, st);
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+const char *fp4kv_status_string(int status)
+{
+    switch (status) {
+    case FP4KV_OK: return "ok";
+    case FP4KV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FP4KV_ERR_UNSUPPORTED: return "unsupported shape";
+    case FP4KV_ERR_MISALIGNED: return "misaligned pointer";
+    case FP4KV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FP4KV_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+    }
+}
+
+int fp4kv_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal interface between the host API (fp4kv_api.cpp) and the HIP kernels
+// (fp4kv_kernels.hip).  Not installed; the public ABI is include/fp4kv.h.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace fp4kv {
+
+// Cache geometry, copied out of a validated fp4kv_cache_layout_t.
+struct CacheGeom {
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int64_t num_pages;
+    int64_t k_codes_off, k_scales_off, v_codes_off, v_scales_off;
+    int64_t head_stride, page_stride;
+};
+
+struct DecodeArgs {
+    CacheGeom geom;
+    const uint8_t *cache;
+    const uint16_t *q;           // bf16 [batch][num_q_heads][D]
+    const int32_t *seq_lens;     // [batch]
+    const int32_t *page_table;   // [batch][max_pages]
+    int32_t batch, num_q_heads, group, max_pages;
+    int32_t splits, pages_per_split;
+    float scale_log2e;           // softmax scale times log2(e): scores kept in base 2
+    float *ws_o;                 // [batch][num_q_heads][splits][D] unnormalised outputs
+    float *ws_ml;                // [batch][num_q_heads][splits][2] running max (base 2), sum
+    float *out;                  // [batch][num_q_heads][D]
+};
+
+hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const uint16_t *v,
+                                  int64_t n_tokens, const int64_t *slots, uint8_t *cache,
+                                  hipStream_t stream);
+
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
+
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t splits,
+                                 int32_t head_dim, float *out, hipStream_t stream);
+
+}  // namespace fp4kv

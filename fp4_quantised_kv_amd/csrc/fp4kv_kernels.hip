@@ -1,0 +1,431 @@
+// HIP kernels for the FP4 KV cache on gfx950 (CDNA4, wave64).
+//
+//   quantize_append_kernel   bf16 K/V rows -> E2M1 codes + E4M3 scales at slots
+//   decode_split_valu        split-K decode attention, one wave per
+//                            (context split, KV head, sequence)
+//   decode_combine           merges the splits' (max, sum, output) partials
+//
+// Number formats ("Quantising the KV cache", numerics-explained, Code
+// section): E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with the sign in bit 3
+// of the nibble; E4M3 (OCP FN) scales, bias 7, largest finite 448, smallest
+// subnormal 2^-9.
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "fp4kv_internal.h"
+
+namespace fp4kv {
+namespace {
+
+constexpr int kPage = 64;                 // tokens per page == lanes per wave
+
+// ------------------------------------------------------------ format helpers
+
+// E4M3 code of y >= 0 (finite), rounded to nearest even, saturating at 448.
+// Subnormal range (y < 2^-6): the grid is 2^-9, so the code is rint(y * 512),
+// exact because the product is exact and rint rounds half to even; 8 carries
+// into the smallest normal, whose code is also 8.  Normal range: round the
+// f32 significand to 3 bits (add half an ulp minus one, plus the kept LSB),
+// then rebias the exponent from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_code_rne_sat(float y)
+{
+    if (y >= 448.0f)
+        return 126u;
+    if (y < 0.015625f)
+        return static_cast<uint32_t>(__builtin_rintf(y * 512.0f));
+    const uint32_t b = __float_as_uint(y);
+    const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+    return r - (120u << 3);
+}
+
+// Value of an E4M3 magnitude code (the sign bit is ignored; 0x7F decodes to
+// 480 instead of NaN so that never-written slots stay finite).
+__device__ __forceinline__ float e4m3_value(uint32_t code)
+{
+    code &= 0x7Fu;
+    return code < 8u ? static_cast<float>(code) * 0.001953125f
+                     : __uint_as_float((code + (120u << 3)) << 20);
+}
+
+// Signed E2M1 value of a nibble (bit 3 sign, bits 2-1 exponent with bias 1,
+// bit 0 mantissa).  Codes 2..7 map onto f32 by placing the 3 bits under an
+// exponent offset of 126; code 1 is the subnormal 0.5 and code 0 is zero.
+__device__ __forceinline__ float e2m1_value(uint32_t nib)
+{
+    const uint32_t c = nib & 7u;
+    uint32_t bits = (c + 252u - (c == 1u ? 1u : 0u)) << 22;
+    bits = c ? bits : 0u;
+    return __uint_as_float(bits | ((nib & 8u) << 28));
+}
+
+// Round-to-nearest-even E2M1 magnitude code of |x| / s, saturating at 6,
+// without dividing: count the rounding thresholds t*s that |x| reaches.  The
+// midpoints between consecutive magnitudes are 0.25, 0.75, 1.25, 1.75, 2.5,
+// 3.5 and 5; at an exact tie the even code wins, so a tie moves up only into
+// codes 2, 4 and 6 (comparison >=) and stays below otherwise (comparison >).
+// Every t*s is exact in fp32 (at most 7 significant bits, above 2^-11).
+struct E2M1Thresholds {
+    float t[7];
+    __device__ __forceinline__ explicit E2M1Thresholds(float s)
+    {
+        t[0] = 0.25f * s; t[1] = 0.75f * s; t[2] = 1.25f * s; t[3] = 1.75f * s;
+        t[4] = 2.5f * s;  t[5] = 3.5f * s;  t[6] = 5.0f * s;
+    }
+    __device__ __forceinline__ uint32_t code(float m) const
+    {
+        return static_cast<uint32_t>(m > t[0]) + static_cast<uint32_t>(m >= t[1]) +
+               static_cast<uint32_t>(m > t[2]) + static_cast<uint32_t>(m >= t[3]) +
+               static_cast<uint32_t>(m > t[4]) + static_cast<uint32_t>(m >= t[5]) +
+               static_cast<uint32_t>(m > t[6]);
+    }
+};
+
+// Quantise one block of 16 bf16 values held as 8 dwords (low half = even
+// channel).  Returns the 16 nibbles packed low-to-high (channel 2i in the low
+// nibble of byte i) and the scale code.
+__device__ __forceinline__ void quantize_block16(const uint32_t w[8], uint32_t &lo, uint32_t &hi,
+                                                 uint32_t &scale_code)
+{
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        amax = max(amax, w[i] & 0x7FFFu);
+        amax = max(amax, (w[i] >> 16) & 0x7FFFu);
+    }
+    // amax / 6 in correctly rounded fp32 gives the same E4M3 code as the exact
+    // quotient for every bf16 amax (checked exhaustively against the oracle).
+    const float a = __uint_as_float(amax << 16);
+    uint32_t sc = e4m3_code_rne_sat(a / 6.0f);
+    sc = sc ? sc : 1u;                                  // zero scale -> smallest subnormal
+    scale_code = sc;
+    const E2M1Thresholds th(e4m3_value(sc));
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
+        const float m = __uint_as_float((bits & 0x7FFFu) << 16);
+        const uint32_t nib = th.code(m) | ((bits >> 12) & 8u);
+        out[c >> 3] |= nib << (4 * (c & 7));
+    }
+    lo = out[0];
+    hi = out[1];
+}
+
+// -------------------------------------------------------- quantise / append
+
+// One thread per (token, KV head, 16-channel block).  Consecutive threads
+// read consecutive 32-byte blocks of the bf16 rows, so loads are coalesced.
+// K codes go to the token's row in the page; V codes are stored transposed
+// (byte (channel pair, token)), so a thread writes its 8 V bytes at a stride
+// of 64 bytes and the wave's lanes for consecutive tokens fill each 64-byte
+// row together.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_append_kernel(
+    CacheGeom g, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t n_tokens,
+    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache)
+{
+    constexpr int NB = D / 16;                          // blocks per row
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = n_tokens * g.num_kv_heads * NB;
+    if (idx >= total)
+        return;
+    const int blk = static_cast<int>(idx % NB);
+    const int64_t th = idx / NB;                        // token * H_kv + head
+    const int head = static_cast<int>(th % g.num_kv_heads);
+    const int64_t tok = th / g.num_kv_heads;
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= g.num_pages * kPage)
+        return;                                         // padding or out of range: skipped
+    const int64_t page = slot / kPage;
+    const int off = static_cast<int>(slot % kPage);
+    uint8_t *base = cache + page * g.page_stride + head * g.head_stride;
+    const int64_t src = th * D + 16 * blk;
+
+    uint32_t w[8], lo, hi, sc;
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(k + src);
+        const uint4 x0 = p[0], x1 = p[1];
+        w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+        w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+        quantize_block16(w, lo, hi, sc);
+        *reinterpret_cast<uint2 *>(base + g.k_codes_off + off * (D / 2) + 8 * blk) = make_uint2(lo, hi);
+        base[g.k_scales_off + off * NB + blk] = static_cast<uint8_t>(sc);
+    }
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(v + src);
+        const uint4 x0 = p[0], x1 = p[1];
+        w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+        w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+        quantize_block16(w, lo, hi, sc);
+        uint8_t *vc = base + g.v_codes_off + (8 * blk) * kPage + off;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t word = i < 4 ? lo : hi;
+            vc[i * kPage] = static_cast<uint8_t>(word >> (8 * (i & 3)));
+        }
+        base[g.v_scales_off + blk * kPage + off] = static_cast<uint8_t>(sc);
+    }
+}
+
+// ----------------------------------------------------------------- decode
+
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b)
+{
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ uint32_t byte_of(const uint4 (&r)[4], int i)
+{
+    const uint4 &q = r[i >> 4];
+    const int j = (i >> 2) & 3;
+    const uint32_t w = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+    return (w >> (8 * (i & 3))) & 0xFFu;
+}
+
+// Split-K decode attention on the vector ALUs, one wave per (split, KV head,
+// sequence).  For each 64-token page of the split:
+//   scores: lane = token; the lane reads its K row (D/2 code bytes and D/16
+//           scale bytes), converts the codes and dots them with the GM query
+//           rows held in LDS (the scale is applied to each 16-channel partial
+//           dot, which is the same sum regrouped);
+//   softmax: running max per query head from a wave reduction, rescale factor
+//           alpha = 2^(m_old - m_new), probabilities p = 2^(z - m_new) into LDS;
+//   values: lane = channel pair; the lane reads its transposed V row (64
+//           token bytes and the 64 scales of its channel block) and
+//           accumulates p * v for both channels of the pair.
+// The split's unnormalised output, max and sum are written to the workspace.
+template <int D, int GM>
+__global__ __launch_bounds__(64) void decode_split_valu(DecodeArgs a)
+{
+    constexpr int NB = D / 16;
+    const int lane = threadIdx.x;
+    const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int G = a.group;
+
+    __shared__ float q_s[GM][D];
+    __shared__ float p_s[GM][kPage];
+
+    for (int i = lane; i < GM * D; i += 64) {
+        const int gq = i / D, c = i % D;
+        q_s[gq][c] = gq < G ? bf16_to_float(a.q[(static_cast<int64_t>(b) * a.num_q_heads + h * G + gq) * D + c])
+                            : 0.0f;
+    }
+    __syncthreads();
+
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
+    const int n_pages = (len + kPage - 1) / kPage;
+    const int p0 = sp * a.pages_per_split;
+    const int p1 = min(p0 + a.pages_per_split, n_pages);
+
+    float m[GM], l[GM], o0[GM], o1[GM];
+#pragma unroll
+    for (int gq = 0; gq < GM; ++gq) {
+        m[gq] = -INFINITY; l[gq] = 0.0f; o0[gq] = 0.0f; o1[gq] = 0.0f;
+    }
+
+    const CacheGeom &g = a.geom;
+    for (int pg = p0; pg < p1; ++pg) {
+        const int pid = a.page_table[static_cast<int64_t>(b) * a.max_pages + pg];
+        if (pid < 0 || pid >= g.num_pages)
+            continue;                                   // not a page of this pool: skipped
+        const uint8_t *blk = a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
+        const int valid = min(kPage, len - pg * kPage);
+
+        // ---- scores, lane = token
+        float z[GM];
+#pragma unroll
+        for (int gq = 0; gq < GM; ++gq)
+            z[gq] = 0.0f;
+        {
+            const uint8_t *krow = blk + g.k_codes_off + lane * (D / 2);
+            const uint8_t *ksc = blk + g.k_scales_off + lane * NB;
+            uint32_t cw[D / 8];
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const uint4 x = reinterpret_cast<const uint4 *>(krow)[i];
+                cw[4 * i] = x.x; cw[4 * i + 1] = x.y; cw[4 * i + 2] = x.z; cw[4 * i + 3] = x.w;
+            }
+            uint32_t sw[NB / 4];
+#pragma unroll
+            for (int i = 0; i < NB / 4; ++i)
+                sw[i] = reinterpret_cast<const uint32_t *>(ksc)[i];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float s = e4m3_value((sw[nb >> 2] >> (8 * (nb & 3))) & 0xFFu);
+                float part[GM];
+#pragma unroll
+                for (int gq = 0; gq < GM; ++gq)
+                    part[gq] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const uint32_t word = cw[2 * nb + (c >> 3)];
+                    const float kv = e2m1_value(word >> (4 * (c & 7)));
+#pragma unroll
+                    for (int gq = 0; gq < GM; ++gq)
+                        part[gq] = fmaf(q_s[gq][16 * nb + c], kv, part[gq]);
+                }
+#pragma unroll
+                for (int gq = 0; gq < GM; ++gq)
+                    z[gq] = fmaf(s, part[gq], z[gq]);
+            }
+        }
+        const bool live = lane < valid;
+
+        // ---- online softmax (base 2)
+#pragma unroll
+        for (int gq = 0; gq < GM; ++gq) {
+            const float zz = live ? z[gq] * a.scale_log2e : -INFINITY;
+            const float mx = wave_max(zz);               // finite: lane 0 is live
+            const float mn = fmaxf(m[gq], mx);
+            const float alpha = exp2f(m[gq] - mn);       // 0 on the first page
+            const float p = live ? exp2f(zz - mn) : 0.0f;
+            l[gq] = fmaf(l[gq], alpha, p);
+            o0[gq] *= alpha;
+            o1[gq] *= alpha;
+            m[gq] = mn;
+            p_s[gq][lane] = p;
+        }
+        __syncthreads();
+
+        // ---- values, lane = channel pair (D/2 lanes)
+        if (lane < D / 2) {
+            uint4 vc[4], vs[4];
+            const uint4 *vrow = reinterpret_cast<const uint4 *>(blk + g.v_codes_off + lane * kPage);
+            const uint4 *vsrow = reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (lane >> 3) * kPage);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vc[i] = vrow[i];
+                vs[i] = vsrow[i];
+            }
+#pragma unroll
+            for (int t = 0; t < kPage; ++t) {
+                const uint32_t byte = byte_of(vc, t);
+                const float s = e4m3_value(byte_of(vs, t));
+                const float ve = e2m1_value(byte) * s;
+                const float vo = e2m1_value(byte >> 4) * s;
+#pragma unroll
+                for (int gq = 0; gq < GM; ++gq) {
+                    const float p = p_s[gq][t];
+                    o0[gq] = fmaf(p, ve, o0[gq]);
+                    o1[gq] = fmaf(p, vo, o1[gq]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- write the split's partial results
+#pragma unroll
+    for (int gq = 0; gq < GM; ++gq) {
+        const float lt = wave_sum(l[gq]);
+        if (gq >= G)
+            continue;
+        const int64_t row = (static_cast<int64_t>(b) * a.num_q_heads + h * G + gq) * a.splits + sp;
+        if (lane == 0) {
+            a.ws_ml[2 * row] = m[gq];
+            a.ws_ml[2 * row + 1] = lt;
+        }
+        if (lane < D / 2)
+            *reinterpret_cast<float2 *>(a.ws_o + row * D + 2 * lane) = make_float2(o0[gq], o1[gq]);
+    }
+}
+
+// Merge the splits of one (sequence, query head): M = max_j m_j,
+// L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L.  Splits with no
+// tokens carry m = -inf and l = 0 and are skipped; a row with no tokens at
+// all is written as zeros.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine(const float *__restrict__ ws_o,
+                                                    const float *__restrict__ ws_ml, int splits,
+                                                    float *__restrict__ out)
+{
+    const int64_t row = blockIdx.x;
+    const int c = threadIdx.x;
+    const float *ml = ws_ml + row * splits * 2;
+    float M = -INFINITY;
+    for (int j = 0; j < splits; ++j)
+        M = fmaxf(M, ml[2 * j]);
+    float L = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+        for (int j = 0; j < splits; ++j) {
+            const float mj = ml[2 * j];
+            if (mj == -INFINITY)
+                continue;
+            const float w = exp2f(mj - M);
+            L = fmaf(ml[2 * j + 1], w, L);
+            O = fmaf(ws_o[(row * splits + j) * D + c], w, O);
+        }
+    }
+    out[row * D + c] = L > 0.0f ? O / L : 0.0f;
+}
+
+template <int D, int GM>
+hipError_t launch_split_t(const DecodeArgs &a, hipStream_t stream)
+{
+    const dim3 grid(a.splits, a.geom.num_kv_heads, a.batch);
+    decode_split_valu<D, GM><<<grid, 64, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_d(const DecodeArgs &a, hipStream_t stream)
+{
+    if (a.group <= 1) return launch_split_t<D, 1>(a, stream);
+    if (a.group <= 2) return launch_split_t<D, 2>(a, stream);
+    if (a.group <= 4) return launch_split_t<D, 4>(a, stream);
+    if (a.group <= 8) return launch_split_t<D, 8>(a, stream);
+    return launch_split_t<D, 16>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const uint16_t *v,
+                                  int64_t n_tokens, const int64_t *slots, uint8_t *cache,
+                                  hipStream_t stream)
+{
+    const int64_t total = n_tokens * g.num_kv_heads * (g.head_dim / 16);
+    const int64_t blocks = (total + 255) / 256;
+    if (g.head_dim == 64)
+        quantize_append_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(
+            g, k, v, n_tokens, slots, cache);
+    else
+        quantize_append_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(
+            g, k, v, n_tokens, slots, cache);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
+{
+    return a.geom.head_dim == 64 ? launch_split_d<64>(a, stream) : launch_split_d<128>(a, stream);
+}
+
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t splits,
+                                 int32_t head_dim, float *out, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(rows));
+    if (head_dim == 64)
+        decode_combine<64><<<grid, 64, 0, stream>>>(ws_o, ws_ml, splits, out);
+    else
+        decode_combine<128><<<grid, 128, 0, stream>>>(ws_o, ws_ml, splits, out);
+    return hipGetLastError();
+}
+
+}  // namespace fp4kv

@@ -1,0 +1,122 @@
+"""GPU-side set-up shared by the tests, the smoke check and the benchmark.
+
+Builds a quantised cache for a workload of fp4kv_workloads (generating the
+bf16 K/V rows on the CPU in seeded chunks, copying them to the device and
+appending them with the library), and reads cache pages back in token-major
+order for comparison with the oracle.  Only the library's entry points touch
+the data on the device.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+import fp4_quantised_kv_amd as fk
+import fp4kv_workloads as wl
+
+APPEND_CHUNK = 16384            # tokens per quantize_append call while filling a cache
+
+
+@dataclass
+class GpuCache:
+    workload: wl.Workload
+    layout: fk.CacheLayout
+    cache: torch.Tensor                   # uint8 [cache_bytes] on the device
+    page_table: torch.Tensor              # int32 [B][max_pages] on the device
+    seq_lens: torch.Tensor                # int32 [B] on the device
+    pt_cpu: wl.PageTable
+    lens_cpu: torch.Tensor                # int64 [B]
+    kept: Dict[int, tuple] = field(default_factory=dict)   # seq -> (k, v) bf16 CPU rows
+
+
+def _append_rows(layout, cache, k, v, slots, device):
+    kd = k.to(device, non_blocking=False)
+    vd = v.to(device, non_blocking=False)
+    sd = slots.to(device)
+    fk.quantize_append(layout, kd, vd, sd, cache)
+
+
+def build_cache(w: wl.Workload, seed: int, device="cuda", keep_seqs=(), extra_tokens=0,
+                seqs: Optional[List[int]] = None, zero=True) -> GpuCache:
+    """Quantise every sequence's context into a fresh cache.
+
+    Contiguous workloads get an identity page table; the paged workload gets
+    seeded lengths and a seeded random page table with room for
+    `extra_tokens` more tokens per sequence.  `seqs` limits which sequences
+    are filled (others stay zero); `keep_seqs` keeps their bf16 rows on the
+    CPU for the oracle."""
+    lens = wl.seq_lengths(w, seed)
+    if w.kind == "paged":
+        pt = wl.random_page_table(lens, extra_tokens, seed, w.name)
+    else:
+        pt = wl.identity_page_table(w.batch, int(lens.max()) + extra_tokens)
+    layout = fk.cache_layout(w.kv_heads, w.head_dim, pt.num_pages)
+    cache = (torch.zeros if zero else torch.empty)(layout.cache_bytes, dtype=torch.uint8, device=device)
+    fk_k = wl.channel_factors(w, seed, "k")
+    fk_v = wl.channel_factors(w, seed, "v")
+    kept = {}
+    for b in (range(w.batch) if seqs is None else seqs):
+        L = int(lens[b])
+        ks, vs = [], []
+        for t0 in range(0, L, APPEND_CHUNK):
+            t1 = min(L, t0 + APPEND_CHUNK)
+            k = wl.kv_tokens(w, seed, b, "k", t0, t1, fk_k)
+            v = wl.kv_tokens(w, seed, b, "v", t0, t1, fk_v)
+            _append_rows(layout, cache, k, v, wl.slots_for(pt.table, b, t0, t1), device)
+            if b in keep_seqs:
+                ks.append(k)
+                vs.append(v)
+        if b in keep_seqs:
+            kept[b] = (torch.cat(ks) if ks else torch.empty(0, w.kv_heads, w.head_dim, dtype=torch.bfloat16),
+                       torch.cat(vs) if vs else torch.empty(0, w.kv_heads, w.head_dim, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    return GpuCache(w, layout, cache, pt.table.to(device), lens.to(torch.int32).to(device),
+                    pt, lens, kept)
+
+
+def read_page(cache_cpu: np.ndarray, layout: fk.CacheLayout, page: int, head: int):
+    """Token-major view of one (page, KV head) block:
+    K code bytes [64][D/2], K scales [64][D/16], V code bytes [64][D/2],
+    V scales [64][D/16] (the V planes are stored transposed and are turned
+    back here)."""
+    D = layout.head_dim
+    base = page * layout.page_stride + head * layout.head_stride
+    blk = cache_cpu[base:base + layout.block_bytes]
+    kc = blk[layout.k_codes_offset:layout.k_codes_offset + 64 * D // 2].reshape(64, D // 2)
+    ks = blk[layout.k_scales_offset:layout.k_scales_offset + 64 * D // 16].reshape(64, D // 16)
+    vc = blk[layout.v_codes_offset:layout.v_codes_offset + 64 * D // 2].reshape(D // 2, 64).T
+    vs = blk[layout.v_scales_offset:layout.v_scales_offset + 64 * D // 16].reshape(D // 16, 64).T
+    return kc, ks, vc, vs
+
+
+def read_pages(cache: torch.Tensor, layout: fk.CacheLayout, pages, n_tokens: int):
+    """Stored bytes of the first n_tokens slots of a list of pages (all KV
+    heads), token-major: K code bytes [n][H][D/2], K scales [n][H][D/16], V
+    code bytes [n][H][D/2], V scales [n][H][D/16].  Only those pages are
+    copied off the device."""
+    H, D = layout.num_kv_heads, layout.head_dim
+    idx = torch.as_tensor(np.asarray(pages, np.int64), device=cache.device)
+    blocks = cache[: layout.cache_bytes].view(-1, H, layout.block_bytes)[idx].cpu().numpy()
+    P = len(pages)
+
+    def plane(off, rows, cols, transposed):
+        x = blocks[:, :, off:off + rows * cols]
+        if transposed:                       # stored [cols][64 tokens]
+            x = x.reshape(P, H, cols, rows).transpose(0, 3, 1, 2)
+        else:                                # stored [64 tokens][cols]
+            x = x.reshape(P, H, rows, cols).transpose(0, 2, 1, 3)
+        return np.ascontiguousarray(x.reshape(P * rows, H, cols)[:n_tokens])
+
+    return (plane(layout.k_codes_offset, 64, D // 2, False),
+            plane(layout.k_scales_offset, 64, D // 16, False),
+            plane(layout.v_codes_offset, 64, D // 2, True),
+            plane(layout.v_scales_offset, 64, D // 16, True))
+
+
+def row_rel_error(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per output row (last axis): max |out - ref| / max |ref| (0 where both
+    rows are zero)."""
+    num = np.max(np.abs(out.astype(np.float64) - ref), axis=-1)
+    den = np.max(np.abs(ref), axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)

@@ -1,0 +1,220 @@
+/*
+ * fp4kv.h -- C ABI of the FP4 KV-cache library for AMD MI355X (gfx950).
+ *
+ * The cache stores every past token's keys and values with FP4 E2M1
+ * elements and one FP8 E4M3 (OCP "FN") scale per 16 consecutive channels of
+ * a token's row: 4 + 8/16 = 4.5 bits per number, 28.125% of an FP16 cache.
+ * ("Quantising the KV cache", numerics-explained: Concept section, paragraph
+ * on FP4 with a fine-grained scale; Maths section for the cost; Code section
+ * for the block quantiser.)
+ *
+ * Calls:
+ *   fp4kv_cache_layout      sizes and lays out a paged cache (host only).
+ *   fp4kv_quantize_append   quantises new tokens' K and V rows into the cache.
+ *   fp4kv_decode_plan       chooses the split count and workspace size.
+ *   fp4kv_decode_attention  split-K decode attention over the packed cache,
+ *                           dequantising on the fly.
+ *   fp4kv_decode_split,     its two halves: per-split partial results, and
+ *   fp4kv_decode_combine    their merge.
+ *   fp4kv_status_string     text of a status code.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are HIP device memory; all others are host.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no
+ *     pointer after returning and holds no mutable global state, so calls
+ *     are re-entrant.  Calls on one stream run in order; calls that write the
+ *     same cache bytes from different streams race.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream) and the call returns without waiting.  Results are valid once
+ *     the stream reaches them.
+ *   - Every host-visible argument is checked before any HIP call; a failed
+ *     check returns a negative status and touches nothing.  Contents of
+ *     device arrays (slots, lengths, page ids) are not visible to the host:
+ *     the kernels skip out-of-range entries instead of faulting, as stated
+ *     per call.  Inputs must be finite; non-finite K, V or Q give
+ *     unspecified results.
+ */
+#ifndef FP4KV_H
+#define FP4KV_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FP4KV_API __attribute__((visibility("default")))
+#else
+#define FP4KV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every call returns FP4KV_OK or one of the negative codes. */
+enum fp4kv_status {
+    FP4KV_OK = 0,
+    FP4KV_ERR_INVALID_ARGUMENT = -1,      /* null pointer, negative or inconsistent size */
+    FP4KV_ERR_UNSUPPORTED = -2,           /* a valid shape this version does not implement */
+    FP4KV_ERR_MISALIGNED = -3,            /* a pointer breaks the stated alignment */
+    FP4KV_ERR_WORKSPACE_TOO_SMALL = -4,   /* workspace_bytes below fp4kv_decode_plan's figure */
+    FP4KV_ERR_HIP = -5                    /* the HIP runtime reported a launch failure */
+};
+
+#define FP4KV_PAGE_SIZE 64                /* tokens per page (the only size in this version) */
+#define FP4KV_MAX_GROUP 16                /* query heads per KV head supported */
+
+/* Shape of one layer's cache.  ("Quantising the KV cache", Maths section:
+ * a token holds 2 x KV heads x head dim numbers per layer; a model keeps one
+ * cache per layer, e.g. one buffer per layer or offsets into one buffer.) */
+typedef struct fp4kv_cache_params {
+    int32_t num_kv_heads;                 /* H_kv >= 1 */
+    int32_t head_dim;                     /* D: 64 or 128 */
+    int32_t page_size;                    /* tokens per page: FP4KV_PAGE_SIZE */
+    int32_t reserved;                     /* must be 0 */
+    int64_t num_pages;                    /* pages in the pool, >= 1 */
+} fp4kv_cache_params;
+
+/* Byte layout of the cache, filled by fp4kv_cache_layout.  Plain data: it
+ * may be copied, stored or sent elsewhere with the cache bytes.
+ *
+ * The cache is num_pages pages; a page holds one block per KV head; a block
+ * (page p, KV head h) starts at p*page_stride + h*head_stride and holds the
+ * page's 64 token slots:
+ *   K codes   [64 tokens][D/2] bytes  at k_codes_offset  (token-major rows)
+ *   K scales  [64 tokens][D/16]       at k_scales_offset
+ *   V codes   [D/2][64 tokens] bytes  at v_codes_offset  (channel-pair-major)
+ *   V scales  [D/16][64 tokens]       at v_scales_offset
+ * A code byte holds two E2M1 codes of one token: channel 2i in the low nibble
+ * and channel 2i+1 in the high nibble; a nibble is sign << 3 | magnitude code
+ * (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  A scale byte is an E4M3 code
+ * (never 0: a zero scale is stored as the smallest subnormal 2^-9).  Token
+ * slot s lives in page s / 64 at offset s % 64.  V is stored transposed in
+ * the page so decode reads each channel pair's tokens contiguously. */
+typedef struct fp4kv_cache_layout_t {
+    fp4kv_cache_params params;
+    int64_t block_bytes;                  /* 64 * D * 9 / 8 */
+    int64_t k_codes_offset;               /* offsets inside a block */
+    int64_t k_scales_offset;
+    int64_t v_codes_offset;
+    int64_t v_scales_offset;
+    int64_t head_stride;                  /* = block_bytes */
+    int64_t page_stride;                  /* = num_kv_heads * block_bytes */
+    int64_t cache_bytes;                  /* = num_pages * page_stride: exactly 9/16 B per number */
+    int64_t bytes_per_token;              /* = 2 * H_kv * D * 9 / 16 */
+} fp4kv_cache_layout_t;
+
+/* Fill *out from *params.  Host only, no HIP call, pure.
+ * Errors: INVALID_ARGUMENT for a null pointer, H_kv < 1, num_pages < 1,
+ * reserved != 0 or a cache size that overflows int64; UNSUPPORTED for
+ * head_dim not in {64, 128} or page_size != 64. */
+FP4KV_API int fp4kv_cache_layout(const fp4kv_cache_params *params, fp4kv_cache_layout_t *out);
+
+/* Quantise n_tokens tokens' K and V rows and store them at their slots.
+ * ("Quantising the KV cache", Code section: each row is cut into blocks of
+ * 16 channels; scale = E4M3 round-to-nearest-even of amax/6, saturating at
+ * 448, with 0 replaced by 2^-9; element code = E2M1 round-to-nearest-even of
+ * x/scale, saturating at 6, sign kept, also for a zero magnitude.  The
+ * quantised K and V are what attention later reads, in place of the real
+ * ones.)  A block never spans tokens, so appending never rewrites older
+ * tokens and the bytes of a token do not depend on the order of calls.
+ *   layout        host, from fp4kv_cache_layout (re-checked).
+ *   k, v          device bf16 [n_tokens][H_kv][D], contiguous, 16-B aligned.
+ *   n_tokens      >= 0; 0 is a no-op (pointers may then be NULL).
+ *   slot_mapping  device int64 [n_tokens], 8-B aligned: slot of token t
+ *                 (page * 64 + offset).  Negative slots and slots at or past
+ *                 num_pages * 64 are skipped.  Two tokens with one slot race.
+ *   cache         device, layout->cache_bytes, 256-B aligned.
+ *   stream        hipStream_t or NULL.
+ * Errors: INVALID_ARGUMENT (null pointer with n_tokens > 0, n_tokens < 0,
+ * layout not produced by fp4kv_cache_layout), MISALIGNED, HIP. */
+FP4KV_API int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout,
+                          const void *k, const void *v, int64_t n_tokens,
+                          const int64_t *slot_mapping, void *cache, void *stream);
+
+/* Split count and workspace bytes for fp4kv_decode_attention.  Host only.
+ * num_splits > 0 asks for that many context chunks (clamped to
+ * max_pages_per_seq, then trimmed so that no chunk is empty for a sequence
+ * of max_pages_per_seq pages); 0 lets the library choose enough chunks to
+ * fill the GPU.  *splits_out gets the count that fp4kv_decode_attention will
+ * use for the same arguments, *workspace_bytes_out the workspace it needs.
+ * Errors: INVALID_ARGUMENT (null pointer, batch < 0, num_q_heads < 1,
+ * max_pages_per_seq < 1, num_splits < 0, num_q_heads not a multiple of
+ * H_kv), UNSUPPORTED (more than FP4KV_MAX_GROUP query heads per KV head). */
+FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t num_q_heads,
+                      int32_t max_pages_per_seq, int32_t num_splits,
+                      int32_t *splits_out, int64_t *workspace_bytes_out);
+
+/* One decode step of attention for `batch` sequences, one query token each,
+ * over the packed cache.  ("Quantising the KV cache", Concept and Code
+ * sections: every new token reads all cached keys and values; Q is not
+ * quantised.  "KV Cache Quantisation", klaylearn, Notes and Common questions:
+ * decode reads the cache, so the scales are applied and the codes converted
+ * inside the attention kernel, not in a separate pass.)
+ * For sequence b and query head h, with G = num_q_heads / H_kv and KV head
+ * h / G, over its tokens t < seq_lens[b]:
+ *   out[b][h] = sum_t softmax_t(softmax_scale * q[b][h] . K^[t]) * V^[t]
+ * where K^, V^ are the stored E2M1 values times their scales.  The context
+ * is cut into splits; each split keeps a running max and sum (online
+ * softmax) and a second kernel merges the splits.  Accumulation is fp32.
+ *   layout, cache      as above (device cache, 256-B aligned).
+ *   q                  device bf16 [batch][num_q_heads][D], 16-B aligned.
+ *   batch              >= 0; 0 is a no-op.
+ *   seq_lens           device int32 [batch], 4-B aligned; lengths are
+ *                      clamped to [0, max_pages_per_seq * 64]; 0 gives a
+ *                      zero output row.
+ *   page_table         device int32 [batch][max_pages_per_seq]: page id of
+ *                      each sequence's i-th 64-token page.  Ids outside
+ *                      [0, num_pages) are skipped (their tokens are not
+ *                      attended).
+ *   softmax_scale      finite and non-zero (usually 1/sqrt(D)).
+ *   num_splits         as for fp4kv_decode_plan.
+ *   workspace          device, 256-B aligned, workspace_bytes >= the plan's.
+ *   out                device fp32 [batch][num_q_heads][D], 16-B aligned.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, MISALIGNED, WORKSPACE_TOO_SMALL,
+ * HIP.  Equivalent to fp4kv_decode_split followed by fp4kv_decode_combine
+ * on the same stream. */
+FP4KV_API int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache,
+                           const void *q, int32_t batch, int32_t num_q_heads,
+                           const int32_t *seq_lens, const int32_t *page_table,
+                           int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
+                           void *workspace, int64_t workspace_bytes, float *out, void *stream);
+
+/* The two halves of fp4kv_decode_attention, for callers that time them or
+ * merge partial results from several places (for example context chunks
+ * attended on different devices, concatenated along the split axis).
+ *
+ * fp4kv_decode_split takes the arguments of fp4kv_decode_attention except
+ * `out` and writes each split's unnormalised partial result to the
+ * workspace, laid out as
+ *   o   fp32 [batch][num_q_heads][S][D]      at byte 0
+ *   ml  fp32 [batch][num_q_heads][S][2]      at byte round_up(batch*num_q_heads*S*D*4, 256)
+ * where S is the plan's split count, o = sum_t 2^(z_t - m) v_t over the
+ * split's tokens, m = max_t z_t with z_t = log2(e) * softmax_scale * q.k_t,
+ * and l = sum_t 2^(z_t - m).  A split without tokens has m = -inf, l = 0,
+ * o = 0.
+ *
+ * fp4kv_decode_combine merges S such partials per (sequence, query head):
+ *   out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M),  M = max_j m_j,
+ * and writes zeros where every split is empty.  `splits` must be the S of
+ * the partials; workspace_bytes must cover the layout above.
+ * Errors: as for fp4kv_decode_attention (combine: INVALID_ARGUMENT for
+ * batch < 0, num_q_heads < 1 or splits < 1; UNSUPPORTED for head_dim not in
+ * {64, 128}). */
+FP4KV_API int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
+                       int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
+                       const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
+                       int32_t num_splits, void *workspace, int64_t workspace_bytes, void *stream);
+
+FP4KV_API int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t splits,
+                         const void *workspace, int64_t workspace_bytes, float *out, void *stream);
+
+/* Static text for a status code (never NULL). */
+FP4KV_API const char *fp4kv_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+FP4KV_API int fp4kv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4KV_H */

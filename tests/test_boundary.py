@@ -1,0 +1,145 @@
+"""The C ABI on the CPU: the library loads, exports what include/fp4kv.h
+declares, and every host-side check fires before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_quantised_kv_amd as fk
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4kv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FP4KV_API\s+[\w\s\*]*?\b(fp4kv_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"fp4kv_cache_layout", "fp4kv_quantize_append", "fp4kv_decode_attention"} <= set(names)
+    lib = fk.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert fk.library().fp4kv_version() >= 100
+    for code in (0, -1, -2, -3, -4, -5):
+        assert fk.status_string(code) not in ("", "unknown status")
+    assert fk.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("H,D,pages", [(1, 64, 4), (8, 128, 512), (8, 128, 1), (3, 64, 1000)])
+def test_layout_sizes(H, D, pages):
+    L = fk.cache_layout(H, D, pages)
+    assert L.block_bytes == 64 * D * 9 // 8
+    assert L.cache_bytes == pages * H * L.block_bytes
+    # 4.5 bits per number, exactly: the cost the oracle's cost model gives
+    assert L.cache_bytes == oracle.fp4_cache_bytes(pages * 64, 1, H, D)
+    assert L.bytes_per_token * 64 * pages == L.cache_bytes
+    offs = [L.k_codes_offset, L.k_scales_offset, L.v_codes_offset, L.v_scales_offset]
+    sizes = [64 * D // 2, 64 * D // 16, 64 * D // 2, 64 * D // 16]
+    assert offs == [0, sizes[0], sizes[0] + sizes[1], sizes[0] + sizes[1] + sizes[2]]
+    assert all(o % 16 == 0 for o in offs) and L.block_bytes % 256 == 0
+    assert L.page_stride == H * L.block_bytes and L.head_stride == L.block_bytes
+
+
+@pytest.mark.parametrize("H,D,P,pages,reserved,code", [
+    (0, 128, 64, 1, 0, fk.ERR_INVALID_ARGUMENT), (8, 128, 64, 0, 0, fk.ERR_INVALID_ARGUMENT),
+    (8, 128, 64, 1, 1, fk.ERR_INVALID_ARGUMENT), (8, 96, 64, 1, 0, fk.ERR_UNSUPPORTED),
+    (8, 100, 64, 1, 0, fk.ERR_UNSUPPORTED), (8, 256, 64, 1, 0, fk.ERR_UNSUPPORTED),
+    (8, 128, 32, 1, 0, fk.ERR_UNSUPPORTED), (8, 128, 64, 1 << 60, 0, fk.ERR_INVALID_ARGUMENT)])
+def test_layout_rejects(H, D, P, pages, reserved, code):
+    p = fk.CacheParams(H, D, P, reserved, pages)
+    out = fk.CacheLayout()
+    assert fk.library().fp4kv_cache_layout(ctypes.byref(p), ctypes.byref(out)) == code
+    assert fk.library().fp4kv_cache_layout(None, ctypes.byref(out)) == fk.ERR_INVALID_ARGUMENT
+
+
+def test_plan():
+    L = fk.cache_layout(8, 128, 32 * 512)
+    assert fk.decode_plan(L, 32, 64, 512, 64)[0] == 64
+    assert fk.decode_plan(L, 32, 64, 512, 64)[1] == 32 * 64 * 64 * 128 * 4 + 32 * 64 * 64 * 8
+    assert fk.decode_plan(L, 1, 32, 8192, 256)[0] == 256
+    assert fk.decode_plan(L, 1, 32, 3, 256)[0] == 3                 # never more splits than pages
+    assert fk.decode_plan(L, 1, 32, 10, 4)[0] == 4                  # 3 pages per split: 4 splits
+    assert fk.decode_plan(L, 1, 32, 9, 4)[0] == 3                   # 3 pages per split: 3 splits
+    s, ws = fk.decode_plan(L, 64, 32, 258, 0)
+    assert 1 <= s <= 258 and ws > 0
+    for args, code in [((32, 65, 512, 64), fk.ERR_INVALID_ARGUMENT),      # Hq % Hkv
+                       ((32, 8 * 17, 512, 64), fk.ERR_UNSUPPORTED),       # group 17
+                       ((-1, 64, 512, 64), fk.ERR_INVALID_ARGUMENT),
+                       ((1, 64, 0, 64), fk.ERR_INVALID_ARGUMENT),
+                       ((1, 64, 8, -1), fk.ERR_INVALID_ARGUMENT)]:
+        with pytest.raises(fk.Fp4KVError) as e:
+            fk.decode_plan(L, *args)
+        assert e.value.status == code
+
+
+def _lib():
+    return fk.library()
+
+
+def test_quantize_append_host_checks():
+    L = fk.cache_layout(8, 128, 4)
+    lib = _lib()
+    ok = 0x10000                                        # aligned fake device addresses: never
+    assert lib.fp4kv_quantize_append(ctypes.byref(L), ok, ok, 0, ok, ok, None) == fk.OK
+    assert lib.fp4kv_quantize_append(ctypes.byref(L), ok, ok, -1, ok, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_quantize_append(ctypes.byref(L), None, ok, 5, ok, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_quantize_append(ctypes.byref(L), ok, ok, 5, None, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_quantize_append(ctypes.byref(L), ok + 8, ok, 5, ok, ok, None) == fk.ERR_MISALIGNED
+    assert lib.fp4kv_quantize_append(ctypes.byref(L), ok, ok, 5, ok + 4, ok, None) == fk.ERR_MISALIGNED
+    assert lib.fp4kv_quantize_append(ctypes.byref(L), ok, ok, 5, ok, ok + 16, None) == fk.ERR_MISALIGNED
+    assert lib.fp4kv_quantize_append(None, ok, ok, 5, ok, ok, None) == fk.ERR_INVALID_ARGUMENT
+    bad = fk.CacheLayout.from_buffer_copy(L)
+    bad.cache_bytes += 1                                # not what fp4kv_cache_layout produced
+    assert lib.fp4kv_quantize_append(ctypes.byref(bad), ok, ok, 5, ok, ok, None) == fk.ERR_INVALID_ARGUMENT
+
+
+def test_decode_host_checks():
+    L = fk.cache_layout(8, 128, 64)
+    lib = _lib()
+    ok = 0x10000
+    s, ws = fk.decode_plan(L, 2, 32, 8, 0)
+
+    def call(**kw):
+        a = dict(cache=ok, q=ok, batch=2, hq=32, lens=ok, pt=ok, maxp=8, scale=0.1, splits=0,
+                 ws=ok, wsb=ws, out=ok)
+        a.update(kw)
+        return lib.fp4kv_decode_attention(ctypes.byref(L), a["cache"], a["q"], a["batch"], a["hq"],
+                                          a["lens"], a["pt"], a["maxp"], a["scale"], a["splits"],
+                                          a["ws"], a["wsb"], a["out"], None)
+
+    assert call(batch=0) == fk.OK
+    assert call(cache=None) == fk.ERR_INVALID_ARGUMENT
+    assert call(out=None) == fk.ERR_INVALID_ARGUMENT
+    assert call(hq=33) == fk.ERR_INVALID_ARGUMENT
+    assert call(hq=8 * 32) == fk.ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == fk.ERR_INVALID_ARGUMENT
+    assert call(scale=0.0) == fk.ERR_INVALID_ARGUMENT
+    assert call(q=ok + 2) == fk.ERR_MISALIGNED
+    assert call(ws=ok + 64) == fk.ERR_MISALIGNED
+    assert call(cache=ok + 128) == fk.ERR_MISALIGNED
+    assert call(out=ok + 4) == fk.ERR_MISALIGNED
+    assert call(wsb=ws - 1) == fk.ERR_WORKSPACE_TOO_SMALL
+    assert call(batch=70000) == fk.ERR_UNSUPPORTED
+    assert lib.fp4kv_decode_combine(2, 32, 128, 0, ok, ws, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_decode_combine(2, 32, 96, 4, ok, ws, ok, None) == fk.ERR_UNSUPPORTED
+    assert lib.fp4kv_decode_combine(2, 32, 128, s, ok, ws - 1, ok, None) == fk.ERR_WORKSPACE_TOO_SMALL
+    assert lib.fp4kv_decode_combine(0, 32, 128, s, None, 0, None, None) == fk.OK
+    assert lib.fp4kv_decode_split(ctypes.byref(L), ok, ok, 2, 32, ok, ok, 8, 0.1, 0, ok, ws - 1,
+                                  None) == fk.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    L = fk.cache_layout(1, 64, 1)
+    k = torch.zeros(1, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fk.quantize_append(L, k, k, torch.zeros(1, dtype=torch.int64),
+                           torch.zeros(L.cache_bytes, dtype=torch.uint8))
