@@ -100,6 +100,10 @@ def main():
     ap.add_argument("--splits", type=int, default=None, help="context splits (default: the workload's)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="also time a plain 2 GiB streaming read (torch sum) as the achievable-bandwidth reference")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="finish with one 1 GiB device copy, the known-size kernel for scaling HBM counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -135,7 +139,7 @@ def main():
     L = gc.layout
     B, Hq, D = w.batch, w.q_heads, w.head_dim
     max_pages = gc.page_table.shape[1]
-    splits, ws_bytes = fk.decode_plan(L, B, Hq, max_pages, splits_req)
+    splits, partials, ws_bytes = fk.decode_plan(L, B, Hq, max_pages, splits_req)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     lens0 = gc.lens_cpu.clone()
@@ -166,7 +170,7 @@ def main():
         fk.decode_split(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
                         softmax_scale=scale, num_splits=splits_req, workspace=ws)
         e[2].record(stream)
-        fk.decode_combine(ws, B, Hq, D, splits, out=out)
+        fk.decode_combine(ws, B, Hq, D, partials, out=out)
         e[3].record(stream)
 
     for s in range(args.warmup):
@@ -220,7 +224,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": w.kv_heads,
                    "head_dim": D, "context": w.context if not paged else f"{w.min_len}..{w.max_len}",
-                   "splits": splits, "page_size": 64, "cache_bytes": L.cache_bytes},
+                   "splits": splits, "partials": partials, "page_size": 64,
+                   "cache_bytes": L.cache_bytes},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
@@ -230,6 +235,27 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes)},
     }
+    if args.hbm_probe:
+        x = torch.ones(1 << 29, dtype=torch.float32, device=dev)     # 2 GiB
+        for _ in range(3):
+            x.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            x.sum()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        result["hbm_read_probe"] = {"kernel": "torch sum of 2 GiB fp32", "bytes": x.numel() * 4,
+                                    "gbs": round(x.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
+        del x
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = src.numel()
+        del src, dst
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         result["cpu_baseline"] = cpu_baseline(w, args.seed, threads)

@@ -15,7 +15,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "library", "cache_layout", "decode_plan",
+__all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
            "quantize_append", "decode_attention", "decode_split", "decode_combine",
            "status_string", "PAGE_SIZE", "MAX_GROUP"]
 
@@ -82,7 +82,7 @@ def library():
                                             _P, _P, _P]
         L.fp4kv_quantize_append.restype = ctypes.c_int
         L.fp4kv_decode_plan.argtypes = [ctypes.POINTER(CacheLayout), ctypes.c_int32, ctypes.c_int32,
-                                        ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
         L.fp4kv_decode_plan.restype = ctypes.c_int
         L.fp4kv_decode_attention.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int32,
@@ -121,15 +121,29 @@ def cache_layout(num_kv_heads: int, head_dim: int, num_pages: int,
     return out
 
 
+class DecodePlan(tuple):
+    """(splits, partials, workspace_bytes) of fp4kv_decode_plan."""
+    __slots__ = ()
+
+    def __new__(cls, splits, partials, workspace_bytes):
+        return tuple.__new__(cls, (splits, partials, workspace_bytes))
+
+    splits = property(lambda self: self[0])
+    partials = property(lambda self: self[1])
+    workspace_bytes = property(lambda self: self[2])
+
+
 def decode_plan(layout: CacheLayout, batch: int, num_q_heads: int, max_pages_per_seq: int,
-                num_splits: int = 0):
-    """(splits, workspace bytes) that decode_attention uses for these arguments."""
+                num_splits: int = 0) -> DecodePlan:
+    """Context chunks, partials per row and workspace bytes that
+    decode_attention uses for these arguments."""
     s = ctypes.c_int32()
+    p = ctypes.c_int32()
     ws = ctypes.c_int64()
     _check("fp4kv_decode_plan", library().fp4kv_decode_plan(
         ctypes.byref(layout), batch, num_q_heads, max_pages_per_seq, num_splits,
-        ctypes.byref(s), ctypes.byref(ws)))
-    return s.value, ws.value
+        ctypes.byref(s), ctypes.byref(p), ctypes.byref(ws)))
+    return DecodePlan(s.value, p.value, ws.value)
 
 
 def _stream(stream):
@@ -182,12 +196,12 @@ def _decode_inputs(layout, cache, q, seq_lens, page_table, num_splits, workspace
     if cache.numel() < layout.cache_bytes:
         raise ValueError("cache is smaller than layout.cache_bytes")
     max_pages = page_table.shape[1]
-    splits, ws_bytes = decode_plan(layout, B, Hq, max_pages, num_splits)
+    plan = decode_plan(layout, B, Hq, max_pages, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=q.device)
     else:
         _need(workspace, "workspace", torch.uint8)
-    return B, Hq, D, max_pages, splits, workspace
+    return B, Hq, D, max_pages, plan, workspace
 
 
 def _out_tensor(out, B, Hq, D, device):
@@ -204,7 +218,7 @@ def decode_attention(layout: CacheLayout, cache, q, seq_lens, page_table, softma
                      num_splits: int = 0, workspace=None, out=None, stream=None):
     """Decode attention of q (bf16 [B][Hq][D]) over the cache; returns fp32
     [B][Hq][D].  seq_lens int32 [B]; page_table int32 [B][max_pages]."""
-    B, Hq, D, max_pages, splits, workspace = _decode_inputs(
+    B, Hq, D, max_pages, plan, workspace = _decode_inputs(
         layout, cache, q, seq_lens, page_table, num_splits, workspace)
     out = _out_tensor(out, B, Hq, D, q.device)
     if softmax_scale is None:
@@ -218,9 +232,9 @@ def decode_attention(layout: CacheLayout, cache, q, seq_lens, page_table, softma
 
 def decode_split(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_scale=None,
                  num_splits: int = 0, workspace=None, stream=None):
-    """First half of decode_attention: per-split partials in the workspace.
-    Returns (workspace, splits)."""
-    B, Hq, D, max_pages, splits, workspace = _decode_inputs(
+    """First half of decode_attention: per-workgroup partials in the
+    workspace.  Returns (workspace, plan)."""
+    B, Hq, D, max_pages, plan, workspace = _decode_inputs(
         layout, cache, q, seq_lens, page_table, num_splits, workspace)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
@@ -228,17 +242,17 @@ def decode_split(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_sc
         ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, Hq, seq_lens.data_ptr(),
         page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
-    return workspace, splits
+    return workspace, plan
 
 
-def decode_combine(workspace, batch: int, num_q_heads: int, head_dim: int, splits: int,
+def decode_combine(workspace, batch: int, num_q_heads: int, head_dim: int, partials: int,
                    out=None, stream=None):
-    """Second half of decode_attention: merge `splits` partials into fp32
-    [batch][num_q_heads][head_dim]."""
+    """Second half of decode_attention: merge `partials` partial results per
+    row into fp32 [batch][num_q_heads][head_dim]."""
     import torch
     _need(workspace, "workspace", torch.uint8)
     out = _out_tensor(out, batch, num_q_heads, head_dim, workspace.device)
     _check("fp4kv_decode_combine", library().fp4kv_decode_combine(
-        batch, num_q_heads, head_dim, splits, workspace.data_ptr(), workspace.numel(),
+        batch, num_q_heads, head_dim, partials, workspace.data_ptr(), workspace.numel(),
         out.data_ptr(), _stream(stream)))
     return out

@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIBRARY = os.path.join(HERE, "libfp4kv.so")
 SOURCES = [os.path.join(HERE, "csrc", "fp4kv_api.cpp"),
-           os.path.join(HERE, "csrc", "fp4kv_kernels.hip")]
+           os.path.join(HERE, "csrc", "fp4kv_kernels.hip"),
+           os.path.join(HERE, "csrc", "fp4kv_decode_mfma.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -19,6 +20,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-result", "-fvisibility=hidden",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the kernels rescale them on
+    # the vector ALUs, and AGPR copies would cost more than they save
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

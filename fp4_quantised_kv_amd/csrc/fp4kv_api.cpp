@@ -14,7 +14,8 @@
 namespace {
 
 constexpr int32_t kPage = FP4KV_PAGE_SIZE;
-constexpr int32_t kTargetWaves = 2048;    // ~8 resident waves per CU on 256 CUs
+constexpr int32_t kTargetWaves = 4096;    // context chunks (one wave each) to cover 256 CUs
+constexpr int32_t kChunksPerGroup = 4;   // chunks merged inside one workgroup
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -85,6 +86,7 @@ fp4kv::CacheGeom geom_of(const fp4kv_cache_layout_t &L)
 struct Plan {
     int32_t splits;
     int32_t pages_per_split;
+    int32_t partials;          // ceil(splits / kChunksPerGroup)
     int64_t ws_o_bytes;        // fp32 partial outputs
     int64_t ws_bytes;          // total, including the (max, sum) pairs
 };
@@ -114,7 +116,8 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
     s = (max_pages + pps - 1) / pps;                          // no split starts past the last page
     plan->splits = static_cast<int32_t>(s);
     plan->pages_per_split = static_cast<int32_t>(pps);
-    const int64_t rows = static_cast<int64_t>(batch) * num_q_heads * s;
+    plan->partials = static_cast<int32_t>((s + kChunksPerGroup - 1) / kChunksPerGroup);
+    const int64_t rows = static_cast<int64_t>(batch) * num_q_heads * plan->partials;
     plan->ws_o_bytes = round_up(rows * L.params.head_dim * 4, 256);
     plan->ws_bytes = plan->ws_o_bytes + round_up(rows * 2 * 4, 256);
     return FP4KV_OK;
@@ -156,18 +159,19 @@ int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout, const void *k, con
 
 int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t num_q_heads,
                       int32_t max_pages_per_seq, int32_t num_splits, int32_t *splits_out,
-                      int64_t *workspace_bytes_out)
+                      int32_t *partials_out, int64_t *workspace_bytes_out)
 {
     int rc = check_layout(layout);
     if (rc != FP4KV_OK)
         return rc;
-    if (!splits_out || !workspace_bytes_out)
+    if (!splits_out || !partials_out || !workspace_bytes_out)
         return FP4KV_ERR_INVALID_ARGUMENT;
     Plan plan;
     rc = make_plan(*layout, batch, num_q_heads, max_pages_per_seq, num_splits, &plan);
     if (rc != FP4KV_OK)
         return rc;
     *splits_out = plan.splits;
+    *partials_out = plan.partials;
     *workspace_bytes_out = plan.ws_bytes;
     return FP4KV_OK;
 }
@@ -218,6 +222,8 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     a->max_pages = max_pages_per_seq;
     a->splits = plan.splits;
     a->pages_per_split = plan.pages_per_split;
+    a->partials = plan.partials;
+    a->staged = true;
     a->scale_log2e = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     a->ws_o = static_cast<float *>(workspace);
     a->ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + plan.ws_o_bytes);
@@ -225,9 +231,9 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     return FP4KV_OK;
 }
 
-int64_t partial_o_bytes(int32_t batch, int32_t num_q_heads, int32_t splits, int32_t head_dim)
+int64_t partial_o_bytes(int32_t batch, int32_t num_q_heads, int32_t partials, int32_t head_dim)
 {
-    return round_up(static_cast<int64_t>(batch) * num_q_heads * splits * head_dim * 4, 256);
+    return round_up(static_cast<int64_t>(batch) * num_q_heads * partials * head_dim * 4, 256);
 }
 
 }  // namespace
@@ -249,10 +255,10 @@ int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void *cache, co
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
 
-int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t splits,
+int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t partials,
                          const void *workspace, int64_t workspace_bytes, float *out, void *stream)
 {
-    if (batch < 0 || num_q_heads < 1 || splits < 1)
+    if (batch < 0 || num_q_heads < 1 || partials < 1)
         return FP4KV_ERR_INVALID_ARGUMENT;
     if (head_dim != 64 && head_dim != 128)
         return FP4KV_ERR_UNSUPPORTED;
@@ -265,12 +271,12 @@ int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, i
     const int64_t rows = static_cast<int64_t>(batch) * num_q_heads;
     if (rows > std::numeric_limits<int32_t>::max())
         return FP4KV_ERR_UNSUPPORTED;
-    const int64_t o_bytes = partial_o_bytes(batch, num_q_heads, splits, head_dim);
-    if (workspace_bytes < o_bytes + round_up(rows * splits * 2 * 4, 256))
+    const int64_t o_bytes = partial_o_bytes(batch, num_q_heads, partials, head_dim);
+    if (workspace_bytes < o_bytes + round_up(rows * partials * 2 * 4, 256))
         return FP4KV_ERR_WORKSPACE_TOO_SMALL;
     const float *ws_o = static_cast<const float *>(workspace);
     const float *ws_ml = reinterpret_cast<const float *>(static_cast<const uint8_t *>(workspace) + o_bytes);
-    const hipError_t e = fp4kv::launch_decode_combine(ws_o, ws_ml, rows, splits, head_dim, out,
+    const hipError_t e = fp4kv::launch_decode_combine(ws_o, ws_ml, rows, partials, head_dim, out,
                                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
@@ -296,7 +302,7 @@ int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache
     if (e != hipSuccess)
         return FP4KV_ERR_HIP;
     e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, static_cast<int64_t>(batch) * num_q_heads,
-                                     a.splits, layout->params.head_dim, out, st);
+                                     a.partials, layout->params.head_dim, out, st);
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
 

@@ -1,0 +1,491 @@
+// Split-K decode attention on the CDNA4 matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// Workgroups of four waves per (4 context chunks, KV head, sequence); each
+// wave attends over one chunk and the four results are merged in LDS into
+// one partial.  For each 64-token page of its chunk, a wave computes:
+//
+//   scores  S^T[token][query] = K^ Q^T as four 16-token tiles.  The A operand
+//           is the page's K codes, converted two at a time by the hardware FP4
+//           conversion (scale 1: the instruction applies only the exponent of
+//           a scale) and multiplied by the token's E4M3 scale in packed fp16;
+//           E2M1 x E4M3 products have at most 6 significant bits, so every
+//           dequantised value is exact in fp16.  The B operand is the group's
+//           query rows (up to 16; missing rows are zero), converted to fp16
+//           after multiplying by a power of two that puts the largest |q|
+//           just under 2^15 (exact for bf16 inputs, undone on the scores).
+//   softmax the C layout gives each lane one query column and 16 of the page's
+//           tokens; the running max per query is a lane max plus two
+//           cross-lane steps.  The reference max is only moved when the page
+//           max exceeds it by more than 8 (base 2), so the accumulators are
+//           rescaled rarely and probabilities stay below 2^8.
+//   values  O^T[channel][query] += V^T P^T.  The 16 tokens a lane holds in the
+//           score tiles are exactly the 16 consecutive tokens it needs as the
+//           B operand of the value product, so P needs no data movement.  V is
+//           stored channel-pair-major, so a lane's 16 tokens of one channel
+//           pair are one 16-byte load; conversion gives (even, odd) pairs per
+//           token, which are regrouped into per-channel token pairs and scaled
+//           by the per-token scales.  P enters as two fp16 parts (hi + lo),
+//           each multiplied on the matrix cores, so the probabilities keep
+//           ~21 significant bits.  The softmax denominator is one more
+//           product, of P with a ones matrix, so it sums exactly the
+//           probabilities used for the values.
+//
+// Page-local token order of score tile a, row r: token 16*(r/4) + 4*a + r%4,
+// so the C-layout lane (query n, row group jj) holds tokens 16*jj + 0..15.
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "fp4kv_internal.h"
+#include "fp4kv_merge.h"
+
+namespace fp4kv {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 64;
+constexpr float kRescaleSlack = 8.0f;      // base-2 headroom before the reference max moves
+
+template <int SEL>
+__device__ __forceinline__ half2_t fp4x2(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+template <bool HI>
+__device__ __forceinline__ half2_t fp8x2(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+__device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d)
+{
+    const half4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const half4_t cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ half2_t pk_rtz(float a, float b)
+{
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// 8 consecutive channels of one token (one code dword) times one scale.
+__device__ __forceinline__ half8_t k_operand(uint32_t w, half2_t s)
+{
+    return cat(fp4x2<0>(w), fp4x2<1>(w), fp4x2<2>(w), fp4x2<3>(w)) *
+           __builtin_shufflevector(s, s, 0, 1, 0, 1, 0, 1, 0, 1);
+}
+
+// Four tokens' code bytes of one channel pair (one dword) with their scales
+// (s01 = tokens 0,1; s23 = tokens 2,3) -> the even channel's and the odd
+// channel's values for those tokens, in token order.
+__device__ __forceinline__ void v_operand4(uint32_t w, half2_t s01, half2_t s23, half4_t &even, half4_t &odd)
+{
+    const half2_t t0 = fp4x2<0>(w), t1 = fp4x2<1>(w), t2 = fp4x2<2>(w), t3 = fp4x2<3>(w);
+    const half4_t e = {t0[0], t1[0], t2[0], t3[0]};
+    const half4_t o = {t0[1], t1[1], t2[1], t3[1]};
+    const half4_t s = __builtin_shufflevector(s01, s23, 0, 1, 2, 3);
+    even = e * s;
+    odd = o * s;
+}
+
+__device__ __forceinline__ float xor_max(float x)
+{
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// Keep the bytes of a dword whose token index (t0 + byte) is below `valid`.
+__device__ __forceinline__ uint32_t keep_valid_bytes(uint32_t w, int t0, int valid)
+{
+    const int n = valid - t0;
+    if (n >= 4)
+        return w;
+    if (n <= 0)
+        return 0u;
+    return w & ((1u << (8 * n)) - 1u);
+}
+
+// Operands of one page as a lane holds them (see the page loaders below).
+template <int D>
+struct PageRegs {
+    static constexpr int KW = D / 32;     // code dwords per lane per score tile
+    static constexpr int NU = D / 32;     // 16-pair blocks of V channel pairs
+    uint32_t kw[4][KW];                   // K codes: tile t, channels jj*D/4 + 8i .. +7 in dword i
+    uint32_t ks[4];                       // K scales of those channels (two bytes for D = 128)
+    uint4 vw[NU];                         // V codes: pair 16u + col, tokens 16jj .. +15
+    uint4 vs[NU];                         // V scales of that pair's block, same tokens
+};
+
+// Running state of one wave over its split.
+template <int D>
+struct SplitState {
+    float m_ref;
+    float4_t acc[D / 16];                 // O^T tiles: (pair block u, parity) -> index 2u + parity
+    float4_t lacc;
+};
+
+// Scores, online softmax and value accumulation of one page whose first
+// `valid` tokens are live.
+template <int D>
+__device__ __forceinline__ void process_page(PageRegs<D> &r, int valid, const half8_t (&qf)[D / 32],
+                                             float zscale, int jj, SplitState<D> &st)
+{
+    constexpr int KW = PageRegs<D>::KW;
+    constexpr int NU = PageRegs<D>::NU;
+    const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+
+    // ---- scores
+    float z[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const half2_t s = fp8x2<false>(r.ks[t]);          // (scale of first 16 channels, of next 16)
+        float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < KW; ++i) {
+            const half2_t si = (KW == 4 && i >= 2) ? __builtin_shufflevector(s, s, 1, 1)
+                                                   : __builtin_shufflevector(s, s, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(r.kw[t][i], si), qf[i], sacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            z[t][e] = sacc[e] * zscale;
+        __builtin_amdgcn_sched_barrier(0);               // one tile's operands live at a time
+    }
+    if (valid < kPage) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                z[t][e] = (16 * jj + 4 * t + e < valid) ? z[t][e] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            r.vs[u].x = keep_valid_bytes(r.vs[u].x, 16 * jj + 0, valid);
+            r.vs[u].y = keep_valid_bytes(r.vs[u].y, 16 * jj + 4, valid);
+            r.vs[u].z = keep_valid_bytes(r.vs[u].z, 16 * jj + 8, valid);
+            r.vs[u].w = keep_valid_bytes(r.vs[u].w, 16 * jj + 12, valid);
+        }
+    }
+
+    // ---- online softmax with a lazily moved reference max
+    float mx = z[0][0];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            mx = fmaxf(mx, z[t][e]);
+    mx = xor_max(mx);
+    const bool move = mx > st.m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float m_new = move ? mx : st.m_ref;
+        const float alpha = move ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
+        st.m_ref = m_new;
+#pragma unroll
+        for (int t = 0; t < 2 * NU; ++t)
+            st.acc[t] *= alpha;
+        st.lacc *= alpha;
+    }
+    // p = hi + lo with both parts in fp16 (hi truncated, lo the truncated
+    // remainder): the value and denominator products see p to ~2^-21
+    // relative, so fp16 operands cost no accuracy against fp32.
+    half8_t pf[2], pl[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        float p[8], q[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(z[2 * kt][e] - st.m_ref);
+            p[4 + e] = __builtin_amdgcn_exp2f(z[2 * kt + 1][e] - st.m_ref);
+        }
+        pf[kt] = cat(pk_rtz(p[0], p[1]), pk_rtz(p[2], p[3]), pk_rtz(p[4], p[5]), pk_rtz(p[6], p[7]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            q[e] = p[e] - static_cast<float>(pf[kt][e]);
+        pl[kt] = cat(pk_rtz(q[0], q[1]), pk_rtz(q[2], q[3]), pk_rtz(q[4], q[5]), pk_rtz(q[6], q[7]));
+        st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[kt], st.lacc, 0, 0, 0);
+        st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pl[kt], st.lacc, 0, 0, 0);
+    }
+
+    // ---- values: tile (u, parity) rows are channels 2*(16u + row) + parity
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const uint32_t cw[4] = {r.vw[u].x, r.vw[u].y, r.vw[u].z, r.vw[u].w};
+        const uint32_t sw[4] = {r.vs[u].x, r.vs[u].y, r.vs[u].z, r.vs[u].w};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            half4_t e0, o0, e1, o1;
+            v_operand4(cw[2 * kt], fp8x2<false>(sw[2 * kt]), fp8x2<true>(sw[2 * kt]), e0, o0);
+            v_operand4(cw[2 * kt + 1], fp8x2<false>(sw[2 * kt + 1]), fp8x2<true>(sw[2 * kt + 1]), e1, o1);
+            const half8_t ev = __builtin_shufflevector(e0, e1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const half8_t od = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
+            st.acc[2 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pf[kt], st.acc[2 * u], 0, 0, 0);
+            st.acc[2 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pl[kt], st.acc[2 * u], 0, 0, 0);
+            st.acc[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pf[kt], st.acc[2 * u + 1], 0, 0, 0);
+            st.acc[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pl[kt], st.acc[2 * u + 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Page-local token of score tile t, row `row`.
+__device__ __forceinline__ int tile_token(int t, int row) { return 16 * (row >> 2) + 4 * t + (row & 3); }
+
+// Direct loader: every operand straight from global memory into registers.
+template <int D>
+__device__ __forceinline__ void load_page_direct(const uint8_t *blk, const CacheGeom &g, int col, int jj,
+                                                 PageRegs<D> &r)
+{
+    constexpr int KW = PageRegs<D>::KW;
+    constexpr int NB = D / 16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tok = tile_token(t, col);
+        const uint8_t *krow = blk + g.k_codes_off + tok * (D / 2) + jj * (D / 8);
+        if constexpr (KW == 4) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(krow);
+            r.kw[t][0] = x.x; r.kw[t][1] = x.y; r.kw[t][2] = x.z; r.kw[t][3] = x.w;
+            r.ks[t] = *reinterpret_cast<const uint16_t *>(blk + g.k_scales_off + tok * NB + 2 * jj);
+        } else {
+            const uint2 x = *reinterpret_cast<const uint2 *>(krow);
+            r.kw[t][0] = x.x; r.kw[t][1] = x.y;
+            const uint32_t s1 = blk[g.k_scales_off + tok * NB + jj];
+            r.ks[t] = s1 | (s1 << 8);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < PageRegs<D>::NU; ++u) {
+        const int pair = 16 * u + col;
+        r.vw[u] = *reinterpret_cast<const uint4 *>(blk + g.v_codes_off + pair * kPage + 16 * jj);
+        r.vs[u] = *reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (pair >> 3) * kPage + 16 * jj);
+    }
+}
+
+// Staged loader for D = 128: the page is copied into the wave's LDS slot by
+// direct-to-LDS loads (no registers held while in flight), each lane fetching
+// exactly the bytes it will read back, so the copy of the next page overlaps
+// the arithmetic on the current one.  Slot layout (bytes):
+//   [0, 4096)      K codes, tile t at t*1024, lane l's 16 bytes at l*16
+//   [4096, 5120)   K scale dwords, tile t at 4096 + t*256, lane l at l*4
+//   [5120, 9216)   V codes, block u at 5120 + u*1024, lane l at l*16
+//   [9216, 9728)   the page's V scale plane [8 blocks][64 tokens]
+constexpr int kStageBytes = 9728;
+
+struct StageOffsets {
+    uint32_t k, ks, v, vs;                // per-lane byte offsets inside a block, tile/block 0
+};
+
+__device__ __forceinline__ StageOffsets stage_offsets(const CacheGeom &g, int lane, int col, int jj)
+{
+    StageOffsets o;
+    const uint32_t tok0 = static_cast<uint32_t>(tile_token(0, col));
+    o.k = static_cast<uint32_t>(g.k_codes_off) + tok0 * 64u + jj * 16u;
+    o.ks = static_cast<uint32_t>(g.k_scales_off) + tok0 * 8u + (jj >> 1) * 4u;
+    o.v = static_cast<uint32_t>(g.v_codes_off) + col * static_cast<uint32_t>(kPage) + 16u * jj;
+    o.vs = static_cast<uint32_t>(g.v_scales_off) + lane * 4u;
+    return o;
+}
+
+// Tile t's token rows are 4t past tile 0's: +256 bytes of K codes, +32 of
+// K scales; V pair block u is 16 pairs (1024 bytes) past block 0.
+__device__ __forceinline__ void stage_page_lds(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
+{
+    const uint8_t *k = blk + o.k, *ks = blk + o.ks, *v = blk + o.v, *vs = blk + o.vs;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        __builtin_amdgcn_global_load_lds(k + 256 * t, slot + t * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ks + 32 * t, slot + 4096 + t * 256, 4, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_global_load_lds(v + 1024 * u, slot + 5120 + u * 1024, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(vs + 256 * i, slot + 9216 + i * 256, 4, 0, 0);
+}
+
+__device__ __forceinline__ void read_staged(const uint8_t *slot, int lane, int col, int jj, PageRegs<128> &r)
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(slot + t * 1024 + lane * 16);
+        r.kw[t][0] = x.x; r.kw[t][1] = x.y; r.kw[t][2] = x.z; r.kw[t][3] = x.w;
+        const uint32_t sd = *reinterpret_cast<const uint32_t *>(slot + 4096 + t * 256 + lane * 4);
+        r.ks[t] = (jj & 1) ? (sd >> 16) : (sd & 0xFFFFu);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        r.vw[u] = *reinterpret_cast<const uint4 *>(slot + 5120 + u * 1024 + lane * 16);
+        r.vs[u] = *reinterpret_cast<const uint4 *>(slot + 9216 + (2 * u + (col >> 3)) * kPage + 16 * jj);
+    }
+}
+
+// gfx9 s_waitcnt immediates: all vector-memory loads done / all LDS accesses done.
+constexpr int kWaitVmem = 0x0F70;
+constexpr int kWaitLds = 0xC07F;
+
+// Each wave's LDS area: the page staging slot, reused at the end for the
+// merge of the workgroup's waves.
+constexpr int kWaveArea = kStageBytes;
+static_assert(merge_area_bytes<128>() <= kWaveArea, "merge area must fit in a staging slot");
+
+template <int D, bool STAGED>
+__global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
+{
+    constexpr int CPL = D / 4;            // channels a lane holds per score tile
+    constexpr int KW = CPL / 8;           // code dwords per lane per score tile (= MFMAs per tile)
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kWavesPerGroup * kWaveArea];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint8_t *slot = smem + wave * kWaveArea;
+    const int col = lane & 15;            // query column / tile row
+    const int jj = lane >> 4;             // lane group
+    const int sp = blockIdx.x * kWavesPerGroup + wave;   // this wave's context chunk
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int G = a.group;
+    const CacheGeom &g = a.geom;
+
+    // ---- query operand: lane (col, jj) holds channels jj*CPL .. +CPL of query col
+    uint32_t qbits[CPL / 2];
+    float qmax = 0.0f;
+    {
+        const bool live = col < G;
+        const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.num_q_heads + h * G + (live ? col : 0)) * D + jj * CPL;
+#pragma unroll
+        for (int i = 0; i < CPL / 8; ++i) {
+            const uint4 x = live ? reinterpret_cast<const uint4 *>(qrow)[i] : make_uint4(0, 0, 0, 0);
+            qbits[4 * i] = x.x; qbits[4 * i + 1] = x.y; qbits[4 * i + 2] = x.z; qbits[4 * i + 3] = x.w;
+        }
+#pragma unroll
+        for (int i = 0; i < CPL / 2; ++i) {
+            qmax = fmaxf(qmax, __uint_as_float((qbits[i] & 0x7FFFu) << 16));
+            qmax = fmaxf(qmax, __uint_as_float(qbits[i] & 0x7FFF0000u));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            qmax = fmaxf(qmax, __shfl_xor(qmax, o));
+    }
+    // 2^kq * qmax in [2^14, 2^15): exact power-of-two rescale of q before fp16
+    int kq = 0;
+    if (qmax > 0.0f)
+        kq = 14 - (static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127);
+    kq = kq > 100 ? 100 : kq;
+    const float qscale = __builtin_ldexpf(1.0f, kq);
+    const float zscale = a.scale_log2e * __builtin_ldexpf(1.0f, -kq);
+    half8_t qf[KW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = qbits[4 * i + e];
+            qf[i][2 * e] = static_cast<_Float16>(__uint_as_float(w << 16) * qscale);
+            qf[i][2 * e + 1] = static_cast<_Float16>(__uint_as_float(w & 0xFFFF0000u) * qscale);
+        }
+    }
+
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
+    const int n_pages = (len + kPage - 1) / kPage;
+    const int p0 = sp * a.pages_per_split;
+    const int p1 = min(p0 + a.pages_per_split, n_pages);
+    const int32_t *ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages;
+
+    SplitState<D> st;
+    st.m_ref = -INFINITY;
+    st.lacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+        st.acc[t] = st.lacc;
+
+    // next page of the split with an id inside the pool (others are skipped)
+    auto next_page = [&](int from, int &pid) {
+        for (; from < p1; ++from) {
+            pid = ptab[from];
+            if (pid >= 0 && pid < g.num_pages)
+                break;
+        }
+        return from;
+    };
+    auto block_of = [&](int pid) {
+        return a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
+    };
+
+    if constexpr (STAGED) {
+        // the chunk's page ids, 64 at a time, one per lane
+        int base = p0;
+        int ids = (p0 + lane < p1) ? ptab[p0 + lane] : -1;
+        auto live_page = [&](int pid) { return pid >= 0 && pid < g.num_pages; };
+        const StageOffsets so = stage_offsets(g, lane, col, jj);
+        int pid = p0 < p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
+        if (live_page(pid))
+            stage_page_lds(block_of(pid), so, slot);
+        for (int pg = p0; pg < p1; ++pg) {
+            const int nxt = pg + 1;
+            if (nxt < p1 && nxt - base == 64) {
+                base = nxt;
+                ids = (base + lane < p1) ? ptab[base + lane] : -1;
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmem);        // this page is in LDS
+            PageRegs<D> r;
+            read_staged(slot, lane, col, jj, r);
+            __builtin_amdgcn_s_waitcnt(kWaitLds);         // ... and in registers: the slot is free
+            const int pid_next = nxt < p1 ? __builtin_amdgcn_readlane(ids, nxt - base) : -1;
+            if (live_page(pid_next))
+                stage_page_lds(block_of(pid_next), so, slot);
+            if (live_page(pid))                           // ids outside the pool are skipped
+                process_page<D>(r, min(kPage, len - pg * kPage), qf, zscale, jj, st);
+            pid = pid_next;
+        }
+    } else {
+        int pid = 0;
+        for (int pg = next_page(p0, pid); pg < p1; pg = next_page(pg + 1, pid)) {
+            PageRegs<D> r;
+            load_page_direct<D>(block_of(pid), g, col, jj, r);
+            process_page<D>(r, min(kPage, len - pg * kPage), qf, zscale, jj, st);
+        }
+    }
+
+    // ---- this wave's state into its area: lane (col = query, jj) holds
+    //      channels 2*(16u + 4jj + r) + parity, i.e. 32u + 8jj + 0..7
+    {
+        const MergeArea<D> ar(slot);
+        if (col < G) {
+            float *o = ar.o + col * D;
+#pragma unroll
+            for (int u = 0; u < D / 32; ++u) {
+                const int c0 = 32 * u + 8 * jj;
+                *reinterpret_cast<float4 *>(o + c0) =
+                    make_float4(st.acc[2 * u][0], st.acc[2 * u + 1][0], st.acc[2 * u][1], st.acc[2 * u + 1][1]);
+                *reinterpret_cast<float4 *>(o + c0 + 4) =
+                    make_float4(st.acc[2 * u][2], st.acc[2 * u + 1][2], st.acc[2 * u][3], st.acc[2 * u + 1][3]);
+            }
+            if (jj == 0) {
+                ar.ml[2 * col] = st.m_ref;
+                ar.ml[2 * col + 1] = st.lacc[0];
+            }
+        }
+    }
+    merge_waves_and_store<D>(smem, kWaveArea, a, b, h, blockIdx.x);
+}
+
+}  // namespace
+
+hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream)
+{
+    const dim3 grid(a.partials, a.geom.num_kv_heads, a.batch);
+    if (a.geom.head_dim == 64)
+        decode_split_mfma<64, false><<<grid, kGroupThreads, 0, stream>>>(a);
+    else if (a.staged)
+        decode_split_mfma<128, true><<<grid, kGroupThreads, 0, stream>>>(a);
+    else
+        decode_split_mfma<128, false><<<grid, kGroupThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace fp4kv

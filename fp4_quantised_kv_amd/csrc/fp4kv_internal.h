@@ -24,20 +24,27 @@ struct DecodeArgs {
     const int32_t *seq_lens;     // [batch]
     const int32_t *page_table;   // [batch][max_pages]
     int32_t batch, num_q_heads, group, max_pages;
-    int32_t splits, pages_per_split;
+    int32_t splits, pages_per_split;   // context chunks and pages per chunk
+    int32_t partials;            // partial slots per row: ceil(splits / 4), one per workgroup
     float scale_log2e;           // softmax scale times log2(e): scores kept in base 2
-    float *ws_o;                 // [batch][num_q_heads][splits][D] unnormalised outputs
-    float *ws_ml;                // [batch][num_q_heads][splits][2] running max (base 2), sum
+    float *ws_o;                 // [batch][num_q_heads][partials][D] unnormalised outputs
+    float *ws_ml;                // [batch][num_q_heads][partials][2] running max (base 2), sum
     float *out;                  // [batch][num_q_heads][D]
+    bool staged;                 // matrix-core kernel: stage pages through LDS (D = 128)
 };
 
 hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const uint16_t *v,
                                   int64_t n_tokens, const int64_t *slots, uint8_t *cache,
                                   hipStream_t stream);
 
+// Decode split kernels: the vector-ALU one and the matrix-core one.
+hipError_t launch_split_valu(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream);
+
+// Chooses between the two (matrix cores unless FP4KV_DECODE_KERNEL=valu).
 hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
 
-hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t splits,
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t partials,
                                  int32_t head_dim, float *out, hipStream_t stream);
 
 }  // namespace fp4kv

@@ -10,10 +10,13 @@
 // of the nibble; E4M3 (OCP FN) scales, bias 7, largest finite 448, smallest
 // subnormal 2^-9.
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include <hip/hip_runtime.h>
 
 #include "fp4kv_internal.h"
+#include "fp4kv_merge.h"
 
 namespace fp4kv {
 namespace {
@@ -191,16 +194,9 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b)
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-__device__ __forceinline__ uint32_t byte_of(const uint4 (&r)[4], int i)
-{
-    const uint4 &q = r[i >> 4];
-    const int j = (i >> 2) & 3;
-    const uint32_t w = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-    return (w >> (8 * (i & 3))) & 0xFFu;
-}
-
-// Split-K decode attention on the vector ALUs, one wave per (split, KV head,
-// sequence).  For each 64-token page of the split:
+// Split-K decode attention on the vector ALUs.  Workgroups of four waves per
+// (4 context chunks, KV head, sequence), one chunk per wave, merged in LDS at
+// the end.  For each 64-token page of a wave's chunk:
 //   scores: lane = token; the lane reads its K row (D/2 code bytes and D/16
 //           scale bytes), converts the codes and dots them with the GM query
 //           rows held in LDS (the scale is applied to each 16-channel partial
@@ -210,19 +206,22 @@ __device__ __forceinline__ uint32_t byte_of(const uint4 (&r)[4], int i)
 //   values: lane = channel pair; the lane reads its transposed V row (64
 //           token bytes and the 64 scales of its channel block) and
 //           accumulates p * v for both channels of the pair.
-// The split's unnormalised output, max and sum are written to the workspace.
 template <int D, int GM>
-__global__ __launch_bounds__(64) void decode_split_valu(DecodeArgs a)
+__global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
 {
     constexpr int NB = D / 16;
-    const int lane = threadIdx.x;
-    const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sp = blockIdx.x * kWavesPerGroup + wave;
+    const int h = blockIdx.y, b = blockIdx.z;
     const int G = a.group;
 
     __shared__ float q_s[GM][D];
-    __shared__ float p_s[GM][kPage];
+    __shared__ float p_all[kWavesPerGroup][GM][kPage];
+    __shared__ __attribute__((aligned(16))) uint8_t areas[kWavesPerGroup * merge_area_bytes<D>()];
+    float (*p_s)[kPage] = p_all[wave];
 
-    for (int i = lane; i < GM * D; i += 64) {
+    for (int i = threadIdx.x; i < GM * D; i += kGroupThreads) {
         const int gq = i / D, c = i % D;
         q_s[gq][c] = gq < G ? bf16_to_float(a.q[(static_cast<int64_t>(b) * a.num_q_heads + h * G + gq) * D + c])
                             : 0.0f;
@@ -255,28 +254,20 @@ __global__ __launch_bounds__(64) void decode_split_valu(DecodeArgs a)
         for (int gq = 0; gq < GM; ++gq)
             z[gq] = 0.0f;
         {
-            const uint8_t *krow = blk + g.k_codes_off + lane * (D / 2);
+            // one 16-channel block at a time, re-reading the query rows from LDS
+            const uint2 *krow = reinterpret_cast<const uint2 *>(blk + g.k_codes_off + lane * (D / 2));
             const uint8_t *ksc = blk + g.k_scales_off + lane * NB;
-            uint32_t cw[D / 8];
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) {
-                const uint4 x = reinterpret_cast<const uint4 *>(krow)[i];
-                cw[4 * i] = x.x; cw[4 * i + 1] = x.y; cw[4 * i + 2] = x.z; cw[4 * i + 3] = x.w;
-            }
-            uint32_t sw[NB / 4];
-#pragma unroll
-            for (int i = 0; i < NB / 4; ++i)
-                sw[i] = reinterpret_cast<const uint32_t *>(ksc)[i];
-#pragma unroll
+#pragma unroll 1
             for (int nb = 0; nb < NB; ++nb) {
-                const float s = e4m3_value((sw[nb >> 2] >> (8 * (nb & 3))) & 0xFFu);
+                const uint2 cw = krow[nb];
+                const float s = e4m3_value(ksc[nb]);
                 float part[GM];
 #pragma unroll
                 for (int gq = 0; gq < GM; ++gq)
                     part[gq] = 0.0f;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
-                    const uint32_t word = cw[2 * nb + (c >> 3)];
+                    const uint32_t word = (c < 8) ? cw.x : cw.y;
                     const float kv = e2m1_value(word >> (4 * (c & 7)));
 #pragma unroll
                     for (int gq = 0; gq < GM; ++gq)
@@ -303,85 +294,105 @@ __global__ __launch_bounds__(64) void decode_split_valu(DecodeArgs a)
             m[gq] = mn;
             p_s[gq][lane] = p;
         }
-        __syncthreads();
+        // the wave's own LDS writes, in order, before its reads below
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- values, lane = channel pair (D/2 lanes)
+        // ---- values, lane = channel pair (D/2 lanes), 16 tokens per chunk
         if (lane < D / 2) {
-            uint4 vc[4], vs[4];
             const uint4 *vrow = reinterpret_cast<const uint4 *>(blk + g.v_codes_off + lane * kPage);
             const uint4 *vsrow = reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (lane >> 3) * kPage);
+#pragma unroll 1
+            for (int ch = 0; ch < kPage / 16; ++ch) {
+                if (16 * ch >= valid)
+                    break;
+                const uint4 vc = vrow[ch], vs = vsrow[ch];
+                const uint32_t cw[4] = {vc.x, vc.y, vc.z, vc.w};
+                const uint32_t sw[4] = {vs.x, vs.y, vs.z, vs.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vc[i] = vrow[i];
-                vs[i] = vsrow[i];
-            }
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t byte = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+                    const float s = e4m3_value((sw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+                    const float ve = e2m1_value(byte) * s;
+                    const float vo = e2m1_value(byte >> 4) * s;
 #pragma unroll
-            for (int t = 0; t < kPage; ++t) {
-                const uint32_t byte = byte_of(vc, t);
-                const float s = e4m3_value(byte_of(vs, t));
-                const float ve = e2m1_value(byte) * s;
-                const float vo = e2m1_value(byte >> 4) * s;
-#pragma unroll
-                for (int gq = 0; gq < GM; ++gq) {
-                    const float p = p_s[gq][t];
-                    o0[gq] = fmaf(p, ve, o0[gq]);
-                    o1[gq] = fmaf(p, vo, o1[gq]);
+                    for (int gq = 0; gq < GM; ++gq) {
+                        const float p = p_s[gq][16 * ch + i];
+                        o0[gq] = fmaf(p, ve, o0[gq]);
+                        o1[gq] = fmaf(p, vo, o1[gq]);
+                    }
                 }
             }
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // ---- write the split's partial results
+    // ---- this wave's state into its merge area, then one partial per workgroup
+    const MergeArea<D> ar(areas + wave * merge_area_bytes<D>());
 #pragma unroll
     for (int gq = 0; gq < GM; ++gq) {
         const float lt = wave_sum(l[gq]);
         if (gq >= G)
             continue;
-        const int64_t row = (static_cast<int64_t>(b) * a.num_q_heads + h * G + gq) * a.splits + sp;
         if (lane == 0) {
-            a.ws_ml[2 * row] = m[gq];
-            a.ws_ml[2 * row + 1] = lt;
+            ar.ml[2 * gq] = m[gq];
+            ar.ml[2 * gq + 1] = lt;
         }
         if (lane < D / 2)
-            *reinterpret_cast<float2 *>(a.ws_o + row * D + 2 * lane) = make_float2(o0[gq], o1[gq]);
+            *reinterpret_cast<float2 *>(ar.o + gq * D + 2 * lane) = make_float2(o0[gq], o1[gq]);
     }
+    merge_waves_and_store<D>(areas, merge_area_bytes<D>(), a, b, h, blockIdx.x);
 }
 
-// Merge the splits of one (sequence, query head): M = max_j m_j,
-// L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L.  Splits with no
-// tokens carry m = -inf and l = 0 and are skipped; a row with no tokens at
-// all is written as zeros.
+// Merge the partials of one (sequence, query head): M = max_j m_j,
+// L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L.  Partials with
+// no tokens carry m = -inf and l = 0 and are skipped; a row with no tokens at
+// all is written as zeros.  One wave per row: lane c covers channels c and
+// c + 64; the (m, l) pairs are read by every lane (one broadcast load each).
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine(const float *__restrict__ ws_o,
-                                                    const float *__restrict__ ws_ml, int splits,
-                                                    float *__restrict__ out)
+__global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ ws_o,
+                                                      const float *__restrict__ ws_ml, int partials,
+                                                      int64_t rows, float *__restrict__ out)
 {
-    const int64_t row = blockIdx.x;
-    const int c = threadIdx.x;
-    const float *ml = ws_ml + row * splits * 2;
+    constexpr int CL = D / 64;                          // channels per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + row * partials;
+    const float *o = ws_o + row * partials * D + lane;
     float M = -INFINITY;
-    for (int j = 0; j < splits; ++j)
-        M = fmaxf(M, ml[2 * j]);
-    float L = 0.0f, O = 0.0f;
+    for (int j = 0; j < partials; ++j)
+        M = fmaxf(M, ml[j].x);
+    float L = 0.0f, O[CL];
+#pragma unroll
+    for (int i = 0; i < CL; ++i)
+        O[i] = 0.0f;
     if (M != -INFINITY) {
-        for (int j = 0; j < splits; ++j) {
-            const float mj = ml[2 * j];
-            if (mj == -INFINITY)
-                continue;
-            const float w = exp2f(mj - M);
-            L = fmaf(ml[2 * j + 1], w, L);
-            O = fmaf(ws_o[(row * splits + j) * D + c], w, O);
+#pragma unroll 4
+        for (int j = 0; j < partials; ++j) {
+            const float2 mj = ml[j];
+            const float w = mj.x == -INFINITY ? 0.0f : exp2f(mj.x - M);
+            L = fmaf(mj.y, w, L);
+#pragma unroll
+            for (int i = 0; i < CL; ++i)
+                O[i] = fmaf(o[j * D + 64 * i], w, O[i]);
         }
     }
-    out[row * D + c] = L > 0.0f ? O / L : 0.0f;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int i = 0; i < CL; ++i)
+        out[row * D + lane + 64 * i] = O[i] * inv;
 }
 
 template <int D, int GM>
 hipError_t launch_split_t(const DecodeArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.splits, a.geom.num_kv_heads, a.batch);
-    decode_split_valu<D, GM><<<grid, 64, 0, stream>>>(a);
+    const dim3 grid(a.partials, a.geom.num_kv_heads, a.batch);
+    decode_split_valu<D, GM><<<grid, kGroupThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -412,19 +423,29 @@ hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const u
     return hipGetLastError();
 }
 
-hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
+hipError_t launch_split_valu(const DecodeArgs &a, hipStream_t stream)
 {
     return a.geom.head_dim == 64 ? launch_split_d<64>(a, stream) : launch_split_d<128>(a, stream);
 }
 
-hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t splits,
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
+{
+    const char *v = std::getenv("FP4KV_DECODE_KERNEL");
+    if (v && std::strcmp(v, "valu") == 0)
+        return launch_split_valu(a, stream);
+    DecodeArgs m = a;
+    m.staged = !(v && std::strcmp(v, "mfma_direct") == 0);
+    return launch_split_mfma(m, stream);
+}
+
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t partials,
                                  int32_t head_dim, float *out, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(rows));
+    const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
     if (head_dim == 64)
-        decode_combine<64><<<grid, 64, 0, stream>>>(ws_o, ws_ml, splits, out);
+        decode_combine<64><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, rows, out);
     else
-        decode_combine<128><<<grid, 128, 0, stream>>>(ws_o, ws_ml, splits, out);
+        decode_combine<128><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, rows, out);
     return hipGetLastError();
 }
 

@@ -1,0 +1,72 @@
+// Merge of the running states of a workgroup's waves into one partial result.
+//
+// A decode workgroup has kWavesPerGroup waves; wave w attends over context
+// chunk 4 * blockIdx.x + w.  Each wave leaves, in its own LDS area, its
+// unnormalised outputs o_w[q][c] (16 query rows x D channels, fp32) and its
+// (m_w[q], l_w[q]) pairs (base-2 running max and sum).  The workgroup then
+// writes one partial per query row, relative to M = max_w m_w:
+//   o = sum_w o_w 2^(m_w - M),  l = sum_w l_w 2^(m_w - M),  m = M,
+// or (m, l, o) = (-inf, 0, 0) when every wave was empty.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "fp4kv_internal.h"
+
+namespace fp4kv {
+
+constexpr int kWavesPerGroup = 4;
+constexpr int kGroupThreads = 64 * kWavesPerGroup;
+
+template <int D>
+constexpr int merge_area_bytes() { return 16 * D * 4 + 16 * 2 * 4; }
+
+// The area of one wave: outputs [16][D], then (max, sum) pairs [16][2].
+template <int D>
+struct MergeArea {
+    float *o;
+    float *ml;
+    __device__ explicit MergeArea(uint8_t *base) : o(reinterpret_cast<float *>(base)), ml(o + 16 * D) {}
+};
+
+// Call with every thread of the workgroup, after each wave has filled its
+// area (areas are area_stride bytes apart starting at `areas`).
+template <int D>
+__device__ __forceinline__ void merge_waves_and_store(uint8_t *areas, int area_stride, const DecodeArgs &a,
+                                                      int b, int h, int part)
+{
+    __syncthreads();
+    const int G = a.group;
+    for (int idx = threadIdx.x; idx < G * D; idx += kGroupThreads) {
+        const int q = idx / D, c = idx % D;
+        float mw[kWavesPerGroup];
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) {
+            mw[w] = MergeArea<D>(areas + w * area_stride).ml[2 * q];
+            M = fmaxf(M, mw[w]);
+        }
+        float O = 0.0f, L = 0.0f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWavesPerGroup; ++w) {
+                if (mw[w] == -INFINITY)
+                    continue;
+                const MergeArea<D> ar(areas + w * area_stride);
+                const float wt = exp2f(mw[w] - M);
+                O = fmaf(ar.o[q * D + c], wt, O);
+                L = fmaf(ar.ml[2 * q + 1], wt, L);
+            }
+        }
+        const int64_t row = (static_cast<int64_t>(b) * a.num_q_heads + h * G + q) * a.partials + part;
+        a.ws_o[row * D + c] = O;
+        if (c == 0) {
+            a.ws_ml[2 * row] = M;
+            a.ws_ml[2 * row + 1] = L;
+        }
+    }
+}
+
+}  // namespace fp4kv

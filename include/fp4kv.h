@@ -131,17 +131,21 @@ FP4KV_API int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout,
                           const int64_t *slot_mapping, void *cache, void *stream);
 
 /* Split count and workspace bytes for fp4kv_decode_attention.  Host only.
- * num_splits > 0 asks for that many context chunks (clamped to
- * max_pages_per_seq, then trimmed so that no chunk is empty for a sequence
- * of max_pages_per_seq pages); 0 lets the library choose enough chunks to
- * fill the GPU.  *splits_out gets the count that fp4kv_decode_attention will
- * use for the same arguments, *workspace_bytes_out the workspace it needs.
+ * The context of every sequence is cut into S chunks of equal page counts;
+ * one wave attends over each chunk, and workgroups of four waves merge their
+ * four chunks into one partial result, so the workspace holds
+ * P = ceil(S / 4) partials per (sequence, query head).
+ * num_splits > 0 asks for S = num_splits (clamped to max_pages_per_seq, then
+ * trimmed so that no chunk starts past page max_pages_per_seq); 0 lets the
+ * library choose S to fill the GPU.  *splits_out gets S, *partials_out P and
+ * *workspace_bytes_out the workspace fp4kv_decode_attention needs, for the
+ * same arguments.
  * Errors: INVALID_ARGUMENT (null pointer, batch < 0, num_q_heads < 1,
  * max_pages_per_seq < 1, num_splits < 0, num_q_heads not a multiple of
  * H_kv), UNSUPPORTED (more than FP4KV_MAX_GROUP query heads per KV head). */
 FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t num_q_heads,
-                      int32_t max_pages_per_seq, int32_t num_splits,
-                      int32_t *splits_out, int64_t *workspace_bytes_out);
+                                int32_t max_pages_per_seq, int32_t num_splits,
+                                int32_t *splits_out, int32_t *partials_out, int64_t *workspace_bytes_out);
 
 /* One decode step of attention for `batch` sequences, one query token each,
  * over the packed cache.  ("Quantising the KV cache", Concept and Code
@@ -183,29 +187,29 @@ FP4KV_API int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const v
  * attended on different devices, concatenated along the split axis).
  *
  * fp4kv_decode_split takes the arguments of fp4kv_decode_attention except
- * `out` and writes each split's unnormalised partial result to the
+ * `out` and writes one unnormalised partial result per workgroup to the
  * workspace, laid out as
- *   o   fp32 [batch][num_q_heads][S][D]      at byte 0
- *   ml  fp32 [batch][num_q_heads][S][2]      at byte round_up(batch*num_q_heads*S*D*4, 256)
- * where S is the plan's split count, o = sum_t 2^(z_t - m) v_t over the
- * split's tokens, m = max_t z_t with z_t = log2(e) * softmax_scale * q.k_t,
- * and l = sum_t 2^(z_t - m).  A split without tokens has m = -inf, l = 0,
- * o = 0.
+ *   o   fp32 [batch][num_q_heads][P][D]      at byte 0
+ *   ml  fp32 [batch][num_q_heads][P][2]      at byte round_up(batch*num_q_heads*P*D*4, 256)
+ * where P is the plan's partial count, m = max_t z_t over the partial's
+ * tokens with z_t = log2(e) * softmax_scale * q.k_t, l = sum_t 2^(z_t - m)
+ * and o = sum_t 2^(z_t - m) v_t.  A partial without tokens has m = -inf,
+ * l = 0, o = 0.
  *
- * fp4kv_decode_combine merges S such partials per (sequence, query head):
+ * fp4kv_decode_combine merges P such partials per (sequence, query head):
  *   out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M),  M = max_j m_j,
- * and writes zeros where every split is empty.  `splits` must be the S of
- * the partials; workspace_bytes must cover the layout above.
+ * and writes zeros where every partial is empty.  `partials` must be the P
+ * of the workspace; workspace_bytes must cover the layout above.
  * Errors: as for fp4kv_decode_attention (combine: INVALID_ARGUMENT for
- * batch < 0, num_q_heads < 1 or splits < 1; UNSUPPORTED for head_dim not in
- * {64, 128}). */
+ * batch < 0, num_q_heads < 1 or partials < 1; UNSUPPORTED for head_dim not
+ * in {64, 128}). */
 FP4KV_API int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
                        int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
                        const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
                        int32_t num_splits, void *workspace, int64_t workspace_bytes, void *stream);
 
-FP4KV_API int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t splits,
-                         const void *workspace, int64_t workspace_bytes, float *out, void *stream);
+FP4KV_API int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t partials,
+                                   const void *workspace, int64_t workspace_bytes, float *out, void *stream);
 
 /* Static text for a status code (never NULL). */
 FP4KV_API const char *fp4kv_status_string(int status);

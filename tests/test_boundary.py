@@ -62,14 +62,15 @@ def test_layout_rejects(H, D, P, pages, reserved, code):
 
 def test_plan():
     L = fk.cache_layout(8, 128, 32 * 512)
-    assert fk.decode_plan(L, 32, 64, 512, 64)[0] == 64
-    assert fk.decode_plan(L, 32, 64, 512, 64)[1] == 32 * 64 * 64 * 128 * 4 + 32 * 64 * 64 * 8
+    assert fk.decode_plan(L, 32, 64, 512, 64)[:2] == (64, 16)       # four chunks per workgroup
+    assert fk.decode_plan(L, 32, 64, 512, 64)[2] == 32 * 64 * 16 * 128 * 4 + 32 * 64 * 16 * 8
+    assert fk.decode_plan(L, 1, 32, 8192, 7).partials == 2
     assert fk.decode_plan(L, 1, 32, 8192, 256)[0] == 256
     assert fk.decode_plan(L, 1, 32, 3, 256)[0] == 3                 # never more splits than pages
     assert fk.decode_plan(L, 1, 32, 10, 4)[0] == 4                  # 3 pages per split: 4 splits
     assert fk.decode_plan(L, 1, 32, 9, 4)[0] == 3                   # 3 pages per split: 3 splits
-    s, ws = fk.decode_plan(L, 64, 32, 258, 0)
-    assert 1 <= s <= 258 and ws > 0
+    s, p, ws = fk.decode_plan(L, 64, 32, 258, 0)
+    assert 1 <= s <= 258 and p == -(-s // 4) and ws > 0
     for args, code in [((32, 65, 512, 64), fk.ERR_INVALID_ARGUMENT),      # Hq % Hkv
                        ((32, 8 * 17, 512, 64), fk.ERR_UNSUPPORTED),       # group 17
                        ((-1, 64, 512, 64), fk.ERR_INVALID_ARGUMENT),
@@ -105,7 +106,7 @@ def test_decode_host_checks():
     L = fk.cache_layout(8, 128, 64)
     lib = _lib()
     ok = 0x10000
-    s, ws = fk.decode_plan(L, 2, 32, 8, 0)
+    s, p, ws = fk.decode_plan(L, 2, 32, 8, 0)
 
     def call(**kw):
         a = dict(cache=ok, q=ok, batch=2, hq=32, lens=ok, pt=ok, maxp=8, scale=0.1, splits=0,
@@ -130,8 +131,8 @@ def test_decode_host_checks():
     assert call(batch=70000) == fk.ERR_UNSUPPORTED
     assert lib.fp4kv_decode_combine(2, 32, 128, 0, ok, ws, ok, None) == fk.ERR_INVALID_ARGUMENT
     assert lib.fp4kv_decode_combine(2, 32, 96, 4, ok, ws, ok, None) == fk.ERR_UNSUPPORTED
-    assert lib.fp4kv_decode_combine(2, 32, 128, s, ok, ws - 1, ok, None) == fk.ERR_WORKSPACE_TOO_SMALL
-    assert lib.fp4kv_decode_combine(0, 32, 128, s, None, 0, None, None) == fk.OK
+    assert lib.fp4kv_decode_combine(2, 32, 128, p, ok, ws - 1, ok, None) == fk.ERR_WORKSPACE_TOO_SMALL
+    assert lib.fp4kv_decode_combine(0, 32, 128, p, None, 0, None, None) == fk.OK
     assert lib.fp4kv_decode_split(ctypes.byref(L), ok, ok, 2, 32, ok, ok, 8, 0.1, 0, ok, ws - 1,
                                   None) == fk.ERR_WORKSPACE_TOO_SMALL
 
