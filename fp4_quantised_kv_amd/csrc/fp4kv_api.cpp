@@ -195,7 +195,7 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     rc = make_plan(*layout, batch, num_q_heads, max_pages_per_seq, num_splits, &plan);
     if (rc != FP4KV_OK)
         return rc;
-    if (!std::isfinite(softmax_scale) || softmax_scale == 0.0f)
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
         return FP4KV_ERR_INVALID_ARGUMENT;
     if (static_cast<int64_t>(max_pages_per_seq) * kPage > std::numeric_limits<int32_t>::max())
         return FP4KV_ERR_UNSUPPORTED;

@@ -95,10 +95,16 @@ __device__ __forceinline__ void v_operand4(uint32_t w, half2_t s01, half2_t s23,
     odd = o * s;
 }
 
+// Max over the four lanes l, l^16, l^32, l^48 (one query column of a C
+// tile), with the gfx950 lane-swap instructions instead of LDS shuffles.
 __device__ __forceinline__ float xor_max(float x)
 {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Keep the bytes of a dword whose token index (t0 + byte) is below `valid`.
@@ -112,18 +118,26 @@ __device__ __forceinline__ uint32_t keep_valid_bytes(uint32_t w, int t0, int val
     return w & ((1u << (8 * n)) - 1u);
 }
 
-// Operands of one page as a lane holds them (see the page loaders below).
+// K operands of one page as a lane holds them: score tile t, code dwords i
+// (channels jj*D/4 + 8i .. +7 of the tile's token) and the two (D = 128) or
+// one (D = 64, repeated) scale bytes of those channels.
 template <int D>
-struct PageRegs {
-    static constexpr int KW = D / 32;     // code dwords per lane per score tile
-    static constexpr int NU = D / 32;     // 16-pair blocks of V channel pairs
-    uint32_t kw[4][KW];                   // K codes: tile t, channels jj*D/4 + 8i .. +7 in dword i
-    uint32_t ks[4];                       // K scales of those channels (two bytes for D = 128)
-    uint4 vw[NU];                         // V codes: pair 16u + col, tokens 16jj .. +15
-    uint4 vs[NU];                         // V scales of that pair's block, same tokens
+struct KRegs {
+    static constexpr int KW = D / 32;
+    uint32_t kw[4][KW];
+    uint32_t ks[4];
 };
 
-// Running state of one wave over its split.
+// V operands of one page: pair block u (pair 16u + col), tokens 16jj .. +15:
+// code bytes and the scale bytes of that pair's 16-channel block.
+template <int D>
+struct VRegs {
+    static constexpr int NU = D / 32;
+    uint4 vw[NU];
+    uint4 vs[NU];
+};
+
+// Running state of one wave over its chunk.
 template <int D>
 struct SplitState {
     float m_ref;
@@ -131,17 +145,16 @@ struct SplitState {
     float4_t lacc;
 };
 
-// Scores, online softmax and value accumulation of one page whose first
-// `valid` tokens are live.
+// Scores and online softmax of one page whose first `valid` tokens are live;
+// leaves the probabilities as the value product's B operands (hi and lo parts
+// for the two 32-token halves).
 template <int D>
-__device__ __forceinline__ void process_page(PageRegs<D> &r, int valid, const half8_t (&qf)[D / 32],
-                                             float zscale, int jj, SplitState<D> &st)
+__device__ __forceinline__ void scores_phase(const KRegs<D> &r, int valid, const half8_t (&qf)[D / 32],
+                                             float zscale, int jj, SplitState<D> &st, half8_t (&pf)[2],
+                                             half8_t (&pl)[2])
 {
-    constexpr int KW = PageRegs<D>::KW;
-    constexpr int NU = PageRegs<D>::NU;
+    constexpr int KW = KRegs<D>::KW;
     const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
-
-    // ---- scores
     float z[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -155,8 +168,7 @@ __device__ __forceinline__ void process_page(PageRegs<D> &r, int valid, const ha
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            z[t][e] = sacc[e] * zscale;
-        __builtin_amdgcn_sched_barrier(0);               // one tile's operands live at a time
+            z[t][e] = sacc[e];                          // scaled inside the exponent below
     }
     if (valid < kPage) {
 #pragma unroll
@@ -164,44 +176,36 @@ __device__ __forceinline__ void process_page(PageRegs<D> &r, int valid, const ha
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 z[t][e] = (16 * jj + 4 * t + e < valid) ? z[t][e] : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            r.vs[u].x = keep_valid_bytes(r.vs[u].x, 16 * jj + 0, valid);
-            r.vs[u].y = keep_valid_bytes(r.vs[u].y, 16 * jj + 4, valid);
-            r.vs[u].z = keep_valid_bytes(r.vs[u].z, 16 * jj + 8, valid);
-            r.vs[u].w = keep_valid_bytes(r.vs[u].w, 16 * jj + 12, valid);
-        }
     }
 
-    // ---- online softmax with a lazily moved reference max
+    // online softmax with a lazily moved reference max
     float mx = z[0][0];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             mx = fmaxf(mx, z[t][e]);
-    mx = xor_max(mx);
+    mx = xor_max(mx) * zscale;                          // zscale > 0: max commutes with it
     const bool move = mx > st.m_ref + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
         const float m_new = move ? mx : st.m_ref;
         const float alpha = move ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
         st.m_ref = m_new;
 #pragma unroll
-        for (int t = 0; t < 2 * NU; ++t)
+        for (int t = 0; t < D / 16; ++t)
             st.acc[t] *= alpha;
         st.lacc *= alpha;
     }
     // p = hi + lo with both parts in fp16 (hi truncated, lo the truncated
     // remainder): the value and denominator products see p to ~2^-21
     // relative, so fp16 operands cost no accuracy against fp32.
-    half8_t pf[2], pl[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
         float p[8], q[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(z[2 * kt][e] - st.m_ref);
-            p[4 + e] = __builtin_amdgcn_exp2f(z[2 * kt + 1][e] - st.m_ref);
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * kt][e], zscale, -st.m_ref));
+            p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * kt + 1][e], zscale, -st.m_ref));
         }
         pf[kt] = cat(pk_rtz(p[0], p[1]), pk_rtz(p[2], p[3]), pk_rtz(p[4], p[5]), pk_rtz(p[6], p[7]));
 #pragma unroll
@@ -211,12 +215,30 @@ __device__ __forceinline__ void process_page(PageRegs<D> &r, int valid, const ha
         st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[kt], st.lacc, 0, 0, 0);
         st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pl[kt], st.lacc, 0, 0, 0);
     }
+}
 
-    // ---- values: tile (u, parity) rows are channels 2*(16u + row) + parity
+// Value accumulation of pair blocks [U0, U0 + N) of one page: tile (u,
+// parity) rows are channels 2*(16u + row) + parity.  Scales of tokens at or
+// past `valid` are zeroed, so never-written slots contribute exact zeros.
+template <int D, int U0, int N>
+__device__ __forceinline__ void values_phase(const uint4 (&vw)[N], uint4 (&vs)[N], int valid, int jj,
+                                             const half8_t (&pf)[2], const half8_t (&pl)[2], SplitState<D> &st)
+{
+    if (valid < kPage) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const uint32_t cw[4] = {r.vw[u].x, r.vw[u].y, r.vw[u].z, r.vw[u].w};
-        const uint32_t sw[4] = {r.vs[u].x, r.vs[u].y, r.vs[u].z, r.vs[u].w};
+        for (int u = 0; u < N; ++u) {
+            vs[u].x = keep_valid_bytes(vs[u].x, 16 * jj + 0, valid);
+            vs[u].y = keep_valid_bytes(vs[u].y, 16 * jj + 4, valid);
+            vs[u].z = keep_valid_bytes(vs[u].z, 16 * jj + 8, valid);
+            vs[u].w = keep_valid_bytes(vs[u].w, 16 * jj + 12, valid);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const uint32_t cw[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
+        const uint32_t sw[4] = {vs[u].x, vs[u].y, vs[u].z, vs[u].w};
+        float4_t &ae = st.acc[2 * (U0 + u)];
+        float4_t &ao = st.acc[2 * (U0 + u) + 1];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             half4_t e0, o0, e1, o1;
@@ -224,30 +246,27 @@ __device__ __forceinline__ void process_page(PageRegs<D> &r, int valid, const ha
             v_operand4(cw[2 * kt + 1], fp8x2<false>(sw[2 * kt + 1]), fp8x2<true>(sw[2 * kt + 1]), e1, o1);
             const half8_t ev = __builtin_shufflevector(e0, e1, 0, 1, 2, 3, 4, 5, 6, 7);
             const half8_t od = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
-            st.acc[2 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pf[kt], st.acc[2 * u], 0, 0, 0);
-            st.acc[2 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pl[kt], st.acc[2 * u], 0, 0, 0);
-            st.acc[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pf[kt], st.acc[2 * u + 1], 0, 0, 0);
-            st.acc[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pl[kt], st.acc[2 * u + 1], 0, 0, 0);
+            ae = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pf[kt], ae, 0, 0, 0);
+            ae = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pl[kt], ae, 0, 0, 0);
+            ao = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pf[kt], ao, 0, 0, 0);
+            ao = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pl[kt], ao, 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Page-local token of score tile t, row `row`.
 __device__ __forceinline__ int tile_token(int t, int row) { return 16 * (row >> 2) + 4 * t + (row & 3); }
 
-// Direct loader: every operand straight from global memory into registers.
+// Direct loads: every operand straight from global memory into registers.
 template <int D>
-__device__ __forceinline__ void load_page_direct(const uint8_t *blk, const CacheGeom &g, int col, int jj,
-                                                 PageRegs<D> &r)
+__device__ __forceinline__ void load_k_direct(const uint8_t *blk, const CacheGeom &g, int col, int jj, KRegs<D> &r)
 {
-    constexpr int KW = PageRegs<D>::KW;
     constexpr int NB = D / 16;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int tok = tile_token(t, col);
         const uint8_t *krow = blk + g.k_codes_off + tok * (D / 2) + jj * (D / 8);
-        if constexpr (KW == 4) {
+        if constexpr (KRegs<D>::KW == 4) {
             const uint4 x = *reinterpret_cast<const uint4 *>(krow);
             r.kw[t][0] = x.x; r.kw[t][1] = x.y; r.kw[t][2] = x.z; r.kw[t][3] = x.w;
             r.ks[t] = *reinterpret_cast<const uint16_t *>(blk + g.k_scales_off + tok * NB + 2 * jj);
@@ -258,23 +277,32 @@ __device__ __forceinline__ void load_page_direct(const uint8_t *blk, const Cache
             r.ks[t] = s1 | (s1 << 8);
         }
     }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v_direct(const uint8_t *blk, const CacheGeom &g, int col, int jj, VRegs<D> &r)
+{
 #pragma unroll
-    for (int u = 0; u < PageRegs<D>::NU; ++u) {
+    for (int u = 0; u < VRegs<D>::NU; ++u) {
         const int pair = 16 * u + col;
         r.vw[u] = *reinterpret_cast<const uint4 *>(blk + g.v_codes_off + pair * kPage + 16 * jj);
         r.vs[u] = *reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (pair >> 3) * kPage + 16 * jj);
     }
 }
 
-// Staged loader for D = 128: the page is copied into the wave's LDS slot by
-// direct-to-LDS loads (no registers held while in flight), each lane fetching
-// exactly the bytes it will read back, so the copy of the next page overlaps
-// the arithmetic on the current one.  Slot layout (bytes):
-//   [0, 4096)      K codes, tile t at t*1024, lane l's 16 bytes at l*16
-//   [4096, 5120)   K scale dwords, tile t at 4096 + t*256, lane l at l*4
-//   [5120, 9216)   V codes, block u at 5120 + u*1024, lane l at l*16
-//   [9216, 9728)   the page's V scale plane [8 blocks][64 tokens]
-constexpr int kStageBytes = 9728;
+// Staged loads for D = 128: direct-to-LDS copies of exactly the bytes each
+// lane will read back, issued a phase ahead of the arithmetic so that no
+// registers are held while the copies are in flight.  K and V have separate
+// LDS slots, so the next page's K copy can start as soon as this page's K
+// operands are in registers, and likewise for V.
+//   K slot [0, 4096): tile t at t*1024, lane l's 16 code bytes at l*16;
+//          [4096, 5120): tile t's scale dwords at 4096 + t*256 + l*4.
+//   V slot [0, 4096): pair block u at u*1024, lane l at l*16;
+//          [4096, 4608): the page's V scale plane [8 blocks][64 tokens].
+constexpr int kKSlotBytes = 5120;
+constexpr int kVSlotBytes = 4608;
+constexpr int kCopiesK = 8;               // direct-to-LDS instructions per K copy
+constexpr int kCopiesV = 6;               // ... per V copy
 
 struct StageOffsets {
     uint32_t k, ks, v, vs;                // per-lane byte offsets inside a block, tile/block 0
@@ -293,23 +321,28 @@ __device__ __forceinline__ StageOffsets stage_offsets(const CacheGeom &g, int la
 
 // Tile t's token rows are 4t past tile 0's: +256 bytes of K codes, +32 of
 // K scales; V pair block u is 16 pairs (1024 bytes) past block 0.
-__device__ __forceinline__ void stage_page_lds(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
+__device__ __forceinline__ void stage_k(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
 {
-    const uint8_t *k = blk + o.k, *ks = blk + o.ks, *v = blk + o.v, *vs = blk + o.vs;
+    const uint8_t *k = blk + o.k, *ks = blk + o.ks;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         __builtin_amdgcn_global_load_lds(k + 256 * t, slot + t * 1024, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(ks + 32 * t, slot + 4096 + t * 256, 4, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_global_load_lds(v + 1024 * u, slot + 5120 + u * 1024, 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(vs + 256 * i, slot + 9216 + i * 256, 4, 0, 0);
 }
 
-__device__ __forceinline__ void read_staged(const uint8_t *slot, int lane, int col, int jj, PageRegs<128> &r)
+__device__ __forceinline__ void stage_v(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
+{
+    const uint8_t *v = blk + o.v, *vs = blk + o.vs;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_global_load_lds(v + 1024 * u, slot + u * 1024, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(vs + 256 * i, slot + 4096 + i * 256, 4, 0, 0);
+}
+
+__device__ __forceinline__ void read_k(const uint8_t *slot, int lane, int jj, KRegs<128> &r)
 {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -318,32 +351,45 @@ __device__ __forceinline__ void read_staged(const uint8_t *slot, int lane, int c
         const uint32_t sd = *reinterpret_cast<const uint32_t *>(slot + 4096 + t * 256 + lane * 4);
         r.ks[t] = (jj & 1) ? (sd >> 16) : (sd & 0xFFFFu);
     }
+}
+
+template <int U0, int N>
+__device__ __forceinline__ void read_v(const uint8_t *slot, int lane, int col, int jj, uint4 (&vw)[N], uint4 (&vs)[N])
+{
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        r.vw[u] = *reinterpret_cast<const uint4 *>(slot + 5120 + u * 1024 + lane * 16);
-        r.vs[u] = *reinterpret_cast<const uint4 *>(slot + 9216 + (2 * u + (col >> 3)) * kPage + 16 * jj);
+    for (int u = 0; u < N; ++u) {
+        vw[u] = *reinterpret_cast<const uint4 *>(slot + (U0 + u) * 1024 + lane * 16);
+        vs[u] = *reinterpret_cast<const uint4 *>(slot + 4096 + (2 * (U0 + u) + (col >> 3)) * kPage + 16 * jj);
     }
 }
 
-// gfx9 s_waitcnt immediates: all vector-memory loads done / all LDS accesses done.
-constexpr int kWaitVmem = 0x0F70;
+// gfx9 s_waitcnt immediates (expcnt and lgkmcnt left free): at most n vector
+// memory operations outstanding; and all LDS accesses done.
+__device__ __forceinline__ void wait_vmem_at_most(int n)
+{
+    // the count is a compile-time constant at every call site
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case kCopiesV: __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesV); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesK); break;
+    }
+}
 constexpr int kWaitLds = 0xC07F;
-
-// Each wave's LDS area: the page staging slot, reused at the end for the
-// merge of the workgroup's waves.
-constexpr int kWaveArea = kStageBytes;
-static_assert(merge_area_bytes<128>() <= kWaveArea, "merge area must fit in a staging slot");
 
 template <int D, bool STAGED>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
 {
     constexpr int CPL = D / 4;            // channels a lane holds per score tile
     constexpr int KW = CPL / 8;           // code dwords per lane per score tile (= MFMAs per tile)
+    static_assert(merge_area_bytes<D>() <= 16 * D * 4 + 128, "merge area layout");
+    static_assert(8 * D * 4 + 128 <= kKSlotBytes && 8 * D * 4 <= kVSlotBytes, "merge area must fit the slots");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kWavesPerGroup * kWaveArea];
+    // separate LDS objects for K and V, so the copies into one never wait on
+    // reads of the other
+    __shared__ __attribute__((aligned(16))) uint8_t kslots[kWavesPerGroup][kKSlotBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t vslots[kWavesPerGroup][kVSlotBytes];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    uint8_t *slot = smem + wave * kWaveArea;
     const int col = lane & 15;            // query column / tile row
     const int jj = lane >> 4;             // lane group
     const int sp = blockIdx.x * kWavesPerGroup + wave;   // this wave's context chunk
@@ -403,60 +449,85 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     for (int t = 0; t < D / 16; ++t)
         st.acc[t] = st.lacc;
 
-    // next page of the split with an id inside the pool (others are skipped)
-    auto next_page = [&](int from, int &pid) {
-        for (; from < p1; ++from) {
-            pid = ptab[from];
-            if (pid >= 0 && pid < g.num_pages)
-                break;
-        }
-        return from;
-    };
+    auto live_page = [&](int pid) { return pid >= 0 && pid < g.num_pages; };   // others are skipped
     auto block_of = [&](int pid) {
         return a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
     };
+    half8_t pf[2], pl[2];
 
     if constexpr (STAGED) {
+        uint8_t *kslot = kslots[wave];
+        uint8_t *vslot = vslots[wave];
+        const StageOffsets so = stage_offsets(g, lane, col, jj);
         // the chunk's page ids, 64 at a time, one per lane
         int base = p0;
         int ids = (p0 + lane < p1) ? ptab[p0 + lane] : -1;
-        auto live_page = [&](int pid) { return pid >= 0 && pid < g.num_pages; };
-        const StageOffsets so = stage_offsets(g, lane, col, jj);
         int pid = p0 < p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
-        if (live_page(pid))
-            stage_page_lds(block_of(pid), so, slot);
+        if (live_page(pid)) {
+            stage_k(block_of(pid), so, kslot);
+            stage_v(block_of(pid), so, vslot);
+        }
         for (int pg = p0; pg < p1; ++pg) {
             const int nxt = pg + 1;
             if (nxt < p1 && nxt - base == 64) {
                 base = nxt;
                 ids = (base + lane < p1) ? ptab[base + lane] : -1;
+                wait_vmem_at_most(0);
             }
-            __builtin_amdgcn_s_waitcnt(kWaitVmem);        // this page is in LDS
-            PageRegs<D> r;
-            read_staged(slot, lane, col, jj, r);
-            __builtin_amdgcn_s_waitcnt(kWaitLds);         // ... and in registers: the slot is free
             const int pid_next = nxt < p1 ? __builtin_amdgcn_readlane(ids, nxt - base) : -1;
-            if (live_page(pid_next))
-                stage_page_lds(block_of(pid_next), so, slot);
-            if (live_page(pid))                           // ids outside the pool are skipped
-                process_page<D>(r, min(kPage, len - pg * kPage), qf, zscale, jj, st);
+            const bool cur = live_page(pid), next = live_page(pid_next);
+            const int valid = min(kPage, len - pg * kPage);
+
+            // K: outstanding now are this page's K then V copies
+            if (cur)
+                wait_vmem_at_most(kCopiesV);
+            KRegs<D> kr;
+            read_k(kslot, lane, jj, kr);
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            if (next)
+                stage_k(block_of(pid_next), so, kslot);
+            if (cur)
+                scores_phase<D>(kr, valid, qf, zscale, jj, st, pf, pl);
+
+            // V: outstanding now are this page's V then the next page's K
+            // copies.  Two pair blocks at a time keep fewer registers live.
+            wait_vmem_at_most(next ? kCopiesK : 0);
+            uint4 vw[2], vs[2];
+            read_v<0, 2>(vslot, lane, col, jj, vw, vs);
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            if (cur)
+                values_phase<D, 0, 2>(vw, vs, valid, jj, pf, pl, st);
+            read_v<2, 2>(vslot, lane, col, jj, vw, vs);
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            if (next)
+                stage_v(block_of(pid_next), so, vslot);
+            if (cur)
+                values_phase<D, 2, 2>(vw, vs, valid, jj, pf, pl, st);
             pid = pid_next;
         }
     } else {
-        int pid = 0;
-        for (int pg = next_page(p0, pid); pg < p1; pg = next_page(pg + 1, pid)) {
-            PageRegs<D> r;
-            load_page_direct<D>(block_of(pid), g, col, jj, r);
-            process_page<D>(r, min(kPage, len - pg * kPage), qf, zscale, jj, st);
+        for (int pg = p0; pg < p1; ++pg) {
+            const int pid = ptab[pg];
+            if (!live_page(pid))
+                continue;
+            const uint8_t *blk = block_of(pid);
+            const int valid = min(kPage, len - pg * kPage);
+            KRegs<D> kr;
+            VRegs<D> vr;
+            load_k_direct<D>(blk, g, col, jj, kr);
+            load_v_direct<D>(blk, g, col, jj, vr);
+            scores_phase<D>(kr, valid, qf, zscale, jj, st, pf, pl);
+            values_phase<D, 0, VRegs<D>::NU>(vr.vw, vr.vs, valid, jj, pf, pl, st);
         }
     }
 
-    // ---- this wave's state into its area: lane (col = query, jj) holds
-    //      channels 2*(16u + 4jj + r) + parity, i.e. 32u + 8jj + 0..7
+    // ---- this wave's state into its merge area: lane (col = query, jj)
+    //      holds channels 2*(16u + 4jj + r) + parity, i.e. 32u + 8jj + 0..7
+    auto area = [&](int w) { return MergeArea<D>(kslots[w], vslots[w]); };
     {
-        const MergeArea<D> ar(slot);
+        const MergeArea<D> ar = area(wave);
         if (col < G) {
-            float *o = ar.o + col * D;
+            float *o = ar.row(col);
 #pragma unroll
             for (int u = 0; u < D / 32; ++u) {
                 const int c0 = 32 * u + 8 * jj;
@@ -471,7 +542,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
             }
         }
     }
-    merge_waves_and_store<D>(smem, kWaveArea, a, b, h, blockIdx.x);
+    merge_waves_and_store<D>(area, a, b, h, blockIdx.x);
 }
 
 }  // namespace

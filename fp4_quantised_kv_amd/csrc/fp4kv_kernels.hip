@@ -331,7 +331,8 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
     }
 
     // ---- this wave's state into its merge area, then one partial per workgroup
-    const MergeArea<D> ar(areas + wave * merge_area_bytes<D>());
+    auto area = [&](int w) { return MergeArea<D>(areas + w * merge_area_bytes<D>()); };
+    const MergeArea<D> ar = area(wave);
 #pragma unroll
     for (int gq = 0; gq < GM; ++gq) {
         const float lt = wave_sum(l[gq]);
@@ -342,9 +343,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
             ar.ml[2 * gq + 1] = lt;
         }
         if (lane < D / 2)
-            *reinterpret_cast<float2 *>(ar.o + gq * D + 2 * lane) = make_float2(o0[gq], o1[gq]);
+            *reinterpret_cast<float2 *>(ar.row(gq) + 2 * lane) = make_float2(o0[gq], o1[gq]);
     }
-    merge_waves_and_store<D>(areas, merge_area_bytes<D>(), a, b, h, blockIdx.x);
+    merge_waves_and_store<D>(area, a, b, h, blockIdx.x);
 }
 
 // Merge the partials of one (sequence, query head): M = max_j m_j,

@@ -23,19 +23,22 @@ constexpr int kGroupThreads = 64 * kWavesPerGroup;
 template <int D>
 constexpr int merge_area_bytes() { return 16 * D * 4 + 16 * 2 * 4; }
 
-// The area of one wave: outputs [16][D], then (max, sum) pairs [16][2].
+// The area of one wave: outputs of query rows 0..7 and the (max, sum) pairs
+// [16][2] in the first block, outputs of rows 8..15 in the second.
 template <int D>
 struct MergeArea {
-    float *o;
-    float *ml;
-    __device__ explicit MergeArea(uint8_t *base) : o(reinterpret_cast<float *>(base)), ml(o + 16 * D) {}
+    float *lo, *hi, *ml;
+    __device__ MergeArea(uint8_t *first, uint8_t *second)
+        : lo(reinterpret_cast<float *>(first)), hi(reinterpret_cast<float *>(second)), ml(lo + 8 * D) {}
+    // one contiguous area of merge_area_bytes<D>()
+    __device__ explicit MergeArea(uint8_t *base) : MergeArea(base, base + 8 * D * 4 + 16 * 2 * 4) {}
+    __device__ float *row(int q) const { return q < 8 ? lo + q * D : hi + (q - 8) * D; }
 };
 
 // Call with every thread of the workgroup, after each wave has filled its
-// area (areas are area_stride bytes apart starting at `areas`).
-template <int D>
-__device__ __forceinline__ void merge_waves_and_store(uint8_t *areas, int area_stride, const DecodeArgs &a,
-                                                      int b, int h, int part)
+// area; area(w) gives wave w's area.
+template <int D, typename AreaOf>
+__device__ __forceinline__ void merge_waves_and_store(AreaOf area, const DecodeArgs &a, int b, int h, int part)
 {
     __syncthreads();
     const int G = a.group;
@@ -45,7 +48,7 @@ __device__ __forceinline__ void merge_waves_and_store(uint8_t *areas, int area_s
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w) {
-            mw[w] = MergeArea<D>(areas + w * area_stride).ml[2 * q];
+            mw[w] = area(w).ml[2 * q];
             M = fmaxf(M, mw[w]);
         }
         float O = 0.0f, L = 0.0f;
@@ -54,9 +57,9 @@ __device__ __forceinline__ void merge_waves_and_store(uint8_t *areas, int area_s
             for (int w = 0; w < kWavesPerGroup; ++w) {
                 if (mw[w] == -INFINITY)
                     continue;
-                const MergeArea<D> ar(areas + w * area_stride);
+                const MergeArea<D> ar = area(w);
                 const float wt = exp2f(mw[w] - M);
-                O = fmaf(ar.o[q * D + c], wt, O);
+                O = fmaf(ar.row(q)[c], wt, O);
                 L = fmaf(ar.ml[2 * q + 1], wt, L);
             }
         }

@@ -169,7 +169,7 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  *                      each sequence's i-th 64-token page.  Ids outside
  *                      [0, num_pages) are skipped (their tokens are not
  *                      attended).
- *   softmax_scale      finite and non-zero (usually 1/sqrt(D)).
+ *   softmax_scale      finite and positive (usually 1/sqrt(D)).
  *   num_splits         as for fp4kv_decode_plan.
  *   workspace          device, 256-B aligned, workspace_bytes >= the plan's.
  *   out                device fp32 [batch][num_q_heads][D], 16-B aligned.

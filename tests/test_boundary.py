@@ -123,6 +123,7 @@ def test_decode_host_checks():
     assert call(hq=8 * 32) == fk.ERR_UNSUPPORTED
     assert call(scale=float("nan")) == fk.ERR_INVALID_ARGUMENT
     assert call(scale=0.0) == fk.ERR_INVALID_ARGUMENT
+    assert call(scale=-0.1) == fk.ERR_INVALID_ARGUMENT
     assert call(q=ok + 2) == fk.ERR_MISALIGNED
     assert call(ws=ok + 64) == fk.ERR_MISALIGNED
     assert call(cache=ok + 128) == fk.ERR_MISALIGNED
