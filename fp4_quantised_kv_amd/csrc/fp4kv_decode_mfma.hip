@@ -218,8 +218,12 @@ __device__ __forceinline__ void scores_phase(const KRegs<D> &r, int valid, const
 }
 
 // Value accumulation of pair blocks [U0, U0 + N) of one page: tile (u,
-// parity) rows are channels 2*(16u + row) + parity.  Scales of tokens at or
-// past `valid` are zeroed, so never-written slots contribute exact zeros.
+// parity) rows are channels 32u + 2*row + parity.  A lane holds, for its
+// channels c = 32u + 2*col and c + 1, the code dwords of tokens 16jj + 0..7
+// and + 8..15 (two tokens per byte, in token order), and the scales of those
+// 16 tokens; each conversion yields two consecutive tokens of one channel,
+// exactly an MFMA operand pair.  Scales of tokens at or past `valid` are
+// zeroed, so never-written slots contribute exact zeros.
 template <int D, int U0, int N>
 __device__ __forceinline__ void values_phase(const uint4 (&vw)[N], uint4 (&vs)[N], int valid, int jj,
                                              const half8_t (&pf)[2], const half8_t (&pl)[2], SplitState<D> &st)
@@ -241,11 +245,11 @@ __device__ __forceinline__ void values_phase(const uint4 (&vw)[N], uint4 (&vs)[N
         float4_t &ao = st.acc[2 * (U0 + u) + 1];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            half4_t e0, o0, e1, o1;
-            v_operand4(cw[2 * kt], fp8x2<false>(sw[2 * kt]), fp8x2<true>(sw[2 * kt]), e0, o0);
-            v_operand4(cw[2 * kt + 1], fp8x2<false>(sw[2 * kt + 1]), fp8x2<true>(sw[2 * kt + 1]), e1, o1);
-            const half8_t ev = __builtin_shufflevector(e0, e1, 0, 1, 2, 3, 4, 5, 6, 7);
-            const half8_t od = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const half8_t sc = cat(fp8x2<false>(sw[2 * kt]), fp8x2<true>(sw[2 * kt]),
+                                   fp8x2<false>(sw[2 * kt + 1]), fp8x2<true>(sw[2 * kt + 1]));
+            const uint32_t we = cw[kt], wo = cw[2 + kt];
+            const half8_t ev = cat(fp4x2<0>(we), fp4x2<1>(we), fp4x2<2>(we), fp4x2<3>(we)) * sc;
+            const half8_t od = cat(fp4x2<0>(wo), fp4x2<1>(wo), fp4x2<2>(wo), fp4x2<3>(wo)) * sc;
             ae = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pf[kt], ae, 0, 0, 0);
             ae = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pl[kt], ae, 0, 0, 0);
             ao = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pf[kt], ao, 0, 0, 0);
@@ -279,14 +283,16 @@ __device__ __forceinline__ void load_k_direct(const uint8_t *blk, const CacheGeo
     }
 }
 
+// V codes: row (slice jj, channel c) of 8 bytes at (jj*D + c)*8; V scales:
+// row (slice jj, block) of 16 bytes at (jj*D/16 + block)*16.
 template <int D>
 __device__ __forceinline__ void load_v_direct(const uint8_t *blk, const CacheGeom &g, int col, int jj, VRegs<D> &r)
 {
 #pragma unroll
     for (int u = 0; u < VRegs<D>::NU; ++u) {
-        const int pair = 16 * u + col;
-        r.vw[u] = *reinterpret_cast<const uint4 *>(blk + g.v_codes_off + pair * kPage + 16 * jj);
-        r.vs[u] = *reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (pair >> 3) * kPage + 16 * jj);
+        const int c = 32 * u + 2 * col;
+        r.vw[u] = *reinterpret_cast<const uint4 *>(blk + g.v_codes_off + (jj * D + c) * 8);
+        r.vs[u] = *reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (jj * (D / 16) + (c >> 4)) * 16);
     }
 }
 
@@ -298,7 +304,7 @@ __device__ __forceinline__ void load_v_direct(const uint8_t *blk, const CacheGeo
 //   K slot [0, 4096): tile t at t*1024, lane l's 16 code bytes at l*16;
 //          [4096, 5120): tile t's scale dwords at 4096 + t*256 + l*4.
 //   V slot [0, 4096): pair block u at u*1024, lane l at l*16;
-//          [4096, 4608): the page's V scale plane [8 blocks][64 tokens].
+//          [4096, 4608): the page's V scale plane [4 slices][8 blocks][16].
 constexpr int kKSlotBytes = 5120;
 constexpr int kVSlotBytes = 4608;
 constexpr int kCopiesK = 8;               // direct-to-LDS instructions per K copy
@@ -314,13 +320,13 @@ __device__ __forceinline__ StageOffsets stage_offsets(const CacheGeom &g, int la
     const uint32_t tok0 = static_cast<uint32_t>(tile_token(0, col));
     o.k = static_cast<uint32_t>(g.k_codes_off) + tok0 * 64u + jj * 16u;
     o.ks = static_cast<uint32_t>(g.k_scales_off) + tok0 * 8u + (jj >> 1) * 4u;
-    o.v = static_cast<uint32_t>(g.v_codes_off) + col * static_cast<uint32_t>(kPage) + 16u * jj;
+    o.v = static_cast<uint32_t>(g.v_codes_off) + (jj * 128u + 2u * col) * 8u;
     o.vs = static_cast<uint32_t>(g.v_scales_off) + lane * 4u;
     return o;
 }
 
 // Tile t's token rows are 4t past tile 0's: +256 bytes of K codes, +32 of
-// K scales; V pair block u is 16 pairs (1024 bytes) past block 0.
+// K scales; V pair block u is 32 channels (256 bytes) past block 0.
 __device__ __forceinline__ void stage_k(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
 {
     const uint8_t *k = blk + o.k, *ks = blk + o.ks;
@@ -336,7 +342,7 @@ __device__ __forceinline__ void stage_v(const uint8_t *blk, const StageOffsets &
     const uint8_t *v = blk + o.v, *vs = blk + o.vs;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_global_load_lds(v + 1024 * u, slot + u * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(v + 256 * u, slot + u * 1024, 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_global_load_lds(vs + 256 * i, slot + 4096 + i * 256, 4, 0, 0);
@@ -359,7 +365,7 @@ __device__ __forceinline__ void read_v(const uint8_t *slot, int lane, int col, i
 #pragma unroll
     for (int u = 0; u < N; ++u) {
         vw[u] = *reinterpret_cast<const uint4 *>(slot + (U0 + u) * 1024 + lane * 16);
-        vs[u] = *reinterpret_cast<const uint4 *>(slot + 4096 + (2 * (U0 + u) + (col >> 3)) * kPage + 16 * jj);
+        vs[u] = *reinterpret_cast<const uint4 *>(slot + 4096 + (jj * 8 + 2 * (U0 + u) + (col >> 3)) * 16);
     }
 }
 

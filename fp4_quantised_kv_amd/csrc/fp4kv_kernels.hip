@@ -22,6 +22,7 @@ namespace fp4kv {
 namespace {
 
 constexpr int kPage = 64;                 // tokens per page == lanes per wave
+constexpr int64_t kRunKernelMinTokens = 512;   // appends this long use 8-token runs
 
 // ------------------------------------------------------------ format helpers
 
@@ -117,58 +118,152 @@ __device__ __forceinline__ void quantize_block16(const uint32_t w[8], uint32_t &
 
 // -------------------------------------------------------- quantise / append
 
-// One thread per (token, KV head, 16-channel block).  Consecutive threads
-// read consecutive 32-byte blocks of the bf16 rows, so loads are coalesced.
-// K codes go to the token's row in the page; V codes are stored transposed
-// (byte (channel pair, token)), so a thread writes its 8 V bytes at a stride
-// of 64 bytes and the wave's lanes for consecutive tokens fill each 64-byte
-// row together.
+// Page-local placement of V.  Codes: the page's 64 tokens form 4 slices of
+// 16; row (slice, channel) is 8 bytes and byte b holds tokens 2b (low nibble)
+// and 2b + 1 (high nibble) of the slice.  Scales: row (slice, 16-channel
+// block) is 16 bytes, one per token of the slice.
 template <int D>
-__global__ __launch_bounds__(256) void quantize_append_kernel(
+__device__ __forceinline__ int v_code_row(int t, int c) { return ((t >> 4) * D + c) * 8; }
+template <int D>
+__device__ __forceinline__ int v_scale_byte(int t, int blk) { return ((t >> 4) * (D / 16) + blk) * 16 + (t & 15); }
+
+__device__ __forceinline__ void load_block16(const uint16_t *src, uint32_t w[8])
+{
+    const uint4 *p = reinterpret_cast<const uint4 *>(src);
+    const uint4 x0 = p[0], x1 = p[1];
+    w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+    w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+}
+
+// K of one token's 16-channel block: its 8 code bytes and its scale byte.
+template <int D>
+__device__ __forceinline__ void append_k(uint8_t *base, const CacheGeom &g, int off, int blk, const uint16_t *src)
+{
+    uint32_t w[8], lo, hi, sc;
+    load_block16(src, w);
+    quantize_block16(w, lo, hi, sc);
+    *reinterpret_cast<uint2 *>(base + g.k_codes_off + off * (D / 2) + 8 * blk) = make_uint2(lo, hi);
+    base[g.k_scales_off + off * (D / 16) + blk] = static_cast<uint8_t>(sc);
+}
+
+// V of one token's block, placed nibble by nibble.  A code byte is shared
+// with the neighbouring token, which another thread of the same call may be
+// writing, so each nibble is changed with one atomic XOR of (old ^ new) on its
+// dword.  The old nibble comes from a plain load: no other thread writes this
+// token's nibble, so the load sees its current value whatever happens to the
+// other nibbles, and XORs on disjoint bits commute.
+template <int D>
+__device__ __forceinline__ void append_v_token(uint8_t *base, const CacheGeom &g, int off, int blk,
+                                               const uint16_t *src)
+{
+    uint32_t w[8], lo, hi, sc;
+    load_block16(src, w);
+    quantize_block16(w, lo, hi, sc);
+    const int shift = 4 * (off & 7);
+    const int word = ((off & 15) >> 3) * 4;
+    uint32_t *dw[16];
+    uint32_t cur[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        dw[i] = reinterpret_cast<uint32_t *>(base + g.v_codes_off + v_code_row<D>(off, 16 * blk + i) + word);
+        cur[i] = *dw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t nib = ((i < 8 ? lo : hi) >> (4 * (i & 7))) & 0xFu;
+        atomicXor(dw[i], (((cur[i] >> shift) ^ nib) & 0xFu) << shift);
+    }
+    base[g.v_scales_off + v_scale_byte<D>(off, blk)] = static_cast<uint8_t>(sc);
+}
+
+// One thread per (token, KV head, 16-channel block); for small appends such
+// as one token per sequence.  Consecutive threads read consecutive 32-byte
+// blocks of the bf16 rows.
+template <int D>
+__global__ __launch_bounds__(256) void append_tokens_kernel(
     CacheGeom g, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t n_tokens,
     const int64_t *__restrict__ slots, uint8_t *__restrict__ cache)
 {
-    constexpr int NB = D / 16;                          // blocks per row
+    constexpr int NB = D / 16;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t total = n_tokens * g.num_kv_heads * NB;
-    if (idx >= total)
+    if (idx >= n_tokens * g.num_kv_heads * NB)
         return;
     const int blk = static_cast<int>(idx % NB);
     const int64_t th = idx / NB;                        // token * H_kv + head
     const int head = static_cast<int>(th % g.num_kv_heads);
-    const int64_t tok = th / g.num_kv_heads;
-    const int64_t slot = slots[tok];
+    const int64_t slot = slots[th / g.num_kv_heads];
     if (slot < 0 || slot >= g.num_pages * kPage)
         return;                                         // padding or out of range: skipped
-    const int64_t page = slot / kPage;
+    uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
     const int off = static_cast<int>(slot % kPage);
-    uint8_t *base = cache + page * g.page_stride + head * g.head_stride;
-    const int64_t src = th * D + 16 * blk;
+    append_k<D>(base, g, off, blk, k + th * D + 16 * blk);
+    append_v_token<D>(base, g, off, blk, v + th * D + 16 * blk);
+}
 
-    uint32_t w[8], lo, hi, sc;
-    {
-        const uint4 *p = reinterpret_cast<const uint4 *>(k + src);
-        const uint4 x0 = p[0], x1 = p[1];
-        w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
-        w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
-        quantize_block16(w, lo, hi, sc);
-        *reinterpret_cast<uint2 *>(base + g.k_codes_off + off * (D / 2) + 8 * blk) = make_uint2(lo, hi);
-        base[g.k_scales_off + off * NB + blk] = static_cast<uint8_t>(sc);
-    }
-    {
-        const uint4 *p = reinterpret_cast<const uint4 *>(v + src);
-        const uint4 x0 = p[0], x1 = p[1];
-        w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
-        w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
-        quantize_block16(w, lo, hi, sc);
-        uint8_t *vc = base + g.v_codes_off + (8 * blk) * kPage + off;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t word = i < 4 ? lo : hi;
-            vc[i * kPage] = static_cast<uint8_t>(word >> (8 * (i & 3)));
+// One thread per (run of 8 consecutive input tokens, KV head, 16-channel
+// block); for prefills and other long appends.  When the run's slots are 8
+// consecutive slots starting at a multiple of 8, the thread owns whole V code
+// dwords (8 tokens of one channel) and whole 8-byte scale runs, and writes
+// them with plain stores; otherwise it places each token as the per-token
+// kernel does.
+template <int D>
+__global__ __launch_bounds__(256) void append_runs_kernel(
+    CacheGeom g, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t n_tokens,
+    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache)
+{
+    constexpr int NB = D / 16;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t n_runs = (n_tokens + 7) / 8;
+    if (idx >= n_runs * g.num_kv_heads * NB)
+        return;
+    const int blk = static_cast<int>(idx % NB);
+    const int64_t rh = idx / NB;                        // run * H_kv + head
+    const int head = static_cast<int>(rh % g.num_kv_heads);
+    const int64_t t0 = (rh / g.num_kv_heads) * 8;
+    const int n = static_cast<int>(n_tokens - t0 < 8 ? n_tokens - t0 : 8);
+    const int64_t s0 = slots[t0];
+    bool whole = n == 8 && s0 >= 0 && s0 % 8 == 0 && s0 + 8 <= g.num_pages * kPage;
+    for (int i = 1; i < n && whole; ++i)
+        whole = slots[t0 + i] == s0 + i;
+
+    const int64_t row_stride = static_cast<int64_t>(g.num_kv_heads) * D;   // one input token
+    const uint16_t *ksrc = k + t0 * row_stride + head * D + 16 * blk;
+    const uint16_t *vsrc = v + t0 * row_stride + head * D + 16 * blk;
+    if (!whole) {
+        for (int i = 0; i < n; ++i) {
+            const int64_t slot = slots[t0 + i];
+            if (slot < 0 || slot >= g.num_pages * kPage)
+                continue;
+            uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
+            const int off = static_cast<int>(slot % kPage);
+            append_k<D>(base, g, off, blk, ksrc + i * row_stride);
+            append_v_token<D>(base, g, off, blk, vsrc + i * row_stride);
         }
-        base[g.v_scales_off + blk * kPage + off] = static_cast<uint8_t>(sc);
+        return;
     }
+    uint8_t *base = cache + (s0 / kPage) * g.page_stride + head * g.head_stride;
+    const int off0 = static_cast<int>(s0 % kPage);
+    uint32_t vd[16];                                    // channel 16*blk + i, tokens off0 .. off0 + 7
+    uint32_t vs[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        vd[i] = 0u;
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) {
+        append_k<D>(base, g, off0 + i, blk, ksrc + i * row_stride);
+        uint32_t w[8], lo, hi, sc;
+        load_block16(vsrc + i * row_stride, w);
+        quantize_block16(w, lo, hi, sc);
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            vd[c] |= (((c < 8 ? lo : hi) >> (4 * (c & 7))) & 0xFu) << (4 * i);
+        vs[i >> 2] |= sc << (8 * (i & 3));
+    }
+    const int word = ((off0 & 15) >> 3) * 4;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        *reinterpret_cast<uint32_t *>(base + g.v_codes_off + v_code_row<D>(off0, 16 * blk + c) + word) = vd[c];
+    *reinterpret_cast<uint2 *>(base + g.v_scales_off + v_scale_byte<D>(off0, blk)) = make_uint2(vs[0], vs[1]);
 }
 
 // ----------------------------------------------------------------- decode
@@ -203,9 +298,9 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b)
 //           dot, which is the same sum regrouped);
 //   softmax: running max per query head from a wave reduction, rescale factor
 //           alpha = 2^(m_old - m_new), probabilities p = 2^(z - m_new) into LDS;
-//   values: lane = channel pair; the lane reads its transposed V row (64
-//           token bytes and the 64 scales of its channel block) and
-//           accumulates p * v for both channels of the pair.
+//   values: lane = channel pair; the lane reads its two channels' V codes
+//           and its block's scales slice by slice and accumulates p * v for
+//           both channels of the pair.
 template <int D, int GM>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
 {
@@ -299,23 +394,23 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- values, lane = channel pair (D/2 lanes), 16 tokens per chunk
+        // ---- values, lane = channel pair (D/2 lanes), one 16-token slice at a
+        //      time: channel 2*lane's 8 code bytes then channel 2*lane + 1's,
+        //      two tokens per byte, and the 16 scales of the pair's block
         if (lane < D / 2) {
-            const uint4 *vrow = reinterpret_cast<const uint4 *>(blk + g.v_codes_off + lane * kPage);
-            const uint4 *vsrow = reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (lane >> 3) * kPage);
 #pragma unroll 1
             for (int ch = 0; ch < kPage / 16; ++ch) {
                 if (16 * ch >= valid)
                     break;
-                const uint4 vc = vrow[ch], vs = vsrow[ch];
-                const uint32_t cw[4] = {vc.x, vc.y, vc.z, vc.w};
+                const uint4 vc = *reinterpret_cast<const uint4 *>(blk + g.v_codes_off + (ch * D + 2 * lane) * 8);
+                const uint4 vs = *reinterpret_cast<const uint4 *>(blk + g.v_scales_off + (ch * NB + (lane >> 3)) * 16);
+                const uint32_t ce[2] = {vc.x, vc.y}, co[2] = {vc.z, vc.w};
                 const uint32_t sw[4] = {vs.x, vs.y, vs.z, vs.w};
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const uint32_t byte = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
                     const float s = e4m3_value((sw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-                    const float ve = e2m1_value(byte) * s;
-                    const float vo = e2m1_value(byte >> 4) * s;
+                    const float ve = e2m1_value(ce[i >> 3] >> (4 * (i & 7))) * s;
+                    const float vo = e2m1_value(co[i >> 3] >> (4 * (i & 7))) * s;
 #pragma unroll
                     for (int gq = 0; gq < GM; ++gq) {
                         const float p = p_s[gq][16 * ch + i];
@@ -413,14 +508,20 @@ hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const u
                                   int64_t n_tokens, const int64_t *slots, uint8_t *cache,
                                   hipStream_t stream)
 {
-    const int64_t total = n_tokens * g.num_kv_heads * (g.head_dim / 16);
-    const int64_t blocks = (total + 255) / 256;
-    if (g.head_dim == 64)
-        quantize_append_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(
-            g, k, v, n_tokens, slots, cache);
-    else
-        quantize_append_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(
-            g, k, v, n_tokens, slots, cache);
+    const int64_t per_token = static_cast<int64_t>(g.num_kv_heads) * (g.head_dim / 16);
+    if (n_tokens >= kRunKernelMinTokens) {
+        const int64_t blocks = ((n_tokens + 7) / 8 * per_token + 255) / 256;
+        if (g.head_dim == 64)
+            append_runs_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+        else
+            append_runs_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+    } else {
+        const int64_t blocks = (n_tokens * per_token + 255) / 256;
+        if (g.head_dim == 64)
+            append_tokens_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+        else
+            append_tokens_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+    }
     return hipGetLastError();
 }
 

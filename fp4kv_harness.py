@@ -75,43 +75,43 @@ def build_cache(w: wl.Workload, seed: int, device="cuda", keep_seqs=(), extra_to
                     pt, lens, kept)
 
 
-def read_page(cache_cpu: np.ndarray, layout: fk.CacheLayout, page: int, head: int):
-    """Token-major view of one (page, KV head) block:
-    K code bytes [64][D/2], K scales [64][D/16], V code bytes [64][D/2],
-    V scales [64][D/16] (the V planes are stored transposed and are turned
-    back here)."""
-    D = layout.head_dim
-    base = page * layout.page_stride + head * layout.head_stride
-    blk = cache_cpu[base:base + layout.block_bytes]
-    kc = blk[layout.k_codes_offset:layout.k_codes_offset + 64 * D // 2].reshape(64, D // 2)
-    ks = blk[layout.k_scales_offset:layout.k_scales_offset + 64 * D // 16].reshape(64, D // 16)
-    vc = blk[layout.v_codes_offset:layout.v_codes_offset + 64 * D // 2].reshape(D // 2, 64).T
-    vs = blk[layout.v_scales_offset:layout.v_scales_offset + 64 * D // 16].reshape(D // 16, 64).T
-    return kc, ks, vc, vs
+def _v_token_major(codes_plane: np.ndarray, scales_plane: np.ndarray, D: int):
+    """V planes of pages [P][H][...] in the stored order -> token-major
+    (code bytes [P][H][64][D/2] with channel 2i in the low nibble, scales
+    [P][H][64][D/16]).  Stored: codes row (slice, channel) of 8 bytes, two
+    tokens per byte (even token low); scales row (slice, block) of 16."""
+    P, H = codes_plane.shape[:2]
+    c = codes_plane.reshape(P, H, 4, D, 8)                          # slice, channel, byte
+    nib = np.stack([c & 0xF, c >> 4], axis=-1).reshape(P, H, 4, D, 16)   # slice, channel, token-in-slice
+    nib = nib.transpose(0, 1, 2, 4, 3).reshape(P, H, 64, D)          # token, channel
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    s = scales_plane.reshape(P, H, 4, D // 16, 16).transpose(0, 1, 2, 4, 3).reshape(P, H, 64, D // 16)
+    return packed, s
 
 
 def read_pages(cache: torch.Tensor, layout: fk.CacheLayout, pages, n_tokens: int):
     """Stored bytes of the first n_tokens slots of a list of pages (all KV
     heads), token-major: K code bytes [n][H][D/2], K scales [n][H][D/16], V
-    code bytes [n][H][D/2], V scales [n][H][D/16].  Only those pages are
-    copied off the device."""
+    code bytes [n][H][D/2], V scales [n][H][D/16] (two codes per byte,
+    channel 2i in the low nibble).  Only those pages are copied off the
+    device."""
     H, D = layout.num_kv_heads, layout.head_dim
     idx = torch.as_tensor(np.asarray(pages, np.int64), device=cache.device)
     blocks = cache[: layout.cache_bytes].view(-1, H, layout.block_bytes)[idx].cpu().numpy()
     P = len(pages)
 
-    def plane(off, rows, cols, transposed):
-        x = blocks[:, :, off:off + rows * cols]
-        if transposed:                       # stored [cols][64 tokens]
-            x = x.reshape(P, H, cols, rows).transpose(0, 3, 1, 2)
-        else:                                # stored [64 tokens][cols]
-            x = x.reshape(P, H, rows, cols).transpose(0, 2, 1, 3)
-        return np.ascontiguousarray(x.reshape(P * rows, H, cols)[:n_tokens])
+    def plane(off, size):
+        return blocks[:, :, off:off + size]
 
-    return (plane(layout.k_codes_offset, 64, D // 2, False),
-            plane(layout.k_scales_offset, 64, D // 16, False),
-            plane(layout.v_codes_offset, 64, D // 2, True),
-            plane(layout.v_scales_offset, 64, D // 16, True))
+    kc = plane(layout.k_codes_offset, 64 * D // 2).reshape(P, H, 64, D // 2)
+    ks = plane(layout.k_scales_offset, 64 * D // 16).reshape(P, H, 64, D // 16)
+    vc, vs = _v_token_major(plane(layout.v_codes_offset, 64 * D // 2),
+                            plane(layout.v_scales_offset, 64 * D // 16), D)
+
+    def tok(x):
+        return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(P * 64, H, x.shape[-1])[:n_tokens])
+
+    return tok(kc), tok(ks), tok(vc), tok(vs)
 
 
 def row_rel_error(out: np.ndarray, ref: np.ndarray) -> np.ndarray:

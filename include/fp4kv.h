@@ -79,16 +79,20 @@ typedef struct fp4kv_cache_params {
  * The cache is num_pages pages; a page holds one block per KV head; a block
  * (page p, KV head h) starts at p*page_stride + h*head_stride and holds the
  * page's 64 token slots:
- *   K codes   [64 tokens][D/2] bytes  at k_codes_offset  (token-major rows)
- *   K scales  [64 tokens][D/16]       at k_scales_offset
- *   V codes   [D/2][64 tokens] bytes  at v_codes_offset  (channel-pair-major)
- *   V scales  [D/16][64 tokens]       at v_scales_offset
- * A code byte holds two E2M1 codes of one token: channel 2i in the low nibble
- * and channel 2i+1 in the high nibble; a nibble is sign << 3 | magnitude code
- * (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  A scale byte is an E4M3 code
- * (never 0: a zero scale is stored as the smallest subnormal 2^-9).  Token
- * slot s lives in page s / 64 at offset s % 64.  V is stored transposed in
- * the page so decode reads each channel pair's tokens contiguously. */
+ *   K codes   [64 tokens][D/2] bytes       at k_codes_offset: byte i of a
+ *             token's row holds channel 2i (low nibble) and 2i+1 (high)
+ *   K scales  [64 tokens][D/16]            at k_scales_offset
+ *   V codes   [4 slices][D channels][8]    at v_codes_offset: slice j holds
+ *             tokens 16j .. 16j+15; byte b of row (j, c) holds channel c of
+ *             tokens 16j+2b (low nibble) and 16j+2b+1 (high)
+ *   V scales  [4 slices][D/16 blocks][16]  at v_scales_offset: byte t of row
+ *             (j, block) is the scale of token 16j+t
+ * A nibble is sign << 3 | magnitude code (magnitudes 0, 0.5, 1, 1.5, 2, 3,
+ * 4, 6).  A scale byte is an E4M3 code (never 0: a zero scale is stored as
+ * the smallest subnormal 2^-9).  Token slot s lives in page s / 64 at
+ * offset s % 64.  V is stored channel-major in 16-token slices so that the
+ * decode kernels read each channel's tokens contiguously and convert two
+ * consecutive tokens of one channel per instruction. */
 typedef struct fp4kv_cache_layout_t {
     fp4kv_cache_params params;
     int64_t block_bytes;                  /* 64 * D * 9 / 8 */
@@ -115,7 +119,9 @@ FP4KV_API int fp4kv_cache_layout(const fp4kv_cache_params *params, fp4kv_cache_l
  * x/scale, saturating at 6, sign kept, also for a zero magnitude.  The
  * quantised K and V are what attention later reads, in place of the real
  * ones.)  A block never spans tokens, so appending never rewrites older
- * tokens and the bytes of a token do not depend on the order of calls.
+ * tokens and the bytes of a token do not depend on the order of calls or on
+ * which tokens share a call (V code bytes shared by two tokens are updated
+ * nibble-wise with atomics unless one call covers both).
  *   layout        host, from fp4kv_cache_layout (re-checked).
  *   k, v          device bf16 [n_tokens][H_kv][D], contiguous, 16-B aligned.
  *   n_tokens      >= 0; 0 is a no-op (pointers may then be NULL).

@@ -165,6 +165,36 @@ def test_append_order_does_not_matter():
     assert torch.equal(ref, c2)
 
 
+@pytest.mark.parametrize("first_slot,n", [(3, 1000), (8, 600), (0, 515), (64, 4096)])
+def test_contiguous_runs_aligned_or_not(first_slot, n):
+    """Long appends take 8-token runs: aligned runs are written whole,
+    misaligned or partial ones nibble by nibble; both give the oracle's bytes
+    and leave the neighbouring slots untouched."""
+    w = wl.WORKLOADS["gqa4_b8_ctx4k"]
+    k = wl.kv_tokens(w, 8, 0, "k", 0, n)
+    v = wl.kv_tokens(w, 8, 0, "v", 0, n)
+    pages = -(-(first_slot + n + 1) // 64)
+    layout = fk.cache_layout(w.kv_heads, w.head_dim, pages)
+    cache = torch.full((layout.cache_bytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    slots = torch.arange(first_slot, first_slot + n, dtype=torch.int64)
+    _say(f"quantize_append: {n} tokens from slot {first_slot}")
+    fk.quantize_append(layout, k.cuda(), v.cuda(), slots.cuda(), cache)
+    torch.cuda.synchronize()
+    kc, ks, vc, vs = hx.read_pages(cache, layout, list(range(pages)), pages * 64)
+    ek, eks = _expect(k)
+    ev, evs = _expect(v)
+    sl = slice(first_slot, first_slot + n)
+    assert np.array_equal(kc[sl], ek) and np.array_equal(ks[sl], eks)
+    assert np.array_equal(vc[sl], ev) and np.array_equal(vs[sl], evs)
+    # V bytes of untouched slots: each stored byte mixes two tokens, so check
+    # the neighbours' nibbles through the token-major view
+    for s in (first_slot - 1, first_slot + n):
+        if 0 <= s < pages * 64:
+            assert (vs[s] == 0x5A).all() and (ks[s] == 0x5A).all()
+            nib = 0xA if s % 2 == 0 else 0x5          # even tokens sit in the low nibble
+            assert (vc[s] == (nib | nib << 4)).all()
+
+
 def test_skipped_slots_leave_bytes_untouched():
     w = wl.WORKLOADS["gqa4_b8_ctx4k"]
     k = wl.kv_tokens(w, 6, 0, "k", 0, 6)
@@ -183,6 +213,8 @@ def test_skipped_slots_leave_bytes_untouched():
             assert np.array_equal(kc[s], ek[written[s]]) and np.array_equal(ks[s], eks[written[s]])
         else:
             assert (kc[s] == 0xA5).all() and (vs[s] == 0xA5).all()
+            nib = 0x5 if s % 2 == 0 else 0xA          # even tokens sit in the low nibble
+            assert (vc[s] == (nib | nib << 4)).all()
 
 
 def test_zero_tokens_is_a_no_op():
