@@ -91,6 +91,33 @@ def cpu_baseline(w, seed, threads):
                       f"decode attention from the oracle's own codes in fp64, {dt:.2f} s wall"}
 
 
+def prefill_append(fk, wl, seed, dev, stream, reps=10):
+    """quantize_append of the prefill workload (8 sequences x 8192 tokens,
+    H_kv 8, D 128, contiguous slots) as one call; bf16 K, V read + packed
+    bytes written, per call."""
+    import torch
+    w = wl.WORKLOADS["prefill_b8_8k"]
+    fkk, fvv = wl.channel_factors(w, seed, "k"), wl.channel_factors(w, seed, "v")
+    k = torch.cat([wl.kv_tokens(w, seed, b, "k", 0, w.context, fkk) for b in range(w.batch)]).to(dev)
+    v = torch.cat([wl.kv_tokens(w, seed, b, "v", 0, w.context, fvv) for b in range(w.batch)]).to(dev)
+    n = k.shape[0]
+    layout = fk.cache_layout(w.kv_heads, w.head_dim, -(-n // 64))
+    cache = torch.empty(layout.cache_bytes, dtype=torch.uint8, device=dev)
+    slots = torch.arange(n, dtype=torch.int64, device=dev)
+    fk.quantize_append(layout, k, v, slots, cache)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fk.quantize_append(layout, k, v, slots, cache)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    bytes_ = 2 * k.numel() * 2 + layout.cache_bytes + n * 8
+    return {"workload": w.name, "tokens": n, "ms": round(ms, 5), "gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
+            "algorithmic_bytes": bytes_}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +129,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="also time a plain 2 GiB streaming read (torch sum) as the achievable-bandwidth reference")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill quantise-append measurement (8 x 8192 tokens)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with one 1 GiB device copy, the known-size kernel for scaling HBM counters")
     args = ap.parse_args()
@@ -235,6 +264,8 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes)},
     }
+    if not args.no_prefill:
+        result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)
     if args.hbm_probe:
         x = torch.ones(1 << 29, dtype=torch.float32, device=dev)     # 2 GiB
         for _ in range(3):

@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
 {
     constexpr int NB = D / 16;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the page loop scalar
     const int sp = blockIdx.x * kWavesPerGroup + wave;
     const int h = blockIdx.y, b = blockIdx.z;
     const int G = a.group;
