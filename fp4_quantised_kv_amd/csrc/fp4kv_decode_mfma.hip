@@ -82,19 +82,6 @@ __device__ __forceinline__ half8_t k_operand(uint32_t w, half2_t s)
            __builtin_shufflevector(s, s, 0, 1, 0, 1, 0, 1, 0, 1);
 }
 
-// Four tokens' code bytes of one channel pair (one dword) with their scales
-// (s01 = tokens 0,1; s23 = tokens 2,3) -> the even channel's and the odd
-// channel's values for those tokens, in token order.
-__device__ __forceinline__ void v_operand4(uint32_t w, half2_t s01, half2_t s23, half4_t &even, half4_t &odd)
-{
-    const half2_t t0 = fp4x2<0>(w), t1 = fp4x2<1>(w), t2 = fp4x2<2>(w), t3 = fp4x2<3>(w);
-    const half4_t e = {t0[0], t1[0], t2[0], t3[0]};
-    const half4_t o = {t0[1], t1[1], t2[1], t3[1]};
-    const half4_t s = __builtin_shufflevector(s01, s23, 0, 1, 2, 3);
-    even = e * s;
-    odd = o * s;
-}
-
 // Max over the four lanes l, l^16, l^32, l^48 (one query column of a C
 // tile), with the gfx950 lane-swap instructions instead of LDS shuffles.
 __device__ __forceinline__ float xor_max(float x)
@@ -199,6 +186,11 @@ __device__ __forceinline__ void scores_phase(const KRegs<D> &r, int valid, const
     // p = hi + lo with both parts in fp16 (hi truncated, lo the truncated
     // remainder): the value and denominator products see p to ~2^-21
     // relative, so fp16 operands cost no accuracy against fp32.
+    // -1 held in a register the compiler cannot see through, so that
+    // p - float(hi) stays one mixed-precision FMA instead of a conversion
+    // and a subtraction
+    float minus_one = -1.0f;
+    asm volatile("" : "+s"(minus_one));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
         float p[8], q[8];
@@ -210,52 +202,53 @@ __device__ __forceinline__ void scores_phase(const KRegs<D> &r, int valid, const
         pf[kt] = cat(pk_rtz(p[0], p[1]), pk_rtz(p[2], p[3]), pk_rtz(p[4], p[5]), pk_rtz(p[6], p[7]));
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            q[e] = p[e] - static_cast<float>(pf[kt][e]);
+            q[e] = __builtin_fmaf(static_cast<float>(pf[kt][e]), minus_one, p[e]);
         pl[kt] = cat(pk_rtz(q[0], q[1]), pk_rtz(q[2], q[3]), pk_rtz(q[4], q[5]), pk_rtz(q[6], q[7]));
         st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[kt], st.lacc, 0, 0, 0);
         st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pl[kt], st.lacc, 0, 0, 0);
     }
 }
 
-// Value accumulation of pair blocks [U0, U0 + N) of one page: tile (u,
+// Value accumulation of pair blocks [u0, u0 + N) of one page: tile (u,
 // parity) rows are channels 32u + 2*row + parity.  A lane holds, for its
 // channels c = 32u + 2*col and c + 1, the code dwords of tokens 16jj + 0..7
-// and + 8..15 (two tokens per byte, in token order), and the scales of those
-// 16 tokens; each conversion yields two consecutive tokens of one channel,
-// exactly an MFMA operand pair.  Scales of tokens at or past `valid` are
-// zeroed, so never-written slots contribute exact zeros.
-template <int D, int U0, int N>
-__device__ __forceinline__ void values_phase(const uint4 (&vw)[N], uint4 (&vs)[N], int valid, int jj,
+// and + 8..15 (two tokens per byte, in token order), and the fp16 scales of
+// those 16 tokens (sv[u][half]); each conversion yields two consecutive
+// tokens of one channel, exactly an MFMA operand pair.
+template <int D, int N>
+__device__ __forceinline__ void values_phase(int u0, const uint4 (&vw)[N], const half8_t (&sv)[N][2],
                                              const half8_t (&pf)[2], const half8_t (&pl)[2], SplitState<D> &st)
 {
-    if (valid < kPage) {
-#pragma unroll
-        for (int u = 0; u < N; ++u) {
-            vs[u].x = keep_valid_bytes(vs[u].x, 16 * jj + 0, valid);
-            vs[u].y = keep_valid_bytes(vs[u].y, 16 * jj + 4, valid);
-            vs[u].z = keep_valid_bytes(vs[u].z, 16 * jj + 8, valid);
-            vs[u].w = keep_valid_bytes(vs[u].w, 16 * jj + 12, valid);
-        }
-    }
 #pragma unroll
     for (int u = 0; u < N; ++u) {
         const uint32_t cw[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
-        const uint32_t sw[4] = {vs[u].x, vs[u].y, vs[u].z, vs[u].w};
-        float4_t &ae = st.acc[2 * (U0 + u)];
-        float4_t &ao = st.acc[2 * (U0 + u) + 1];
+        float4_t &ae = st.acc[2 * (u0 + u)];
+        float4_t &ao = st.acc[2 * (u0 + u) + 1];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            const half8_t sc = cat(fp8x2<false>(sw[2 * kt]), fp8x2<true>(sw[2 * kt]),
-                                   fp8x2<false>(sw[2 * kt + 1]), fp8x2<true>(sw[2 * kt + 1]));
             const uint32_t we = cw[kt], wo = cw[2 + kt];
-            const half8_t ev = cat(fp4x2<0>(we), fp4x2<1>(we), fp4x2<2>(we), fp4x2<3>(we)) * sc;
-            const half8_t od = cat(fp4x2<0>(wo), fp4x2<1>(wo), fp4x2<2>(wo), fp4x2<3>(wo)) * sc;
+            const half8_t ev = cat(fp4x2<0>(we), fp4x2<1>(we), fp4x2<2>(we), fp4x2<3>(we)) * sv[u][kt];
+            const half8_t od = cat(fp4x2<0>(wo), fp4x2<1>(wo), fp4x2<2>(wo), fp4x2<3>(wo)) * sv[u][kt];
             ae = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pf[kt], ae, 0, 0, 0);
             ae = __builtin_amdgcn_mfma_f32_16x16x32_f16(ev, pl[kt], ae, 0, 0, 0);
             ao = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pf[kt], ao, 0, 0, 0);
             ao = __builtin_amdgcn_mfma_f32_16x16x32_f16(od, pl[kt], ao, 0, 0, 0);
         }
     }
+}
+
+// fp16 scales of a lane's 16 tokens (16jj + 0..15) from their 16 E4M3 bytes,
+// zero for tokens at or past `valid` so never-written slots add exact zeros.
+__device__ __forceinline__ void v_scales(uint4 raw, int valid, int jj, half8_t (&sv)[2])
+{
+    if (valid < kPage) {
+        raw.x = keep_valid_bytes(raw.x, 16 * jj + 0, valid);
+        raw.y = keep_valid_bytes(raw.y, 16 * jj + 4, valid);
+        raw.z = keep_valid_bytes(raw.z, 16 * jj + 8, valid);
+        raw.w = keep_valid_bytes(raw.w, 16 * jj + 12, valid);
+    }
+    sv[0] = cat(fp8x2<false>(raw.x), fp8x2<true>(raw.x), fp8x2<false>(raw.y), fp8x2<true>(raw.y));
+    sv[1] = cat(fp8x2<false>(raw.z), fp8x2<true>(raw.z), fp8x2<false>(raw.w), fp8x2<true>(raw.w));
 }
 
 // Page-local token of score tile t, row `row`.
@@ -296,18 +289,19 @@ __device__ __forceinline__ void load_v_direct(const uint8_t *blk, const CacheGeo
     }
 }
 
-// Staged loads for D = 128: direct-to-LDS copies of exactly the bytes each
-// lane will read back, issued a phase ahead of the arithmetic so that no
-// registers are held while the copies are in flight.  K and V have separate
-// LDS slots, so the next page's K copy can start as soon as this page's K
-// operands are in registers, and likewise for V.
+// Staged loads for D = 128: direct-to-LDS copies issued a phase ahead of the
+// arithmetic, so that no registers are held while the copies are in flight.
+// K and V have separate LDS slots, so the next page's K copy can start as
+// soon as this page's K operands are in registers, and likewise for V.
 //   K slot [0, 4096): tile t at t*1024, lane l's 16 code bytes at l*16;
-//          [4096, 5120): tile t's scale dwords at 4096 + t*256 + l*4.
+//          [4096, 4608): the page's K scale plane [64 tokens][8].
 //   V slot [0, 4096): pair block u at u*1024, lane l at l*16;
-//          [4096, 4608): the page's V scale plane [4 slices][8 blocks][16].
-constexpr int kKSlotBytes = 5120;
-constexpr int kVSlotBytes = 4608;
-constexpr int kCopiesK = 8;               // direct-to-LDS instructions per K copy
+//          [4096, 4608): the page's V scale plane [4 slices][8 blocks][16];
+//          [4608, 5632): the same scales converted to fp16 once per page
+//          (each lane converts 8), instead of by every lane that needs them.
+constexpr int kKSlotBytes = 4608;
+constexpr int kVSlotBytes = 5632;
+constexpr int kCopiesK = 6;               // direct-to-LDS instructions per K copy
 constexpr int kCopiesV = 6;               // ... per V copy
 
 struct StageOffsets {
@@ -319,22 +313,24 @@ __device__ __forceinline__ StageOffsets stage_offsets(const CacheGeom &g, int la
     StageOffsets o;
     const uint32_t tok0 = static_cast<uint32_t>(tile_token(0, col));
     o.k = static_cast<uint32_t>(g.k_codes_off) + tok0 * 64u + jj * 16u;
-    o.ks = static_cast<uint32_t>(g.k_scales_off) + tok0 * 8u + (jj >> 1) * 4u;
+    o.ks = static_cast<uint32_t>(g.k_scales_off) + lane * 4u;
     o.v = static_cast<uint32_t>(g.v_codes_off) + (jj * 128u + 2u * col) * 8u;
     o.vs = static_cast<uint32_t>(g.v_scales_off) + lane * 4u;
     return o;
 }
 
-// Tile t's token rows are 4t past tile 0's: +256 bytes of K codes, +32 of
-// K scales; V pair block u is 32 channels (256 bytes) past block 0.
+// Tile t's token rows are 4t past tile 0's (+256 bytes of K codes); V pair
+// block u is 32 channels (256 bytes) past block 0; the scale planes are
+// copied whole, 256 bytes per instruction.
 __device__ __forceinline__ void stage_k(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
 {
     const uint8_t *k = blk + o.k, *ks = blk + o.ks;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t)
         __builtin_amdgcn_global_load_lds(k + 256 * t, slot + t * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ks + 32 * t, slot + 4096 + t * 256, 4, 0, 0);
-    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(ks + 256 * i, slot + 4096 + i * 256, 4, 0, 0);
 }
 
 __device__ __forceinline__ void stage_v(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
@@ -348,24 +344,40 @@ __device__ __forceinline__ void stage_v(const uint8_t *blk, const StageOffsets &
         __builtin_amdgcn_global_load_lds(vs + 256 * i, slot + 4096 + i * 256, 4, 0, 0);
 }
 
-__device__ __forceinline__ void read_k(const uint8_t *slot, int lane, int jj, KRegs<128> &r)
+__device__ __forceinline__ void read_k(const uint8_t *slot, int lane, int col, int jj, KRegs<128> &r)
 {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint4 x = *reinterpret_cast<const uint4 *>(slot + t * 1024 + lane * 16);
         r.kw[t][0] = x.x; r.kw[t][1] = x.y; r.kw[t][2] = x.z; r.kw[t][3] = x.w;
-        const uint32_t sd = *reinterpret_cast<const uint32_t *>(slot + 4096 + t * 256 + lane * 4);
-        r.ks[t] = (jj & 1) ? (sd >> 16) : (sd & 0xFFFFu);
+        r.ks[t] = *reinterpret_cast<const uint16_t *>(slot + 4096 + tile_token(t, col) * 8 + 2 * jj);
     }
 }
 
-template <int U0, int N>
-__device__ __forceinline__ void read_v(const uint8_t *slot, int lane, int col, int jj, uint4 (&vw)[N], uint4 (&vs)[N])
+// Convert the page's V scales to fp16 in the slot: lane l takes bytes
+// 8l .. 8l+7 of the plane, i.e. tokens 16*(l/16) + 8*(l%2) + 0..7.
+__device__ __forceinline__ void convert_v_scales(uint8_t *slot, int lane, int valid)
+{
+    uint2 raw = *reinterpret_cast<const uint2 *>(slot + 4096 + lane * 8);
+    if (valid < kPage) {
+        const int t0 = 16 * (lane >> 4) + 8 * (lane & 1);
+        raw.x = keep_valid_bytes(raw.x, t0, valid);
+        raw.y = keep_valid_bytes(raw.y, t0 + 4, valid);
+    }
+    const half8_t h = cat(fp8x2<false>(raw.x), fp8x2<true>(raw.x), fp8x2<false>(raw.y), fp8x2<true>(raw.y));
+    *reinterpret_cast<half8_t *>(slot + 4608 + lane * 16) = h;
+}
+
+template <int N>
+__device__ __forceinline__ void read_v(const uint8_t *slot, int u0, int lane, int col, int jj, uint4 (&vw)[N],
+                                       half8_t (&sv)[N][2])
 {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-        vw[u] = *reinterpret_cast<const uint4 *>(slot + (U0 + u) * 1024 + lane * 16);
-        vs[u] = *reinterpret_cast<const uint4 *>(slot + 4096 + (jj * 8 + 2 * (U0 + u) + (col >> 3)) * 16);
+        vw[u] = *reinterpret_cast<const uint4 *>(slot + (u0 + u) * 1024 + lane * 16);
+        const half8_t *sp = reinterpret_cast<const half8_t *>(slot + 4608 + (jj * 8 + 2 * (u0 + u) + (col >> 3)) * 32);
+        sv[u][0] = sp[0];
+        sv[u][1] = sp[1];
     }
 }
 
@@ -373,14 +385,80 @@ __device__ __forceinline__ void read_v(const uint8_t *slot, int lane, int col, i
 // memory operations outstanding; and all LDS accesses done.
 __device__ __forceinline__ void wait_vmem_at_most(int n)
 {
-    // the count is a compile-time constant at every call site
-    switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case kCopiesV: __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesV); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesK); break;
-    }
+    static_assert(kCopiesK == kCopiesV, "one immediate serves both waits");
+    // the count is one of two compile-time constants at every call site
+    if (n == 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesK);
 }
 constexpr int kWaitLds = 0xC07F;
+
+// The page loop of the staged kernel.  The slots are restrict-qualified so
+// that the compiler knows the direct-to-LDS copies into one never alias
+// reads of the other; without that it waits for every copy in flight before
+// any LDS read, and the next page's K copy would stall this page's V reads.
+template <int D>
+__device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
+                                             const DecodeArgs &a, int lane, int col, int jj, int h, int p0,
+                                             int p1, int len, const int32_t *ptab, const half8_t (&qf)[D / 32],
+                                             float zscale, SplitState<D> &st)
+{
+    const CacheGeom &g = a.geom;
+    auto live_page = [&](int pid) { return pid >= 0 && pid < g.num_pages; };   // others are skipped
+    auto block_of = [&](int pid) {
+        return a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
+    };
+    half8_t pf[2], pl[2];
+    const StageOffsets so = stage_offsets(g, lane, col, jj);
+    // the chunk's page ids, 64 at a time, one per lane
+    int base = p0;
+    int ids = (p0 + lane < p1) ? ptab[p0 + lane] : -1;
+    int pid = p0 < p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
+    if (live_page(pid)) {
+        stage_k(block_of(pid), so, kslot);
+        stage_v(block_of(pid), so, vslot);
+    }
+    for (int pg = p0; pg < p1; ++pg) {
+        const int nxt = pg + 1;
+        if (nxt < p1 && nxt - base == 64) {
+            base = nxt;
+            ids = (base + lane < p1) ? ptab[base + lane] : -1;
+            wait_vmem_at_most(0);
+        }
+        const int pid_next = nxt < p1 ? __builtin_amdgcn_readlane(ids, nxt - base) : -1;
+        const bool cur = live_page(pid), next = live_page(pid_next);
+        const int valid = min(kPage, len - pg * kPage);
+
+        // K: outstanding now are this page's K then V copies
+        if (cur)
+            wait_vmem_at_most(kCopiesV);
+        KRegs<D> kr;
+        read_k(kslot, lane, col, jj, kr);
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        if (next)
+            stage_k(block_of(pid_next), so, kslot);
+        if (cur)
+            scores_phase<D>(kr, valid, qf, zscale, jj, st, pf, pl);
+
+        // V: outstanding now are this page's V then the next page's K
+        // copies.  One pair block at a time keeps few registers live.
+        wait_vmem_at_most(next ? kCopiesK : 0);
+        convert_v_scales(vslot, lane, valid);          // the wave's own LDS writes precede its reads
+        uint4 vw[1];
+        half8_t sv[1][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            read_v<1>(vslot, u, lane, col, jj, vw, sv);
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            if (u == 3 && next)
+                stage_v(block_of(pid_next), so, vslot);
+            if (cur)
+                values_phase<D, 1>(u, vw, sv, pf, pl, st);
+        }
+        pid = pid_next;
+    }
+}
 
 template <int D, bool STAGED>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
@@ -389,13 +467,14 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     constexpr int KW = CPL / 8;           // code dwords per lane per score tile (= MFMAs per tile)
     static_assert(merge_area_bytes<D>() <= 16 * D * 4 + 128, "merge area layout");
     static_assert(8 * D * 4 + 128 <= kKSlotBytes && 8 * D * 4 <= kVSlotBytes, "merge area must fit the slots");
+    static_assert(kWavesPerGroup * (kKSlotBytes + kVSlotBytes) <= 40 * 1024, "four workgroups per CU");
 
     // separate LDS objects for K and V, so the copies into one never wait on
     // reads of the other
     __shared__ __attribute__((aligned(16))) uint8_t kslots[kWavesPerGroup][kKSlotBytes];
     __shared__ __attribute__((aligned(16))) uint8_t vslots[kWavesPerGroup][kVSlotBytes];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the page loop scalar
     const int col = lane & 15;            // query column / tile row
     const int jj = lane >> 4;             // lane group
     const int sp = blockIdx.x * kWavesPerGroup + wave;   // this wave's context chunk
@@ -455,75 +534,26 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     for (int t = 0; t < D / 16; ++t)
         st.acc[t] = st.lacc;
 
-    auto live_page = [&](int pid) { return pid >= 0 && pid < g.num_pages; };   // others are skipped
-    auto block_of = [&](int pid) {
-        return a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
-    };
-    half8_t pf[2], pl[2];
-
     if constexpr (STAGED) {
-        uint8_t *kslot = kslots[wave];
-        uint8_t *vslot = vslots[wave];
-        const StageOffsets so = stage_offsets(g, lane, col, jj);
-        // the chunk's page ids, 64 at a time, one per lane
-        int base = p0;
-        int ids = (p0 + lane < p1) ? ptab[p0 + lane] : -1;
-        int pid = p0 < p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
-        if (live_page(pid)) {
-            stage_k(block_of(pid), so, kslot);
-            stage_v(block_of(pid), so, vslot);
-        }
-        for (int pg = p0; pg < p1; ++pg) {
-            const int nxt = pg + 1;
-            if (nxt < p1 && nxt - base == 64) {
-                base = nxt;
-                ids = (base + lane < p1) ? ptab[base + lane] : -1;
-                wait_vmem_at_most(0);
-            }
-            const int pid_next = nxt < p1 ? __builtin_amdgcn_readlane(ids, nxt - base) : -1;
-            const bool cur = live_page(pid), next = live_page(pid_next);
-            const int valid = min(kPage, len - pg * kPage);
-
-            // K: outstanding now are this page's K then V copies
-            if (cur)
-                wait_vmem_at_most(kCopiesV);
-            KRegs<D> kr;
-            read_k(kslot, lane, jj, kr);
-            __builtin_amdgcn_s_waitcnt(kWaitLds);
-            if (next)
-                stage_k(block_of(pid_next), so, kslot);
-            if (cur)
-                scores_phase<D>(kr, valid, qf, zscale, jj, st, pf, pl);
-
-            // V: outstanding now are this page's V then the next page's K
-            // copies.  Two pair blocks at a time keep fewer registers live.
-            wait_vmem_at_most(next ? kCopiesK : 0);
-            uint4 vw[2], vs[2];
-            read_v<0, 2>(vslot, lane, col, jj, vw, vs);
-            __builtin_amdgcn_s_waitcnt(kWaitLds);
-            if (cur)
-                values_phase<D, 0, 2>(vw, vs, valid, jj, pf, pl, st);
-            read_v<2, 2>(vslot, lane, col, jj, vw, vs);
-            __builtin_amdgcn_s_waitcnt(kWaitLds);
-            if (next)
-                stage_v(block_of(pid_next), so, vslot);
-            if (cur)
-                values_phase<D, 2, 2>(vw, vs, valid, jj, pf, pl, st);
-            pid = pid_next;
-        }
+        staged_pages<D>(kslots[wave], vslots[wave], a, lane, col, jj, h, p0, p1, len, ptab, qf, zscale, st);
     } else {
+        half8_t pf[2], pl[2];
         for (int pg = p0; pg < p1; ++pg) {
             const int pid = ptab[pg];
-            if (!live_page(pid))
+            if (pid < 0 || pid >= g.num_pages)            // skipped, like the staged loop
                 continue;
-            const uint8_t *blk = block_of(pid);
+            const uint8_t *blk = a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
             const int valid = min(kPage, len - pg * kPage);
             KRegs<D> kr;
             VRegs<D> vr;
             load_k_direct<D>(blk, g, col, jj, kr);
             load_v_direct<D>(blk, g, col, jj, vr);
             scores_phase<D>(kr, valid, qf, zscale, jj, st, pf, pl);
-            values_phase<D, 0, VRegs<D>::NU>(vr.vw, vr.vs, valid, jj, pf, pl, st);
+            half8_t sv[VRegs<D>::NU][2];
+#pragma unroll
+            for (int u = 0; u < VRegs<D>::NU; ++u)
+                v_scales(vr.vs[u], valid, jj, sv[u]);
+            values_phase<D, VRegs<D>::NU>(0, vr.vw, sv, pf, pl, st);
         }
     }
 
