@@ -28,13 +28,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP4-KV decode attention: achieved HBM GB/s (% of peak) and decode steps/s"
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E peak, GB/s
-KERNEL_SOURCE = os.path.join(ROOT, "fp4_quantised_kv_amd", "csrc", "fp4kv_kernels.hip")
+# sources of the split kernel whose HBM counters profiles/ may hold
+KERNEL_SOURCES = [os.path.join(ROOT, "fp4_quantised_kv_amd", "csrc", n)
+                  for n in ("fp4kv_decode_mfma.hip", "fp4kv_merge.h", "fp4kv_internal.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -127,8 +132,8 @@ def main():
     ap.add_argument("--splits", type=int, default=None, help="context splits (default: the workload's)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--hbm-probe", action="store_true",
-                    help="also time a plain 2 GiB streaming read (torch sum) as the achievable-bandwidth reference")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the streaming-read probe (the achievable HBM read rate for this access pattern)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill quantise-append measurement (8 x 8192 tokens)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -221,6 +226,18 @@ def main():
     t_comb = sum(e[2].elapsed_time(e[3]) for e in timed) / args.steps
     ms_per_step = total_ms / args.steps
 
+    # the split kernel alone, launched back to back with no event between
+    # launches: its average duration for the roofline figure
+    last = total_steps - 1
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fk.decode_split(L, gc.cache, qs[last % len(qs)], lens_dev[last % len(lens_dev)], gc.page_table,
+                        softmax_scale=scale, num_splits=splits_req, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_split_b2b = e0.elapsed_time(e1) / args.steps
+
     # algorithmic bytes
     if paged:
         ctx = [int(lens0[b]) + args.warmup + 1 for b in range(B)]   # mid-run lengths, +1 per step
@@ -235,7 +252,7 @@ def main():
     if paged:
         step_bytes += B * w.kv_heads * D * 2 * 2 + B * L.bytes_per_token + B * 8
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    split_gbs = split_bytes / (t_split * 1e-3) / 1e9
+    split_gbs = split_bytes / (t_split_b2b * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
 
     result = {
@@ -258,27 +275,32 @@ def main():
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
-                      "decode_combine": round(t_comb, 5)},
+                      "decode_combine": round(t_comb, 5), "decode_split_back_to_back": round(t_split_b2b, 5)},
         "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(split_gbs, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_split_mfma<128, staged>" if D == 128 else "decode_split_mfma<64>",
+                     "achieved": round(split_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes)},
     }
     if not args.no_prefill:
         result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)
-    if args.hbm_probe:
-        x = torch.ones(1 << 29, dtype=torch.float32, device=dev)     # 2 GiB
+    if not args.no_read_probe:
+        # the achievable read rate: the same number of 9216-byte blocks as
+        # the cache, streamed once by the library's read probe
+        buf = torch.full((L.cache_bytes,), 1, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
         for _ in range(3):
-            x.sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fk.read_probe(buf, sink)
         e0.record(stream)
         for _ in range(10):
-            x.sum()
+            fk.read_probe(buf, sink)
         e1.record(stream)
         torch.cuda.synchronize()
-        result["hbm_read_probe"] = {"kernel": "torch sum of 2 GiB fp32", "bytes": x.numel() * 4,
-                                    "gbs": round(x.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
-        del x
+        result["hbm_read_probe"] = {"kernel": "read_probe: 16-byte loads, one 9216-byte block per wave",
+                                    "bytes": buf.numel(),
+                                    "gbs": round(buf.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
+        result["roofline"]["frac_of_read_probe"] = round(split_gbs / result["hbm_read_probe"]["gbs"], 4)
+        del buf
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -96,6 +96,8 @@ def library():
         L.fp4kv_decode_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
         L.fp4kv_decode_combine.restype = ctypes.c_int
+        L.fp4kv_read_probe.argtypes = [_P, ctypes.c_int64, _P, _P]
+        L.fp4kv_read_probe.restype = ctypes.c_int
         L.fp4kv_status_string.argtypes = [ctypes.c_int]
         L.fp4kv_status_string.restype = ctypes.c_char_p
         L.fp4kv_version.argtypes = []
@@ -256,3 +258,13 @@ def decode_combine(workspace, batch: int, num_q_heads: int, head_dim: int, parti
         batch, num_q_heads, head_dim, partials, workspace.data_ptr(), workspace.numel(),
         out.data_ptr(), _stream(stream)))
     return out
+
+
+def read_probe(buf, sink, stream=None):
+    """Measurement utility: stream `buf` (uint8, a multiple of 9216 bytes) once
+    through 16-byte loads and discard it; `sink` is a 4-byte device tensor."""
+    import torch
+    _need(buf, "buf", torch.uint8)
+    _need(sink, "sink", torch.int32)
+    _check("fp4kv_read_probe", library().fp4kv_read_probe(buf.data_ptr(), buf.numel(), sink.data_ptr(),
+                                                          _stream(stream)))

@@ -319,6 +319,18 @@ const char *fp4kv_status_string(int status)
     }
 }
 
+int fp4kv_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream)
+{
+    constexpr int64_t kBlock = 9216;
+    if (!buf || !sink || bytes <= 0 || bytes % kBlock != 0)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(buf, 256) || !aligned(sink, 4))
+        return FP4KV_ERR_MISALIGNED;
+    const hipError_t e = fp4kv::launch_read_probe(static_cast<const uint8_t *>(buf), bytes / kBlock, sink,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
 int fp4kv_version(void) { return 100; }
 
 }  // extern "C"

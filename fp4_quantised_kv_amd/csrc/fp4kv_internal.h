@@ -47,4 +47,7 @@ hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t partials,
                                  int32_t head_dim, float *out, hipStream_t stream);
 
+// Streaming read of `blocks` 9216-byte blocks (measurement utility).
+hipError_t launch_read_probe(const uint8_t *buf, int64_t blocks, uint32_t *sink, hipStream_t stream);
+
 }  // namespace fp4kv

@@ -446,42 +446,92 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
 // Merge the partials of one (sequence, query head): M = max_j m_j,
 // L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L.  Partials with
 // no tokens carry m = -inf and l = 0 and are skipped; a row with no tokens at
-// all is written as zeros.  One wave per row: lane c covers channels c and
-// c + 64; the (m, l) pairs are read by every lane (one broadcast load each).
+// all is written as zeros.  One workgroup per row: each of its four waves
+// sums a quarter of the partials (lane c covering D/64 consecutive channels),
+// and the four sums are added in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ ws_o,
                                                       const float *__restrict__ ws_ml, int partials,
-                                                      int64_t rows, float *__restrict__ out)
+                                                      float *__restrict__ out)
 {
-    constexpr int CL = D / 64;                          // channels per lane
+    constexpr int CL = D / 64;                          // consecutive channels per lane
+    __shared__ float part[4][D + 1];                    // per wave: its output sum, then its weight sum
     const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= rows)
-        return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row = blockIdx.x;
     const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + row * partials;
-    const float *o = ws_o + row * partials * D + lane;
+
+    // the largest partial maximum, in every wave
     float M = -INFINITY;
-    for (int j = 0; j < partials; ++j)
+    for (int j = lane; j < partials; j += 64)
         M = fmaxf(M, ml[j].x);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        M = fmaxf(M, __shfl_xor(M, o));
+
+    // wave w sums partials [w*per, (w+1)*per); the loads of one batch of
+    // partials are all in flight together
+    const int per = (partials + 3) / 4;
+    const int j0 = wave * per, j1 = min(partials, j0 + per);
     float L = 0.0f, O[CL];
 #pragma unroll
     for (int i = 0; i < CL; ++i)
         O[i] = 0.0f;
     if (M != -INFINITY) {
-#pragma unroll 4
-        for (int j = 0; j < partials; ++j) {
+        const float *o = ws_o + row * partials * D + lane * CL;
+#pragma unroll 8
+        for (int j = j0; j < j1; ++j) {
             const float2 mj = ml[j];
             const float w = mj.x == -INFINITY ? 0.0f : exp2f(mj.x - M);
             L = fmaf(mj.y, w, L);
-#pragma unroll
-            for (int i = 0; i < CL; ++i)
-                O[i] = fmaf(o[j * D + 64 * i], w, O[i]);
+            if constexpr (CL == 2) {
+                const float2 x = *reinterpret_cast<const float2 *>(o + static_cast<int64_t>(j) * D);
+                O[0] = fmaf(x.x, w, O[0]);
+                O[1] = fmaf(x.y, w, O[1]);
+            } else {
+                O[0] = fmaf(o[static_cast<int64_t>(j) * D], w, O[0]);
+            }
         }
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
     for (int i = 0; i < CL; ++i)
-        out[row * D + lane + 64 * i] = O[i] * inv;
+        part[wave][lane * CL + i] = O[i];
+    if (lane == 0)
+        part[wave][D] = L;
+    __syncthreads();
+    if (wave == 0) {
+        const float Lt = part[0][D] + part[1][D] + part[2][D] + part[3][D];
+        const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+#pragma unroll
+        for (int i = 0; i < CL; ++i) {
+            const int c = lane * CL + i;
+            out[row * D + c] = (part[0][c] + part[1][c] + part[2][c] + part[3][c]) * inv;
+        }
+    }
+}
+
+// Each wave reads one 9216-byte block per iteration: nine 1 KB rows, lane l
+// taking bytes 16l .. 16l+15 of each, all nine loads in flight together.
+__global__ __launch_bounds__(256) void read_probe(const uint8_t *__restrict__ buf, int64_t blocks,
+                                                  uint32_t *sink)
+{
+    constexpr int64_t kBlock = 9216;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
+    uint32_t acc = 0;
+    for (int64_t b = wave; b < blocks; b += stride) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(buf + b * kBlock) + lane;
+        uint4 x[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k)
+            x[k] = p[64 * k];
+#pragma unroll
+        for (int k = 0; k < 9; ++k)
+            acc ^= x[k].x ^ x[k].y ^ x[k].z ^ x[k].w;
+    }
+    if (acc == 0x9E3779B9u)
+        sink[0] = acc;
 }
 
 template <int D, int GM>
@@ -543,11 +593,19 @@ hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t partials,
                                  int32_t head_dim, float *out, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+    const dim3 grid(static_cast<unsigned>(rows));         // one workgroup per output row
     if (head_dim == 64)
-        decode_combine<64><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, rows, out);
+        decode_combine<64><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, out);
     else
-        decode_combine<128><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, rows, out);
+        decode_combine<128><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const uint8_t *buf, int64_t blocks, uint32_t *sink, hipStream_t stream)
+{
+    const int64_t groups = (blocks + 3) / 4;
+    const dim3 grid(static_cast<unsigned>(groups < 8192 ? groups : 8192));
+    read_probe<<<grid, 256, 0, stream>>>(buf, blocks, sink);
     return hipGetLastError();
 }
 

@@ -217,6 +217,17 @@ FP4KV_API int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void 
 FP4KV_API int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t partials,
                                    const void *workspace, int64_t workspace_bytes, float *out, void *stream);
 
+/* Measurement utility, not a step of the method: reads `bytes` of device
+ * memory at `buf` (device) once with 16-byte loads and discards the data.
+ * Each wave reads whole 9216-byte blocks, the size of one page of one KV head
+ * at D = 128, so the rate it reaches is the achievable HBM read rate for the
+ * decode kernel's access pattern.  `bytes` must be a positive multiple of
+ * 9216 and `buf` 256-byte aligned; `sink` (device, 4 bytes) is written only
+ * if the XOR of everything read equals 0x9E3779B9, which keeps the loads
+ * from being optimised away.  Returns FP4KV_OK, or INVALID_ARGUMENT /
+ * MISALIGNED before any HIP call, or FP4KV_ERR_HIP. */
+FP4KV_API int fp4kv_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 /* Static text for a status code (never NULL). */
 FP4KV_API const char *fp4kv_status_string(int status);
 

@@ -145,3 +145,14 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         fk.quantize_append(L, k, k, torch.zeros(1, dtype=torch.int64),
                            torch.zeros(L.cache_bytes, dtype=torch.uint8))
+
+
+def test_read_probe_host_checks():
+    lib = _lib()
+    ok = 0x10000
+    assert lib.fp4kv_read_probe(None, 9216, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_read_probe(ok, 0, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_read_probe(ok, 9215, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_read_probe(ok, 9216, None, None) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_read_probe(ok + 16, 9216, ok, None) == fk.ERR_MISALIGNED
+    assert lib.fp4kv_read_probe(ok, 9216, ok + 2, None) == fk.ERR_MISALIGNED
