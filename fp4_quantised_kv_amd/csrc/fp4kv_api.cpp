@@ -14,8 +14,9 @@
 namespace {
 
 constexpr int32_t kPage = FP4KV_PAGE_SIZE;
-constexpr int32_t kTargetWaves = 4096;    // context chunks (one wave each) to cover 256 CUs
+constexpr int32_t kTargetWaves = 16384;   // context chunks (one wave each): 4x the waves 256 CUs hold at once, so ragged lengths balance
 constexpr int32_t kChunksPerGroup = 4;   // chunks merged inside one workgroup
+constexpr int64_t kMaxPartials = 65535;  // partials per row: the split kernel's third grid dimension
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -110,6 +111,8 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
     }
     if (s > max_pages)
         s = max_pages;
+    if (s > static_cast<int64_t>(kChunksPerGroup) * kMaxPartials)
+        s = static_cast<int64_t>(kChunksPerGroup) * kMaxPartials;
     if (s < 1)
         s = 1;
     const int64_t pps = (max_pages + s - 1) / s;

@@ -477,8 +477,13 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the page loop scalar
     const int col = lane & 15;            // query column / tile row
     const int jj = lane >> 4;             // lane group
-    const int sp = blockIdx.x * kWavesPerGroup + wave;   // this wave's context chunk
-    const int h = blockIdx.y, b = blockIdx.z;
+    // grid (KV head, sequence, partial): the partial index varies slowest, so
+    // the chunks nearest the start of every sequence (never empty) are
+    // dispatched first, and consecutive workgroups -- which the hardware
+    // deals round-robin to the XCDs -- belong to different KV heads
+    const int part = blockIdx.z;
+    const int sp = part * kWavesPerGroup + wave;   // this wave's context chunk
+    const int h = blockIdx.x, b = blockIdx.y;
     const int G = a.group;
     const CacheGeom &g = a.geom;
 
@@ -578,14 +583,14 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
             }
         }
     }
-    merge_waves_and_store<D>(area, a, b, h, blockIdx.x);
+    merge_waves_and_store<D>(area, a, b, h, part);
 }
 
 }  // namespace
 
 hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.partials, a.geom.num_kv_heads, a.batch);
+    const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
     if (a.geom.head_dim == 64)
         decode_split_mfma<64, false><<<grid, kGroupThreads, 0, stream>>>(a);
     else if (a.staged)

@@ -307,8 +307,13 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
     constexpr int NB = D / 16;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the page loop scalar
-    const int sp = blockIdx.x * kWavesPerGroup + wave;
-    const int h = blockIdx.y, b = blockIdx.z;
+    // grid (KV head, sequence, partial): the partial index varies slowest, so
+    // the chunks nearest the start of every sequence (never empty) are
+    // dispatched first, and consecutive workgroups -- which the hardware
+    // deals round-robin to the XCDs -- belong to different KV heads
+    const int part = blockIdx.z;
+    const int sp = part * kWavesPerGroup + wave;
+    const int h = blockIdx.x, b = blockIdx.y;
     const int G = a.group;
 
     __shared__ float q_s[GM][D];
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
         if (lane < D / 2)
             *reinterpret_cast<float2 *>(ar.row(gq) + 2 * lane) = make_float2(o0[gq], o1[gq]);
     }
-    merge_waves_and_store<D>(area, a, b, h, blockIdx.x);
+    merge_waves_and_store<D>(area, a, b, h, part);
 }
 
 // Merge the partials of one (sequence, query head): M = max_j m_j,
@@ -537,7 +542,7 @@ __global__ __launch_bounds__(256) void read_probe(const uint8_t *__restrict__ bu
 template <int D, int GM>
 hipError_t launch_split_t(const DecodeArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.partials, a.geom.num_kv_heads, a.batch);
+    const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
     decode_split_valu<D, GM><<<grid, kGroupThreads, 0, stream>>>(a);
     return hipGetLastError();
 }

@@ -1,9 +1,10 @@
 // Merge of the running states of a workgroup's waves into one partial result.
 //
 // A decode workgroup has kWavesPerGroup waves; wave w attends over context
-// chunk 4 * blockIdx.x + w.  Each wave leaves, in its own LDS area, its
-// unnormalised outputs o_w[q][c] (16 query rows x D channels, fp32) and its
-// (m_w[q], l_w[q]) pairs (base-2 running max and sum).  The workgroup then
+// chunk 4 * part + w, part being the workgroup's partial index.  Each wave
+// leaves, in its own LDS area, its unnormalised outputs o_w[q][c] (16 query
+// rows x D channels, fp32) and its (m_w[q], l_w[q]) pairs (base-2 running
+// max and sum).  The workgroup then
 // writes one partial per query row, relative to M = max_w m_w:
 //   o = sum_w o_w 2^(m_w - M),  l = sum_w l_w 2^(m_w - M),  m = M,
 // or (m, l, o) = (-inf, 0, 0) when every wave was empty.

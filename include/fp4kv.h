@@ -141,9 +141,11 @@ FP4KV_API int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout,
  * one wave attends over each chunk, and workgroups of four waves merge their
  * four chunks into one partial result, so the workspace holds
  * P = ceil(S / 4) partials per (sequence, query head).
- * num_splits > 0 asks for S = num_splits (clamped to max_pages_per_seq, then
- * trimmed so that no chunk starts past page max_pages_per_seq); 0 lets the
- * library choose S to fill the GPU.  *splits_out gets S, *partials_out P and
+ * num_splits > 0 asks for S = num_splits (clamped to max_pages_per_seq and
+ * to 4 * 65535, then trimmed so that no chunk starts past page
+ * max_pages_per_seq); 0 lets the library choose S, about 16384 chunks in
+ * total over batch x H_kv, so that the GPU stays full even when sequence
+ * lengths differ.  *splits_out gets S, *partials_out P and
  * *workspace_bytes_out the workspace fp4kv_decode_attention needs, for the
  * same arguments.
  * Errors: INVALID_ARGUMENT (null pointer, batch < 0, num_q_heads < 1,
