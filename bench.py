@@ -195,21 +195,25 @@ def main():
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total_steps)]
 
-    def step(s):
-        e = ev[s]
-        e[0].record(stream)
+    def step(s, e=None):
+        if e is not None:
+            e[0].record(stream)
         if paged:
             fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
-        e[1].record(stream)
+        if e is not None:
+            e[1].record(stream)
         fk.decode_split(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
                         softmax_scale=scale, num_splits=splits_req, workspace=ws)
-        e[2].record(stream)
+        if e is not None:
+            e[2].record(stream)
         fk.decode_combine(ws, B, Hq, D, partials, out=out)
-        e[3].record(stream)
+        if e is not None:
+            e[3].record(stream)
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    # the timed region: K steps with no event between their launches
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -217,14 +221,21 @@ def main():
     for s in range(args.warmup, total_steps):
         step(s)
     stop.record(stream)
+    host_enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    # per-kernel breakdown: the same steps again (appends rewrite the same
+    # slots with the same bytes), with an event between launches
+    for s in range(args.warmup, total_steps):
+        step(s, ev[s])
+    torch.cuda.synchronize()
     timed = ev[args.warmup:]
     t_append = sum(e[0].elapsed_time(e[1]) for e in timed) / args.steps
     t_split = sum(e[1].elapsed_time(e[2]) for e in timed) / args.steps
     t_comb = sum(e[2].elapsed_time(e[3]) for e in timed) / args.steps
-    ms_per_step = total_ms / args.steps
 
     # the split kernel alone, launched back to back with no event between
     # launches: its average duration for the roofline figure
@@ -252,7 +263,14 @@ def main():
     if paged:
         step_bytes += B * w.kv_heads * D * 2 * 2 + B * L.bytes_per_token + B * 8
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    split_gbs = split_bytes / (t_split_b2b * 1e-3) / 1e9
+    # the back-to-back launches all attend over the last step's lengths
+    if paged:
+        ctx_last = [int(lens0[b]) + total_steps for b in range(B)]
+        split_bytes_b2b = (sum(ctx_last) * L.bytes_per_token + B * Hq * D * 2
+                           + sum(-(-c // 64) for c in ctx_last) * 4 + B * 4)
+    else:
+        split_bytes_b2b = split_bytes
+    split_gbs = split_bytes_b2b / (t_split_b2b * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
 
     result = {
@@ -277,10 +295,11 @@ def main():
         "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
                       "decode_combine": round(t_comb, 5), "decode_split_back_to_back": round(t_split_b2b, 5)},
         "wall_s_timed": round(wall, 4),
+        "host_enqueue_ms_per_step": round(1e3 * host_enqueue / args.steps, 5),
         "roofline": {"bound": "hbm", "kernel": "decode_split_mfma<128, staged>" if D == 128 else "decode_split_mfma<64>",
                      "achieved": round(split_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes)},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes_b2b)},
     }
     if not args.no_prefill:
         result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)

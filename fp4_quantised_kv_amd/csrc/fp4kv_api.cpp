@@ -230,6 +230,7 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     a->scale_log2e = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     a->ws_o = static_cast<float *>(workspace);
     a->ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + plan.ws_o_bytes);
+
     a->out = nullptr;
     return FP4KV_OK;
 }
@@ -279,7 +280,7 @@ int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, i
         return FP4KV_ERR_WORKSPACE_TOO_SMALL;
     const float *ws_o = static_cast<const float *>(workspace);
     const float *ws_ml = reinterpret_cast<const float *>(static_cast<const uint8_t *>(workspace) + o_bytes);
-    const hipError_t e = fp4kv::launch_decode_combine(ws_o, ws_ml, rows, partials, head_dim, out,
+    const hipError_t e = fp4kv::launch_decode_combine(ws_o, ws_ml, batch, num_q_heads, partials, head_dim, out,
                                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
@@ -304,8 +305,8 @@ int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache
     hipError_t e = fp4kv::launch_decode_split(a, st);
     if (e != hipSuccess)
         return FP4KV_ERR_HIP;
-    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, static_cast<int64_t>(batch) * num_q_heads,
-                                     a.partials, layout->params.head_dim, out, st);
+    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
+                                     out, st);
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
 

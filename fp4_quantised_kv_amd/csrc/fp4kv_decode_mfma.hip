@@ -292,20 +292,27 @@ __device__ __forceinline__ void load_v_direct(const uint8_t *blk, const CacheGeo
 // Staged loads for D = 128: direct-to-LDS copies issued a phase ahead of the
 // arithmetic, so that no registers are held while the copies are in flight.
 // K and V have separate LDS slots, so the next page's K copy can start as
-// soon as this page's K operands are in registers, and likewise for V.
+// soon as this page's K operands are in registers, and likewise for V.  All
+// copies are 16 bytes per lane; the two scale planes of a page travel in one
+// instruction with the K codes.
 //   K slot [0, 4096): tile t at t*1024, lane l's 16 code bytes at l*16;
-//          [4096, 4608): the page's K scale plane [64 tokens][8].
+//          [4096, 4608): the page's K scale plane [64 tokens][8];
+//          [4608, 5120): its V scale plane [4 slices][8 blocks][16].
 //   V slot [0, 4096): pair block u at u*1024, lane l at l*16;
-//          [4096, 4608): the page's V scale plane [4 slices][8 blocks][16];
-//          [4608, 5632): the same scales converted to fp16 once per page
-//          (each lane converts 8), instead of by every lane that needs them.
-constexpr int kKSlotBytes = 4608;
-constexpr int kVSlotBytes = 5632;
-constexpr int kCopiesK = 6;               // direct-to-LDS instructions per K copy
-constexpr int kCopiesV = 6;               // ... per V copy
+//          [4096, 5120): the page's V scales in fp16, converted once per page
+//          during the K phase (each lane converts 8).
+// Cache policy of the copies: non-temporal.  The cache is read once per
+// step; without the hint the stream evicts the partial results this kernel
+// writes from L2, and their write-back to HBM interleaved with the stream
+// costs about 10 % of the kernel's time (measured at 32 x 32K context).
+constexpr int kStream = 2;                // the NT bit of the instruction's cache-policy field
+constexpr int kKSlotBytes = 5120;
+constexpr int kVSlotBytes = 5120;
+constexpr int kCopiesK = 5;               // direct-to-LDS instructions per K copy
+constexpr int kCopiesV = 4;               // ... per V copy
 
 struct StageOffsets {
-    uint32_t k, ks, v, vs;                // per-lane byte offsets inside a block, tile/block 0
+    uint32_t k, s, v;                     // per-lane byte offsets inside a block: tile/block 0, scales
 };
 
 __device__ __forceinline__ StageOffsets stage_offsets(const CacheGeom &g, int lane, int col, int jj)
@@ -313,35 +320,29 @@ __device__ __forceinline__ StageOffsets stage_offsets(const CacheGeom &g, int la
     StageOffsets o;
     const uint32_t tok0 = static_cast<uint32_t>(tile_token(0, col));
     o.k = static_cast<uint32_t>(g.k_codes_off) + tok0 * 64u + jj * 16u;
-    o.ks = static_cast<uint32_t>(g.k_scales_off) + lane * 4u;
+    // lanes 0..31: the K scale plane, lanes 32..63: the V scale plane
+    o.s = static_cast<uint32_t>(lane < 32 ? g.k_scales_off : g.v_scales_off) + (lane & 31) * 16u;
     o.v = static_cast<uint32_t>(g.v_codes_off) + (jj * 128u + 2u * col) * 8u;
-    o.vs = static_cast<uint32_t>(g.v_scales_off) + lane * 4u;
     return o;
 }
 
 // Tile t's token rows are 4t past tile 0's (+256 bytes of K codes); V pair
-// block u is 32 channels (256 bytes) past block 0; the scale planes are
-// copied whole, 256 bytes per instruction.
+// block u is 32 channels (256 bytes) past block 0.
 __device__ __forceinline__ void stage_k(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
 {
-    const uint8_t *k = blk + o.k, *ks = blk + o.ks;
+    const uint8_t *k = blk + o.k;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_global_load_lds(k + 256 * t, slot + t * 1024, 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(ks + 256 * i, slot + 4096 + i * 256, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(k + 256 * t, slot + t * 1024, 16, 0, kStream);
+    __builtin_amdgcn_global_load_lds(blk + o.s, slot + 4096, 16, 0, kStream);
 }
 
 __device__ __forceinline__ void stage_v(const uint8_t *blk, const StageOffsets &o, uint8_t *slot)
 {
-    const uint8_t *v = blk + o.v, *vs = blk + o.vs;
+    const uint8_t *v = blk + o.v;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_global_load_lds(v + 256 * u, slot + u * 1024, 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(vs + 256 * i, slot + 4096 + i * 256, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(v + 256 * u, slot + u * 1024, 16, 0, kStream);
 }
 
 __device__ __forceinline__ void read_k(const uint8_t *slot, int lane, int col, int jj, KRegs<128> &r)
@@ -354,18 +355,20 @@ __device__ __forceinline__ void read_k(const uint8_t *slot, int lane, int col, i
     }
 }
 
-// Convert the page's V scales to fp16 in the slot: lane l takes bytes
-// 8l .. 8l+7 of the plane, i.e. tokens 16*(l/16) + 8*(l%2) + 0..7.
-__device__ __forceinline__ void convert_v_scales(uint8_t *slot, int lane, int valid)
+// V scales of the page in the K slot -> fp16 in the V slot: lane l takes
+// bytes 8l .. 8l+7 of the plane, i.e. tokens 16*(l/16) + 8*(l%2) + 0..7;
+// scales of tokens at or past `valid` become zero, so never-written slots
+// add exact zeros.
+__device__ __forceinline__ void convert_v_scales(const uint8_t *kslot, uint8_t *vslot, int lane, int valid)
 {
-    uint2 raw = *reinterpret_cast<const uint2 *>(slot + 4096 + lane * 8);
+    uint2 raw = *reinterpret_cast<const uint2 *>(kslot + 4608 + lane * 8);
     if (valid < kPage) {
         const int t0 = 16 * (lane >> 4) + 8 * (lane & 1);
         raw.x = keep_valid_bytes(raw.x, t0, valid);
         raw.y = keep_valid_bytes(raw.y, t0 + 4, valid);
     }
     const half8_t h = cat(fp8x2<false>(raw.x), fp8x2<true>(raw.x), fp8x2<false>(raw.y), fp8x2<true>(raw.y));
-    *reinterpret_cast<half8_t *>(slot + 4608 + lane * 16) = h;
+    *reinterpret_cast<half8_t *>(vslot + 4096 + lane * 16) = h;
 }
 
 template <int N>
@@ -375,7 +378,7 @@ __device__ __forceinline__ void read_v(const uint8_t *slot, int u0, int lane, in
 #pragma unroll
     for (int u = 0; u < N; ++u) {
         vw[u] = *reinterpret_cast<const uint4 *>(slot + (u0 + u) * 1024 + lane * 16);
-        const half8_t *sp = reinterpret_cast<const half8_t *>(slot + 4608 + (jj * 8 + 2 * (u0 + u) + (col >> 3)) * 32);
+        const half8_t *sp = reinterpret_cast<const half8_t *>(slot + 4096 + (jj * 8 + 2 * (u0 + u) + (col >> 3)) * 32);
         sv[u][0] = sp[0];
         sv[u][1] = sp[1];
     }
@@ -383,14 +386,11 @@ __device__ __forceinline__ void read_v(const uint8_t *slot, int u0, int lane, in
 
 // gfx9 s_waitcnt immediates (expcnt and lgkmcnt left free): at most n vector
 // memory operations outstanding; and all LDS accesses done.
-__device__ __forceinline__ void wait_vmem_at_most(int n)
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most()
 {
-    static_assert(kCopiesK == kCopiesV, "one immediate serves both waits");
-    // the count is one of two compile-time constants at every call site
-    if (n == 0)
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-    else
-        __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesK);
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 constexpr int kWaitLds = 0xC07F;
 
@@ -398,33 +398,28 @@ constexpr int kWaitLds = 0xC07F;
 // that the compiler knows the direct-to-LDS copies into one never alias
 // reads of the other; without that it waits for every copy in flight before
 // any LDS read, and the next page's K copy would stall this page's V reads.
+// On entry `ids` holds the page ids of pages p0 .. p0+63 (one per lane) and
+// the copies of page p0 (id `pid`) have been issued, K then V, if it is live.
 template <int D>
 __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
-                                             const DecodeArgs &a, int lane, int col, int jj, int h, int p0,
-                                             int p1, int len, const int32_t *ptab, const half8_t (&qf)[D / 32],
-                                             float zscale, SplitState<D> &st)
+                                             const DecodeArgs &a, const StageOffsets &so, int lane, int col,
+                                             int jj, int h, int p0, int p1, int len, const int32_t *ptab,
+                                             int ids, int pid, const half8_t (&qf)[D / 32], float zscale,
+                                             SplitState<D> &st)
 {
     const CacheGeom &g = a.geom;
-    auto live_page = [&](int pid) { return pid >= 0 && pid < g.num_pages; };   // others are skipped
-    auto block_of = [&](int pid) {
-        return a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
+    auto live_page = [&](int id) { return id >= 0 && id < g.num_pages; };   // others are skipped
+    auto block_of = [&](int id) {
+        return a.cache + static_cast<int64_t>(id) * g.page_stride + h * g.head_stride;
     };
     half8_t pf[2], pl[2];
-    const StageOffsets so = stage_offsets(g, lane, col, jj);
-    // the chunk's page ids, 64 at a time, one per lane
     int base = p0;
-    int ids = (p0 + lane < p1) ? ptab[p0 + lane] : -1;
-    int pid = p0 < p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
-    if (live_page(pid)) {
-        stage_k(block_of(pid), so, kslot);
-        stage_v(block_of(pid), so, vslot);
-    }
     for (int pg = p0; pg < p1; ++pg) {
         const int nxt = pg + 1;
         if (nxt < p1 && nxt - base == 64) {
             base = nxt;
             ids = (base + lane < p1) ? ptab[base + lane] : -1;
-            wait_vmem_at_most(0);
+            wait_vmem_at_most<0>();
         }
         const int pid_next = nxt < p1 ? __builtin_amdgcn_readlane(ids, nxt - base) : -1;
         const bool cur = live_page(pid), next = live_page(pid_next);
@@ -432,7 +427,8 @@ __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_
 
         // K: outstanding now are this page's K then V copies
         if (cur)
-            wait_vmem_at_most(kCopiesV);
+            wait_vmem_at_most<kCopiesV>();
+        convert_v_scales(kslot, vslot, lane, valid);   // the V slot's fp16 plane is free since the last page
         KRegs<D> kr;
         read_k(kslot, lane, col, jj, kr);
         __builtin_amdgcn_s_waitcnt(kWaitLds);
@@ -443,8 +439,10 @@ __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_
 
         // V: outstanding now are this page's V then the next page's K
         // copies.  One pair block at a time keeps few registers live.
-        wait_vmem_at_most(next ? kCopiesK : 0);
-        convert_v_scales(vslot, lane, valid);          // the wave's own LDS writes precede its reads
+        if (next)
+            wait_vmem_at_most<kCopiesK>();
+        else
+            wait_vmem_at_most<0>();
         uint4 vw[1];
         half8_t sv[1][2];
 #pragma unroll
@@ -460,11 +458,128 @@ __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_
     }
 }
 
+// ---- pieces shared by the kernels below
+
+// Query rows of (sequence b, KV head h) as bf16 bits: lane (col, jj) holds
+// channels jj*D/4 .. +D/4 of query col; columns past the group load a valid
+// row and are zeroed after the load (no divergent loads).
+template <int D>
+__device__ __forceinline__ void load_q_bits(const DecodeArgs &a, int b, int h, int col, int jj,
+                                            uint32_t (&qbits)[D / 8])
+{
+    constexpr int CPL = D / 4;
+    const int G = a.group;
+    const bool live = col < G;
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.num_q_heads + h * G + (live ? col : 0)) * D + jj * CPL;
+#pragma unroll
+    for (int i = 0; i < CPL / 8; ++i) {
+        const uint4 x = reinterpret_cast<const uint4 *>(qrow)[i];
+        qbits[4 * i] = x.x; qbits[4 * i + 1] = x.y; qbits[4 * i + 2] = x.z; qbits[4 * i + 3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i)
+        qbits[i] = live ? qbits[i] : 0u;
+}
+
+// The B operand of the score product: q times 2^kq, kq putting the wave's
+// largest |q| in [2^14, 2^15) (exact for bf16 inputs), in fp16; zscale
+// undoes 2^kq and applies softmax_scale * log2(e).  Every lane of the wave
+// must take part (wave-wide maximum).
+template <int D>
+__device__ __forceinline__ void make_q_operand(const uint32_t (&qbits)[D / 8], float scale_log2e,
+                                               half8_t (&qf)[D / 32], float &zscale)
+{
+    float qmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+        qmax = fmaxf(qmax, __uint_as_float((qbits[i] & 0x7FFFu) << 16));
+        qmax = fmaxf(qmax, __uint_as_float(qbits[i] & 0x7FFF0000u));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        qmax = fmaxf(qmax, __shfl_xor(qmax, o));
+    int kq = 0;
+    if (qmax > 0.0f)
+        kq = 14 - (static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127);
+    kq = kq > 100 ? 100 : kq;
+    const float qscale = __builtin_ldexpf(1.0f, kq);
+    zscale = scale_log2e * __builtin_ldexpf(1.0f, -kq);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = qbits[4 * i + e];
+            qf[i][2 * e] = static_cast<_Float16>(__uint_as_float(w << 16) * qscale);
+            qf[i][2 * e + 1] = static_cast<_Float16>(__uint_as_float(w & 0xFFFF0000u) * qscale);
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void init_state(SplitState<D> &st)
+{
+    st.m_ref = -INFINITY;
+    st.lacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+        st.acc[t] = st.lacc;
+}
+
+// A wave's state into its merge area: lane (col = query, jj) holds channels
+// 2*(16u + 4jj + r) + parity, i.e. 32u + 8jj + 0..7.
+template <int D>
+__device__ __forceinline__ void state_to_area(const MergeArea<D> &ar, const SplitState<D> &st, int col, int jj, int G)
+{
+    if (col < G) {
+        float *o = ar.row(col);
+#pragma unroll
+        for (int u = 0; u < D / 32; ++u) {
+            const int c0 = 32 * u + 8 * jj;
+            *reinterpret_cast<float4 *>(o + c0) =
+                make_float4(st.acc[2 * u][0], st.acc[2 * u + 1][0], st.acc[2 * u][1], st.acc[2 * u + 1][1]);
+            *reinterpret_cast<float4 *>(o + c0 + 4) =
+                make_float4(st.acc[2 * u][2], st.acc[2 * u + 1][2], st.acc[2 * u][3], st.acc[2 * u + 1][3]);
+        }
+        if (jj == 0) {
+            ar.ml[2 * col] = st.m_ref;
+            ar.ml[2 * col + 1] = st.lacc[0];
+        }
+    }
+}
+
+// Page range of a wave's chunk and its first 64 page ids.  The ids are
+// bounded by the table, not by the length, so their load need not wait for
+// the length.
+struct Chunk {
+    int h, b, part;
+    int p0, p1, len;
+    const int32_t *ptab;
+};
+
+__device__ __forceinline__ Chunk chunk_of(const DecodeArgs &a, int h, int b, int part, int wave)
+{
+    Chunk c;
+    c.h = h; c.b = b; c.part = part;
+    c.ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages;
+    c.p0 = (part * kWavesPerGroup + wave) * a.pages_per_split;
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
+    c.len = len;
+    c.p1 = min(c.p0 + a.pages_per_split, (len + kPage - 1) / kPage);
+    return c;
+}
+
+__device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, int lane)
+{
+    const int end = min(c.p0 + a.pages_per_split, a.max_pages);
+    return c.p0 + lane < end ? c.ptab[c.p0 + lane] : -1;
+}
+
+// ---- one workgroup per (KV head, sequence, partial)
+
 template <int D, bool STAGED>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
 {
-    constexpr int CPL = D / 4;            // channels a lane holds per score tile
-    constexpr int KW = CPL / 8;           // code dwords per lane per score tile (= MFMAs per tile)
     static_assert(merge_area_bytes<D>() <= 16 * D * 4 + 128, "merge area layout");
     static_assert(8 * D * 4 + 128 <= kKSlotBytes && 8 * D * 4 <= kVSlotBytes, "merge area must fit the slots");
     static_assert(kWavesPerGroup * (kKSlotBytes + kVSlotBytes) <= 40 * 1024, "four workgroups per CU");
@@ -477,78 +592,44 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the page loop scalar
     const int col = lane & 15;            // query column / tile row
     const int jj = lane >> 4;             // lane group
-    // grid (KV head, sequence, partial): the partial index varies slowest, so
-    // the chunks nearest the start of every sequence (never empty) are
-    // dispatched first, and consecutive workgroups -- which the hardware
-    // deals round-robin to the XCDs -- belong to different KV heads
-    const int part = blockIdx.z;
-    const int sp = part * kWavesPerGroup + wave;   // this wave's context chunk
-    const int h = blockIdx.x, b = blockIdx.y;
     const int G = a.group;
     const CacheGeom &g = a.geom;
 
-    // ---- query operand: lane (col, jj) holds channels jj*CPL .. +CPL of query col
-    uint32_t qbits[CPL / 2];
-    float qmax = 0.0f;
-    {
-        const bool live = col < G;
-        const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.num_q_heads + h * G + (live ? col : 0)) * D + jj * CPL;
-#pragma unroll
-        for (int i = 0; i < CPL / 8; ++i) {
-            const uint4 x = live ? reinterpret_cast<const uint4 *>(qrow)[i] : make_uint4(0, 0, 0, 0);
-            qbits[4 * i] = x.x; qbits[4 * i + 1] = x.y; qbits[4 * i + 2] = x.z; qbits[4 * i + 3] = x.w;
-        }
-#pragma unroll
-        for (int i = 0; i < CPL / 2; ++i) {
-            qmax = fmaxf(qmax, __uint_as_float((qbits[i] & 0x7FFFu) << 16));
-            qmax = fmaxf(qmax, __uint_as_float(qbits[i] & 0x7FFF0000u));
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1)
-            qmax = fmaxf(qmax, __shfl_xor(qmax, o));
-    }
-    // 2^kq * qmax in [2^14, 2^15): exact power-of-two rescale of q before fp16
-    int kq = 0;
-    if (qmax > 0.0f)
-        kq = 14 - (static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127);
-    kq = kq > 100 ? 100 : kq;
-    const float qscale = __builtin_ldexpf(1.0f, kq);
-    const float zscale = a.scale_log2e * __builtin_ldexpf(1.0f, -kq);
-    half8_t qf[KW];
-#pragma unroll
-    for (int i = 0; i < KW; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t w = qbits[4 * i + e];
-            qf[i][2 * e] = static_cast<_Float16>(__uint_as_float(w << 16) * qscale);
-            qf[i][2 * e + 1] = static_cast<_Float16>(__uint_as_float(w & 0xFFFF0000u) * qscale);
-        }
-    }
-
-    int len = a.seq_lens[b];
-    len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
-    const int n_pages = (len + kPage - 1) / kPage;
-    const int p0 = sp * a.pages_per_split;
-    const int p1 = min(p0 + a.pages_per_split, n_pages);
-    const int32_t *ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages;
+    // grid (KV head, sequence, partial): the partial index varies slowest, so
+    // the chunks nearest the start of every sequence (never empty) are
+    // dispatched first, and consecutive workgroups -- which the hardware
+    // deals round-robin to the XCDs -- belong to different KV heads.  Every
+    // independent load is issued before any is waited on.
+    const Chunk c = chunk_of(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
+    const int ids = STAGED ? chunk_ids(a, c, lane) : -1;
+    uint32_t qbits[D / 8];
+    load_q_bits<D>(a, c.b, c.h, col, jj, qbits);
+    half8_t qf[D / 32];
+    float zscale;
+    make_q_operand<D>(qbits, a.scale_log2e, qf, zscale);
 
     SplitState<D> st;
-    st.m_ref = -INFINITY;
-    st.lacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-        st.acc[t] = st.lacc;
-
+    init_state(st);
     if constexpr (STAGED) {
-        staged_pages<D>(kslots[wave], vslots[wave], a, lane, col, jj, h, p0, p1, len, ptab, qf, zscale, st);
+        // the query and page-id loads were in flight together, so converting
+        // the query before the first page's copies costs no extra wait
+        const StageOffsets so = stage_offsets(g, lane, col, jj);
+        const int pid = c.p0 < c.p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
+        if (pid >= 0 && pid < g.num_pages) {
+            const uint8_t *blk = a.cache + static_cast<int64_t>(pid) * g.page_stride + c.h * g.head_stride;
+            stage_k(blk, so, kslots[wave]);
+            stage_v(blk, so, vslots[wave]);
+        }
+        staged_pages<D>(kslots[wave], vslots[wave], a, so, lane, col, jj, c.h, c.p0, c.p1, c.len, c.ptab, ids,
+                        pid, qf, zscale, st);
     } else {
         half8_t pf[2], pl[2];
-        for (int pg = p0; pg < p1; ++pg) {
-            const int pid = ptab[pg];
-            if (pid < 0 || pid >= g.num_pages)            // skipped, like the staged loop
+        for (int pg = c.p0; pg < c.p1; ++pg) {
+            const int id = c.ptab[pg];
+            if (id < 0 || id >= g.num_pages)            // skipped, like the staged loop
                 continue;
-            const uint8_t *blk = a.cache + static_cast<int64_t>(pid) * g.page_stride + h * g.head_stride;
-            const int valid = min(kPage, len - pg * kPage);
+            const uint8_t *blk = a.cache + static_cast<int64_t>(id) * g.page_stride + c.h * g.head_stride;
+            const int valid = min(kPage, c.len - pg * kPage);
             KRegs<D> kr;
             VRegs<D> vr;
             load_k_direct<D>(blk, g, col, jj, kr);
@@ -562,28 +643,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
         }
     }
 
-    // ---- this wave's state into its merge area: lane (col = query, jj)
-    //      holds channels 2*(16u + 4jj + r) + parity, i.e. 32u + 8jj + 0..7
     auto area = [&](int w) { return MergeArea<D>(kslots[w], vslots[w]); };
-    {
-        const MergeArea<D> ar = area(wave);
-        if (col < G) {
-            float *o = ar.row(col);
-#pragma unroll
-            for (int u = 0; u < D / 32; ++u) {
-                const int c0 = 32 * u + 8 * jj;
-                *reinterpret_cast<float4 *>(o + c0) =
-                    make_float4(st.acc[2 * u][0], st.acc[2 * u + 1][0], st.acc[2 * u][1], st.acc[2 * u + 1][1]);
-                *reinterpret_cast<float4 *>(o + c0 + 4) =
-                    make_float4(st.acc[2 * u][2], st.acc[2 * u + 1][2], st.acc[2 * u][3], st.acc[2 * u + 1][3]);
-            }
-            if (jj == 0) {
-                ar.ml[2 * col] = st.m_ref;
-                ar.ml[2 * col + 1] = st.lacc[0];
-            }
-        }
-    }
-    merge_waves_and_store<D>(area, a, b, h, part);
+    state_to_area<D>(area(wave), st, col, jj, G);
+    merge_waves_and_store<D>(area, a, c.b, c.h, c.part);
 }
 
 }  // namespace
@@ -591,12 +653,13 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
 hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream)
 {
     const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
-    if (a.geom.head_dim == 64)
+    if (a.geom.head_dim == 64) {
         decode_split_mfma<64, false><<<grid, kGroupThreads, 0, stream>>>(a);
-    else if (a.staged)
+    } else if (a.staged) {
         decode_split_mfma<128, true><<<grid, kGroupThreads, 0, stream>>>(a);
-    else
+    } else {
         decode_split_mfma<128, false><<<grid, kGroupThreads, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -27,8 +27,8 @@ struct DecodeArgs {
     int32_t splits, pages_per_split;   // context chunks and pages per chunk
     int32_t partials;            // partial slots per row: ceil(splits / 4), one per workgroup
     float scale_log2e;           // softmax scale times log2(e): scores kept in base 2
-    float *ws_o;                 // [batch][num_q_heads][partials][D] unnormalised outputs
-    float *ws_ml;                // [batch][num_q_heads][partials][2] running max (base 2), sum
+    float *ws_o;                 // [batch][partials][num_q_heads][D] unnormalised outputs
+    float *ws_ml;                // [batch][partials][num_q_heads][2] running max (base 2), sum
     float *out;                  // [batch][num_q_heads][D]
     bool staged;                 // matrix-core kernel: stage pages through LDS (D = 128)
 };
@@ -41,11 +41,13 @@ hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const u
 hipError_t launch_split_valu(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream);
 
-// Chooses between the two (matrix cores unless FP4KV_DECODE_KERNEL=valu).
+// Chooses the kernel: matrix cores with LDS staging for D = 128, unless
+// FP4KV_DECODE_KERNEL names another (valu: vector ALU; mfma_direct: matrix
+// cores with operands loaded straight into registers).
 hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
 
-hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t partials,
-                                 int32_t head_dim, float *out, hipStream_t stream);
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,
+                                 int32_t partials, int32_t head_dim, float *out, hipStream_t stream);
 
 // Streaming read of `blocks` 9216-byte blocks (measurement utility).
 hipError_t launch_read_probe(const uint8_t *buf, int64_t blocks, uint32_t *sink, hipStream_t stream);

@@ -456,20 +456,23 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
 // and the four sums are added in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ ws_o,
-                                                      const float *__restrict__ ws_ml, int partials,
-                                                      float *__restrict__ out)
+                                                      const float *__restrict__ ws_ml, int num_q_heads,
+                                                      int partials, float *__restrict__ out)
 {
     constexpr int CL = D / 64;                          // consecutive channels per lane
     __shared__ float part[4][D + 1];                    // per wave: its output sum, then its weight sum
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t row = blockIdx.x;
-    const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + row * partials;
+    const int64_t row = blockIdx.x;                     // b * num_q_heads + query head
+    const int64_t b = row / num_q_heads, hq = row % num_q_heads;
+    // partial j of this row: index (b * partials + j) * num_q_heads + hq
+    const int64_t first = b * partials * num_q_heads + hq;
+    const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + first;
 
     // the largest partial maximum, in every wave
     float M = -INFINITY;
     for (int j = lane; j < partials; j += 64)
-        M = fmaxf(M, ml[j].x);
+        M = fmaxf(M, ml[static_cast<int64_t>(j) * num_q_heads].x);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
         M = fmaxf(M, __shfl_xor(M, o));
@@ -483,18 +486,19 @@ __global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ 
     for (int i = 0; i < CL; ++i)
         O[i] = 0.0f;
     if (M != -INFINITY) {
-        const float *o = ws_o + row * partials * D + lane * CL;
+        const float *o = ws_o + first * D + lane * CL;
+        const int64_t stride = static_cast<int64_t>(num_q_heads) * D;
 #pragma unroll 8
         for (int j = j0; j < j1; ++j) {
-            const float2 mj = ml[j];
+            const float2 mj = ml[static_cast<int64_t>(j) * num_q_heads];
             const float w = mj.x == -INFINITY ? 0.0f : exp2f(mj.x - M);
             L = fmaf(mj.y, w, L);
             if constexpr (CL == 2) {
-                const float2 x = *reinterpret_cast<const float2 *>(o + static_cast<int64_t>(j) * D);
+                const float2 x = *reinterpret_cast<const float2 *>(o + j * stride);
                 O[0] = fmaf(x.x, w, O[0]);
                 O[1] = fmaf(x.y, w, O[1]);
             } else {
-                O[0] = fmaf(o[static_cast<int64_t>(j) * D], w, O[0]);
+                O[0] = fmaf(o[j * stride], w, O[0]);
             }
         }
     }
@@ -595,14 +599,14 @@ hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
     return launch_split_mfma(m, stream);
 }
 
-hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int64_t rows, int32_t partials,
-                                 int32_t head_dim, float *out, hipStream_t stream)
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,
+                                 int32_t partials, int32_t head_dim, float *out, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(rows));         // one workgroup per output row
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(batch) * num_q_heads));   // one workgroup per row
     if (head_dim == 64)
-        decode_combine<64><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, out);
+        decode_combine<64><<<grid, 256, 0, stream>>>(ws_o, ws_ml, num_q_heads, partials, out);
     else
-        decode_combine<128><<<grid, 256, 0, stream>>>(ws_o, ws_ml, partials, out);
+        decode_combine<128><<<grid, 256, 0, stream>>>(ws_o, ws_ml, num_q_heads, partials, out);
     return hipGetLastError();
 }
 

@@ -37,14 +37,18 @@ struct MergeArea {
 };
 
 // Call with every thread of the workgroup, after each wave has filled its
-// area; area(w) gives wave w's area.
+// area; area(w) gives wave w's area.  The partial of query row q goes to
+// ws_o[b][part][h*G + q][:] and ws_ml[b][part][h*G + q][:], so a
+// workgroup's G rows are one contiguous block of G*D floats (and of G
+// (m, l) pairs), written with 16-byte stores.
 template <int D, typename AreaOf>
 __device__ __forceinline__ void merge_waves_and_store(AreaOf area, const DecodeArgs &a, int b, int h, int part)
 {
     __syncthreads();
     const int G = a.group;
-    for (int idx = threadIdx.x; idx < G * D; idx += kGroupThreads) {
-        const int q = idx / D, c = idx % D;
+    const int64_t row0 = (static_cast<int64_t>(b) * a.partials + part) * a.num_q_heads + static_cast<int64_t>(h) * G;
+    for (int idx = threadIdx.x; idx < G * (D / 4); idx += kGroupThreads) {
+        const int q = idx / (D / 4), c = 4 * (idx % (D / 4));
         float mw[kWavesPerGroup];
         float M = -INFINITY;
 #pragma unroll
@@ -52,7 +56,8 @@ __device__ __forceinline__ void merge_waves_and_store(AreaOf area, const DecodeA
             mw[w] = area(w).ml[2 * q];
             M = fmaxf(M, mw[w]);
         }
-        float O = 0.0f, L = 0.0f;
+        float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float L = 0.0f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < kWavesPerGroup; ++w) {
@@ -60,16 +65,17 @@ __device__ __forceinline__ void merge_waves_and_store(AreaOf area, const DecodeA
                     continue;
                 const MergeArea<D> ar = area(w);
                 const float wt = exp2f(mw[w] - M);
-                O = fmaf(ar.row(q)[c], wt, O);
+                const float4 x = *reinterpret_cast<const float4 *>(ar.row(q) + c);
+                O.x = fmaf(x.x, wt, O.x);
+                O.y = fmaf(x.y, wt, O.y);
+                O.z = fmaf(x.z, wt, O.z);
+                O.w = fmaf(x.w, wt, O.w);
                 L = fmaf(ar.ml[2 * q + 1], wt, L);
             }
         }
-        const int64_t row = (static_cast<int64_t>(b) * a.num_q_heads + h * G + q) * a.partials + part;
-        a.ws_o[row * D + c] = O;
-        if (c == 0) {
-            a.ws_ml[2 * row] = M;
-            a.ws_ml[2 * row + 1] = L;
-        }
+        *reinterpret_cast<float4 *>(a.ws_o + (row0 + q) * D + c) = O;
+        if (c == 0)
+            *reinterpret_cast<float2 *>(a.ws_ml + (row0 + q) * 2) = make_float2(M, L);
     }
 }
 

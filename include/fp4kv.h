@@ -23,7 +23,8 @@
  *   - The caller owns every buffer.  The library allocates nothing, keeps no
  *     pointer after returning and holds no mutable global state, so calls
  *     are re-entrant.  Calls on one stream run in order; calls that write the
- *     same cache bytes from different streams race.
+ *     same cache bytes, or use the same decode workspace, from different
+ *     streams race.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
  *     stream) and the call returns without waiting.  Results are valid once
  *     the stream reaches them.
@@ -179,7 +180,8 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  *                      attended).
  *   softmax_scale      finite and positive (usually 1/sqrt(D)).
  *   num_splits         as for fp4kv_decode_plan.
- *   workspace          device, 256-B aligned, workspace_bytes >= the plan's.
+ *   workspace          device, 256-B aligned, workspace_bytes >= the plan's;
+ *                      its contents on entry do not matter.
  *   out                device fp32 [batch][num_q_heads][D], 16-B aligned.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, MISALIGNED, WORKSPACE_TOO_SMALL,
  * HIP.  Equivalent to fp4kv_decode_split followed by fp4kv_decode_combine
@@ -197,8 +199,8 @@ FP4KV_API int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const v
  * fp4kv_decode_split takes the arguments of fp4kv_decode_attention except
  * `out` and writes one unnormalised partial result per workgroup to the
  * workspace, laid out as
- *   o   fp32 [batch][num_q_heads][P][D]      at byte 0
- *   ml  fp32 [batch][num_q_heads][P][2]      at byte round_up(batch*num_q_heads*P*D*4, 256)
+ *   o   fp32 [batch][P][num_q_heads][D]   at byte 0
+ *   ml  fp32 [batch][P][num_q_heads][2]   at byte round_up(batch*P*num_q_heads*D*4, 256)
  * where P is the plan's partial count, m = max_t z_t over the partial's
  * tokens with z_t = log2(e) * softmax_scale * q.k_t, l = sum_t 2^(z_t - m)
  * and o = sum_t 2^(z_t - m) v_t.  A partial without tokens has m = -inf,

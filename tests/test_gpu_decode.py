@@ -199,3 +199,27 @@ def test_softmax_scale_argument():
     torch.cuda.synchronize()
     ref = _oracle_decode(q, kept, lens, 128, 0.3)
     _assert_close(out.cpu().numpy(), ref, [(0, slice(None))])
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """One workspace, filled with garbage first, serves consecutive calls of
+    different batch sizes and split counts: every result equals the result
+    with a fresh workspace."""
+    lens = [0, 1, 63, 64, 65, 1000, 3000, 129]
+    Hkv, G, D = 2, 4, 128
+    layout, cache, table, kept, q = _custom_cache(len(lens), G * Hkv, Hkv, D, lens, 21, page_order="random")
+    lens_d = torch.tensor(lens, dtype=torch.int32).cuda()
+    q_d, table_d = q.cuda(), table.cuda()
+    cases = [(8, 0), (3, 7), (8, 1), (5, 64), (8, 0)]
+    plans = {c: fk.decode_plan(layout, c[0], G * Hkv, table.shape[1], c[1]) for c in cases}
+    ws = torch.full((max(p.workspace_bytes for p in plans.values()),), 0xC3, dtype=torch.uint8, device="cuda")
+    _say(f"decode_attention: one workspace for (batch, splits) = {cases}")
+    for B, s in cases:
+        out = fk.decode_attention(layout, cache, q_d[:B].contiguous(), lens_d[:B].contiguous(),
+                                  table_d[:B].contiguous(), num_splits=s, workspace=ws)
+        fresh = fk.decode_attention(layout, cache, q_d[:B].contiguous(), lens_d[:B].contiguous(),
+                                    table_d[:B].contiguous(), num_splits=s)
+        torch.cuda.synchronize()
+        assert torch.equal(out, fresh), (B, s)
+    ref = _oracle_decode(q, kept, lens, D, D ** -0.5)
+    _assert_close(out.cpu().numpy(), ref, [(b, slice(None)) for b in range(1, len(lens))])
