@@ -243,21 +243,40 @@ __global__ __launch_bounds__(256) void append_runs_kernel(
     }
     uint8_t *base = cache + (s0 / kPage) * g.page_stride + head * g.head_stride;
     const int off0 = static_cast<int>(s0 % kPage);
+    // K: the eight tokens' blocks are loaded together (256 bytes in flight
+    // per thread), then quantised and stored token by token
+    {
+        uint32_t w[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            load_block16(ksrc + i * row_stride, w[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t lo, hi, sc;
+            quantize_block16(w[i], lo, hi, sc);
+            *reinterpret_cast<uint2 *>(base + g.k_codes_off + (off0 + i) * (D / 2) + 8 * blk) = make_uint2(lo, hi);
+            base[g.k_scales_off + (off0 + i) * (D / 16) + blk] = static_cast<uint8_t>(sc);
+        }
+    }
     uint32_t vd[16];                                    // channel 16*blk + i, tokens off0 .. off0 + 7
     uint32_t vs[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         vd[i] = 0u;
-#pragma unroll 1
-    for (int i = 0; i < 8; ++i) {
-        append_k<D>(base, g, off0 + i, blk, ksrc + i * row_stride);
-        uint32_t w[8], lo, hi, sc;
-        load_block16(vsrc + i * row_stride, w);
-        quantize_block16(w, lo, hi, sc);
+    {
+        uint32_t w[8][8];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-            vd[c] |= (((c < 8 ? lo : hi) >> (4 * (c & 7))) & 0xFu) << (4 * i);
-        vs[i >> 2] |= sc << (8 * (i & 3));
+        for (int i = 0; i < 8; ++i)
+            load_block16(vsrc + i * row_stride, w[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t lo, hi, sc;
+            quantize_block16(w[i], lo, hi, sc);
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                vd[c] |= (((c < 8 ? lo : hi) >> (4 * (c & 7))) & 0xFu) << (4 * i);
+            vs[i >> 2] |= sc << (8 * (i & 3));
+        }
     }
     const int word = ((off0 & 15) >> 3) * 4;
 #pragma unroll
