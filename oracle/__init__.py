@@ -1,4 +1,5 @@
-"""CPU oracle for the FP4 (E2M1 elements, E4M3 scale per 16 channels) KV cache.
+"""CPU oracle for the FP4 (E2M1 elements, E4M3 scale per 16 channels) KV cache,
+and for its FP8 E4M3 variant with one scale per tensor.
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline leg use it; the product library never imports, loads or calls it,
@@ -16,6 +17,8 @@ Sources (page title, section):
     for this format); a token holds 2 x layers x KV heads x head dim numbers.
   * Same page, Code and Concept sections: quantised K and V replace the real
     ones ahead of an unchanged attention; Q stays unquantised.
+  * Same page, Concept section, results table: FP8 E4M3 with one scale per
+    tensor, 8 bits per number.
 
 Parity status: every function here is pinned by the CPU tests (format tables,
 exhaustive scale and element rules against independent exact checkers and a
@@ -57,6 +60,21 @@ def lib():
                                              ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                              ctypes.c_int64, ctypes.c_double, ctypes.c_void_p]
+        L.fp4kv_oracle_quantize_fp8.restype = ctypes.c_int
+        L.fp4kv_oracle_quantize_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                                ctypes.c_void_p]
+        L.fp4kv_oracle_attention_fp8.restype = ctypes.c_int
+        L.fp4kv_oracle_attention_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                                                 ctypes.c_double, ctypes.c_void_p]
+        L.fp4kv_oracle_attention_fp8_batch.restype = ctypes.c_int
+        L.fp4kv_oracle_attention_fp8_batch.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.c_void_p, ctypes.c_void_p,
+                                                       ctypes.c_void_p, ctypes.c_void_p,
+                                                       ctypes.c_int64, ctypes.c_double,
+                                                       ctypes.c_double, ctypes.c_double,
+                                                       ctypes.c_void_p, ctypes.c_int]
         L.fp4kv_oracle_attention_batch.restype = ctypes.c_int
         L.fp4kv_oracle_attention_batch.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                                    ctypes.c_void_p, ctypes.c_void_p,
@@ -166,6 +184,27 @@ def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return np.where(c & 8, -mag, mag)
 
 
+def quantize_fp8(x_bits, scale):
+    """FP8 E4M3 with one scale per tensor ("Quantising the KV cache", Concept,
+    results table): codes uint8 of the same shape, sign in bit 7, magnitude
+    RNE_sat_E4M3(|x| / scale) for a finite positive fp32 scale."""
+    x = as_bf16_bits(x_bits)
+    codes = np.empty(x.shape, np.uint8)
+    s = np.float32(scale)
+    rc = lib().fp4kv_oracle_quantize_fp8(_ptr(x), x.size, ctypes.c_float(s), _ptr(codes))
+    if rc:
+        raise ValueError("non-finite input or scale")
+    return codes
+
+
+def dequantize_fp8(codes, scale) -> np.ndarray:
+    """+-E4M3(code) * scale in float64 (scale taken as fp32)."""
+    e4 = np.concatenate([e4m3_table(), [np.nan]])
+    c = np.asarray(codes, np.uint8)
+    mag = e4[c & 0x7F] * float(np.float32(scale))
+    return np.where(c & 0x80, -mag, mag)
+
+
 # ---------------------------------------------------------------- attention
 
 def attention(q_bits, k_codes, k_scales, v_codes, v_scales, scale):
@@ -237,6 +276,61 @@ def decode_attention(q_bits, k_codes, k_scales, v_codes, v_scales, seq_lens, sca
     return out
 
 
+def attention_fp8(q_bits, k_codes, v_codes, k_scale, v_scale, scale):
+    """fp64 attention of G bf16 query rows [G][D] over T tokens of FP8 codes
+    [T][D] with per-tensor scales; returns [G][D]."""
+    q = as_bf16_bits(q_bits)
+    G, D = q.shape
+    kc = np.ascontiguousarray(k_codes, np.uint8)
+    vc = np.ascontiguousarray(v_codes, np.uint8)
+    out = np.zeros((G, D), np.float64)
+    rc = lib().fp4kv_oracle_attention_fp8(_ptr(q), G, D, kc.shape[0], _ptr(kc), _ptr(vc), D,
+                                          float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                          float(scale), _ptr(out))
+    if rc:
+        raise ValueError("bad arguments")
+    return out
+
+
+def decode_attention_fp8(q_bits, k_codes, v_codes, k_scale, v_scale, seq_lens, scale,
+                         heads=None, n_threads=None):
+    """decode_attention for an FP8 cache: k_codes / v_codes per sequence b,
+    uint8 [>= len_b][Hkv][D]; per-tensor scales k_scale, v_scale."""
+    q = as_bf16_bits(q_bits)
+    B, Hq, D = q.shape
+    Hkv = np.asarray(k_codes[0]).shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), np.float64)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hkv)]
+    keep, qp, Tp, kp, vp, op = [], [], [], [], [], []
+    for (b, h) in heads:
+        kc = np.ascontiguousarray(k_codes[b], np.uint8)
+        vc = np.ascontiguousarray(v_codes[b], np.uint8)
+        qg = np.ascontiguousarray(q[b, h * G:(h + 1) * G])
+        ob = np.zeros((G, D), np.float64)
+        keep += [kc, vc, qg, ob]
+        qp.append(_ptr(qg))
+        Tp.append(int(seq_lens[b]))
+        kp.append(_ptr(kc) + h * D)
+        vp.append(_ptr(vc) + h * D)
+        op.append((b, h, ob))
+    n = len(qp)
+    P = ctypes.c_void_p * max(n, 1)
+    T_arr = np.array(Tp if n else [0], np.int64)
+    outs = P(*[_ptr(o[2]) for o in op]) if n else P()
+    rc = lib().fp4kv_oracle_attention_fp8_batch(
+        n, G, D, P(*qp), _ptr(T_arr), P(*kp), P(*vp), Hkv * D, float(np.float32(k_scale)),
+        float(np.float32(v_scale)), float(scale), outs, n_threads or default_threads())
+    if rc:
+        raise ValueError("bad arguments")
+    for (b, h, ob) in op:
+        out[b, h * G:(h + 1) * G] = ob
+    return out
+
+
 # --------------------------------------------------------------- cost model
 
 def bits_per_number(elem_bits: float, scale_bits: float, group: float) -> float:
@@ -249,6 +343,12 @@ def numbers_per_token(n_layers: int, n_kv_heads: int, head_dim: int) -> int:
     """K and V numbers a token adds to the cache (same section):
     2 x layers x KV heads x head dim."""
     return 2 * n_layers * n_kv_heads * head_dim
+
+
+def fp8_cache_bytes(n_tokens: int, n_layers: int, n_kv_heads: int, head_dim: int) -> float:
+    """Resident bytes of an FP8 E4M3 cache with one scale per tensor: 8 bits
+    per number (the per-tensor scale is negligible per number)."""
+    return n_tokens * numbers_per_token(n_layers, n_kv_heads, head_dim) * bits_per_number(8, 0, 0) / 8
 
 
 def fp4_cache_bytes(n_tokens: int, n_layers: int, n_kv_heads: int, head_dim: int) -> float:

@@ -23,6 +23,11 @@
  *   and value).  Attention is written out from its definition in fp64:
  *   z_t = scale * <q, k_t>,  w_t = exp(z_t - max z),  o = sum w_t v_t / sum w_t.
  *
+ *   FP8 variant -- same page, Concept section, results table: FP8 E4M3 with
+ *   one scale per tensor.  Each element divided by the tensor's scale is
+ *   rounded to E4M3 (nearest, ties to even, saturating, as the FP4 encoder
+ *   does); the stored value is that E4M3 number times the scale.
+ *
  * Readings where the pages are silent are listed with the functions that
  * make them.  Every arithmetic step here is exact except the exp/sum/divide
  * of the attention, which runs in fp64.
@@ -90,6 +95,32 @@ static int round_ratio_rne_sat(double num, double den, double (*value)(int), int
     if (twice > mid2)
         return lo + 1;
     return (lo % 2 == 0) ? lo : lo + 1;         /* exactly halfway: the even code */
+}
+
+/* E4M3 code of num/den by bisection over the monotone table (same result as
+ * round_ratio_rne_sat with the E4M3 table, in 7 steps instead of up to 126):
+ * lo = the largest code whose value*den <= num, then the same halfway rule.
+ * For den a finite positive fp32 value every product and sum below has at
+ * most 24 + 5 significant bits, so it is exact in double. */
+static int e4m3_ratio_rne_sat(double num, double den)
+{
+    if (num >= fp4kv_oracle_e4m3_value(E4M3_MAX_CODE) * den)
+        return E4M3_MAX_CODE;
+    int lo = 0, hi = E4M3_MAX_CODE;               /* value(lo)*den <= num < value(hi)*den */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (fp4kv_oracle_e4m3_value(mid) * den <= num)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double twice = 2.0 * num;
+    double mid2 = (fp4kv_oracle_e4m3_value(lo) + fp4kv_oracle_e4m3_value(lo + 1)) * den;
+    if (twice < mid2)
+        return lo;
+    if (twice > mid2)
+        return lo + 1;
+    return (lo % 2 == 0) ? lo : lo + 1;
 }
 
 /* bf16 bit pattern -> its exact value. */
@@ -211,6 +242,28 @@ int fp4kv_oracle_quantize_rows(const uint16_t *x, int64_t n_rows, int row_len,
     return rc;
 }
 
+/* FP8 E4M3 with one scale per tensor: code = sign << 7 | RNE_sat_E4M3(|x| / s)
+ * for n bf16 values and a finite positive fp32 scale s.  Readings: the
+ * per-tensor scale is given (the pages leave how it is chosen open; a cache
+ * that grows token by token needs it fixed in advance); rounding and
+ * saturation as in the FP4 encoder; the sign is kept for magnitudes that
+ * round to zero (code 0x80), as for the FP4 nibbles.  Returns -1 if an input
+ * is not finite or the scale is not finite and positive. */
+int fp4kv_oracle_quantize_fp8(const uint16_t *x, int64_t n, float scale, uint8_t *codes)
+{
+    double s = (double)scale;
+    if (!isfinite(s) || !(s > 0.0))
+        return -1;
+    for (int64_t i = 0; i < n; i++) {
+        double v = bf16_value(x[i]);
+        if (!isfinite(v))
+            return -1;
+        int neg = signbit(v) ? 1 : 0;
+        codes[i] = (uint8_t)((neg << 7) | e4m3_ratio_rne_sat(fabs(v), s));
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------- attention */
 
 /* Dequantised cache value: E2M1(code) * scale, signed by the nibble's sign
@@ -276,6 +329,108 @@ int fp4kv_oracle_attention(const uint16_t *q, int G, int D, int64_t T,
     free(z);
     free(kv);
     return 0;
+}
+
+/* Dequantised FP8 value: +-E4M3(code) * scale. */
+static double fp8_value(uint8_t code, double scale)
+{
+    double v = fp4kv_oracle_e4m3_value(code & 0x7F) * scale;
+    return (code & 0x80) ? -v : v;
+}
+
+/* The same attention for an FP8 cache with per-tensor scales k_scale and
+ * v_scale: token t's D codes at k_codes + t*stride (and v_codes). */
+int fp4kv_oracle_attention_fp8(const uint16_t *q, int G, int D, int64_t T,
+                               const uint8_t *k_codes, const uint8_t *v_codes, int64_t stride,
+                               double k_scale, double v_scale, double scale, double *out)
+{
+    if (G < 1 || D < 1 || T < 0)
+        return -1;
+    for (int i = 0; i < G * D; i++)
+        out[i] = 0.0;
+    if (T == 0)
+        return 0;
+    double *z = (double *)malloc(sizeof(double) * (size_t)T);
+    if (!z)
+        return -3;
+    for (int g = 0; g < G; g++) {
+        const uint16_t *qg = q + (int64_t)g * D;
+        double zmax = -INFINITY;
+        for (int64_t t = 0; t < T; t++) {
+            double dot = 0.0;
+            for (int c = 0; c < D; c++)
+                dot += bf16_value(qg[c]) * fp8_value(k_codes[t * stride + c], k_scale);
+            z[t] = scale * dot;
+            if (z[t] > zmax)
+                zmax = z[t];
+        }
+        double wsum = 0.0;
+        double *og = out + (int64_t)g * D;
+        for (int64_t t = 0; t < T; t++) {
+            double w = exp(z[t] - zmax);
+            wsum += w;
+            for (int c = 0; c < D; c++)
+                og[c] += w * fp8_value(v_codes[t * stride + c], v_scale);
+        }
+        for (int c = 0; c < D; c++)
+            og[c] /= wsum;
+    }
+    free(z);
+    return 0;
+}
+
+typedef struct {
+    int64_t i0, i1;
+    int G, D;
+    const uint16_t *const *q;
+    const int64_t *T;
+    const uint8_t *const *kc, *const *vc;
+    int64_t stride;
+    double k_scale, v_scale, scale;
+    double *const *out;
+    int rc;
+} attn8_job;
+
+static void *attn8_worker(void *arg)
+{
+    attn8_job *j = (attn8_job *)arg;
+    for (int64_t i = j->i0; i < j->i1; i++) {
+        int rc = fp4kv_oracle_attention_fp8(j->q[i], j->G, j->D, j->T[i], j->kc[i], j->vc[i], j->stride,
+                                            j->k_scale, j->v_scale, j->scale, j->out[i]);
+        if (rc)
+            j->rc = rc;
+    }
+    return NULL;
+}
+
+int fp4kv_oracle_attention_fp8_batch(int64_t n_problems, int G, int D, const uint16_t *const *q,
+                                     const int64_t *T, const uint8_t *const *k_codes,
+                                     const uint8_t *const *v_codes, int64_t stride, double k_scale,
+                                     double v_scale, double scale, double *const *out, int n_threads)
+{
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if ((int64_t)n_threads > n_problems)
+        n_threads = n_problems > 0 ? (int)n_problems : 1;
+    pthread_t tid[256];
+    attn8_job job[256];
+    int64_t per = (n_problems + n_threads - 1) / n_threads;
+    for (int i = 0; i < n_threads; i++) {
+        int64_t i0 = i * per, i1 = i0 + per > n_problems ? n_problems : i0 + per;
+        if (i0 > i1)
+            i0 = i1;
+        job[i] = (attn8_job){i0, i1, G, D, q, T, k_codes, v_codes, stride, k_scale, v_scale, scale, out, 0};
+        pthread_create(&tid[i], NULL, attn8_worker, &job[i]);
+    }
+    int rc = 0;
+    for (int i = 0; i < n_threads; i++) {
+        pthread_join(tid[i], NULL);
+        if (job[i].rc)
+            rc = job[i].rc;
+    }
+    return rc;
 }
 
 /* A batch of independent (sequence, KV head) attention problems, run on
