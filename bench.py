@@ -29,24 +29,32 @@ sys.path.insert(0, ROOT)
 METRIC = "FP4-KV decode attention: achieved HBM GB/s (% of peak) and decode steps/s"
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E peak, GB/s
 SETTLE_CALLS = 100                          # untimed decode calls before the warm-up steps
-# sources of the split kernel whose HBM counters profiles/ may hold
-KERNEL_SOURCES = [os.path.join(ROOT, "fp4_quantised_kv_amd", "csrc", n)
-                  for n in ("fp4kv_decode_mfma.hip", "fp4kv_merge.h", "fp4kv_internal.h")]
+# sources of the split kernel (per cache format) whose HBM counters profiles/ may hold
+_CSRC = os.path.join(ROOT, "fp4_quantised_kv_amd", "csrc")
+KERNEL_SOURCES = {
+    "fp4": ["fp4kv_decode_mfma.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h"],
+    "fp8": ["fp4kv_decode_fp8.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h"],
+}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(fmt: str = "fp4") -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
+    for name in KERNEL_SOURCES[fmt]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def _counter_file(workload: str, fmt: str) -> str:
+    prefix = "decode_split" if fmt == "fp4" else "decode_split_fp8"
+    return os.path.join(PROFILES, f"{prefix}_{workload}_hbm_counters.txt")
+
+
+def measured_traffic(workload: str, fmt: str = "fp4"):
     """Per-launch HBM bytes of the split kernel from the committed counter
     summary, if it was taken from the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"decode_split_{workload}_hbm_counters.txt")
+    path = _counter_file(workload, fmt)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -54,7 +62,7 @@ def measured_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_digest():
+    if fields.get("kernel_source_sha256_16") != kernel_source_digest(fmt):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -62,7 +70,7 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, seed, threads):
+def cpu_baseline(w, seed, threads, fmt="fp4"):
     """The oracle (fp64 decode attention from its own codes) on a bounded
     sample: whole sequences of the workload, all their KV heads."""
     import numpy as np
@@ -75,23 +83,33 @@ def cpu_baseline(w, seed, threads):
     kc, ks, vc, vs = [], [], [], []
     budget_tokens = 1 << 17                    # cap the sample at 131072 tokens per sequence
     sample_lens = [min(int(lens[b]), budget_tokens) for b in range(w.batch)]
+    k_scale, v_scale = wl.fp8_tensor_scales(w, seed)
     for b in range(w.batch):
         if b in seqs:
             k = wl.kv_tokens(w, seed, b, "k", 0, sample_lens[b])
             v = wl.kv_tokens(w, seed, b, "v", 0, sample_lens[b])
-            a, sa, _ = oracle.quantize(wl.bf16_bits(k), want_xhat=False, n_threads=threads)
-            c, sc, _ = oracle.quantize(wl.bf16_bits(v), want_xhat=False, n_threads=threads)
+            if fmt == "fp8":
+                a, c = oracle.quantize_fp8(wl.bf16_bits(k), k_scale), oracle.quantize_fp8(wl.bf16_bits(v), v_scale)
+                sa = sc = None
+            else:
+                a, sa, _ = oracle.quantize(wl.bf16_bits(k), want_xhat=False, n_threads=threads)
+                c, sc, _ = oracle.quantize(wl.bf16_bits(v), want_xhat=False, n_threads=threads)
         else:
             a = c = np.zeros((0, w.kv_heads, w.head_dim), np.uint8)
             sa = sc = np.zeros((0, w.kv_heads, w.head_dim // 16), np.uint8)
         kc.append(a); ks.append(sa); vc.append(c); vs.append(sc)
     heads = [(b, h) for b in seqs for h in range(w.kv_heads)]
     t0 = time.perf_counter()
-    oracle.decode_attention(wl.bf16_bits(q), kc, ks, vc, vs, sample_lens, w.head_dim ** -0.5,
-                            heads=heads, n_threads=threads)
+    if fmt == "fp8":
+        oracle.decode_attention_fp8(wl.bf16_bits(q), kc, vc, k_scale, v_scale, sample_lens, w.head_dim ** -0.5,
+                                    heads=heads, n_threads=threads)
+    else:
+        oracle.decode_attention(wl.bf16_bits(q), kc, ks, vc, vs, sample_lens, w.head_dim ** -0.5,
+                                heads=heads, n_threads=threads)
     dt = time.perf_counter() - t0
     tokens = sum(sample_lens[b] for b in seqs)
-    bytes_ = tokens * 2 * w.kv_heads * w.head_dim * 9 // 16 + n_seq * w.q_heads * w.head_dim * 6
+    per_number = 1.0 if fmt == "fp8" else 9 / 16
+    bytes_ = int(tokens * 2 * w.kv_heads * w.head_dim * per_number) + n_seq * w.q_heads * w.head_dim * 6
     return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_seq} of {w.batch} sequences, {tokens} tokens, all {w.kv_heads} KV heads; "
                       f"decode attention from the oracle's own codes in fp64, {dt:.2f} s wall"}
@@ -132,6 +150,8 @@ def main():
     ap.add_argument("--workload", default="gqa8_b32_ctx32k")
     ap.add_argument("--splits", type=int, default=None, help="context splits (default: the workload's)")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--format", choices=("fp4", "fp8"), default="fp4",
+                    help="cache format: FP4 E2M1 + E4M3 per 16 (default) or FP8 E4M3 with per-tensor scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the streaming-read probe (the achievable HBM read rate for this access pattern)")
@@ -168,7 +188,7 @@ def main():
     total_steps = args.warmup + args.steps
     t_setup = time.perf_counter()
     print(f"# building cache for {w.name}: {w.description}", file=sys.stderr, flush=True)
-    gc = hx.build_cache(w, args.seed, extra_tokens=total_steps if paged else 0, zero=False)
+    gc = hx.build_cache(w, args.seed, extra_tokens=total_steps if paged else 0, zero=False, fmt=args.format)
     print(f"# cache built in {time.perf_counter() - t_setup:.1f} s "
           f"({gc.layout.cache_bytes / 1e9:.3f} GB)", file=sys.stderr, flush=True)
     L = gc.layout
@@ -281,7 +301,7 @@ def main():
     else:
         split_bytes_b2b = split_bytes
     split_gbs = split_bytes_b2b / (t_split_b2b * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name, args.format)
 
     result = {
         "metric": METRIC,
@@ -298,6 +318,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": w.kv_heads,
                    "head_dim": D, "context": w.context if not paged else f"{w.min_len}..{w.max_len}",
+                   "format": ("fp8_e4m3_per_tensor_scale" if args.format == "fp8" else "fp4_e2m1_e4m3_per16"),
                    "splits": splits, "partials": partials, "page_size": 64,
                    "cache_bytes": L.cache_bytes},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
@@ -307,7 +328,9 @@ def main():
         "settle_decode_calls": SETTLE_CALLS,
         "wall_s_timed": round(wall, 4),
         "host_enqueue_ms_per_step": round(1e3 * host_enqueue / args.steps, 5),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_mfma<128, staged>" if D == 128 else "decode_split_mfma<64>",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("decode_split_fp8" if args.format == "fp8" else
+                                "decode_split_mfma<128, staged>" if D == 128 else "decode_split_mfma<64>"),
                      "achieved": round(split_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes_b2b)},
@@ -315,9 +338,9 @@ def main():
     if not args.no_prefill:
         result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)
     if not args.no_read_probe:
-        # the achievable read rate: the same number of 9216-byte blocks as
-        # the cache, streamed once by the library's read probe
-        buf = torch.full((L.cache_bytes,), 1, dtype=torch.uint8, device=dev)
+        # the achievable read rate: the cache's size in 9216-byte blocks,
+        # streamed once by the library's read probe
+        buf = torch.full((L.cache_bytes // 9216 * 9216,), 1, dtype=torch.uint8, device=dev)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         for _ in range(3):
             fk.read_probe(buf, sink)
@@ -341,7 +364,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
-        result["cpu_baseline"] = cpu_baseline(w, args.seed, threads)
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, threads, args.format)
     print(json.dumps(result), flush=True)
 
 

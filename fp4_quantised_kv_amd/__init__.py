@@ -17,7 +17,7 @@ import os
 
 __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
            "quantize_append", "decode_attention", "decode_split", "decode_combine",
-           "status_string", "PAGE_SIZE", "MAX_GROUP"]
+           "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(HERE, "libfp4kv.so")
@@ -38,10 +38,15 @@ class Fp4KVError(RuntimeError):
         self.status = status
 
 
+FORMAT_FP4_E2M1 = 0        # E2M1 elements, one E4M3 scale per 16 channels
+FORMAT_FP8_E4M3 = 1        # E4M3 elements, one fp32 scale per tensor
+
+
 class CacheParams(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("num_pages", ctypes.c_int64)]
+                ("page_size", ctypes.c_int32), ("format", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
 
 
 class CacheLayout(ctypes.Structure):
@@ -62,6 +67,14 @@ class CacheLayout(ctypes.Structure):
     @property
     def num_pages(self):
         return self.params.num_pages
+
+    @property
+    def format(self):
+        return self.params.format
+
+    @property
+    def fp8(self):
+        return self.params.format == FORMAT_FP8_E4M3
 
 
 _LIB = None
@@ -115,9 +128,11 @@ def _check(call, rc):
         raise Fp4KVError(call, rc)
 
 
-def cache_layout(num_kv_heads: int, head_dim: int, num_pages: int,
-                 page_size: int = PAGE_SIZE) -> CacheLayout:
-    p = CacheParams(num_kv_heads, head_dim, page_size, 0, num_pages)
+def cache_layout(num_kv_heads: int, head_dim: int, num_pages: int, page_size: int = PAGE_SIZE,
+                 format: int = FORMAT_FP4_E2M1, k_scale: float = 0.0, v_scale: float = 0.0) -> CacheLayout:
+    """Layout of a paged cache.  FP8 (format=FORMAT_FP8_E4M3) takes the K and V
+    tensors' scales; FP4 takes none (0)."""
+    p = CacheParams(num_kv_heads, head_dim, page_size, format, num_pages, k_scale, v_scale)
     out = CacheLayout()
     _check("fp4kv_cache_layout", library().fp4kv_cache_layout(ctypes.byref(p), ctypes.byref(out)))
     return out

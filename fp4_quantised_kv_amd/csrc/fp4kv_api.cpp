@@ -20,19 +20,33 @@ constexpr int64_t kMaxPartials = 65535;  // partials per row: the split kernel's
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Layout of one (page, KV head) block: K codes, K scales, V codes, V scales.
+// FP8 per-tensor scales the quantiser handles exactly: 2^-64 .. 2^64.
+bool in_scale_range(float s) { return s >= 0x1p-64f && s <= 0x1p64f; }
+
+// Layout of one (page, KV head) block.  FP4: K codes, K scales, V codes, V
+// scales.  FP8: K codes, V codes (empty scale planes at their ends).
 int fill_layout(const fp4kv_cache_params &p, fp4kv_cache_layout_t *out)
 {
-    if (p.num_kv_heads < 1 || p.num_pages < 1 || p.reserved != 0)
+    if (p.num_kv_heads < 1 || p.num_pages < 1)
         return FP4KV_ERR_INVALID_ARGUMENT;
+    const bool fp8 = p.format == FP4KV_FORMAT_FP8_E4M3;
+    if (p.format != FP4KV_FORMAT_FP4_E2M1 && !fp8)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (fp8 ? !(std::isfinite(p.k_scale) && p.k_scale > 0.0f && std::isfinite(p.v_scale) && p.v_scale > 0.0f)
+            : (p.k_scale != 0.0f || p.v_scale != 0.0f))
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (fp8 && !(in_scale_range(p.k_scale) && in_scale_range(p.v_scale)))
+        return FP4KV_ERR_UNSUPPORTED;
     if (p.head_dim != 64 && p.head_dim != 128)
+        return FP4KV_ERR_UNSUPPORTED;
+    if (fp8 && p.head_dim != 128)
         return FP4KV_ERR_UNSUPPORTED;
     if (p.page_size != kPage)
         return FP4KV_ERR_UNSUPPORTED;
     const int64_t D = p.head_dim;
-    const int64_t codes = static_cast<int64_t>(kPage) * D / 2;
-    const int64_t scales = static_cast<int64_t>(kPage) * D / 16;
-    const int64_t block = 2 * (codes + scales);               // = 64 * D * 9 / 8
+    const int64_t codes = fp8 ? kPage * D : kPage * D / 2;
+    const int64_t scales = fp8 ? 0 : kPage * D / 16;
+    const int64_t block = 2 * (codes + scales);               // FP4: 64 * D * 9 / 8; FP8: 128 * D
     const int64_t page_stride = block * p.num_kv_heads;
     if (p.num_pages > std::numeric_limits<int64_t>::max() / page_stride)
         return FP4KV_ERR_INVALID_ARGUMENT;
@@ -46,7 +60,7 @@ int fill_layout(const fp4kv_cache_params &p, fp4kv_cache_layout_t *out)
     L.head_stride = block;
     L.page_stride = page_stride;
     L.cache_bytes = page_stride * p.num_pages;
-    L.bytes_per_token = 2 * static_cast<int64_t>(p.num_kv_heads) * D * 9 / 16;
+    L.bytes_per_token = page_stride / kPage;
     *out = L;
     return FP4KV_OK;
 }
@@ -81,6 +95,9 @@ fp4kv::CacheGeom geom_of(const fp4kv_cache_layout_t &L)
     g.v_scales_off = L.v_scales_offset;
     g.head_stride = L.head_stride;
     g.page_stride = L.page_stride;
+    g.fp8 = L.params.format == FP4KV_FORMAT_FP8_E4M3;
+    g.k_scale = L.params.k_scale;
+    g.v_scale = L.params.v_scale;
     return g;
 }
 
@@ -227,7 +244,9 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     a->pages_per_split = plan.pages_per_split;
     a->partials = plan.partials;
     a->staged = true;
-    a->scale_log2e = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+    // scores are kept in base 2; an FP8 cache's K tensor scale multiplies every score
+    const double k_scale = layout->params.format == FP4KV_FORMAT_FP8_E4M3 ? layout->params.k_scale : 1.0;
+    a->scale_log2e = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634 * k_scale);
     a->ws_o = static_cast<float *>(workspace);
     a->ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + plan.ws_o_bytes);
 

@@ -15,6 +15,8 @@ struct CacheGeom {
     int64_t num_pages;
     int64_t k_codes_off, k_scales_off, v_codes_off, v_scales_off;
     int64_t head_stride, page_stride;
+    bool fp8;                    // FP8 E4M3 elements with per-tensor scales (else FP4)
+    float k_scale, v_scale;      // FP8 per-tensor scales
 };
 
 struct DecodeArgs {
@@ -40,8 +42,11 @@ hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const u
 // Decode split kernels: the vector-ALU one and the matrix-core one.
 hipError_t launch_split_valu(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream);
+// The FP8 cache's kernel (D = 128).
+hipError_t launch_split_fp8(const DecodeArgs &a, hipStream_t stream);
 
-// Chooses the kernel: matrix cores with LDS staging for D = 128, unless
+// Chooses the kernel: the FP8 kernel for an FP8 cache; for FP4, matrix
+// cores with LDS staging for D = 128, unless
 // FP4KV_DECODE_KERNEL names another (valu: vector ALU; mfma_direct: matrix
 // cores with operands loaded straight into registers).
 hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);

@@ -285,6 +285,84 @@ __global__ __launch_bounds__(256) void append_runs_kernel(
     *reinterpret_cast<uint2 *>(base + g.v_scales_off + v_scale_byte<D>(off0, blk)) = make_uint2(vs[0], vs[1]);
 }
 
+// -------------------------------------------------- FP8 (per-tensor scale)
+
+// E4M3 code of |x| / s, rounded to nearest even and saturating at 448
+// ("Quantising the KV cache", Concept section, results table: FP8 E4M3
+// with one scale per tensor; rounding as the page's encoder does it).  The
+// fp32 quotient is correctly rounded, so it lies on the same side of every
+// E4M3 rounding midpoint as the exact quotient, except that it can land
+// exactly on one; then the sign of q*s - |x|, exact in one FMA, decides.
+// The bound on s (2^-64 .. 2^64, checked on the host) keeps that FMA's
+// result away from underflow.
+__device__ __forceinline__ uint32_t fp8_code(uint32_t bits16, float s)
+{
+    const float x = __uint_as_float((bits16 & 0x7FFFu) << 16);
+    const float q = x / s;
+    uint32_t c;
+    if (!(q < 448.0f)) {
+        c = 126u;
+    } else {
+        c = e4m3_code_rne_sat(q);
+        uint32_t lo;
+        bool mid;
+        if (q < 0.015625f) {                            // subnormal grid 2^-9
+            const float t = q * 512.0f;                 // exact
+            const float f = __builtin_floorf(t);
+            lo = static_cast<uint32_t>(f);
+            mid = t - f == 0.5f;
+        } else {
+            const uint32_t b = __float_as_uint(q);
+            lo = (b >> 20) - (120u << 3);               // truncated: the lower neighbour
+            mid = (b & 0xFFFFFu) == 0x80000u;
+        }
+        if (mid) {
+            const float r = __builtin_fmaf(q, s, -x);
+            c = r > 0.0f ? lo : (r < 0.0f ? lo + 1u : c);
+        }
+    }
+    return c | ((bits16 >> 8) & 0x80u);
+}
+
+// One thread per (token, KV head, 16-channel block).  K: the block's 16
+// codes are one 16-byte store into the token's row.  V: channel 16*blk + i
+// of the token goes to byte (off % 8) of row (slice, half, channel); every
+// byte belongs to one token, so no read-modify-write is needed.
+template <int D>
+__global__ __launch_bounds__(256) void append_fp8_kernel(
+    CacheGeom g, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t n_tokens,
+    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache)
+{
+    constexpr int NB = D / 16;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= n_tokens * g.num_kv_heads * NB)
+        return;
+    const int blk = static_cast<int>(idx % NB);
+    const int64_t th = idx / NB;                        // token * H_kv + head
+    const int head = static_cast<int>(th % g.num_kv_heads);
+    const int64_t slot = slots[th / g.num_kv_heads];
+    if (slot < 0 || slot >= g.num_pages * kPage)
+        return;
+    uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
+    const int off = static_cast<int>(slot % kPage);
+    uint32_t w[8];
+    load_block16(k + th * D + 16 * blk, w);
+    uint32_t kc[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
+        kc[c >> 2] |= fp8_code(bits, g.k_scale) << (8 * (c & 3));
+    }
+    *reinterpret_cast<uint4 *>(base + g.k_codes_off + off * D + 16 * blk) = make_uint4(kc[0], kc[1], kc[2], kc[3]);
+    load_block16(v + th * D + 16 * blk, w);
+    uint8_t *vrow = base + g.v_codes_off + ((((off >> 4) * 2 + ((off >> 3) & 1)) * D + 16 * blk) * 8) + (off & 7);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
+        vrow[8 * c] = static_cast<uint8_t>(fp8_code(bits, g.v_scale));
+    }
+}
+
 // ----------------------------------------------------------------- decode
 
 __device__ __forceinline__ float wave_max(float x)
@@ -587,7 +665,10 @@ hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const u
                                   hipStream_t stream)
 {
     const int64_t per_token = static_cast<int64_t>(g.num_kv_heads) * (g.head_dim / 16);
-    if (n_tokens >= kRunKernelMinTokens) {
+    if (g.fp8) {
+        const int64_t blocks = (n_tokens * per_token + 255) / 256;
+        append_fp8_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+    } else if (n_tokens >= kRunKernelMinTokens) {
         const int64_t blocks = ((n_tokens + 7) / 8 * per_token + 255) / 256;
         if (g.head_dim == 64)
             append_runs_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
@@ -610,6 +691,8 @@ hipError_t launch_split_valu(const DecodeArgs &a, hipStream_t stream)
 
 hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
 {
+    if (a.geom.fp8)
+        return launch_split_fp8(a, stream);
     const char *v = std::getenv("FP4KV_DECODE_KERNEL");
     if (v && std::strcmp(v, "valu") == 0)
         return launch_split_valu(a, stream);

@@ -38,20 +38,26 @@ def _append_rows(layout, cache, k, v, slots, device):
 
 
 def build_cache(w: wl.Workload, seed: int, device="cuda", keep_seqs=(), extra_tokens=0,
-                seqs: Optional[List[int]] = None, zero=True) -> GpuCache:
+                seqs: Optional[List[int]] = None, zero=True, fmt: str = "fp4") -> GpuCache:
     """Quantise every sequence's context into a fresh cache.
 
     Contiguous workloads get an identity page table; the paged workload gets
     seeded lengths and a seeded random page table with room for
     `extra_tokens` more tokens per sequence.  `seqs` limits which sequences
     are filled (others stay zero); `keep_seqs` keeps their bf16 rows on the
-    CPU for the oracle."""
+    CPU for the oracle.  fmt "fp8" builds an FP8 E4M3 cache with the
+    workload's per-tensor scales."""
     lens = wl.seq_lengths(w, seed)
     if w.kind == "paged":
         pt = wl.random_page_table(lens, extra_tokens, seed, w.name)
     else:
         pt = wl.identity_page_table(w.batch, int(lens.max()) + extra_tokens)
-    layout = fk.cache_layout(w.kv_heads, w.head_dim, pt.num_pages)
+    if fmt == "fp8":
+        ks, vs = wl.fp8_tensor_scales(w, seed)
+        layout = fk.cache_layout(w.kv_heads, w.head_dim, pt.num_pages, format=fk.FORMAT_FP8_E4M3,
+                                 k_scale=ks, v_scale=vs)
+    else:
+        layout = fk.cache_layout(w.kv_heads, w.head_dim, pt.num_pages)
     cache = (torch.zeros if zero else torch.empty)(layout.cache_bytes, dtype=torch.uint8, device=device)
     fk_k = wl.channel_factors(w, seed, "k")
     fk_v = wl.channel_factors(w, seed, "v")
@@ -112,6 +118,24 @@ def read_pages(cache: torch.Tensor, layout: fk.CacheLayout, pages, n_tokens: int
         return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(P * 64, H, x.shape[-1])[:n_tokens])
 
     return tok(kc), tok(ks), tok(vc), tok(vs)
+
+
+def read_pages_fp8(cache: torch.Tensor, layout: fk.CacheLayout, pages, n_tokens: int):
+    """Stored codes of the first n_tokens slots of a list of pages of an FP8
+    cache, token-major: K [n][H][D], V [n][H][D] (V un-laid from its
+    [slice][half][channel][8 tokens] rows)."""
+    H, D = layout.num_kv_heads, layout.head_dim
+    idx = torch.as_tensor(np.asarray(pages, np.int64), device=cache.device)
+    blocks = cache[: layout.cache_bytes].view(-1, H, layout.block_bytes)[idx].cpu().numpy()
+    P = len(pages)
+    kc = blocks[:, :, layout.k_codes_offset:layout.k_codes_offset + 64 * D].reshape(P, H, 64, D)
+    v = blocks[:, :, layout.v_codes_offset:layout.v_codes_offset + 64 * D].reshape(P, H, 4, 2, D, 8)
+    vc = v.transpose(0, 1, 2, 3, 5, 4).reshape(P, H, 64, D)         # token = 16*slice + 8*half + i
+
+    def tok(x):
+        return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(P * 64, H, D)[:n_tokens])
+
+    return tok(kc), tok(vc)
 
 
 def row_rel_error(out: np.ndarray, ref: np.ndarray) -> np.ndarray:

@@ -122,6 +122,18 @@ def channel_factors(w: Workload, seed: int, tensor: str) -> torch.Tensor:
     return f
 
 
+def fp8_tensor_scales(w: Workload, seed: int) -> Tuple[float, float]:
+    """(k_scale, v_scale) for an FP8 cache of this workload: the per-tensor
+    scale is an input of that format, fixed before any token is stored (as a
+    calibrated scale would be).  Chosen here as 6 x the largest channel
+    factor of the tensor over 448, so that a 6-sigma value of the widest
+    channel maps to the top of the E4M3 range; rounded to fp32."""
+    import numpy as np
+    ks = np.float32(6.0 * float(channel_factors(w, seed, "k").max()) / 448.0)
+    vs = np.float32(6.0 * float(channel_factors(w, seed, "v").max()) / 448.0)
+    return float(ks), float(vs)
+
+
 def kv_tokens(w: Workload, seed: int, seq: int, tensor: str, t0: int, t1: int,
               factors: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 [t1 - t0][Hkv][D] K or V rows of tokens [t0, t1) of sequence seq."""

@@ -63,15 +63,25 @@ enum fp4kv_status {
 #define FP4KV_PAGE_SIZE 64                /* tokens per page (the only size in this version) */
 #define FP4KV_MAX_GROUP 16                /* query heads per KV head supported */
 
+/* Number formats of a cache.  ("Quantising the KV cache", Concept section,
+ * results table: "FP4 E2M1, E4M3 scale per 16" at 4.5 bits per number and
+ * "FP8 E4M3, one scale per tensor" at 8.) */
+enum fp4kv_format {
+    FP4KV_FORMAT_FP4_E2M1 = 0,            /* E2M1 elements, one E4M3 scale per 16 channels */
+    FP4KV_FORMAT_FP8_E4M3 = 1             /* E4M3 elements, one fp32 scale per tensor (K, V) */
+};
+
 /* Shape of one layer's cache.  ("Quantising the KV cache", Maths section:
  * a token holds 2 x KV heads x head dim numbers per layer; a model keeps one
  * cache per layer, e.g. one buffer per layer or offsets into one buffer.) */
 typedef struct fp4kv_cache_params {
     int32_t num_kv_heads;                 /* H_kv >= 1 */
-    int32_t head_dim;                     /* D: 64 or 128 */
+    int32_t head_dim;                     /* D: 64 or 128 (FP8: 128) */
     int32_t page_size;                    /* tokens per page: FP4KV_PAGE_SIZE */
-    int32_t reserved;                     /* must be 0 */
+    int32_t format;                       /* enum fp4kv_format */
     int64_t num_pages;                    /* pages in the pool, >= 1 */
+    float k_scale;                        /* FP8: the K tensor's scale, 2^-64 .. 2^64; FP4: 0 */
+    float v_scale;                        /* FP8: the V tensor's scale, 2^-64 .. 2^64; FP4: 0 */
 } fp4kv_cache_params;
 
 /* Byte layout of the cache, filled by fp4kv_cache_layout.  Plain data: it
@@ -93,24 +103,34 @@ typedef struct fp4kv_cache_params {
  * the smallest subnormal 2^-9).  Token slot s lives in page s / 64 at
  * offset s % 64.  V is stored channel-major in 16-token slices so that the
  * decode kernels read each channel's tokens contiguously and convert two
- * consecutive tokens of one channel per instruction. */
+ * consecutive tokens of one channel per instruction.
+ *
+ * FP8 format: a block holds
+ *   K codes   [64 tokens][D] bytes         at k_codes_offset (0)
+ *   V codes   [4 slices][2 halves][D][8]   at v_codes_offset (64*D): row
+ *             (j, h, c) holds channel c of tokens 16j+8h .. 16j+8h+7
+ * and no scale planes (k_scales_offset = 64*D and v_scales_offset = 128*D
+ * mark empty planes).  A code byte is sign << 7 | E4M3 magnitude code; the
+ * stored value is E4M3(code) times the tensor's scale from the params. */
 typedef struct fp4kv_cache_layout_t {
     fp4kv_cache_params params;
-    int64_t block_bytes;                  /* 64 * D * 9 / 8 */
+    int64_t block_bytes;                  /* FP4: 64 * D * 9 / 8; FP8: 128 * D */
     int64_t k_codes_offset;               /* offsets inside a block */
     int64_t k_scales_offset;
     int64_t v_codes_offset;
     int64_t v_scales_offset;
     int64_t head_stride;                  /* = block_bytes */
     int64_t page_stride;                  /* = num_kv_heads * block_bytes */
-    int64_t cache_bytes;                  /* = num_pages * page_stride: exactly 9/16 B per number */
-    int64_t bytes_per_token;              /* = 2 * H_kv * D * 9 / 16 */
+    int64_t cache_bytes;                  /* = num_pages * page_stride: exactly 9/16 B (FP8: 1 B) per number */
+    int64_t bytes_per_token;              /* = 2 * H_kv * D * 9 / 16 (FP8: 2 * H_kv * D) */
 } fp4kv_cache_layout_t;
 
 /* Fill *out from *params.  Host only, no HIP call, pure.
- * Errors: INVALID_ARGUMENT for a null pointer, H_kv < 1, num_pages < 1,
- * reserved != 0 or a cache size that overflows int64; UNSUPPORTED for
- * head_dim not in {64, 128} or page_size != 64. */
+ * Errors: INVALID_ARGUMENT for a null pointer, H_kv < 1, num_pages < 1, an
+ * unknown format, FP4 scales not 0 or FP8 scales not finite and positive,
+ * or a cache size that overflows int64; UNSUPPORTED for head_dim not in
+ * {64, 128} (FP8: not 128), page_size != 64 or FP8 scales outside
+ * 2^-64 .. 2^64. */
 FP4KV_API int fp4kv_cache_layout(const fp4kv_cache_params *params, fp4kv_cache_layout_t *out);
 
 /* Quantise n_tokens tokens' K and V rows and store them at their slots.
@@ -123,6 +143,9 @@ FP4KV_API int fp4kv_cache_layout(const fp4kv_cache_params *params, fp4kv_cache_l
  * tokens and the bytes of a token do not depend on the order of calls or on
  * which tokens share a call (V code bytes shared by two tokens are updated
  * nibble-wise with atomics unless one call covers both).
+ * FP8 format ("Quantising the KV cache", Concept section, results table):
+ * code = sign << 7 | E4M3 round-to-nearest-even of |x| / scale with the
+ * tensor's scale from the layout, saturating at 448, sign kept.
  *   layout        host, from fp4kv_cache_layout (re-checked).
  *   k, v          device bf16 [n_tokens][H_kv][D], contiguous, 16-B aligned.
  *   n_tokens      >= 0; 0 is a no-op (pointers may then be NULL).

@@ -48,16 +48,35 @@ def test_layout_sizes(H, D, pages):
     assert L.page_stride == H * L.block_bytes and L.head_stride == L.block_bytes
 
 
-@pytest.mark.parametrize("H,D,P,pages,reserved,code", [
-    (0, 128, 64, 1, 0, fk.ERR_INVALID_ARGUMENT), (8, 128, 64, 0, 0, fk.ERR_INVALID_ARGUMENT),
-    (8, 128, 64, 1, 1, fk.ERR_INVALID_ARGUMENT), (8, 96, 64, 1, 0, fk.ERR_UNSUPPORTED),
-    (8, 100, 64, 1, 0, fk.ERR_UNSUPPORTED), (8, 256, 64, 1, 0, fk.ERR_UNSUPPORTED),
-    (8, 128, 32, 1, 0, fk.ERR_UNSUPPORTED), (8, 128, 64, 1 << 60, 0, fk.ERR_INVALID_ARGUMENT)])
-def test_layout_rejects(H, D, P, pages, reserved, code):
-    p = fk.CacheParams(H, D, P, reserved, pages)
+@pytest.mark.parametrize("H,D,P,pages,fmt,ks,vs,code", [
+    (0, 128, 64, 1, 0, 0, 0, fk.ERR_INVALID_ARGUMENT), (8, 128, 64, 0, 0, 0, 0, fk.ERR_INVALID_ARGUMENT),
+    (8, 128, 64, 1, 2, 0, 0, fk.ERR_INVALID_ARGUMENT), (8, 96, 64, 1, 0, 0, 0, fk.ERR_UNSUPPORTED),
+    (8, 100, 64, 1, 0, 0, 0, fk.ERR_UNSUPPORTED), (8, 256, 64, 1, 0, 0, 0, fk.ERR_UNSUPPORTED),
+    (8, 128, 32, 1, 0, 0, 0, fk.ERR_UNSUPPORTED), (8, 128, 64, 1 << 60, 0, 0, 0, fk.ERR_INVALID_ARGUMENT),
+    (8, 128, 64, 1, 0, 1.0, 0, fk.ERR_INVALID_ARGUMENT),            # FP4 takes no scales
+    (8, 128, 64, 1, 1, 0.0, 1.0, fk.ERR_INVALID_ARGUMENT),          # FP8 needs both scales
+    (8, 128, 64, 1, 1, 1.0, -1.0, fk.ERR_INVALID_ARGUMENT),
+    (8, 128, 64, 1, 1, float("inf"), 1.0, fk.ERR_INVALID_ARGUMENT),
+    (8, 128, 64, 1, 1, 1.0, float("nan"), fk.ERR_INVALID_ARGUMENT),
+    (8, 128, 64, 1, 1, 2.0 ** -70, 1.0, fk.ERR_UNSUPPORTED),        # outside 2^-64 .. 2^64
+    (8, 128, 64, 1, 1, 1.0, 2.0 ** 70, fk.ERR_UNSUPPORTED),
+    (8, 64, 64, 1, 1, 1.0, 1.0, fk.ERR_UNSUPPORTED)])               # FP8 is D = 128 only
+def test_layout_rejects(H, D, P, pages, fmt, ks, vs, code):
+    p = fk.CacheParams(H, D, P, fmt, pages, ks, vs)
     out = fk.CacheLayout()
     assert fk.library().fp4kv_cache_layout(ctypes.byref(p), ctypes.byref(out)) == code
     assert fk.library().fp4kv_cache_layout(None, ctypes.byref(out)) == fk.ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("H,pages", [(1, 1), (8, 512), (3, 1000)])
+def test_fp8_layout_sizes(H, pages):
+    L = fk.cache_layout(H, 128, pages, format=fk.FORMAT_FP8_E4M3, k_scale=0.5, v_scale=3.0)
+    assert L.block_bytes == 64 * 128 * 2 and L.fp8
+    # 8 bits per number, exactly: the oracle's cost model for FP8 with one scale per tensor
+    assert L.cache_bytes == pages * H * L.block_bytes == oracle.fp8_cache_bytes(pages * 64, 1, H, 128)
+    assert [L.k_codes_offset, L.k_scales_offset, L.v_codes_offset, L.v_scales_offset] == [0, 8192, 8192, 16384]
+    assert L.bytes_per_token * 64 == L.page_stride == H * L.block_bytes
+    assert (L.params.k_scale, L.params.v_scale) == (0.5, 3.0)
 
 
 def test_plan():
