@@ -39,26 +39,33 @@ struct Fp8Offsets {
     uint32_t k, v;
 };
 
-__device__ __forceinline__ Fp8Offsets fp8_offsets(const CacheGeom &g, int col, int jj)
+// K copies fetch whole 128-byte token rows: in copy (tile i, part p), lane l
+// fetches 16-byte chunk l % 8 of the row of tile row 8p + l / 8, i.e. token
+// 32p + 16(l / 32) + 4t + (l / 8) % 4 (t = the tile) -- with the non-temporal
+// hint a row split over two copies could be fetched twice.  The lane that
+// needs chunks 2jj, 2jj+1 of tile row col finds them at lane slots
+// 8(col % 8) + 2jj, +1 of copy (i, col / 8).
+__device__ __forceinline__ Fp8Offsets fp8_offsets(const CacheGeom &g, int lane, int col, int jj)
 {
     Fp8Offsets o;
-    // K: lane (col, jj) reads channels 32jj .. 32jj+31 of token tile_token(t, col)
-    o.k = static_cast<uint32_t>(g.k_codes_off) + static_cast<uint32_t>(tile_token(0, col)) * kD + jj * 32u;
+    o.k = static_cast<uint32_t>(g.k_codes_off) +
+          (16u * (lane >> 5) + ((lane >> 3) & 3)) * kD + (lane & 7) * 16u;
     // V: channels 2col, 2col+1 of slice jj, 8 tokens each
     o.v = static_cast<uint32_t>(g.v_codes_off) + ((jj * 2u) * kD + 2u * col) * 8u;
     return o;
 }
 
-// Half page h of K: tiles 2h, 2h+1; each lane copies the two 16-byte halves
-// of its 32 code bytes.  Slot layout: (tile i, part p) at (2i + p) * 1024.
+// Half page h of K: tiles 2h, 2h+1 (tile t starts 4t token rows past tile
+// 0; part 1 is 32 token rows past part 0).  Slot layout: copy (tile i, part
+// p) at (2i + p) * 1024.
 __device__ __forceinline__ void stage_k8(const uint8_t *blk, const Fp8Offsets &o, int h, uint8_t *slot)
 {
-    const uint8_t *k = blk + o.k + h * 8 * kD;          // tile 2h is 8 token rows past tile 0
+    const uint8_t *k = blk + o.k + h * 8 * kD;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
-            __builtin_amdgcn_global_load_lds(k + i * 4 * kD + 16 * p, slot + (2 * i + p) * 1024, 16, 0, kStream);
+            __builtin_amdgcn_global_load_lds(k + (4 * i + 32 * p) * kD, slot + (2 * i + p) * 1024, 16, 0, kStream);
 }
 
 // Half page h of V: pair block u (32 channels, 256 bytes of rows) at u*1024.
@@ -79,13 +86,14 @@ __device__ __forceinline__ half8_t fp8x8(uint32_t a, uint32_t b)
 // Scores of half page h: tiles 2h + i, A operand of MFMA m = channels
 // 32jj + 8m .. +7 of the lane's token, the same channel order as the query
 // operand.  Tokens at or past `valid` get -inf.
-__device__ __forceinline__ void scores8(const uint8_t *slot, int lane, int jj, int h, int valid,
+__device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, int h, int valid,
                                         const half8_t (&qf)[kD / 32], float (&z)[2][4])
 {
+    const int at = (col >> 3) * 1024 + (((col & 7) << 3) + 2 * jj) * 16;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(slot + (2 * i) * 1024 + lane * 16);
-        const uint4 b = *reinterpret_cast<const uint4 *>(slot + (2 * i + 1) * 1024 + lane * 16);
+        const uint4 a = *reinterpret_cast<const uint4 *>(slot + 2 * i * 1024 + at);
+        const uint4 b = *reinterpret_cast<const uint4 *>(slot + 2 * i * 1024 + at + 16);
         float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8(a.x, a.y), qf[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8(a.z, a.w), qf[1], acc, 0, 0, 0);
@@ -126,7 +134,7 @@ __device__ __forceinline__ void values8(uint4 w, int u, int jj, int h, int valid
 // restrict-qualified so that the compiler's LDS-copy wait tracking knows
 // they never alias.
 __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
-                                          const DecodeArgs &a, const Fp8Offsets &o, int lane, int jj, int h,
+                                          const DecodeArgs &a, const Fp8Offsets &o, int lane, int col, int jj, int h,
                                           int p0, int p1, int len, const int32_t *ptab, int ids, int pid,
                                           const half8_t (&qf)[kD / 32], float zscale, SplitState<kD> &st)
 {
@@ -159,7 +167,7 @@ __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *
             if (cur)
                 wait_vmem_at_most<kCopies>();
             float z[2][4];
-            scores8(kslot, lane, jj, hf, valid, qf, z);
+            scores8(kslot, col, jj, hf, valid, qf, z);
             __builtin_amdgcn_s_waitcnt(kWaitLds);
             if (next)
                 stage_k8(nblk, o, nh, kslot);
@@ -210,14 +218,14 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
 
     SplitState<kD> st;
     init_state(st);
-    const Fp8Offsets o = fp8_offsets(g, col, jj);
+    const Fp8Offsets o = fp8_offsets(g, lane, col, jj);
     const int pid = c.p0 < c.p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
     if (pid >= 0 && pid < g.num_pages) {
         const uint8_t *blk = a.cache + static_cast<int64_t>(pid) * g.page_stride + c.h * g.head_stride;
         stage_k8(blk, o, 0, kslots[wave]);
         stage_v8(blk, o, 0, vslots[wave]);
     }
-    fp8_pages(kslots[wave], vslots[wave], a, o, lane, jj, c.h, c.p0, c.p1, c.len, c.ptab, ids, pid, qf, zscale, st);
+    fp8_pages(kslots[wave], vslots[wave], a, o, lane, col, jj, c.h, c.p0, c.p1, c.len, c.ptab, ids, pid, qf, zscale, st);
 
     // the V tensor's scale multiplies every value, so it multiplies o
 #pragma unroll
