@@ -82,6 +82,22 @@ def lib():
                                                    ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_int64, ctypes.c_int64,
                                                    ctypes.c_double, ctypes.c_void_p, ctypes.c_int]
+        L.fp4kv_oracle_fp16_value.restype = ctypes.c_double
+        L.fp4kv_oracle_fp16_value.argtypes = [ctypes.c_int]
+        L.fp4kv_oracle_quantize_int.restype = ctypes.c_int
+        L.fp4kv_oracle_quantize_int.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_void_p]
+        L.fp4kv_oracle_attention_values.restype = ctypes.c_int
+        L.fp4kv_oracle_attention_values.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_int64, ctypes.c_double, ctypes.c_void_p]
+        L.fp4kv_oracle_attention_values_batch.restype = ctypes.c_int
+        L.fp4kv_oracle_attention_values_batch.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                          ctypes.c_void_p, ctypes.c_void_p,
+                                                          ctypes.c_void_p, ctypes.c_void_p,
+                                                          ctypes.c_int64, ctypes.c_double,
+                                                          ctypes.c_void_p, ctypes.c_int]
         _LIB = L
     return _LIB
 
@@ -324,6 +340,121 @@ def decode_attention_fp8(q_bits, k_codes, v_codes, k_scale, v_scale, seq_lens, s
     rc = lib().fp4kv_oracle_attention_fp8_batch(
         n, G, D, P(*qp), _ptr(T_arr), P(*kp), P(*vp), Hkv * D, float(np.float32(k_scale)),
         float(np.float32(v_scale)), float(scale), outs, n_threads or default_threads())
+    if rc:
+        raise ValueError("bad arguments")
+    for (b, h, ob) in op:
+        out[b, h * G:(h + 1) * G] = ob
+    return out
+
+
+# ------------------------------------------- integer formats (bit-width sweep)
+
+def fp16_value(code: int) -> float:
+    return lib().fp4kv_oracle_fp16_value(int(code))
+
+
+def fp16_table() -> np.ndarray:
+    """Magnitudes of the finite fp16 codes 0 .. 0x7BFF."""
+    return np.array([fp16_value(c) for c in range(0x7C00)], np.float64)
+
+
+GRANULARITIES = ("token", "channel")
+
+
+def quantize_int(x_bits, bits: int, granularity: str):
+    """Symmetric bits-bit integer codes with one fp16 scale per group
+    ("Quantising the KV cache", Concept section, results table: INT8 / INT4 /
+    INT2 per token and per channel).
+
+    x_bits: bf16 [T][H][D] of one sequence.  granularity "token": a group is
+    one token's D channels of one head, scales [T][H]; "channel": a group is
+    one channel of one head across the T tokens, scales [H][D].
+    Returns (codes int8 [T][H][D], scale codes uint16 (fp16 bit patterns))."""
+    x = as_bf16_bits(x_bits)
+    if x.ndim != 3:
+        raise ValueError("expected [T][H][D]")
+    T, H, D = x.shape
+    codes = np.zeros(x.shape, np.int8)
+    if granularity == "token":
+        scales = np.zeros((T, H), np.uint16)
+        args = (T * H, D, D, 1)
+    elif granularity == "channel":
+        scales = np.zeros((H, D), np.uint16)
+        args = (H * D, T, 1, H * D)
+    else:
+        raise ValueError("granularity is 'token' or 'channel'")
+    if T == 0:
+        return codes, scales
+    rc = lib().fp4kv_oracle_quantize_int(_ptr(x), *args, int(bits), _ptr(codes), _ptr(scales))
+    if rc:
+        raise ValueError("bad arguments or non-finite input")
+    return codes, scales
+
+
+def dequantize_int(codes, scales, granularity: str) -> np.ndarray:
+    """code * fp16(scale) in float64 (exact: at most 7 + 11 significant bits)."""
+    c = np.asarray(codes, np.int8).astype(np.float64)
+    s = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)
+    if granularity == "token":
+        return c * s[..., None]
+    if granularity == "channel":
+        return c * s[None]
+    raise ValueError("granularity is 'token' or 'channel'")
+
+
+def bf16_values(x_bits) -> np.ndarray:
+    """Exact float64 values of bf16 bit patterns (the unquantised cache)."""
+    x = as_bf16_bits(x_bits)
+    return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def attention_values(q_bits, k, v, scale):
+    """fp64 attention of G bf16 query rows [G][D] over T tokens of exact K and
+    V values (float64 [T][D]); returns [G][D]."""
+    q = as_bf16_bits(q_bits)
+    G, D = q.shape
+    k = np.ascontiguousarray(k, np.float64)
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.zeros((G, D), np.float64)
+    rc = lib().fp4kv_oracle_attention_values(_ptr(q), G, D, k.shape[0], _ptr(k), _ptr(v), D,
+                                             float(scale), _ptr(out))
+    if rc:
+        raise ValueError("bad arguments")
+    return out
+
+
+def decode_attention_values(q_bits, k_vals, v_vals, seq_lens, scale, heads=None, n_threads=None):
+    """decode_attention over exact K and V values: k_vals / v_vals per
+    sequence b, float64 [>= len_b][Hkv][D].  Query head h reads KV head
+    h // (Hq / Hkv).  Returns float64 [B][Hq][D]."""
+    q = as_bf16_bits(q_bits)
+    B, Hq, D = q.shape
+    Hkv = np.asarray(k_vals[0]).shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), np.float64)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hkv)]
+    keep, qp, Tp, kp, vp, op = [], [], [], [], [], []
+    for (b, h) in heads:
+        kb = np.ascontiguousarray(k_vals[b], np.float64)
+        vb = np.ascontiguousarray(v_vals[b], np.float64)
+        qg = np.ascontiguousarray(q[b, h * G:(h + 1) * G])
+        ob = np.zeros((G, D), np.float64)
+        keep += [kb, vb, qg, ob]
+        qp.append(_ptr(qg))
+        Tp.append(int(seq_lens[b]))
+        kp.append(_ptr(kb) + h * D * 8)
+        vp.append(_ptr(vb) + h * D * 8)
+        op.append((b, h, ob))
+    n = len(qp)
+    P = ctypes.c_void_p * max(n, 1)
+    T_arr = np.array(Tp if n else [0], np.int64)
+    outs = P(*[_ptr(o[2]) for o in op]) if n else P()
+    rc = lib().fp4kv_oracle_attention_values_batch(
+        n, G, D, P(*qp), _ptr(T_arr), P(*kp), P(*vp), Hkv * D, float(scale), outs,
+        n_threads or default_threads())
     if rc:
         raise ValueError("bad arguments")
     for (b, h, ob) in op:

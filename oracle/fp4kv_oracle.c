@@ -28,6 +28,14 @@
  *   rounded to E4M3 (nearest, ties to even, saturating, as the FP4 encoder
  *   does); the stored value is that E4M3 number times the scale.
  *
+ *   Integer formats for the bit-width sweep -- same page, Concept section,
+ *   results table (INT8/INT4/INT2 per token, and K per channel with V per
+ *   token) and Maths section (cost b + s/g with one FP16 scale per group);
+ *   "Week 6 -- FP4 KV Caches and Bounded Replay", Lab section (quantise
+ *   synthetic KV at several bit widths and measure the attention output's
+ *   error).  The page prints no integer encoder: the symmetric, round-to-
+ *   nearest-even rule below is a reading, stated where it is made.
+ *
  * Readings where the pages are silent are listed with the functions that
  * make them.  Every arithmetic step here is exact except the exp/sum/divide
  * of the attention, which runs in fp64.
@@ -485,6 +493,213 @@ int fp4kv_oracle_attention_batch(int64_t n_problems, int G, int D,
         job[i] = (attn_job){i0, i1, G, D, q, T, k_nib, k_sc, v_nib, v_sc,
                             nib_stride, sc_stride, scale, out, 0};
         pthread_create(&tid[i], NULL, attn_worker, &job[i]);
+    }
+    int rc = 0;
+    for (int i = 0; i < n_threads; i++) {
+        pthread_join(tid[i], NULL);
+        if (job[i].rc)
+            rc = job[i].rc;
+    }
+    return rc;
+}
+
+/* ------------------------------------------------ integer formats (sweep) */
+
+/* IEEE binary16 magnitude of a 15-bit code: 5 exponent bits with bias 15,
+ * 10 mantissa bits, subnormals at exponent 0; codes 0..0x7BFF are finite and
+ * 0x7BFF = 65504 is the largest. */
+double fp4kv_oracle_fp16_value(int code)
+{
+    int e = (code >> 10) & 31, m = code & 1023;
+    if (e == 0)
+        return ldexp((double)m, -24);           /* m/1024 * 2^(1-15) */
+    return ldexp(1.0 + m / 1024.0, e - 15);
+}
+
+#define FP16_MAX_CODE 0x7BFF
+
+/* fp16 code of num/den (num >= 0, den a small positive integer), nearest,
+ * ties to the even code, saturating at 65504 -- the E4M3 bisection again over
+ * the binary16 table.  value*den has at most 11 + 7 significant bits and the
+ * sum of two neighbours times den at most 12 + 7, so both are exact. */
+static int fp16_ratio_rne_sat(double num, double den)
+{
+    if (num >= fp4kv_oracle_fp16_value(FP16_MAX_CODE) * den)
+        return FP16_MAX_CODE;
+    int lo = 0, hi = FP16_MAX_CODE;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (fp4kv_oracle_fp16_value(mid) * den <= num)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double twice = 2.0 * num;
+    double mid2 = (fp4kv_oracle_fp16_value(lo) + fp4kv_oracle_fp16_value(lo + 1)) * den;
+    if (twice < mid2)
+        return lo;
+    if (twice > mid2)
+        return lo + 1;
+    return (lo % 2 == 0) ? lo : lo + 1;
+}
+
+/* Nearest integer to num/den (num >= 0, den > 0), ties to the even integer,
+ * capped at cap.  Only integers up to cap + 1 are tried, so every product
+ * k*den (k <= 128, den an fp16 value) is exact in double. */
+static int int_ratio_rne_cap(double num, double den, int cap)
+{
+    if (num >= (cap + 0.5) * den)               /* at or past the last halfway point */
+        return cap;
+    int k = 0;                                  /* k*den <= num < (k+1)*den */
+    while ((k + 1) * den <= num)
+        k++;
+    double twice = 2.0 * num;
+    double mid2 = (2.0 * k + 1.0) * den;
+    if (twice < mid2)
+        return k;
+    if (twice > mid2)
+        return k + 1;
+    return (k % 2 == 0) ? k : k + 1;
+}
+
+/* Symmetric integer quantisation of bits-bit numbers (bits 2..8) with one
+ * fp16 scale per group -- the INT rows of "Quantising the KV cache", Concept
+ * section, results table, at the cost b + 16/g of its Maths section.
+ *
+ * The page prints no integer encoder, so each step is a reading, the
+ * plainest the page supports:
+ *   qmax = 2^(bits-1) - 1 (a symmetric range: the cost formula counts one
+ *   16-bit number per group, a scale and no zero point);
+ *   scale code = fp16 nearest-even, saturating, of amax / qmax; a scale that
+ *   rounds to zero becomes the smallest fp16 subnormal (as the page's FP4
+ *   encoder does with its E4M3 scale);
+ *   code = sign(x) * nearest-even integer of |x| / s, capped at qmax
+ *   (the same rounding mode as the page's encoder);
+ *   the stored value is code * s.
+ *
+ * Group i's element j is x[i*group_stride + j*elem_stride]; its code goes to
+ * the same index of codes, its scale code to scale_codes[i].  A group is one
+ * token's channels of one head (per token, elem_stride 1) or one channel of
+ * one head across the tokens (per channel, elem_stride = heads * head_dim).
+ * Returns -1 on bad arguments or a non-finite input. */
+int fp4kv_oracle_quantize_int(const uint16_t *x, int64_t n_groups, int64_t group_len,
+                              int64_t group_stride, int64_t elem_stride, int bits,
+                              int8_t *codes, uint16_t *scale_codes)
+{
+    if (bits < 2 || bits > 8 || n_groups < 0 || group_len < 1)
+        return -1;
+    const int qmax = (1 << (bits - 1)) - 1;
+    for (int64_t i = 0; i < n_groups; i++) {
+        const int64_t base = i * group_stride;
+        double amax = 0.0;
+        for (int64_t j = 0; j < group_len; j++) {
+            double v = bf16_value(x[base + j * elem_stride]);
+            if (!isfinite(v))
+                return -1;
+            if (fabs(v) > amax)
+                amax = fabs(v);
+        }
+        int sc = fp16_ratio_rne_sat(amax, (double)qmax);
+        if (sc == 0)
+            sc = 1;
+        scale_codes[i] = (uint16_t)sc;
+        const double s = fp4kv_oracle_fp16_value(sc);
+        for (int64_t j = 0; j < group_len; j++) {
+            double v = bf16_value(x[base + j * elem_stride]);
+            int c = int_ratio_rne_cap(fabs(v), s, qmax);
+            codes[base + j * elem_stride] = (int8_t)(signbit(v) ? -c : c);
+        }
+    }
+    return 0;
+}
+
+/* Attention of G bf16 query rows over T tokens whose K and V are given as
+ * exact values (fp64, token t's D values at k + t*stride): the same fp64
+ * definition as above, for any format once it is dequantised, and for the
+ * unquantised bf16 cache itself. */
+int fp4kv_oracle_attention_values(const uint16_t *q, int G, int D, int64_t T,
+                                  const double *k, const double *v, int64_t stride,
+                                  double scale, double *out)
+{
+    if (G < 1 || D < 1 || T < 0)
+        return -1;
+    for (int i = 0; i < G * D; i++)
+        out[i] = 0.0;
+    if (T == 0)
+        return 0;
+    double *z = (double *)malloc(sizeof(double) * (size_t)T);
+    if (!z)
+        return -3;
+    for (int g = 0; g < G; g++) {
+        const uint16_t *qg = q + (int64_t)g * D;
+        double zmax = -INFINITY;
+        for (int64_t t = 0; t < T; t++) {
+            double dot = 0.0;
+            for (int c = 0; c < D; c++)
+                dot += bf16_value(qg[c]) * k[t * stride + c];
+            z[t] = scale * dot;
+            if (z[t] > zmax)
+                zmax = z[t];
+        }
+        double wsum = 0.0;
+        double *og = out + (int64_t)g * D;
+        for (int64_t t = 0; t < T; t++) {
+            double w = exp(z[t] - zmax);
+            wsum += w;
+            for (int c = 0; c < D; c++)
+                og[c] += w * v[t * stride + c];
+        }
+        for (int c = 0; c < D; c++)
+            og[c] /= wsum;
+    }
+    free(z);
+    return 0;
+}
+
+typedef struct {
+    int64_t i0, i1;
+    int G, D;
+    const uint16_t *const *q;
+    const int64_t *T;
+    const double *const *k, *const *v;
+    int64_t stride;
+    double scale;
+    double *const *out;
+    int rc;
+} attnv_job;
+
+static void *attnv_worker(void *arg)
+{
+    attnv_job *j = (attnv_job *)arg;
+    for (int64_t i = j->i0; i < j->i1; i++) {
+        int rc = fp4kv_oracle_attention_values(j->q[i], j->G, j->D, j->T[i], j->k[i], j->v[i],
+                                               j->stride, j->scale, j->out[i]);
+        if (rc)
+            j->rc = rc;
+    }
+    return NULL;
+}
+
+int fp4kv_oracle_attention_values_batch(int64_t n_problems, int G, int D, const uint16_t *const *q,
+                                        const int64_t *T, const double *const *k,
+                                        const double *const *v, int64_t stride, double scale,
+                                        double *const *out, int n_threads)
+{
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if ((int64_t)n_threads > n_problems)
+        n_threads = n_problems > 0 ? (int)n_problems : 1;
+    pthread_t tid[256];
+    attnv_job job[256];
+    int64_t per = (n_problems + n_threads - 1) / n_threads;
+    for (int i = 0; i < n_threads; i++) {
+        int64_t i0 = i * per, i1 = i0 + per > n_problems ? n_problems : i0 + per;
+        if (i0 > i1)
+            i0 = i1;
+        job[i] = (attnv_job){i0, i1, G, D, q, T, k, v, stride, scale, out, 0};
+        pthread_create(&tid[i], NULL, attnv_worker, &job[i]);
     }
     int rc = 0;
     for (int i = 0; i < n_threads; i++) {
