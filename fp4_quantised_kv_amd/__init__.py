@@ -17,12 +17,16 @@ import os
 
 __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
            "quantize_append", "decode_attention", "decode_split", "decode_combine",
-           "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3"]
+           "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3",
+           "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "int_sizes", "int_quantize", "int_decode_plan",
+           "int_decode_attention"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(HERE, "libfp4kv.so")
 PAGE_SIZE = 64
 MAX_GROUP = 16
+INT_PER_TOKEN = 0
+INT_PER_CHANNEL = 1
 
 OK = 0
 ERR_INVALID_ARGUMENT = -1
@@ -81,6 +85,12 @@ _LIB = None
 _P = ctypes.c_void_p
 
 
+class IntDims(ctypes.Structure):
+    """fp4kv_int_dims: B sequences of T tokens, H KV heads of D channels."""
+    _fields_ = [("batch", ctypes.c_int32), ("tokens", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
 def library():
     """The loaded libfp4kv.so.  Raises if it has not been built."""
     global _LIB
@@ -111,6 +121,20 @@ def library():
         L.fp4kv_decode_combine.restype = ctypes.c_int
         L.fp4kv_read_probe.argtypes = [_P, ctypes.c_int64, _P, _P]
         L.fp4kv_read_probe.restype = ctypes.c_int
+        L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        L.fp4kv_int_sizes.restype = ctypes.c_int
+        L.fp4kv_int_quantize.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
+                                         _P, _P, _P, _P]
+        L.fp4kv_int_quantize.restype = ctypes.c_int
+        L.fp4kv_int_decode_plan.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
+        L.fp4kv_int_decode_plan.restype = ctypes.c_int
+        L.fp4kv_int_decode_attention.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                                 ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64,
+                                                 _P, _P]
+        L.fp4kv_int_decode_attention.restype = ctypes.c_int
         L.fp4kv_status_string.argtypes = [ctypes.c_int]
         L.fp4kv_status_string.restype = ctypes.c_char_p
         L.fp4kv_version.argtypes = []
@@ -283,3 +307,91 @@ def read_probe(buf, sink, stream=None):
     _need(sink, "sink", torch.int32)
     _check("fp4kv_read_probe", library().fp4kv_read_probe(buf.data_ptr(), buf.numel(), sink.data_ptr(),
                                                           _stream(stream)))
+
+
+# ------------------------------------------- integer formats (include/fp4kv_int.h)
+
+def _gran(g):
+    return {"token": INT_PER_TOKEN, "channel": INT_PER_CHANNEL}.get(g, g)
+
+
+def int_sizes(batch: int, tokens: int, num_kv_heads: int, head_dim: int, bits: int, granularity="token"):
+    """(code bytes, scale bytes) of one tensor in an integer format (bits 2, 4,
+    8, or 16 for the unquantised bf16 copy)."""
+    d = IntDims(batch, tokens, num_kv_heads, head_dim)
+    c, s = ctypes.c_int64(), ctypes.c_int64()
+    _check("fp4kv_int_sizes", library().fp4kv_int_sizes(ctypes.byref(d), int(bits), _gran(granularity),
+                                                        ctypes.byref(c), ctypes.byref(s)))
+    return c.value, s.value
+
+
+def int_quantize(x, bits: int, granularity="token", stream=None):
+    """Quantise x (bf16 [B][T][H][D]) to symmetric bits-bit codes with fp16
+    scales per token or per channel.  Returns (codes uint8 [B][H][T][D*bits/8],
+    scales int16 fp16 bit patterns: [B][H][T] per token, [B][H][D] per
+    channel, empty for bits 16)."""
+    import torch
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 4:
+        raise ValueError("x must be [B][T][H][D]")
+    B, T, H, D = x.shape
+    d = IntDims(B, T, H, D)
+    nc, ns = int_sizes(B, T, H, D, bits, granularity)
+    codes = torch.empty(max(nc, 16), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(max(ns // 2, 8), dtype=torch.int16, device=x.device)
+    _check("fp4kv_int_quantize", library().fp4kv_int_quantize(
+        ctypes.byref(d), int(bits), _gran(granularity), x.data_ptr(), codes.data_ptr(),
+        scales.data_ptr(), _stream(stream)))
+    codes = codes[:nc].view(B, H, T, D * bits // 8)
+    if bits == 16:
+        scales = scales[:0]
+    elif _gran(granularity) == INT_PER_TOKEN:
+        scales = scales[: ns // 2].view(B, H, T)
+    else:
+        scales = scales[: ns // 2].view(B, H, D)
+    return codes, scales
+
+
+def int_decode_plan(batch: int, tokens: int, num_kv_heads: int, head_dim: int, num_q_heads: int,
+                    num_splits: int = 0):
+    """(splits, workspace bytes) of int_decode_attention."""
+    d = IntDims(batch, tokens, num_kv_heads, head_dim)
+    s, ws = ctypes.c_int32(), ctypes.c_int64()
+    _check("fp4kv_int_decode_plan", library().fp4kv_int_decode_plan(
+        ctypes.byref(d), num_q_heads, num_splits, ctypes.byref(s), ctypes.byref(ws)))
+    return s.value, ws.value
+
+
+def int_decode_attention(q, bits: int, k, v, tokens: int, k_granularity="token", v_granularity="token",
+                         softmax_scale=None, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Decode attention of q (bf16 [B][Hq][D]) over K and V in an integer
+    format: k and v are the (codes, scales) pairs int_quantize returns for
+    [B][tokens][H][D] tensors.  Returns fp32 [B][Hq][D]."""
+    import torch
+    _need(q, "q", torch.bfloat16)
+    B, Hq, D = q.shape
+    (kc, ks), (vc, vs) = k, v
+    for t, n in ((kc, "k codes"), (vc, "v codes")):
+        _need(t, n, torch.uint8)
+    for t, n in ((ks, "k scales"), (vs, "v scales")):
+        _need(t, n, torch.int16)
+    H = kc.shape[1]
+    d = IntDims(B, tokens, H, D)
+    for (c, sc), g in ((k, k_granularity), (v, v_granularity)):
+        nc, ns = int_sizes(B, tokens, H, D, bits, g)
+        if c.numel() != nc or sc.numel() * 2 != ns:
+            raise ValueError("codes or scales do not match the dims, bits and granularity")
+    splits, ws_bytes = int_decode_plan(B, tokens, H, D, Hq, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    out = _out_tensor(out, B, Hq, D, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    _check("fp4kv_int_decode_attention", library().fp4kv_int_decode_attention(
+        ctypes.byref(d), int(bits), _gran(k_granularity), _gran(v_granularity), ptr(kc), ptr(ks),
+        ptr(vc), ptr(vs), q.data_ptr(), Hq, float(softmax_scale), num_splits, workspace.data_ptr(),
+        workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out

@@ -13,7 +13,9 @@ LIBRARY = os.path.join(HERE, "libfp4kv.so")
 SOURCES = [os.path.join(HERE, "csrc", "fp4kv_api.cpp"),
            os.path.join(HERE, "csrc", "fp4kv_kernels.hip"),
            os.path.join(HERE, "csrc", "fp4kv_decode_mfma.hip"),
-           os.path.join(HERE, "csrc", "fp4kv_decode_fp8.hip")]
+           os.path.join(HERE, "csrc", "fp4kv_decode_fp8.hip"),
+           os.path.join(HERE, "csrc", "fp4kv_int_api.cpp"),
+           os.path.join(HERE, "csrc", "fp4kv_int.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

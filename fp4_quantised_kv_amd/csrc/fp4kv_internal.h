@@ -57,4 +57,31 @@ hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t 
 // Streaming read of `blocks` 9216-byte blocks (measurement utility).
 hipError_t launch_read_probe(const uint8_t *buf, int64_t blocks, uint32_t *sink, hipStream_t stream);
 
+// Integer formats of the bit-width sweep (fp4kv_int.hip).
+struct IntQuantArgs {
+    const uint16_t *x;           // bf16 [batch][tokens][H][D]
+    uint8_t *codes;              // [batch][H][tokens][D * bits / 8]
+    uint16_t *scales;            // fp16: per token [batch][H][tokens], per channel [batch][H][D]
+    int64_t batch, tokens;
+    int32_t num_kv_heads, head_dim, bits;   // bits 2, 4, 8, or 16 (bf16 copy)
+    bool per_channel;
+};
+
+struct IntDecodeArgs {
+    const uint8_t *k_codes, *v_codes;
+    const uint16_t *k_scales, *v_scales;
+    const uint16_t *q;           // bf16 [batch][num_q_heads][D]
+    int64_t tokens;
+    int32_t batch, num_kv_heads, num_q_heads, group, head_dim, bits;
+    int32_t splits, chunks_per_split;       // 256-token chunks per split
+    bool k_per_channel, v_per_channel;
+    float scale_log2e;
+    float *ws_o, *ws_ml;         // partials, as for the FP4 decode
+    float *out;
+};
+
+hipError_t launch_int_quantize(const IntQuantArgs &q, hipStream_t stream);
+// split kernel followed by the combine kernel
+hipError_t launch_int_decode(const IntDecodeArgs &a, hipStream_t stream);
+
 }  // namespace fp4kv

@@ -144,3 +144,28 @@ def row_rel_error(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
     num = np.max(np.abs(out.astype(np.float64) - ref), axis=-1)
     den = np.max(np.abs(ref), axis=-1)
     return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def unpack_int_codes(codes, bits: int, head_dim: int) -> np.ndarray:
+    """Integer-format code bytes [B][H][T][D * bits / 8] (device or host) ->
+    signed codes int8 [B][T][H][D], token-major like the input rows.  Within
+    a row, channel i sits in bits bits*(i % (8/bits)) .. of byte i*bits/8,
+    two's complement."""
+    c = codes.cpu().numpy() if hasattr(codes, "cpu") else np.asarray(codes)
+    B, H, T, _ = c.shape
+    if bits == 8:
+        v = c.view(np.int8).astype(np.int8)
+    else:
+        per = 8 // bits
+        shifts = (np.arange(per) * bits).astype(np.uint8)
+        f = (c[..., None] >> shifts) & ((1 << bits) - 1)                # [B][H][T][R][per]
+        f = f.reshape(B, H, T, head_dim).astype(np.int16)
+        v = np.where(f >= (1 << (bits - 1)), f - (1 << bits), f).astype(np.int8)
+    return np.ascontiguousarray(v.reshape(B, H, T, head_dim).transpose(0, 2, 1, 3))
+
+
+def int_scales_host(scales, granularity: str) -> np.ndarray:
+    """Device fp16 scale patterns -> uint16, per token [B][T][H] (from
+    [B][H][T]) or per channel [B][H][D] (as stored)."""
+    s = scales.cpu().numpy().view(np.uint16)
+    return np.ascontiguousarray(s.transpose(0, 2, 1)) if granularity == "token" else s

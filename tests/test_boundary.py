@@ -1,6 +1,7 @@
-"""The C ABI on the CPU: the library loads, exports what include/fp4kv.h
+"""The C ABI on the CPU: the library loads, exports what include/*.h
 declares, and every host-side check fires before any HIP call."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,17 +11,18 @@ import fp4_quantised_kv_amd as fk
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fp4kv.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"FP4KV_API\s+[\w\s\*]*?\b(fp4kv_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fp4kv_cache_layout", "fp4kv_quantize_append", "fp4kv_decode_attention"} <= set(names)
+    assert {"fp4kv_cache_layout", "fp4kv_quantize_append", "fp4kv_decode_attention",
+            "fp4kv_int_quantize", "fp4kv_int_decode_attention"} <= set(names)
     lib = fk.library()
     for n in names:
         assert hasattr(lib, n), n
@@ -175,3 +177,69 @@ def test_read_probe_host_checks():
     assert lib.fp4kv_read_probe(ok, 9216, None, None) == fk.ERR_INVALID_ARGUMENT
     assert lib.fp4kv_read_probe(ok + 16, 9216, ok, None) == fk.ERR_MISALIGNED
     assert lib.fp4kv_read_probe(ok, 9216, ok + 2, None) == fk.ERR_MISALIGNED
+
+
+# ------------------------------------------------ integer formats (fp4kv_int.h)
+
+@pytest.mark.parametrize("B,T,H,D,bits,gran", [(2, 100, 3, 128, 8, "token"), (1, 7, 1, 64, 4, "channel"),
+                                               (4, 33, 8, 128, 2, "token"), (2, 5, 2, 64, 16, "channel")])
+def test_int_sizes(B, T, H, D, bits, gran):
+    nc, ns = fk.int_sizes(B, T, H, D, bits, gran)
+    assert nc == B * T * H * D * bits // 8
+    if bits == 16:
+        assert ns == 0
+    elif gran == "token":
+        assert ns == B * T * H * 2
+    else:
+        assert ns == B * H * D * 2
+    # bits per number b + 16/g with g = D (per token) or T (per channel)
+    if bits != 16:
+        per = (8 * (nc + ns)) / (B * T * H * D)
+        g = D if gran == "token" else T
+        assert per == pytest.approx(oracle.bits_per_number(bits, 16, g))
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 4, 1, 128, 3, 0), fk.ERR_INVALID_ARGUMENT), ((1, 4, 1, 128, 8, 2), fk.ERR_INVALID_ARGUMENT),
+    ((1, 4, 0, 128, 8, 0), fk.ERR_INVALID_ARGUMENT), ((-1, 4, 1, 128, 8, 0), fk.ERR_INVALID_ARGUMENT),
+    ((1, -4, 1, 128, 8, 0), fk.ERR_INVALID_ARGUMENT), ((1, 4, 1, 96, 8, 0), fk.ERR_UNSUPPORTED)])
+def test_int_sizes_rejects(args, code):
+    with pytest.raises(fk.Fp4KVError) as e:
+        fk.int_sizes(*args)
+    assert e.value.status == code
+
+
+def test_int_plan_and_workspace():
+    # T = 1000 tokens: 4 chunks of 256; ask for 3 splits -> 2 chunks each -> 2 splits
+    s, ws = fk.int_decode_plan(2, 1000, 4, 128, 16, 3)
+    assert s == 2
+    rows = 2 * 16 * s
+    assert ws == -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+    assert fk.int_decode_plan(2, 1000, 4, 128, 16, 100)[0] == 4       # clamped to the chunks
+    assert fk.int_decode_plan(2, 0, 4, 128, 16, 0)[0] == 1            # empty context: one empty split
+    auto = fk.int_decode_plan(8, 4096, 8, 128, 32, 0)[0]
+    assert 1 <= auto <= 16 and 8 * 8 * auto >= 512
+    for bad, code in (((2, 1000, 4, 128, 6, 0), fk.ERR_INVALID_ARGUMENT),      # 6 % 4
+                      ((2, 1000, 1, 128, 17, 0), fk.ERR_UNSUPPORTED),          # group of 17
+                      ((2, 1000, 4, 128, 16, -1), fk.ERR_INVALID_ARGUMENT)):
+        with pytest.raises(fk.Fp4KVError) as e:
+            fk.int_decode_plan(*bad)
+        assert e.value.status == code
+
+
+def test_int_calls_reject_before_any_hip_call():
+    L = fk.library()
+    d = fk.IntDims(1, 16, 1, 128)
+    # null data pointers, misalignment and a small workspace are refused on the host
+    assert L.fp4kv_int_quantize(ctypes.byref(d), 8, 0, None, None, None, None) == fk.ERR_INVALID_ARGUMENT
+    assert L.fp4kv_int_quantize(ctypes.byref(d), 8, 0, 16, 32, 49, None) == fk.ERR_MISALIGNED
+    assert L.fp4kv_int_quantize(ctypes.byref(d), 5, 0, 16, 32, 48, None) == fk.ERR_INVALID_ARGUMENT
+    z = fk.IntDims(0, 16, 1, 128)
+    assert L.fp4kv_int_quantize(ctypes.byref(z), 8, 0, None, None, None, None) == fk.OK   # nothing to do
+    args = [ctypes.byref(d), 8, 0, 0, 256, 512, 256, 512, 256, 1, ctypes.c_float(0.1), 0, 256]
+    assert L.fp4kv_int_decode_attention(*args, 10, 256, None) == fk.ERR_WORKSPACE_TOO_SMALL
+    args[10] = ctypes.c_float(0.0)
+    assert L.fp4kv_int_decode_attention(*args, 1 << 20, 256, None) == fk.ERR_INVALID_ARGUMENT
+    args[10] = ctypes.c_float(0.1)
+    args[4] = 264                                       # k codes not 16-B aligned
+    assert L.fp4kv_int_decode_attention(*args, 1 << 20, 256, None) == fk.ERR_MISALIGNED
