@@ -132,7 +132,7 @@ def test_fp4_cost_figures(oracle_mod):
     bits = oracle_mod.bits_per_number(4, 8, 16)
     assert bits == 4.5
     assert bits / 16 == 0.28125                 # printed as 28.1% of FP16
-    assert bits / 8 == 0.5625                   # "nearly halves" an FP8 cache
+    assert bits / 8 == 0.5625                   # a little over half of an FP8 cache
     # one token of one layer with 8 KV heads of 128: 2*8*128 numbers, 1152 bytes
     assert oracle_mod.numbers_per_token(1, 8, 128) == 2048
     assert oracle_mod.fp4_cache_bytes(1, 1, 8, 128) == 1152
