@@ -202,7 +202,7 @@ VECTORS = [
     ("amax one", [1], 0x23, [0x7], [0x07], [1.03125]),
     # 20/6 = 3.33 -> 3.25 (0x45); 20/3.25 = 6.15 saturates to 6; 1/3.25 = 0.31
     # > 0.25 -> 0.5; 0.5/3.25 and smaller round to 0 (negative keeps its sign)
-    ("outlier wrecks group", [20, 1, -1, 0.5, -0.5, 0.25, 0.30078125], 0x45,
+    ("outlier sets the block scale", [20, 1, -1, 0.5, -0.5, 0.25, 0.30078125], 0x45,
      [0x7, 0x1, 0x9, 0x0, 0x8, 0x0, 0x0], [0x17, 0x09, 0x08],
      [19.5, 1.625, -1.625, 0, 0, 0, 0]),
     # 6.375/6 = 1.0625, exactly halfway between 1 (0x38) and 1.125 (0x39): even
