@@ -5,7 +5,8 @@ Default workload: 32 sequences of 32768 tokens, 64 query heads over 8 KV heads
 (group 8), head dim 128, 64 context splits -- 1.2 GB of packed cache, larger
 than the GPU's last-level cache, so every step streams it from HBM.  A step
 is one decode-attention call (split kernel + combine kernel); for the paged
-workload a step also appends one token per sequence first.  The cache, the
+workload a step also appends one token per sequence first, inside the split
+kernel (--unfused: with a separate quantize_append call).  The cache, the
 queries and every argument are resident on the device before timing starts.
 
 Prints one JSON line: achieved HBM GB/s over the step's algorithmic bytes
@@ -152,6 +153,9 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--format", choices=("fp4", "fp8"), default="fp4",
                     help="cache format: FP4 E2M1 + E4M3 per 16 (default) or FP8 E4M3 with per-tensor scales")
+    ap.add_argument("--unfused", action="store_true",
+                    help="paged workload: append with quantize_append, then decode (default: the decode "
+                         "kernel stores the new tokens itself)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the streaming-read probe (the achievable HBM read rate for this access pattern)")
@@ -216,15 +220,22 @@ def main():
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total_steps)]
 
+    fused = paged and not args.unfused
+
     def step(s, e=None):
         if e is not None:
             e[0].record(stream)
-        if paged:
+        if paged and not fused:
             fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
         if e is not None:
             e[1].record(stream)
-        fk.decode_split(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
-                        softmax_scale=scale, num_splits=splits_req, workspace=ws)
+        if fused:
+            # the split kernel stores each sequence's new token itself
+            fk.decode_append_split(L, gc.cache, news[s][0], news[s][1], qs[s % len(qs)], lens_dev[s],
+                                   gc.page_table, softmax_scale=scale, num_splits=splits_req, workspace=ws)
+        else:
+            fk.decode_split(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
+                            softmax_scale=scale, num_splits=splits_req, workspace=ws)
         if e is not None:
             e[2].record(stream)
         fk.decode_combine(ws, B, Hq, D, partials, out=out)
@@ -323,6 +334,7 @@ def main():
                    "cache_bytes": L.cache_bytes},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "append": (None if not paged else "fused into the split kernel" if fused else "quantize_append"),
         "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
                       "decode_combine": round(t_comb, 5), "decode_split_back_to_back": round(t_split_b2b, 5)},
         "settle_decode_calls": SETTLE_CALLS,

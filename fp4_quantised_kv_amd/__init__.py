@@ -17,6 +17,7 @@ import os
 
 __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
            "quantize_append", "decode_attention", "decode_split", "decode_combine",
+           "decode_append_attention", "decode_append_split",
            "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3",
            "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "int_sizes", "int_quantize", "int_decode_plan",
            "int_decode_attention"]
@@ -119,6 +120,14 @@ def library():
         L.fp4kv_decode_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
         L.fp4kv_decode_combine.restype = ctypes.c_int
+        L.fp4kv_decode_append_attention.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, _P, _P,
+                                                    ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
+                                                    ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
+        L.fp4kv_decode_append_attention.restype = ctypes.c_int
+        L.fp4kv_decode_append_split.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, _P, _P,
+                                                ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
+                                                ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64, _P]
+        L.fp4kv_decode_append_split.restype = ctypes.c_int
         L.fp4kv_read_probe.argtypes = [_P, ctypes.c_int64, _P, _P]
         L.fp4kv_read_probe.restype = ctypes.c_int
         L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
@@ -282,6 +291,50 @@ def decode_split(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_sc
     _check("fp4kv_decode_split", library().fp4kv_decode_split(
         ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, Hq, seq_lens.data_ptr(),
         page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return workspace, plan
+
+
+def _new_token_rows(layout, k_new, v_new, B):
+    import torch
+    _need(k_new, "k_new", torch.bfloat16)
+    _need(v_new, "v_new", torch.bfloat16)
+    want = (B, layout.num_kv_heads, layout.head_dim)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+        raise ValueError(f"k_new and v_new must have shape {want}")
+
+
+def decode_append_attention(layout: CacheLayout, cache, k_new, v_new, q, seq_lens, page_table,
+                            softmax_scale=None, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """One decode step with its own token: k_new, v_new (bf16 [B][H_kv][D])
+    are stored at position seq_lens[b] - 1 of each sequence (seq_lens include
+    the new token), then q attends over all seq_lens[b] tokens.  Returns fp32
+    [B][Hq][D]."""
+    B, Hq, D, max_pages, plan, workspace = _decode_inputs(
+        layout, cache, q, seq_lens, page_table, num_splits, workspace)
+    _new_token_rows(layout, k_new, v_new, B)
+    out = _out_tensor(out, B, Hq, D, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _check("fp4kv_decode_append_attention", library().fp4kv_decode_append_attention(
+        ctypes.byref(layout), cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), B, Hq,
+        seq_lens.data_ptr(), page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
+        workspace.data_ptr(), workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def decode_append_split(layout: CacheLayout, cache, k_new, v_new, q, seq_lens, page_table,
+                        softmax_scale=None, num_splits: int = 0, workspace=None, stream=None):
+    """decode_append_attention without the combine: returns (workspace,
+    plan) as decode_split does."""
+    B, Hq, D, max_pages, plan, workspace = _decode_inputs(
+        layout, cache, q, seq_lens, page_table, num_splits, workspace)
+    _new_token_rows(layout, k_new, v_new, B)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _check("fp4kv_decode_append_split", library().fp4kv_decode_append_split(
+        ctypes.byref(layout), cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), B, Hq,
+        seq_lens.data_ptr(), page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return workspace, plan
 

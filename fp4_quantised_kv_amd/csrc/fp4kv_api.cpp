@@ -251,6 +251,21 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     a->ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + plan.ws_o_bytes);
 
     a->out = nullptr;
+    a->k_new = a->v_new = nullptr;
+    a->cache_w = nullptr;
+    return FP4KV_OK;
+}
+
+// The step's own token for the append variants: rows [batch][H_kv][D].
+int prepare_append(void *cache, const void *k_new, const void *v_new, fp4kv::DecodeArgs *a)
+{
+    if (!k_new || !v_new)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+        return FP4KV_ERR_MISALIGNED;
+    a->k_new = static_cast<const uint16_t *>(k_new);
+    a->v_new = static_cast<const uint16_t *>(v_new);
+    a->cache_w = static_cast<uint8_t *>(cache);
     return FP4KV_OK;
 }
 
@@ -315,6 +330,51 @@ int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache
                            max_pages_per_seq, softmax_scale, num_splits, workspace,
                            workspace_bytes, &a);
     if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    if (!out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(out, 16))
+        return FP4KV_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = fp4kv::launch_decode_split(a, st);
+    if (e != hipSuccess)
+        return FP4KV_ERR_HIP;
+    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
+                                     out, st);
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+int fp4kv_decode_append_split(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,
+                              const void *v_new, const void *q, int32_t batch, int32_t num_q_heads,
+                              const int32_t *seq_lens, const int32_t *page_table, int32_t max_pages_per_seq,
+                              float softmax_scale, int32_t num_splits, void *workspace, int64_t workspace_bytes,
+                              void *stream)
+{
+    fp4kv::DecodeArgs a;
+    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
+                           softmax_scale, num_splits, workspace, workspace_bytes, &a);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    rc = prepare_append(cache, k_new, v_new, &a);
+    if (rc != FP4KV_OK)
+        return rc;
+    const hipError_t e = fp4kv::launch_decode_split(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+int fp4kv_decode_append_attention(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,
+                                  const void *v_new, const void *q, int32_t batch, int32_t num_q_heads,
+                                  const int32_t *seq_lens, const int32_t *page_table,
+                                  int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
+                                  void *workspace, int64_t workspace_bytes, float *out, void *stream)
+{
+    fp4kv::DecodeArgs a;
+    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
+                           softmax_scale, num_splits, workspace, workspace_bytes, &a);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    rc = prepare_append(cache, k_new, v_new, &a);
+    if (rc != FP4KV_OK)
         return rc;
     if (!out)
         return FP4KV_ERR_INVALID_ARGUMENT;

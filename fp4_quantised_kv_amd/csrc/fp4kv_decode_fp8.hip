@@ -193,6 +193,7 @@ __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *
     }
 }
 
+template <bool APPEND>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
 {
     static_assert(merge_area_bytes<kD>() <= 2 * kSlotBytes, "merge area layout");
@@ -215,6 +216,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
     half8_t qf[kD / 32];
     float zscale;
     make_q_operand<kD>(qbits, a.scale_log2e, qf, zscale);   // scale_log2e includes the K tensor's scale
+
+    if constexpr (APPEND)
+        append_if_last_chunk<kD, true>(a, c, lane);
 
     SplitState<kD> st;
     init_state(st);
@@ -241,7 +245,10 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
 hipError_t launch_split_fp8(const DecodeArgs &a, hipStream_t stream)
 {
     const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
-    decode_split_fp8<<<grid, kGroupThreads, 0, stream>>>(a);
+    if (a.k_new)
+        decode_split_fp8<true><<<grid, kGroupThreads, 0, stream>>>(a);
+    else
+        decode_split_fp8<false><<<grid, kGroupThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -339,7 +339,7 @@ __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_
 
 // ---- one workgroup per (KV head, sequence, partial)
 
-template <int D, bool STAGED>
+template <int D, bool STAGED, bool APPEND>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
 {
     static_assert(merge_area_bytes<D>() <= 16 * D * 4 + 128, "merge area layout");
@@ -369,6 +369,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     half8_t qf[D / 32];
     float zscale;
     make_q_operand<D>(qbits, a.scale_log2e, qf, zscale);
+
+    if constexpr (APPEND)
+        append_if_last_chunk<D, false>(a, c, lane);
 
     SplitState<D> st;
     init_state(st);
@@ -416,11 +419,14 @@ hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream)
 {
     const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
     if (a.geom.head_dim == 64) {
-        decode_split_mfma<64, false><<<grid, kGroupThreads, 0, stream>>>(a);
+        decode_split_mfma<64, false, false><<<grid, kGroupThreads, 0, stream>>>(a);
     } else if (a.staged) {
-        decode_split_mfma<128, true><<<grid, kGroupThreads, 0, stream>>>(a);
+        if (a.k_new)
+            decode_split_mfma<128, true, true><<<grid, kGroupThreads, 0, stream>>>(a);
+        else
+            decode_split_mfma<128, true, false><<<grid, kGroupThreads, 0, stream>>>(a);
     } else {
-        decode_split_mfma<128, false><<<grid, kGroupThreads, 0, stream>>>(a);
+        decode_split_mfma<128, false, false><<<grid, kGroupThreads, 0, stream>>>(a);
     }
     return hipGetLastError();
 }

@@ -33,6 +33,12 @@ struct DecodeArgs {
     float *ws_ml;                // [batch][partials][num_q_heads][2] running max (base 2), sum
     float *out;                  // [batch][num_q_heads][D]
     bool staged;                 // matrix-core kernel: stage pages through LDS (D = 128)
+    // The step's own token, appended before attending (all null: no append):
+    // bf16 K and V rows [batch][H_kv][D] of one token per sequence, placed at
+    // position seq_lens[b] - 1 through the page table, in the cache at cache_w
+    // (the same bytes as `cache`).
+    const uint16_t *k_new, *v_new;
+    uint8_t *cache_w;
 };
 
 hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const uint16_t *v,
@@ -50,6 +56,13 @@ hipError_t launch_split_fp8(const DecodeArgs &a, hipStream_t stream);
 // FP4KV_DECODE_KERNEL names another (valu: vector ALU; mfma_direct: matrix
 // cores with operands loaded straight into registers).
 hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
+
+// Places each sequence's k_new / v_new row at position seq_lens[b] - 1 (a
+// kernel of its own, for the decode kernels that do not append themselves).
+hipError_t launch_append_last(const DecodeArgs &a, hipStream_t stream);
+// True when launch_decode_split appends the step's token inside the split
+// kernel for these arguments.
+bool split_appends_itself(const DecodeArgs &a);
 
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,
                                  int32_t partials, int32_t head_dim, float *out, hipStream_t stream);

@@ -17,123 +17,15 @@
 
 #include "fp4kv_internal.h"
 #include "fp4kv_merge.h"
+#include "fp4kv_quant.h"
 
 namespace fp4kv {
 namespace {
 
+using namespace quant;
+
 constexpr int kPage = 64;                 // tokens per page == lanes per wave
 constexpr int64_t kRunKernelMinTokens = 512;   // appends this long use 8-token runs
-
-// ------------------------------------------------------------ format helpers
-
-// E4M3 code of y >= 0 (finite), rounded to nearest even, saturating at 448.
-// Subnormal range (y < 2^-6): the grid is 2^-9, so the code is rint(y * 512),
-// exact because the product is exact and rint rounds half to even; 8 carries
-// into the smallest normal, whose code is also 8.  Normal range: round the
-// f32 significand to 3 bits (add half an ulp minus one, plus the kept LSB),
-// then rebias the exponent from 127 to 7.
-__device__ __forceinline__ uint32_t e4m3_code_rne_sat(float y)
-{
-    if (y >= 448.0f)
-        return 126u;
-    if (y < 0.015625f)
-        return static_cast<uint32_t>(__builtin_rintf(y * 512.0f));
-    const uint32_t b = __float_as_uint(y);
-    const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
-    return r - (120u << 3);
-}
-
-// Value of an E4M3 magnitude code (the sign bit is ignored; 0x7F decodes to
-// 480 instead of NaN so that never-written slots stay finite).
-__device__ __forceinline__ float e4m3_value(uint32_t code)
-{
-    code &= 0x7Fu;
-    return code < 8u ? static_cast<float>(code) * 0.001953125f
-                     : __uint_as_float((code + (120u << 3)) << 20);
-}
-
-// Signed E2M1 value of a nibble (bit 3 sign, bits 2-1 exponent with bias 1,
-// bit 0 mantissa).  Codes 2..7 map onto f32 by placing the 3 bits under an
-// exponent offset of 126; code 1 is the subnormal 0.5 and code 0 is zero.
-__device__ __forceinline__ float e2m1_value(uint32_t nib)
-{
-    const uint32_t c = nib & 7u;
-    uint32_t bits = (c + 252u - (c == 1u ? 1u : 0u)) << 22;
-    bits = c ? bits : 0u;
-    return __uint_as_float(bits | ((nib & 8u) << 28));
-}
-
-// Round-to-nearest-even E2M1 magnitude code of |x| / s, saturating at 6,
-// without dividing: count the rounding thresholds t*s that |x| reaches.  The
-// midpoints between consecutive magnitudes are 0.25, 0.75, 1.25, 1.75, 2.5,
-// 3.5 and 5; at an exact tie the even code wins, so a tie moves up only into
-// codes 2, 4 and 6 (comparison >=) and stays below otherwise (comparison >).
-// Every t*s is exact in fp32 (at most 7 significant bits, above 2^-11).
-struct E2M1Thresholds {
-    float t[7];
-    __device__ __forceinline__ explicit E2M1Thresholds(float s)
-    {
-        t[0] = 0.25f * s; t[1] = 0.75f * s; t[2] = 1.25f * s; t[3] = 1.75f * s;
-        t[4] = 2.5f * s;  t[5] = 3.5f * s;  t[6] = 5.0f * s;
-    }
-    __device__ __forceinline__ uint32_t code(float m) const
-    {
-        return static_cast<uint32_t>(m > t[0]) + static_cast<uint32_t>(m >= t[1]) +
-               static_cast<uint32_t>(m > t[2]) + static_cast<uint32_t>(m >= t[3]) +
-               static_cast<uint32_t>(m > t[4]) + static_cast<uint32_t>(m >= t[5]) +
-               static_cast<uint32_t>(m > t[6]);
-    }
-};
-
-// Quantise one block of 16 bf16 values held as 8 dwords (low half = even
-// channel).  Returns the 16 nibbles packed low-to-high (channel 2i in the low
-// nibble of byte i) and the scale code.
-__device__ __forceinline__ void quantize_block16(const uint32_t w[8], uint32_t &lo, uint32_t &hi,
-                                                 uint32_t &scale_code)
-{
-    uint32_t amax = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        amax = max(amax, w[i] & 0x7FFFu);
-        amax = max(amax, (w[i] >> 16) & 0x7FFFu);
-    }
-    // amax / 6 in correctly rounded fp32 gives the same E4M3 code as the exact
-    // quotient for every bf16 amax (checked exhaustively against the oracle).
-    const float a = __uint_as_float(amax << 16);
-    uint32_t sc = e4m3_code_rne_sat(a / 6.0f);
-    sc = sc ? sc : 1u;                                  // zero scale -> smallest subnormal
-    scale_code = sc;
-    const E2M1Thresholds th(e4m3_value(sc));
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
-        const float m = __uint_as_float((bits & 0x7FFFu) << 16);
-        const uint32_t nib = th.code(m) | ((bits >> 12) & 8u);
-        out[c >> 3] |= nib << (4 * (c & 7));
-    }
-    lo = out[0];
-    hi = out[1];
-}
-
-// -------------------------------------------------------- quantise / append
-
-// Page-local placement of V.  Codes: the page's 64 tokens form 4 slices of
-// 16; row (slice, channel) is 8 bytes and byte b holds tokens 2b (low nibble)
-// and 2b + 1 (high nibble) of the slice.  Scales: row (slice, 16-channel
-// block) is 16 bytes, one per token of the slice.
-template <int D>
-__device__ __forceinline__ int v_code_row(int t, int c) { return ((t >> 4) * D + c) * 8; }
-template <int D>
-__device__ __forceinline__ int v_scale_byte(int t, int blk) { return ((t >> 4) * (D / 16) + blk) * 16 + (t & 15); }
-
-__device__ __forceinline__ void load_block16(const uint16_t *src, uint32_t w[8])
-{
-    const uint4 *p = reinterpret_cast<const uint4 *>(src);
-    const uint4 x0 = p[0], x1 = p[1];
-    w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
-    w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
-}
 
 // K of one token's 16-channel block: its 8 code bytes and its scale byte.
 template <int D>
@@ -176,6 +68,20 @@ __device__ __forceinline__ void append_v_token(uint8_t *base, const CacheGeom &g
     base[g.v_scales_off + v_scale_byte<D>(off, blk)] = static_cast<uint8_t>(sc);
 }
 
+// One token's block `blk` of KV head `head` at `slot`; slots outside the
+// pool (padding, negative) are skipped.
+template <int D>
+__device__ __forceinline__ void append_token_fp4(const CacheGeom &g, const uint16_t *ksrc, const uint16_t *vsrc,
+                                                 int64_t slot, int head, int blk, uint8_t *cache)
+{
+    if (slot < 0 || slot >= g.num_pages * kPage)
+        return;
+    uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
+    const int off = static_cast<int>(slot % kPage);
+    append_k<D>(base, g, off, blk, ksrc);
+    append_v_token<D>(base, g, off, blk, vsrc);
+}
+
 // One thread per (token, KV head, 16-channel block); for small appends such
 // as one token per sequence.  Consecutive threads read consecutive 32-byte
 // blocks of the bf16 rows.
@@ -191,13 +97,8 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(
     const int blk = static_cast<int>(idx % NB);
     const int64_t th = idx / NB;                        // token * H_kv + head
     const int head = static_cast<int>(th % g.num_kv_heads);
-    const int64_t slot = slots[th / g.num_kv_heads];
-    if (slot < 0 || slot >= g.num_pages * kPage)
-        return;                                         // padding or out of range: skipped
-    uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
-    const int off = static_cast<int>(slot % kPage);
-    append_k<D>(base, g, off, blk, k + th * D + 16 * blk);
-    append_v_token<D>(base, g, off, blk, v + th * D + 16 * blk);
+    append_token_fp4<D>(g, k + th * D + 16 * blk, v + th * D + 16 * blk, slots[th / g.num_kv_heads], head, blk,
+                        cache);
 }
 
 // One thread per (run of 8 consecutive input tokens, KV head, 16-channel
@@ -287,41 +188,32 @@ __global__ __launch_bounds__(256) void append_runs_kernel(
 
 // -------------------------------------------------- FP8 (per-tensor scale)
 
-// E4M3 code of |x| / s, rounded to nearest even and saturating at 448
-// ("Quantising the KV cache", Concept section, results table: FP8 E4M3
-// with one scale per tensor; rounding as the page's encoder does it).  The
-// fp32 quotient is correctly rounded, so it lies on the same side of every
-// E4M3 rounding midpoint as the exact quotient, except that it can land
-// exactly on one; then the sign of q*s - |x|, exact in one FMA, decides.
-// The bound on s (2^-64 .. 2^64, checked on the host) keeps that FMA's
-// result away from underflow.
-__device__ __forceinline__ uint32_t fp8_code(uint32_t bits16, float s)
+// One token's block `blk` of KV head `head` at `slot` in an FP8 cache; slots
+// outside the pool are skipped.
+template <int D>
+__device__ __forceinline__ void append_token_fp8(const CacheGeom &g, const uint16_t *ksrc, const uint16_t *vsrc,
+                                                 int64_t slot, int head, int blk, uint8_t *cache)
 {
-    const float x = __uint_as_float((bits16 & 0x7FFFu) << 16);
-    const float q = x / s;
-    uint32_t c;
-    if (!(q < 448.0f)) {
-        c = 126u;
-    } else {
-        c = e4m3_code_rne_sat(q);
-        uint32_t lo;
-        bool mid;
-        if (q < 0.015625f) {                            // subnormal grid 2^-9
-            const float t = q * 512.0f;                 // exact
-            const float f = __builtin_floorf(t);
-            lo = static_cast<uint32_t>(f);
-            mid = t - f == 0.5f;
-        } else {
-            const uint32_t b = __float_as_uint(q);
-            lo = (b >> 20) - (120u << 3);               // truncated: the lower neighbour
-            mid = (b & 0xFFFFFu) == 0x80000u;
-        }
-        if (mid) {
-            const float r = __builtin_fmaf(q, s, -x);
-            c = r > 0.0f ? lo : (r < 0.0f ? lo + 1u : c);
-        }
+    if (slot < 0 || slot >= g.num_pages * kPage)
+        return;
+    uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
+    const int off = static_cast<int>(slot % kPage);
+    uint32_t w[8];
+    load_block16(ksrc, w);
+    uint32_t kc[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
+        kc[c >> 2] |= fp8_code(bits, g.k_scale) << (8 * (c & 3));
     }
-    return c | ((bits16 >> 8) & 0x80u);
+    *reinterpret_cast<uint4 *>(base + g.k_codes_off + off * D + 16 * blk) = make_uint4(kc[0], kc[1], kc[2], kc[3]);
+    load_block16(vsrc, w);
+    uint8_t *vrow = base + g.v_codes_off + ((((off >> 4) * 2 + ((off >> 3) & 1)) * D + 16 * blk) * 8) + (off & 7);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
+        vrow[8 * c] = static_cast<uint8_t>(fp8_code(bits, g.v_scale));
+    }
 }
 
 // One thread per (token, KV head, 16-channel block).  K: the block's 16
@@ -340,27 +232,38 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(
     const int blk = static_cast<int>(idx % NB);
     const int64_t th = idx / NB;                        // token * H_kv + head
     const int head = static_cast<int>(th % g.num_kv_heads);
-    const int64_t slot = slots[th / g.num_kv_heads];
-    if (slot < 0 || slot >= g.num_pages * kPage)
+    append_token_fp8<D>(g, k + th * D + 16 * blk, v + th * D + 16 * blk, slots[th / g.num_kv_heads], head, blk,
+                        cache);
+}
+
+// The decode step's own token, for the split kernels that do not append it
+// themselves: one thread per (sequence, KV head, 16-channel block) places
+// k_new / v_new of sequence b at position seq_lens[b] - 1 through the page
+// table.  Empty sequences and out-of-range page ids are skipped.
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void append_last_kernel(DecodeArgs a)
+{
+    constexpr int NB = D / 16;
+    const CacheGeom &g = a.geom;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= static_cast<int64_t>(a.batch) * g.num_kv_heads * NB)
         return;
-    uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
-    const int off = static_cast<int>(slot % kPage);
-    uint32_t w[8];
-    load_block16(k + th * D + 16 * blk, w);
-    uint32_t kc[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
-        kc[c >> 2] |= fp8_code(bits, g.k_scale) << (8 * (c & 3));
-    }
-    *reinterpret_cast<uint4 *>(base + g.k_codes_off + off * D + 16 * blk) = make_uint4(kc[0], kc[1], kc[2], kc[3]);
-    load_block16(v + th * D + 16 * blk, w);
-    uint8_t *vrow = base + g.v_codes_off + ((((off >> 4) * 2 + ((off >> 3) & 1)) * D + 16 * blk) * 8) + (off & 7);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
-        vrow[8 * c] = static_cast<uint8_t>(fp8_code(bits, g.v_scale));
-    }
+    const int blk = static_cast<int>(idx % NB);
+    const int64_t bh = idx / NB;                        // sequence * H_kv + head
+    const int head = static_cast<int>(bh % g.num_kv_heads);
+    const int b = static_cast<int>(bh / g.num_kv_heads);
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
+    if (len == 0)
+        return;
+    const int id = a.page_table[static_cast<int64_t>(b) * a.max_pages + (len - 1) / kPage];
+    const int64_t slot = (id >= 0 && id < g.num_pages) ? static_cast<int64_t>(id) * kPage + (len - 1) % kPage : -1;
+    const uint16_t *ks = a.k_new + bh * D + 16 * blk;
+    const uint16_t *vs = a.v_new + bh * D + 16 * blk;
+    if constexpr (FP8)
+        append_token_fp8<D>(g, ks, vs, slot, head, blk, a.cache_w);
+    else
+        append_token_fp4<D>(g, ks, vs, slot, head, blk, a.cache_w);
 }
 
 // ----------------------------------------------------------------- decode
@@ -689,16 +592,63 @@ hipError_t launch_split_valu(const DecodeArgs &a, hipStream_t stream)
     return a.geom.head_dim == 64 ? launch_split_d<64>(a, stream) : launch_split_d<128>(a, stream);
 }
 
-hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
+hipError_t launch_append_last(const DecodeArgs &a, hipStream_t stream)
+{
+    const int64_t threads = static_cast<int64_t>(a.batch) * a.geom.num_kv_heads * (a.geom.head_dim / 16);
+    const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+    if (a.geom.fp8)
+        append_last_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+    else if (a.geom.head_dim == 64)
+        append_last_kernel<64, false><<<grid, 256, 0, stream>>>(a);
+    else
+        append_last_kernel<128, false><<<grid, 256, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+namespace {
+enum class SplitKernel { fp8, valu, mfma_staged, mfma_direct };
+
+SplitKernel split_kernel_for(const DecodeArgs &a)
 {
     if (a.geom.fp8)
-        return launch_split_fp8(a, stream);
+        return SplitKernel::fp8;
     const char *v = std::getenv("FP4KV_DECODE_KERNEL");
     if (v && std::strcmp(v, "valu") == 0)
-        return launch_split_valu(a, stream);
+        return SplitKernel::valu;
+    if (a.geom.head_dim == 64 || (v && std::strcmp(v, "mfma_direct") == 0))
+        return SplitKernel::mfma_direct;
+    return SplitKernel::mfma_staged;
+}
+}  // namespace
+
+bool split_appends_itself(const DecodeArgs &a)
+{
+    const SplitKernel k = split_kernel_for(a);
+    return k == SplitKernel::fp8 || k == SplitKernel::mfma_staged;
+}
+
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
+{
     DecodeArgs m = a;
-    m.staged = !(v && std::strcmp(v, "mfma_direct") == 0);
-    return launch_split_mfma(m, stream);
+    if (a.k_new && !split_appends_itself(a)) {
+        const hipError_t e = launch_append_last(a, stream);
+        if (e != hipSuccess)
+            return e;
+        m.k_new = m.v_new = nullptr;
+        m.cache_w = nullptr;
+    }
+    switch (split_kernel_for(m)) {
+    case SplitKernel::fp8:
+        return launch_split_fp8(m, stream);
+    case SplitKernel::valu:
+        return launch_split_valu(m, stream);
+    case SplitKernel::mfma_direct:
+        m.staged = false;
+        return launch_split_mfma(m, stream);
+    default:
+        m.staged = true;
+        return launch_split_mfma(m, stream);
+    }
 }
 
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,

@@ -10,6 +10,7 @@
 
 #include "fp4kv_internal.h"
 #include "fp4kv_merge.h"
+#include "fp4kv_quant.h"
 
 namespace fp4kv {
 namespace mfma {
@@ -264,6 +265,27 @@ __device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, in
 {
     const int end = min(c.p0 + a.pages_per_split, a.max_pages);
     return c.p0 + lane < end ? c.ptab[c.p0 + lane] : -1;
+}
+
+// The step's own token (decode with append): the one wave whose chunk holds
+// position len - 1 quantises the sequence's new K and V rows for its KV head
+// and stores them before it copies any page, then waits for the stores, so
+// its own copy of that page reads them.  Only this wave touches that
+// (page, KV head) block in the kernel.
+template <int D, bool FP8>
+__device__ __forceinline__ void append_if_last_chunk(const DecodeArgs &a, const Chunk &c, int lane)
+{
+    const CacheGeom &g = a.geom;
+    const int last = c.len - 1;
+    if (last < 0 || last / kPage < c.p0 || last / kPage >= c.p1)
+        return;
+    const int id = c.ptab[last / kPage];
+    if (id < 0 || id >= g.num_pages)
+        return;
+    uint8_t *base = a.cache_w + static_cast<int64_t>(id) * g.page_stride + c.h * g.head_stride;
+    const int64_t row = (static_cast<int64_t>(c.b) * g.num_kv_heads + c.h) * D;
+    quant::append_token_in_wave<D, FP8>(g, a.k_new + row, a.v_new + row, base, last % kPage, lane);
+    wait_vmem_at_most<0>();
 }
 
 }  // namespace mfma

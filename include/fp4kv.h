@@ -16,6 +16,9 @@
  *                           dequantising on the fly.
  *   fp4kv_decode_split,     its two halves: per-split partial results, and
  *   fp4kv_decode_combine    their merge.
+ *   fp4kv_decode_append_attention, fp4kv_decode_append_split
+ *                           a decode step that first stores each sequence's
+ *                           new token (fused into the decode kernel).
  *   fp4kv_status_string     text of a status code.
  *
  * Conventions for every call:
@@ -243,6 +246,44 @@ FP4KV_API int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void 
 
 FP4KV_API int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t partials,
                                    const void *workspace, int64_t workspace_bytes, float *out, void *stream);
+
+/* One decode step with its own token: for every sequence b with
+ * seq_lens[b] >= 1, quantise the new K and V rows k_new[b], v_new[b] (as
+ * fp4kv_quantize_append does) into position seq_lens[b] - 1 -- slot
+ * page_table[b][(seq_lens[b]-1) / 64] * 64 + (seq_lens[b]-1) % 64 -- then
+ * attend over all seq_lens[b] tokens, new one included, exactly as
+ * fp4kv_decode_attention.  ("Quantising the KV cache", Code and Concept
+ * sections: the hook quantises each new token's K and V, and attention then
+ * reads every cached token; "KV Cache Quantisation", Common questions: the
+ * gain from a quantised cache depends on fused kernels.)  For the FP4 cache
+ * at D = 128 and for the FP8 cache, the decode kernel places the token
+ * itself: the one wave that attends over the token's page writes it first,
+ * so the step is one kernel plus the combine; otherwise a small kernel places
+ * the tokens first.  Results are identical to fp4kv_quantize_append followed
+ * by fp4kv_decode_attention.
+ *   cache          device, as for the other calls, and written.
+ *   k_new, v_new   device bf16 [batch][H_kv][D], 16-B aligned.
+ *   other arguments as for fp4kv_decode_attention; seq_lens are the lengths
+ *                  including the new token.  A sequence of length 0 appends
+ *                  nothing; an out-of-range page id skips the append (and,
+ *                  as always, the page's tokens).  The page that receives a
+ *                  sequence's token must not be shared with another
+ *                  sequence in the same call.
+ * Errors: as for fp4kv_decode_attention, plus INVALID_ARGUMENT for a null
+ * k_new or v_new and MISALIGNED.  fp4kv_decode_append_split is the same
+ * without the combine (see fp4kv_decode_split). */
+FP4KV_API int fp4kv_decode_append_attention(const fp4kv_cache_layout_t *layout, void *cache,
+                                            const void *k_new, const void *v_new, const void *q,
+                                            int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
+                                            const int32_t *page_table, int32_t max_pages_per_seq,
+                                            float softmax_scale, int32_t num_splits, void *workspace,
+                                            int64_t workspace_bytes, float *out, void *stream);
+
+FP4KV_API int fp4kv_decode_append_split(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,
+                                        const void *v_new, const void *q, int32_t batch, int32_t num_q_heads,
+                                        const int32_t *seq_lens, const int32_t *page_table,
+                                        int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
+                                        void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Measurement utility, not a step of the method: reads `bytes` of device
  * memory at `buf` (device) once with 16-byte loads and discards the data.

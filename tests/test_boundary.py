@@ -243,3 +243,15 @@ def test_int_calls_reject_before_any_hip_call():
     args[10] = ctypes.c_float(0.1)
     args[4] = 264                                       # k codes not 16-B aligned
     assert L.fp4kv_int_decode_attention(*args, 1 << 20, 256, None) == fk.ERR_MISALIGNED
+
+
+def test_append_decode_rejects_missing_or_misaligned_rows():
+    """fp4kv_decode_append_attention checks the new-token rows on the host
+    (the other arguments are valid, aligned stand-ins; nothing is launched)."""
+    L = fk.cache_layout(1, 128, 4)
+    lib = fk.library()
+    args = lambda kn: (ctypes.byref(L), 256, kn, 256, 256, 1, 4, 256, 256, 4, ctypes.c_float(0.1), 0, 256,
+                       1 << 20, 256, None)
+    assert lib.fp4kv_decode_append_attention(*args(None)) == fk.ERR_INVALID_ARGUMENT
+    assert lib.fp4kv_decode_append_attention(*args(264)) == fk.ERR_MISALIGNED
+    assert lib.fp4kv_decode_append_split(*args(None)[:-2], None) == fk.ERR_INVALID_ARGUMENT
