@@ -17,7 +17,7 @@ import os
 
 __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
            "quantize_append", "decode_attention", "decode_split", "decode_combine",
-           "decode_append_attention", "decode_append_split",
+           "decode_append_attention", "decode_append_split", "decode_multi_attention",
            "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3",
            "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "int_sizes", "int_quantize", "int_decode_plan",
            "int_decode_attention"]
@@ -128,6 +128,10 @@ def library():
                                                 ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                                 ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64, _P]
         L.fp4kv_decode_append_split.restype = ctypes.c_int
+        L.fp4kv_decode_multi_attention.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
+                                                   ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
+        L.fp4kv_decode_multi_attention.restype = ctypes.c_int
         L.fp4kv_read_probe.argtypes = [_P, ctypes.c_int64, _P, _P]
         L.fp4kv_read_probe.restype = ctypes.c_int
         L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
@@ -293,6 +297,45 @@ def decode_split(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_sc
         page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return workspace, plan
+
+
+def decode_multi_attention(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_scale=None,
+                           num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Causal attention of several query tokens per sequence: q bf16
+    [B][S][Hq][D] holds the last S positions of each context; query token i
+    attends over the first seq_lens[b] - (S - 1 - i) tokens.  Returns fp32
+    [B][S][Hq][D]."""
+    import torch
+    _need(cache, "cache", torch.uint8)
+    _need(q, "q", torch.bfloat16)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_table, "page_table", torch.int32)
+    if q.dim() != 4:
+        raise ValueError("q must be [B][S][Hq][D]")
+    B, S, Hq, D = q.shape
+    if D != layout.head_dim:
+        raise ValueError("q's last dimension must equal the cache head_dim")
+    if tuple(seq_lens.shape) != (B,) or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("seq_lens must be [B] and page_table [B][max_pages]")
+    max_pages = page_table.shape[1]
+    plan = decode_plan(layout, B, S * Hq, max_pages, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty(B, S, Hq, D, dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", torch.float32)
+        if tuple(out.shape) != (B, S, Hq, D):
+            raise ValueError("out must be [B][S][Hq][D]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _check("fp4kv_decode_multi_attention", library().fp4kv_decode_multi_attention(
+        ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, S, Hq, seq_lens.data_ptr(),
+        page_table.data_ptr(), max_pages, float(softmax_scale), num_splits, workspace.data_ptr(),
+        workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
 
 
 def _new_token_rows(layout, k_new, v_new, B):

@@ -85,7 +85,8 @@ __device__ __forceinline__ half8_t fp8x8(uint32_t a, uint32_t b)
 
 // Scores of half page h: tiles 2h + i, A operand of MFMA m = channels
 // 32jj + 8m .. +7 of the lane's token, the same channel order as the query
-// operand.  Tokens at or past `valid` get -inf.
+// operand.  Tokens at or past `valid` (the lane's query column's limit in
+// this page) get -inf.
 __device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, int h, int valid,
                                         const half8_t (&qf)[kD / 32], float (&z)[2][4])
 {
@@ -135,7 +136,7 @@ __device__ __forceinline__ void values8(uint4 w, int u, int jj, int h, int valid
 // they never alias.
 __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
                                           const DecodeArgs &a, const Fp8Offsets &o, int lane, int col, int jj, int h,
-                                          int p0, int p1, int len, const int32_t *ptab, int ids, int pid,
+                                          int p0, int p1, int len, int shortfall, const int32_t *ptab, int ids, int pid,
                                           const half8_t (&qf)[kD / 32], float zscale, SplitState<kD> &st)
 {
     const CacheGeom &g = a.geom;
@@ -167,7 +168,7 @@ __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *
             if (cur)
                 wait_vmem_at_most<kCopies>();
             float z[2][4];
-            scores8(kslot, col, jj, hf, valid, qf, z);
+            scores8(kslot, col, jj, hf, min(kPage, len - pg * kPage - shortfall), qf, z);
             __builtin_amdgcn_s_waitcnt(kWaitLds);
             if (next)
                 stage_k8(nblk, o, nh, kslot);
@@ -229,14 +230,15 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
         stage_k8(blk, o, 0, kslots[wave]);
         stage_v8(blk, o, 0, vslots[wave]);
     }
-    fp8_pages(kslots[wave], vslots[wave], a, o, lane, col, jj, c.h, c.p0, c.p1, c.len, c.ptab, ids, pid, qf, zscale, st);
+    fp8_pages(kslots[wave], vslots[wave], a, o, lane, col, jj, c.h, c.p0, c.p1, c.len, column_shortfall(a, col),
+              c.ptab, ids, pid, qf, zscale, st);
 
     // the V tensor's scale multiplies every value, so it multiplies o
 #pragma unroll
     for (int t = 0; t < kD / 16; ++t)
         st.acc[t] *= g.v_scale;
     auto area = [&](int w) { return MergeArea<kD>(kslots[w], vslots[w]); };
-    state_to_area<kD>(area(wave), st, col, jj, a.group);
+    state_to_area<kD>(area(wave), st, col, jj, query_columns(a));
     merge_waves_and_store<kD>(area, a, c.b, c.h, c.part);
 }
 

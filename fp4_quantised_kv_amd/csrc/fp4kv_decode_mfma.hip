@@ -71,9 +71,9 @@ struct VRegs {
     uint4 vs[NU];
 };
 
-// Scores and online softmax of one page whose first `valid` tokens are live;
-// leaves the probabilities as the value product's B operands (hi and lo parts
-// for the two 32-token halves).
+// Scores and online softmax of one page of which the lane's query column
+// sees the first `valid` tokens; leaves the probabilities as the value
+// product's B operands (hi and lo parts for the two 32-token halves).
 template <int D>
 __device__ __forceinline__ void scores_phase(const KRegs<D> &r, int valid, const half8_t (&qf)[D / 32],
                                              float zscale, int jj, SplitState<D> &st, half8_t (&pf)[2],
@@ -282,9 +282,9 @@ __device__ __forceinline__ void read_v(const uint8_t *slot, int u0, int lane, in
 template <int D>
 __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
                                              const DecodeArgs &a, const StageOffsets &so, int lane, int col,
-                                             int jj, int h, int p0, int p1, int len, const int32_t *ptab,
-                                             int ids, int pid, const half8_t (&qf)[D / 32], float zscale,
-                                             SplitState<D> &st)
+                                             int jj, int h, int p0, int p1, int len, int shortfall,
+                                             const int32_t *ptab, int ids, int pid, const half8_t (&qf)[D / 32],
+                                             float zscale, SplitState<D> &st)
 {
     const CacheGeom &g = a.geom;
     auto live_page = [&](int id) { return id >= 0 && id < g.num_pages; };   // others are skipped
@@ -314,7 +314,7 @@ __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_
         if (next)
             stage_k(block_of(pid_next), so, kslot);
         if (cur)
-            scores_phase<D>(kr, valid, qf, zscale, jj, st, pf, pl);
+            scores_phase<D>(kr, min(kPage, len - pg * kPage - shortfall), qf, zscale, jj, st, pf, pl);
 
         // V: outstanding now are this page's V then the next page's K
         // copies.  One pair block at a time keeps few registers live.
@@ -354,7 +354,6 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the page loop scalar
     const int col = lane & 15;            // query column / tile row
     const int jj = lane >> 4;             // lane group
-    const int G = a.group;
     const CacheGeom &g = a.geom;
 
     // grid (KV head, sequence, partial): the partial index varies slowest, so
@@ -373,6 +372,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     if constexpr (APPEND)
         append_if_last_chunk<D, false>(a, c, lane);
 
+    const int shortfall = column_shortfall(a, col);
     SplitState<D> st;
     init_state(st);
     if constexpr (STAGED) {
@@ -385,8 +385,8 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
             stage_k(blk, so, kslots[wave]);
             stage_v(blk, so, vslots[wave]);
         }
-        staged_pages<D>(kslots[wave], vslots[wave], a, so, lane, col, jj, c.h, c.p0, c.p1, c.len, c.ptab, ids,
-                        pid, qf, zscale, st);
+        staged_pages<D>(kslots[wave], vslots[wave], a, so, lane, col, jj, c.h, c.p0, c.p1, c.len, shortfall,
+                        c.ptab, ids, pid, qf, zscale, st);
     } else {
         half8_t pf[2], pl[2];
         for (int pg = c.p0; pg < c.p1; ++pg) {
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
             VRegs<D> vr;
             load_k_direct<D>(blk, g, col, jj, kr);
             load_v_direct<D>(blk, g, col, jj, vr);
-            scores_phase<D>(kr, valid, qf, zscale, jj, st, pf, pl);
+            scores_phase<D>(kr, min(kPage, c.len - pg * kPage - shortfall), qf, zscale, jj, st, pf, pl);
             half8_t sv[VRegs<D>::NU][2];
 #pragma unroll
             for (int u = 0; u < VRegs<D>::NU; ++u)
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     }
 
     auto area = [&](int w) { return MergeArea<D>(kslots[w], vslots[w]); };
-    state_to_area<D>(area(wave), st, col, jj, G);
+    state_to_area<D>(area(wave), st, col, jj, query_columns(a));
     merge_waves_and_store<D>(area, a, c.b, c.h, c.part);
 }
 

@@ -525,6 +525,7 @@ __global__ __launch_bounds__(256) void int_decode_split(IntDecodeArgs a)
     }
     DecodeArgs ma{};
     ma.group = G;
+    ma.q_tokens = 1;
     ma.partials = a.splits;
     ma.num_q_heads = a.num_q_heads;
     ma.ws_o = a.ws_o;

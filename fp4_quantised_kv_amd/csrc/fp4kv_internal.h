@@ -22,16 +22,17 @@ struct CacheGeom {
 struct DecodeArgs {
     CacheGeom geom;
     const uint8_t *cache;
-    const uint16_t *q;           // bf16 [batch][num_q_heads][D]
+    const uint16_t *q;           // bf16 [batch][q_tokens][num_q_heads][D]
     const int32_t *seq_lens;     // [batch]
     const int32_t *page_table;   // [batch][max_pages]
     int32_t batch, num_q_heads, group, max_pages;
+    int32_t q_tokens;            // query tokens per sequence (1: plain decode); q_tokens * group <= 16
     int32_t splits, pages_per_split;   // context chunks and pages per chunk
     int32_t partials;            // partial slots per row: ceil(splits / 4), one per workgroup
     float scale_log2e;           // softmax scale times log2(e): scores kept in base 2
-    float *ws_o;                 // [batch][partials][num_q_heads][D] unnormalised outputs
-    float *ws_ml;                // [batch][partials][num_q_heads][2] running max (base 2), sum
-    float *out;                  // [batch][num_q_heads][D]
+    float *ws_o;                 // [batch][partials][q_tokens * num_q_heads][D] unnormalised outputs
+    float *ws_ml;                // [batch][partials][q_tokens * num_q_heads][2] running max (base 2), sum
+    float *out;                  // [batch][q_tokens * num_q_heads][D]
     bool staged;                 // matrix-core kernel: stage pages through LDS (D = 128)
     // The step's own token, appended before attending (all null: no append):
     // bf16 K and V rows [batch][H_kv][D] of one token per sequence, placed at

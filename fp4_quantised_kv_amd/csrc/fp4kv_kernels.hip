@@ -613,7 +613,7 @@ SplitKernel split_kernel_for(const DecodeArgs &a)
     if (a.geom.fp8)
         return SplitKernel::fp8;
     const char *v = std::getenv("FP4KV_DECODE_KERNEL");
-    if (v && std::strcmp(v, "valu") == 0)
+    if (v && std::strcmp(v, "valu") == 0 && a.q_tokens <= 1)   // the vector-ALU kernel takes one query token
         return SplitKernel::valu;
     if (a.geom.head_dim == 64 || (v && std::strcmp(v, "mfma_direct") == 0))
         return SplitKernel::mfma_direct;

@@ -37,18 +37,21 @@ struct MergeArea {
 };
 
 // Call with every thread of the workgroup, after each wave has filled its
-// area; area(w) gives wave w's area.  The partial of query row q goes to
-// ws_o[b][part][h*G + q][:] and ws_ml[b][part][h*G + q][:], so a
-// workgroup's G rows are one contiguous block of G*D floats (and of G
-// (m, l) pairs), written with 16-byte stores.
+// area; area(w) gives wave w's area.  Area row q is query token q / G, head
+// h*G + q % G of the group; its partial goes to row
+// (q / G) * num_q_heads + h*G + q % G of ws_o[b][part] and ws_ml[b][part],
+// so with one query token a workgroup's G rows are one contiguous block of
+// G*D floats (and of G (m, l) pairs), written with 16-byte stores.
 template <int D, typename AreaOf>
 __device__ __forceinline__ void merge_waves_and_store(AreaOf area, const DecodeArgs &a, int b, int h, int part)
 {
     __syncthreads();
     const int G = a.group;
-    const int64_t row0 = (static_cast<int64_t>(b) * a.partials + part) * a.num_q_heads + static_cast<int64_t>(h) * G;
-    for (int idx = threadIdx.x; idx < G * (D / 4); idx += kGroupThreads) {
+    const int S = a.q_tokens > 1 ? a.q_tokens : 1;
+    const int64_t row0 = (static_cast<int64_t>(b) * a.partials + part) * S * a.num_q_heads + static_cast<int64_t>(h) * G;
+    for (int idx = threadIdx.x; idx < S * G * (D / 4); idx += kGroupThreads) {
         const int q = idx / (D / 4), c = 4 * (idx % (D / 4));
+        const int64_t row = row0 + static_cast<int64_t>(q / G) * a.num_q_heads + q % G;
         float mw[kWavesPerGroup];
         float M = -INFINITY;
 #pragma unroll
@@ -73,9 +76,9 @@ __device__ __forceinline__ void merge_waves_and_store(AreaOf area, const DecodeA
                 L = fmaf(ar.ml[2 * q + 1], wt, L);
             }
         }
-        *reinterpret_cast<float4 *>(a.ws_o + (row0 + q) * D + c) = O;
+        *reinterpret_cast<float4 *>(a.ws_o + row * D + c) = O;
         if (c == 0)
-            *reinterpret_cast<float2 *>(a.ws_ml + (row0 + q) * 2) = make_float2(M, L);
+            *reinterpret_cast<float2 *>(a.ws_ml + row * 2) = make_float2(M, L);
     }
 }
 

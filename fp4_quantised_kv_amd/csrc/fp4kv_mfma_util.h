@@ -116,13 +116,17 @@ __device__ __forceinline__ void softmax_tiles(const float (&z)[NT][4], SplitStat
     // and a subtraction
     float minus_one = -1.0f;
     asm volatile("" : "+s"(minus_one));
+    // a column that has seen no token yet (possible with several query
+    // tokens: its causal limit can lie before this page) keeps m = -inf and
+    // must get p = 0, not exp2(-inf + inf)
+    const float m_sub = st.m_ref == -INFINITY ? 0.0f : st.m_ref;
 #pragma unroll
     for (int kt = 0; kt < NT / 2; ++kt) {
         float p[8], q[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * kt][e], zscale, -st.m_ref));
-            p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * kt + 1][e], zscale, -st.m_ref));
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * kt][e], zscale, -m_sub));
+            p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * kt + 1][e], zscale, -m_sub));
         }
         pf[kt] = cat(pk_rtz(p[0], p[1]), pk_rtz(p[2], p[3]), pk_rtz(p[4], p[5]), pk_rtz(p[6], p[7]));
 #pragma unroll
@@ -152,17 +156,31 @@ constexpr int kWaitLds = 0xC07F;
 
 // ---- query operand, per-wave state, chunk geometry
 
+// Query columns: column col is query token col / G, head h*G + col % G of
+// the group (q_tokens * G <= 16 columns; one query token: column = head).
+__device__ __forceinline__ int query_columns(const DecodeArgs &a) { return (a.q_tokens > 1 ? a.q_tokens : 1) * a.group; }
+
+// Tokens a column may not see at the end of the context: query token i of
+// q_tokens sees the first len - (q_tokens - 1 - i) tokens (causal).
+__device__ __forceinline__ int column_shortfall(const DecodeArgs &a, int col)
+{
+    return col < query_columns(a) ? (a.q_tokens > 1 ? a.q_tokens : 1) - 1 - col / a.group : 0;
+}
+
 // Query rows of (sequence b, KV head h) as bf16 bits: lane (col, jj) holds
-// channels jj*D/4 .. +D/4 of query col; columns past the group load a valid
-// row and are zeroed after the load (no divergent loads).
+// channels jj*D/4 .. +D/4 of query column col; columns past the last load a
+// valid row and are zeroed after the load (no divergent loads).
 template <int D>
 __device__ __forceinline__ void load_q_bits(const DecodeArgs &a, int b, int h, int col, int jj,
                                             uint32_t (&qbits)[D / 8])
 {
     constexpr int CPL = D / 4;
     const int G = a.group;
-    const bool live = col < G;
-    const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.num_q_heads + h * G + (live ? col : 0)) * D + jj * CPL;
+    const int S = a.q_tokens > 1 ? a.q_tokens : 1;
+    const bool live = col < S * G;
+    const int c = live ? col : 0;
+    const int64_t row = (static_cast<int64_t>(b) * S + c / G) * a.num_q_heads + h * G + c % G;
+    const uint16_t *qrow = a.q + row * D + jj * CPL;
 #pragma unroll
     for (int i = 0; i < CPL / 8; ++i) {
         const uint4 x = reinterpret_cast<const uint4 *>(qrow)[i];
@@ -217,12 +235,13 @@ __device__ __forceinline__ void init_state(SplitState<D> &st)
         st.acc[t] = st.lacc;
 }
 
-// A wave's state into its merge area: lane (col = query, jj) holds channels
-// 2*(16u + 4jj + r) + parity, i.e. 32u + 8jj + 0..7.
+// A wave's state into its merge area: lane (col = query column, jj) holds
+// channels 2*(16u + 4jj + r) + parity, i.e. 32u + 8jj + 0..7.
 template <int D>
-__device__ __forceinline__ void state_to_area(const MergeArea<D> &ar, const SplitState<D> &st, int col, int jj, int G)
+__device__ __forceinline__ void state_to_area(const MergeArea<D> &ar, const SplitState<D> &st, int col, int jj,
+                                              int columns)
 {
-    if (col < G) {
+    if (col < columns) {
         float *o = ar.row(col);
 #pragma unroll
         for (int u = 0; u < D / 32; ++u) {

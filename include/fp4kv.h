@@ -19,6 +19,8 @@
  *   fp4kv_decode_append_attention, fp4kv_decode_append_split
  *                           a decode step that first stores each sequence's
  *                           new token (fused into the decode kernel).
+ *   fp4kv_decode_multi_attention
+ *                           several query tokens per sequence, causal.
  *   fp4kv_status_string     text of a status code.
  *
  * Conventions for every call:
@@ -284,6 +286,31 @@ FP4KV_API int fp4kv_decode_append_split(const fp4kv_cache_layout_t *layout, void
                                         const int32_t *seq_lens, const int32_t *page_table,
                                         int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
                                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Attention of several consecutive query tokens per sequence over the
+ * packed cache, with causal masking: q_tokens query tokens sit at the last
+ * q_tokens positions of each context (speculative tokens being verified, or
+ * a chunk of a prefill), and query token i of sequence b attends over its
+ * first seq_lens[b] - (q_tokens - 1 - i) tokens.  Their K and V must already
+ * be in the cache (fp4kv_quantize_append).  ("Quantising the KV cache",
+ * Concept: attention reads every cached token up to the query's own; the
+ * same codec and kernels as fp4kv_decode_attention.)  The matrix-core
+ * kernels take q_tokens x (num_q_heads / H_kv) <= 16 query columns per KV
+ * head, so one pass over the cache serves all of them.
+ *   q     device bf16 [batch][q_tokens][num_q_heads][D], 16-B aligned.
+ *   out   device fp32 [batch][q_tokens][num_q_heads][D], 16-B aligned.
+ *   workspace  as fp4kv_decode_plan gives for q_tokens * num_q_heads query
+ *         heads (its group limit is the 16 columns above).
+ *   other arguments as for fp4kv_decode_attention.  A query token whose
+ *   limit is 0 or below gets a zero row.  q_tokens = 1 is
+ *   fp4kv_decode_attention.
+ * Errors: as for fp4kv_decode_attention; INVALID_ARGUMENT for q_tokens < 1;
+ * UNSUPPORTED for more than 16 query columns per KV head. */
+FP4KV_API int fp4kv_decode_multi_attention(const fp4kv_cache_layout_t *layout, const void *cache,
+                                           const void *q, int32_t batch, int32_t q_tokens, int32_t num_q_heads,
+                                           const int32_t *seq_lens, const int32_t *page_table,
+                                           int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
+                                           void *workspace, int64_t workspace_bytes, float *out, void *stream);
 
 /* Measurement utility, not a step of the method: reads `bytes` of device
  * memory at `buf` (device) once with 16-byte loads and discards the data.
