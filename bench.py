@@ -33,8 +33,8 @@ SETTLE_CALLS = 100                          # untimed decode calls before the wa
 # sources of the split kernel (per cache format) whose HBM counters profiles/ may hold
 _CSRC = os.path.join(ROOT, "fp4_quantised_kv_amd", "csrc")
 KERNEL_SOURCES = {
-    "fp4": ["fp4kv_decode_mfma.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h"],
-    "fp8": ["fp4kv_decode_fp8.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h"],
+    "fp4": ["fp4kv_decode_mfma.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h", "fp4kv_quant.h"],
+    "fp8": ["fp4kv_decode_fp8.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h", "fp4kv_quant.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
