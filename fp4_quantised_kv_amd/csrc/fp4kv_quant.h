@@ -53,31 +53,38 @@ __device__ __forceinline__ float e2m1_value(uint32_t nib)
     return __uint_as_float(bits | ((nib & 8u) << 28));
 }
 
-// Round-to-nearest-even E2M1 magnitude code of |x| / s, saturating at 6,
-// without dividing: count the rounding thresholds t*s that |x| reaches.  The
-// midpoints between consecutive magnitudes are 0.25, 0.75, 1.25, 1.75, 2.5,
-// 3.5 and 5; at an exact tie the even code wins, so a tie moves up only into
-// codes 2, 4 and 6 (comparison >=) and stays below otherwise (comparison >).
-// Every t*s is exact in fp32 (at most 7 significant bits, above 2^-11).
-struct E2M1Thresholds {
-    float t[7];
-    __device__ __forceinline__ explicit E2M1Thresholds(float s)
-    {
-        t[0] = 0.25f * s; t[1] = 0.75f * s; t[2] = 1.25f * s; t[3] = 1.75f * s;
-        t[4] = 2.5f * s;  t[5] = 3.5f * s;  t[6] = 5.0f * s;
-    }
-    __device__ __forceinline__ uint32_t code(float m) const
-    {
-        return static_cast<uint32_t>(m > t[0]) + static_cast<uint32_t>(m >= t[1]) +
-               static_cast<uint32_t>(m > t[2]) + static_cast<uint32_t>(m >= t[3]) +
-               static_cast<uint32_t>(m > t[4]) + static_cast<uint32_t>(m >= t[5]) +
-               static_cast<uint32_t>(m > t[6]);
-    }
-};
+// The quotient x / s rounded once to fp32, without a division per element:
+// q = x * r with r = 1/s (correctly rounded, once per block), then one
+// Newton step with the exact residual, q - (q*s - x)*r, in two FMAs.  The
+// result is within 2^-46 (relative) of the exact quotient.  A bf16 x over an
+// E4M3 s is either exactly an E2M1 rounding midpoint (0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5) or at least 2^-8 (relative) away from every one, so the
+// corrected quotient rounds to the same E2M1 code as the exact one, ties
+// included (an exact midpoint comes out exactly).  The plain product x * r
+// does not: with s = 1.875 * 2^k it overshoots the ties at 1.25, 2.5 and 5.
+// Checked on the CPU for every bf16 value and every scale; within a block
+// |x| / s stays below 9 (s is rounded from amax / 6), so nothing overflows.
+__device__ __forceinline__ float quotient(float x, float s, float r)
+{
+    const float q = x * r;
+    return __builtin_fmaf(-__builtin_fmaf(q, s, -x), r, q);
+}
+
+// Channels 2i, 2i+1 (the dword w of two bf16 values) into byte I of d.
+template <int I>
+__device__ __forceinline__ uint32_t pack_pair(uint32_t d, uint32_t w, float s, float r)
+{
+    const float x0 = __uint_as_float(w << 16);
+    const float x1 = __uint_as_float(w & 0xFFFF0000u);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, quotient(x0, s, r), quotient(x1, s, r), 1.0f, I);
+}
 
 // Quantise one block of 16 bf16 values held as 8 dwords (low half = even
 // channel).  Returns the 16 nibbles packed low-to-high (channel 2i in the low
-// nibble of byte i) and the scale code.
+// nibble of byte i) and the scale code.  The E2M1 rounding (nearest, ties to
+// even, saturating at 6, sign kept) is the hardware conversion, two values
+// per instruction, applied to the exactly rounding quotient above with a
+// unit scale (the conversion would use only the exponent of a scale).
 __device__ __forceinline__ void quantize_block16(const uint32_t w[8], uint32_t &lo, uint32_t &hi,
                                                  uint32_t &scale_code)
 {
@@ -93,17 +100,16 @@ __device__ __forceinline__ void quantize_block16(const uint32_t w[8], uint32_t &
     uint32_t sc = e4m3_code_rne_sat(a / 6.0f);
     sc = sc ? sc : 1u;                                  // zero scale -> smallest subnormal
     scale_code = sc;
-    const E2M1Thresholds th(e4m3_value(sc));
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
-        const float m = __uint_as_float((bits & 0x7FFFu) << 16);
-        const uint32_t nib = th.code(m) | ((bits >> 12) & 8u);
-        out[c >> 3] |= nib << (4 * (c & 7));
-    }
-    lo = out[0];
-    hi = out[1];
+    const float s = e4m3_value(sc);
+    const float r = 1.0f / s;
+    lo = pack_pair<0>(0u, w[0], s, r);
+    lo = pack_pair<1>(lo, w[1], s, r);
+    lo = pack_pair<2>(lo, w[2], s, r);
+    lo = pack_pair<3>(lo, w[3], s, r);
+    hi = pack_pair<0>(0u, w[4], s, r);
+    hi = pack_pair<1>(hi, w[5], s, r);
+    hi = pack_pair<2>(hi, w[6], s, r);
+    hi = pack_pair<3>(hi, w[7], s, r);
 }
 
 // -------------------------------------------------------- quantise / append
