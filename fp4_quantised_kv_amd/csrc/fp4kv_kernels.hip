@@ -25,7 +25,7 @@ namespace {
 using namespace quant;
 
 constexpr int kPage = 64;                 // tokens per page == lanes per wave
-constexpr int64_t kRunKernelMinTokens = 512;   // appends this long use 8-token runs
+constexpr int64_t kRunKernelMinTokens = 512;   // appends this long use 16-token slices
 
 // K of one token's 16-channel block: its 8 code bytes and its scale byte.
 template <int D>
@@ -101,29 +101,58 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(
                         cache);
 }
 
-// One thread per (run of 8 consecutive input tokens, KV head, 16-channel
-// block); for prefills and other long appends.  When the run's slots are 8
-// consecutive slots starting at a multiple of 8, the thread owns whole V code
-// dwords (8 tokens of one channel) and whole 8-byte scale runs, and writes
-// them with plain stores; otherwise it places each token as the per-token
-// kernel does.
+// Transpose an 8 x 8 matrix of nibbles held as 8 dwords (dword i, nibble j
+// -> dword j, nibble i): swap the off-diagonal 1x1, then 2x2, then 4x4
+// nibble blocks of each 2x2 block pair.
+__device__ __forceinline__ void transpose_nibbles8(uint32_t *r)
+{
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const uint32_t a = r[i], b = r[i + 1];
+        r[i] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+        r[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += (i % 4 == 1) ? 3 : 1) {
+        const uint32_t a = r[i], b = r[i + 2];
+        r[i] = (a & 0x00FF00FFu) | ((b << 8) & 0xFF00FF00u);
+        r[i + 2] = ((a >> 8) & 0x00FF00FFu) | (b & 0xFF00FF00u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a = r[i], b = r[i + 4];
+        r[i] = (a & 0x0000FFFFu) | (b << 16);
+        r[i + 4] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+}
+
+// One thread per (slice of 16 consecutive input tokens, KV head, 16-channel
+// block); for prefills and other long appends.  When the slice's slots are
+// 16 consecutive slots starting at a multiple of 16 -- one 16-token slice of
+// a page -- the thread owns whole V code rows (16 tokens of one channel, 8
+// bytes) and the slice's 16 V scale bytes of its block: its 16 channels'
+// rows are 128 contiguous bytes, written with 16-byte stores, and the
+// lanes of a wave (the blocks of one head) cover whole 1 KB stretches.
+// Otherwise it places each token as the per-token kernel does.  k and v are
+// not restrict-qualified here: with the qualifier the compiler may move their
+// loads across the barriers that keep only a few rows live at a time.
 template <int D>
-__global__ __launch_bounds__(256) void append_runs_kernel(
-    CacheGeom g, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t n_tokens,
+__global__ __launch_bounds__(256) void append_slices_kernel(
+    CacheGeom g, const uint16_t *k, const uint16_t *v, int64_t n_tokens,
     const int64_t *__restrict__ slots, uint8_t *__restrict__ cache)
 {
     constexpr int NB = D / 16;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t n_runs = (n_tokens + 7) / 8;
-    if (idx >= n_runs * g.num_kv_heads * NB)
+    const int64_t n_slices = (n_tokens + 15) / 16;
+    if (idx >= n_slices * g.num_kv_heads * NB)
         return;
     const int blk = static_cast<int>(idx % NB);
-    const int64_t rh = idx / NB;                        // run * H_kv + head
-    const int head = static_cast<int>(rh % g.num_kv_heads);
-    const int64_t t0 = (rh / g.num_kv_heads) * 8;
-    const int n = static_cast<int>(n_tokens - t0 < 8 ? n_tokens - t0 : 8);
+    const int64_t sh = idx / NB;                        // slice * H_kv + head
+    const int head = static_cast<int>(sh % g.num_kv_heads);
+    const int64_t t0 = (sh / g.num_kv_heads) * 16;
+    const int n = static_cast<int>(n_tokens - t0 < 16 ? n_tokens - t0 : 16);
     const int64_t s0 = slots[t0];
-    bool whole = n == 8 && s0 >= 0 && s0 % 8 == 0 && s0 + 8 <= g.num_pages * kPage;
+    bool whole = n == 16 && s0 >= 0 && s0 % 16 == 0 && s0 + 16 <= g.num_pages * kPage;
     for (int i = 1; i < n && whole; ++i)
         whole = slots[t0 + i] == s0 + i;
 
@@ -131,62 +160,63 @@ __global__ __launch_bounds__(256) void append_runs_kernel(
     const uint16_t *ksrc = k + t0 * row_stride + head * D + 16 * blk;
     const uint16_t *vsrc = v + t0 * row_stride + head * D + 16 * blk;
     if (!whole) {
-        for (int i = 0; i < n; ++i) {
-            const int64_t slot = slots[t0 + i];
-            if (slot < 0 || slot >= g.num_pages * kPage)
-                continue;
-            uint8_t *base = cache + (slot / kPage) * g.page_stride + head * g.head_stride;
-            const int off = static_cast<int>(slot % kPage);
-            append_k<D>(base, g, off, blk, ksrc + i * row_stride);
-            append_v_token<D>(base, g, off, blk, vsrc + i * row_stride);
-        }
+        for (int i = 0; i < n; ++i)
+            append_token_fp4<D>(g, ksrc + i * row_stride, vsrc + i * row_stride, slots[t0 + i], head, blk, cache);
         return;
     }
     uint8_t *base = cache + (s0 / kPage) * g.page_stride + head * g.head_stride;
     const int off0 = static_cast<int>(s0 % kPage);
-    // K: the eight tokens' blocks are loaded together (256 bytes in flight
-    // per thread), then quantised and stored token by token
-    {
+    // K: eight tokens' blocks loaded together (256 bytes in flight per
+    // thread), then quantised and stored token by token
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
         uint32_t w[8][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            load_block16(ksrc + i * row_stride, w[i]);
+            load_block16(ksrc + (8 * h + i) * row_stride, w[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t lo, hi, sc;
             quantize_block16(w[i], lo, hi, sc);
-            *reinterpret_cast<uint2 *>(base + g.k_codes_off + (off0 + i) * (D / 2) + 8 * blk) = make_uint2(lo, hi);
-            base[g.k_scales_off + (off0 + i) * (D / 16) + blk] = static_cast<uint8_t>(sc);
+            const int off = off0 + 8 * h + i;
+            *reinterpret_cast<uint2 *>(base + g.k_codes_off + off * (D / 2) + 8 * blk) = make_uint2(lo, hi);
+            base[g.k_scales_off + off * (D / 16) + blk] = static_cast<uint8_t>(sc);
         }
+        asm volatile("" ::: "memory");
     }
-    uint32_t vd[16];                                    // channel 16*blk + i, tokens off0 .. off0 + 7
-    uint32_t vs[2] = {0u, 0u};
+    // V: nibble rows of channels 16*blk + c, tokens off0 .. off0 + 15.  Per
+    // 8 tokens the codes come out token-major (dword i = token i, nibble c =
+    // channel c); an 8 x 8 nibble transpose makes them channel-major (dword
+    // c = channel c, nibble i = token i), which is a V code row's half.
+    uint32_t vd[2][16];                                 // [token half][channel]
+    uint32_t vs[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        vd[i] = 0u;
-    {
-        uint32_t w[8][8];
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            load_block16(vsrc + i * row_stride, w[i]);
+        for (int q = 0; q < 2; ++q) {               // four tokens' rows in flight at a time
+            uint32_t w[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t lo, hi, sc;
-            quantize_block16(w[i], lo, hi, sc);
+            for (int i = 0; i < 4; ++i)
+                load_block16(vsrc + (8 * h + 4 * q + i) * row_stride, w[i]);
 #pragma unroll
-            for (int c = 0; c < 16; ++c)
-                vd[c] |= (((c < 8 ? lo : hi) >> (4 * (c & 7))) & 0xFu) << (4 * i);
-            vs[i >> 2] |= sc << (8 * (i & 3));
+            for (int i = 0; i < 4; ++i) {
+                uint32_t sc;
+                quantize_block16(w[i], vd[h][4 * q + i], vd[h][8 + 4 * q + i], sc);
+                vs[2 * h + q] |= sc << (8 * i);
+            }
+            // the next rows' loads stay after this arithmetic, so that only
+            // four rows are held at once
+            asm volatile("" ::: "memory");
         }
+        transpose_nibbles8(&vd[h][0]);
+        transpose_nibbles8(&vd[h][8]);
     }
-    const int word = ((off0 & 15) >> 3) * 4;
+    uint4 *vrow = reinterpret_cast<uint4 *>(base + g.v_codes_off + v_code_row<D>(off0, 16 * blk));
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-        *reinterpret_cast<uint32_t *>(base + g.v_codes_off + v_code_row<D>(off0, 16 * blk + c) + word) = vd[c];
-    *reinterpret_cast<uint2 *>(base + g.v_scales_off + v_scale_byte<D>(off0, blk)) = make_uint2(vs[0], vs[1]);
+    for (int c = 0; c < 16; c += 2)
+        vrow[c / 2] = make_uint4(vd[0][c], vd[1][c], vd[0][c + 1], vd[1][c + 1]);
+    *reinterpret_cast<uint4 *>(base + g.v_scales_off + v_scale_byte<D>(off0, blk)) = make_uint4(vs[0], vs[1], vs[2], vs[3]);
 }
-
-// -------------------------------------------------- FP8 (per-tensor scale)
 
 // One token's block `blk` of KV head `head` at `slot` in an FP8 cache; slots
 // outside the pool are skipped.
@@ -572,11 +602,11 @@ hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const u
         const int64_t blocks = (n_tokens * per_token + 255) / 256;
         append_fp8_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
     } else if (n_tokens >= kRunKernelMinTokens) {
-        const int64_t blocks = ((n_tokens + 7) / 8 * per_token + 255) / 256;
+        const int64_t blocks = ((n_tokens + 15) / 16 * per_token + 255) / 256;
         if (g.head_dim == 64)
-            append_runs_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+            append_slices_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
         else
-            append_runs_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+            append_slices_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
     } else {
         const int64_t blocks = (n_tokens * per_token + 255) / 256;
         if (g.head_dim == 64)

@@ -165,11 +165,11 @@ def test_append_order_does_not_matter():
     assert torch.equal(ref, c2)
 
 
-@pytest.mark.parametrize("first_slot,n", [(3, 1000), (8, 600), (0, 515), (64, 4096)])
+@pytest.mark.parametrize("first_slot,n", [(3, 1000), (8, 600), (0, 515), (64, 4096), (48, 530)])
 def test_contiguous_runs_aligned_or_not(first_slot, n):
-    """Long appends take 8-token runs: aligned runs are written whole,
-    misaligned or partial ones nibble by nibble; both give the oracle's bytes
-    and leave the neighbouring slots untouched."""
+    """Long appends take 16-token slices: slices on 16-slot boundaries are
+    written whole, misaligned or partial ones token by token; both give the
+    oracle's bytes and leave the neighbouring slots untouched."""
     w = wl.WORKLOADS["gqa4_b8_ctx4k"]
     k = wl.kv_tokens(w, 8, 0, "k", 0, n)
     v = wl.kv_tokens(w, 8, 0, "v", 0, n)
