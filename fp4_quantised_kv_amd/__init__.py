@@ -18,6 +18,7 @@ import os
 __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
            "quantize_append", "decode_attention", "decode_split", "decode_combine",
            "decode_append_attention", "decode_append_split", "decode_multi_attention",
+           "decode_window_plan", "decode_window_attention",
            "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3",
            "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "int_sizes", "int_quantize", "int_decode_plan",
            "int_decode_attention"]
@@ -132,6 +133,16 @@ def library():
                                                    ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                                    ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
         L.fp4kv_decode_multi_attention.restype = ctypes.c_int
+        L.fp4kv_decode_window_plan.argtypes = [ctypes.POINTER(CacheLayout), ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                               ctypes.POINTER(ctypes.c_int64)]
+        L.fp4kv_decode_window_plan.restype = ctypes.c_int
+        L.fp4kv_decode_window_attention.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_float, ctypes.c_int32, _P,
+                                                    ctypes.c_int64, _P, _P]
+        L.fp4kv_decode_window_attention.restype = ctypes.c_int
         L.fp4kv_read_probe.argtypes = [_P, ctypes.c_int64, _P, _P]
         L.fp4kv_read_probe.restype = ctypes.c_int
         L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
@@ -334,6 +345,53 @@ def decode_multi_attention(layout: CacheLayout, cache, q, seq_lens, page_table, 
     _check("fp4kv_decode_multi_attention", library().fp4kv_decode_multi_attention(
         ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, S, Hq, seq_lens.data_ptr(),
         page_table.data_ptr(), max_pages, float(softmax_scale), num_splits, workspace.data_ptr(),
+        workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def decode_window_plan(layout: CacheLayout, batch: int, q_tokens: int, num_q_heads: int, max_pages_per_seq: int,
+                       window: int, num_splits: int = 0) -> "DecodePlan":
+    s, p, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check("fp4kv_decode_window_plan", library().fp4kv_decode_window_plan(
+        ctypes.byref(layout), batch, q_tokens, num_q_heads, max_pages_per_seq, window, num_splits,
+        ctypes.byref(s), ctypes.byref(p), ctypes.byref(ws)))
+    return DecodePlan(s.value, p.value, ws.value)
+
+
+def decode_window_attention(layout: CacheLayout, cache, q, seq_lens, page_table, window: int,
+                            softmax_scale=None, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Sliding-window causal attention: q bf16 [B][S][Hq][D] (the last S
+    positions of each context); query token i sees the last `window` tokens
+    of its prefix (window 0: all of it).  Returns fp32 [B][S][Hq][D]."""
+    import torch
+    _need(cache, "cache", torch.uint8)
+    _need(q, "q", torch.bfloat16)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_table, "page_table", torch.int32)
+    if q.dim() != 4:
+        raise ValueError("q must be [B][S][Hq][D]")
+    B, S, Hq, D = q.shape
+    if D != layout.head_dim:
+        raise ValueError("q's last dimension must equal the cache head_dim")
+    if tuple(seq_lens.shape) != (B,) or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("seq_lens must be [B] and page_table [B][max_pages]")
+    max_pages = page_table.shape[1]
+    plan = decode_window_plan(layout, B, S, Hq, max_pages, window, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty(B, S, Hq, D, dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", torch.float32)
+        if tuple(out.shape) != (B, S, Hq, D):
+            raise ValueError("out must be [B][S][Hq][D]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _check("fp4kv_decode_window_attention", library().fp4kv_decode_window_attention(
+        ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, S, Hq, seq_lens.data_ptr(),
+        page_table.data_ptr(), max_pages, int(window), float(softmax_scale), num_splits, workspace.data_ptr(),
         workspace.numel(), out.data_ptr(), _stream(stream)))
     return out
 

@@ -202,22 +202,36 @@ namespace {
 
 // Checks shared by fp4kv_decode_split and fp4kv_decode_attention; fills the
 // kernel arguments (out is left null).
+// Pages a split plan has to cover: the whole table, or with a sliding
+// window the pages from the first query token's window start to the end of
+// the context (at most ceil((window + q_tokens - 1) / 64) + 1).
+int32_t window_span_pages(int32_t max_pages, int32_t q_tokens, int32_t window)
+{
+    if (window <= 0)
+        return max_pages;
+    const int64_t span = (static_cast<int64_t>(window) + q_tokens - 1 + kPage - 1) / kPage + 1;
+    return static_cast<int32_t>(span < max_pages ? span : max_pages);
+}
+
 int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
                   int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
                   const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
                   int32_t num_splits, void *workspace, int64_t workspace_bytes,
-                  fp4kv::DecodeArgs *a, int32_t q_tokens = 1)
+                  fp4kv::DecodeArgs *a, int32_t q_tokens = 1, int32_t window = 0)
 {
     int rc = check_layout(layout);
     if (rc != FP4KV_OK)
         return rc;
+    if (window < 0)
+        return FP4KV_ERR_INVALID_ARGUMENT;
     if (q_tokens < 1 || num_q_heads < 1 || num_q_heads % layout->params.num_kv_heads ||
         static_cast<int64_t>(q_tokens) * num_q_heads > std::numeric_limits<int32_t>::max())
         return FP4KV_ERR_INVALID_ARGUMENT;
     Plan plan;
     // several query tokens: the plan's rows (and its group limit) count
     // q_tokens x num_q_heads query rows
-    rc = make_plan(*layout, batch, q_tokens * num_q_heads, max_pages_per_seq, num_splits, &plan);
+    rc = make_plan(*layout, batch, q_tokens * num_q_heads, window_span_pages(max_pages_per_seq, q_tokens, window),
+                   num_splits, &plan);
     if (rc != FP4KV_OK)
         return rc;
     if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
@@ -245,6 +259,7 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     a->num_q_heads = num_q_heads;
     a->group = num_q_heads / layout->params.num_kv_heads;
     a->q_tokens = q_tokens;
+    a->window = window;
     a->max_pages = max_pages_per_seq;
     a->splits = plan.splits;
     a->pages_per_split = plan.pages_per_split;
@@ -404,6 +419,51 @@ int fp4kv_decode_multi_attention(const fp4kv_cache_layout_t *layout, const void 
     fp4kv::DecodeArgs a;
     int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
                            softmax_scale, num_splits, workspace, workspace_bytes, &a, q_tokens);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    if (!out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(out, 16))
+        return FP4KV_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = fp4kv::launch_decode_split(a, st);
+    if (e != hipSuccess)
+        return FP4KV_ERR_HIP;
+    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, q_tokens * num_q_heads, a.partials,
+                                     layout->params.head_dim, out, st);
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+int fp4kv_decode_window_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t q_tokens,
+                             int32_t num_q_heads, int32_t max_pages_per_seq, int32_t window, int32_t num_splits,
+                             int32_t *splits_out, int32_t *partials_out, int64_t *workspace_bytes_out)
+{
+    int rc = check_layout(layout);
+    if (rc != FP4KV_OK)
+        return rc;
+    if (!splits_out || !partials_out || !workspace_bytes_out || q_tokens < 1 || window < 0 || num_q_heads < 1 ||
+        max_pages_per_seq < 1 || static_cast<int64_t>(q_tokens) * num_q_heads > std::numeric_limits<int32_t>::max())
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    Plan plan;
+    rc = make_plan(*layout, batch, q_tokens * num_q_heads, window_span_pages(max_pages_per_seq, q_tokens, window),
+                   num_splits, &plan);
+    if (rc != FP4KV_OK)
+        return rc;
+    *splits_out = plan.splits;
+    *partials_out = plan.partials;
+    *workspace_bytes_out = plan.ws_bytes;
+    return FP4KV_OK;
+}
+
+int fp4kv_decode_window_attention(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
+                                  int32_t batch, int32_t q_tokens, int32_t num_q_heads, const int32_t *seq_lens,
+                                  const int32_t *page_table, int32_t max_pages_per_seq, int32_t window,
+                                  float softmax_scale, int32_t num_splits, void *workspace,
+                                  int64_t workspace_bytes, float *out, void *stream)
+{
+    fp4kv::DecodeArgs a;
+    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
+                           softmax_scale, num_splits, workspace, workspace_bytes, &a, q_tokens, window);
     if (rc != FP4KV_OK || batch == 0)
         return rc;
     if (!out)

@@ -85,9 +85,9 @@ __device__ __forceinline__ half8_t fp8x8(uint32_t a, uint32_t b)
 
 // Scores of half page h: tiles 2h + i, A operand of MFMA m = channels
 // 32jj + 8m .. +7 of the lane's token, the same channel order as the query
-// operand.  Tokens at or past `valid` (the lane's query column's limit in
-// this page) get -inf.
-__device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, int h, int valid,
+// operand.  Tokens outside lo .. valid-1 (the lane's query column's window
+// in this page) get -inf.
+__device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, int h, int lo, int valid,
                                         const half8_t (&qf)[kD / 32], float (&z)[2][4])
 {
     const int at = (col >> 3) * 1024 + (((col & 7) << 3) + 2 * jj) * 16;
@@ -102,7 +102,7 @@ __device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, in
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8(b.z, b.w), qf[3], acc, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            z[i][e] = (16 * jj + 8 * h + 4 * i + e < valid) ? acc[e] : -INFINITY;
+            z[i][e] = (16 * jj + 8 * h + 4 * i + e < valid && 16 * jj + 8 * h + 4 * i + e >= lo) ? acc[e] : -INFINITY;
     }
 }
 
@@ -136,7 +136,8 @@ __device__ __forceinline__ void values8(uint4 w, int u, int jj, int h, int valid
 // they never alias.
 __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
                                           const DecodeArgs &a, const Fp8Offsets &o, int lane, int col, int jj, int h,
-                                          int p0, int p1, int len, int shortfall, const int32_t *ptab, int ids, int pid,
+                                          int p0, int p1, int len, int shortfall, int first, const int32_t *ptab,
+                                          int ids, int pid,
                                           const half8_t (&qf)[kD / 32], float zscale, SplitState<kD> &st)
 {
     const CacheGeom &g = a.geom;
@@ -168,7 +169,7 @@ __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *
             if (cur)
                 wait_vmem_at_most<kCopies>();
             float z[2][4];
-            scores8(kslot, col, jj, hf, min(kPage, len - pg * kPage - shortfall), qf, z);
+            scores8(kslot, col, jj, hf, first - pg * kPage, min(kPage, len - pg * kPage - shortfall), qf, z);
             __builtin_amdgcn_s_waitcnt(kWaitLds);
             if (next)
                 stage_k8(nblk, o, nh, kslot);
@@ -230,8 +231,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
         stage_k8(blk, o, 0, kslots[wave]);
         stage_v8(blk, o, 0, vslots[wave]);
     }
-    fp8_pages(kslots[wave], vslots[wave], a, o, lane, col, jj, c.h, c.p0, c.p1, c.len, column_shortfall(a, col),
-              c.ptab, ids, pid, qf, zscale, st);
+    const int shortfall = column_shortfall(a, col);
+    fp8_pages(kslots[wave], vslots[wave], a, o, lane, col, jj, c.h, c.p0, c.p1, c.len, shortfall,
+              column_first_token(a, c.len, shortfall), c.ptab, ids, pid, qf, zscale, st);
 
     // the V tensor's scale multiplies every value, so it multiplies o
 #pragma unroll

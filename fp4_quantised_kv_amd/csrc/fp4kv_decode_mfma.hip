@@ -72,10 +72,10 @@ struct VRegs {
 };
 
 // Scores and online softmax of one page of which the lane's query column
-// sees the first `valid` tokens; leaves the probabilities as the value
-// product's B operands (hi and lo parts for the two 32-token halves).
+// sees the tokens lo .. valid-1 (page-local); leaves the probabilities as the
+// value product's B operands (hi and lo parts for the two 32-token halves).
 template <int D>
-__device__ __forceinline__ void scores_phase(const KRegs<D> &r, int valid, const half8_t (&qf)[D / 32],
+__device__ __forceinline__ void scores_phase(const KRegs<D> &r, int lo, int valid, const half8_t (&qf)[D / 32],
                                              float zscale, int jj, SplitState<D> &st, half8_t (&pf)[2],
                                              half8_t (&pl)[2])
 {
@@ -95,12 +95,14 @@ __device__ __forceinline__ void scores_phase(const KRegs<D> &r, int valid, const
         for (int e = 0; e < 4; ++e)
             z[t][e] = sacc[e];                          // scaled inside the exponent below
     }
-    if (valid < kPage) {
+    if (valid < kPage || lo > 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                z[t][e] = (16 * jj + 4 * t + e < valid) ? z[t][e] : -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+                const int tok = 16 * jj + 4 * t + e;
+                z[t][e] = (tok < valid && tok >= lo) ? z[t][e] : -INFINITY;
+            }
     }
 
     softmax_tiles<D, 4>(z, st, zscale, pf, pl);
@@ -282,7 +284,7 @@ __device__ __forceinline__ void read_v(const uint8_t *slot, int u0, int lane, in
 template <int D>
 __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
                                              const DecodeArgs &a, const StageOffsets &so, int lane, int col,
-                                             int jj, int h, int p0, int p1, int len, int shortfall,
+                                             int jj, int h, int p0, int p1, int len, int shortfall, int first,
                                              const int32_t *ptab, int ids, int pid, const half8_t (&qf)[D / 32],
                                              float zscale, SplitState<D> &st)
 {
@@ -314,7 +316,8 @@ __device__ __forceinline__ void staged_pages(uint8_t *__restrict__ kslot, uint8_
         if (next)
             stage_k(block_of(pid_next), so, kslot);
         if (cur)
-            scores_phase<D>(kr, min(kPage, len - pg * kPage - shortfall), qf, zscale, jj, st, pf, pl);
+            scores_phase<D>(kr, first - pg * kPage, min(kPage, len - pg * kPage - shortfall), qf, zscale, jj, st,
+                            pf, pl);
 
         // V: outstanding now are this page's V then the next page's K
         // copies.  One pair block at a time keeps few registers live.
@@ -373,6 +376,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
         append_if_last_chunk<D, false>(a, c, lane);
 
     const int shortfall = column_shortfall(a, col);
+    const int first = column_first_token(a, c.len, shortfall);
     SplitState<D> st;
     init_state(st);
     if constexpr (STAGED) {
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
             stage_k(blk, so, kslots[wave]);
             stage_v(blk, so, vslots[wave]);
         }
-        staged_pages<D>(kslots[wave], vslots[wave], a, so, lane, col, jj, c.h, c.p0, c.p1, c.len, shortfall,
+        staged_pages<D>(kslots[wave], vslots[wave], a, so, lane, col, jj, c.h, c.p0, c.p1, c.len, shortfall, first,
                         c.ptab, ids, pid, qf, zscale, st);
     } else {
         half8_t pf[2], pl[2];
@@ -399,7 +403,8 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
             VRegs<D> vr;
             load_k_direct<D>(blk, g, col, jj, kr);
             load_v_direct<D>(blk, g, col, jj, vr);
-            scores_phase<D>(kr, min(kPage, c.len - pg * kPage - shortfall), qf, zscale, jj, st, pf, pl);
+            scores_phase<D>(kr, first - pg * kPage, min(kPage, c.len - pg * kPage - shortfall), qf, zscale, jj,
+                            st, pf, pl);
             half8_t sv[VRegs<D>::NU][2];
 #pragma unroll
             for (int u = 0; u < VRegs<D>::NU; ++u)

@@ -27,7 +27,8 @@ struct DecodeArgs {
     const int32_t *page_table;   // [batch][max_pages]
     int32_t batch, num_q_heads, group, max_pages;
     int32_t q_tokens;            // query tokens per sequence (1: plain decode); q_tokens * group <= 16
-    int32_t splits, pages_per_split;   // context chunks and pages per chunk
+    int32_t window;              // > 0: a query sees only the last `window` tokens of its prefix (sliding window)
+    int32_t splits, pages_per_split;   // context chunks and pages per chunk (from the window's first page)
     int32_t partials;            // partial slots per row: ceil(splits / 4), one per workgroup
     float scale_log2e;           // softmax scale times log2(e): scores kept in base 2
     float *ws_o;                 // [batch][partials][q_tokens * num_q_heads][D] unnormalised outputs

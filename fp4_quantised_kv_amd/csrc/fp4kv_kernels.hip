@@ -643,7 +643,8 @@ SplitKernel split_kernel_for(const DecodeArgs &a)
     if (a.geom.fp8)
         return SplitKernel::fp8;
     const char *v = std::getenv("FP4KV_DECODE_KERNEL");
-    if (v && std::strcmp(v, "valu") == 0 && a.q_tokens <= 1)   // the vector-ALU kernel takes one query token
+    // the vector-ALU kernel takes one query token and no window
+    if (v && std::strcmp(v, "valu") == 0 && a.q_tokens <= 1 && a.window <= 0)
         return SplitKernel::valu;
     if (a.geom.head_dim == 64 || (v && std::strcmp(v, "mfma_direct") == 0))
         return SplitKernel::mfma_direct;

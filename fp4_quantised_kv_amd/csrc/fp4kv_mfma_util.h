@@ -276,8 +276,22 @@ __device__ __forceinline__ Chunk chunk_of(const DecodeArgs &a, int h, int b, int
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
     c.len = len;
+    if (a.window > 0) {
+        // chunks start at the page of the earliest token any query column
+        // sees: the first query token's prefix end minus the window
+        const int first = len - ((a.q_tokens > 1 ? a.q_tokens : 1) - 1) - a.window;
+        c.p0 += first > 0 ? first / kPage : 0;
+    }
     c.p1 = min(c.p0 + a.pages_per_split, (len + kPage - 1) / kPage);
     return c;
+}
+
+// First token of the context the lane's query column sees (0 without a
+// window), for a column whose prefix ends `shortfall` tokens before len.
+__device__ __forceinline__ int column_first_token(const DecodeArgs &a, int len, int shortfall)
+{
+    const int first = len - shortfall - a.window;
+    return (a.window > 0 && first > 0) ? first : 0;
 }
 
 __device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, int lane)

@@ -21,6 +21,8 @@
  *                           new token (fused into the decode kernel).
  *   fp4kv_decode_multi_attention
  *                           several query tokens per sequence, causal.
+ *   fp4kv_decode_window_plan, fp4kv_decode_window_attention
+ *                           the same with a sliding window.
  *   fp4kv_status_string     text of a status code.
  *
  * Conventions for every call:
@@ -311,6 +313,34 @@ FP4KV_API int fp4kv_decode_multi_attention(const fp4kv_cache_layout_t *layout, c
                                            const int32_t *seq_lens, const int32_t *page_table,
                                            int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
                                            void *workspace, int64_t workspace_bytes, float *out, void *stream);
+
+/* Sliding-window attention over the packed cache: as
+ * fp4kv_decode_multi_attention (q_tokens query tokens per sequence at the
+ * end of each context, causal), and query token i sees only the last
+ * `window` tokens of its prefix, positions max(0, L_i - window) .. L_i - 1
+ * with L_i = seq_lens[b] - (q_tokens - 1 - i); window = 0 means no window.
+ * Only the pages that hold those tokens are read.  ("Week 6 -- FP4 KV Caches
+ * and Bounded Replay", Overview and Core Concepts: sliding-window layers keep
+ * their KV in FP8 and attend over the last n_win tokens; the same cache
+ * formats and kernels as fp4kv_decode_attention.)
+ * fp4kv_decode_window_plan gives the split count S, partials P and the
+ * workspace bytes for the same arguments (the splits cover the window's
+ * pages, not the whole table).
+ *   window       >= 0.
+ *   other arguments as for fp4kv_decode_multi_attention.
+ * Errors: as for fp4kv_decode_multi_attention; INVALID_ARGUMENT for a
+ * negative window. */
+FP4KV_API int fp4kv_decode_window_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t q_tokens,
+                                       int32_t num_q_heads, int32_t max_pages_per_seq, int32_t window,
+                                       int32_t num_splits, int32_t *splits_out, int32_t *partials_out,
+                                       int64_t *workspace_bytes_out);
+
+FP4KV_API int fp4kv_decode_window_attention(const fp4kv_cache_layout_t *layout, const void *cache,
+                                            const void *q, int32_t batch, int32_t q_tokens,
+                                            int32_t num_q_heads, const int32_t *seq_lens,
+                                            const int32_t *page_table, int32_t max_pages_per_seq,
+                                            int32_t window, float softmax_scale, int32_t num_splits,
+                                            void *workspace, int64_t workspace_bytes, float *out, void *stream);
 
 /* Measurement utility, not a step of the method: reads `bytes` of device
  * memory at `buf` (device) once with 16-byte loads and discards the data.

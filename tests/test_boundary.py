@@ -255,3 +255,17 @@ def test_append_decode_rejects_missing_or_misaligned_rows():
     assert lib.fp4kv_decode_append_attention(*args(None)) == fk.ERR_INVALID_ARGUMENT
     assert lib.fp4kv_decode_append_attention(*args(264)) == fk.ERR_MISALIGNED
     assert lib.fp4kv_decode_append_split(*args(None)[:-2], None) == fk.ERR_INVALID_ARGUMENT
+
+
+def test_window_rejects_negative_window():
+    L = fk.cache_layout(2, 128, 16)
+    with pytest.raises(fk.Fp4KVError) as e:
+        fk.decode_window_plan(L, 1, 1, 4, 16, -1)
+    assert e.value.status == fk.ERR_INVALID_ARGUMENT
+    s = fk.decode_window_plan(L, 1, 1, 4, 16, 64)
+    assert s.splits <= 2
+    # the splits cover the window's pages, not the whole table
+    big = fk.cache_layout(8, 128, 4096)
+    full = fk.decode_plan(big, 4, 32, 512, 0)
+    win = fk.decode_window_plan(big, 4, 1, 32, 512, 256, 0)
+    assert win.splits <= 6 < full.splits

@@ -1,0 +1,88 @@
+"""GPU parity of sliding-window attention over the packed cache
+(fp4kv_decode_window_attention): query token i of S sees the last `window`
+tokens of its causal prefix; each row within 1e-3 of the oracle's fp64
+attention over exactly those tokens; window 0 is the unwindowed call."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantised_kv_amd as fk
+import fp4kv_harness as hx
+import fp4kv_workloads as wl
+import oracle
+from test_gpu_multi_query import _cache
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _codes(kv, lens, fmt, L, D, Hkv):
+    out = []
+    for b, n in enumerate(lens):
+        if fmt == "fp8":
+            kc = oracle.quantize_fp8(wl.bf16_bits(kv[b][0]), L.params.k_scale) if n else np.zeros((1, Hkv, D), np.uint8)
+            vc = oracle.quantize_fp8(wl.bf16_bits(kv[b][1]), L.params.v_scale) if n else np.zeros((1, Hkv, D), np.uint8)
+            out.append((kc, vc))
+        else:
+            kq = oracle.quantize(wl.bf16_bits(kv[b][0]), want_xhat=False) if n else None
+            vq = oracle.quantize(wl.bf16_bits(kv[b][1]), want_xhat=False) if n else None
+            out.append((kq, vq))
+    return out
+
+
+def _reference(codes, lens, q, window, fmt, L, D, Hkv):
+    """Oracle attention of query token i over tokens [lo_i, L_i)."""
+    B, S, Hq, _ = q.shape
+    ref = np.zeros((B, S, Hq, D))
+    for b, n in enumerate(lens):
+        for i in range(S):
+            Li = n - (S - 1 - i)
+            if Li <= 0:
+                continue
+            lo = max(0, Li - window) if window > 0 else 0
+            qi = wl.bf16_bits(q[b:b + 1, i].contiguous())
+            if fmt == "fp8":
+                kc, vc = codes[b]
+                r = oracle.decode_attention_fp8(qi, [kc[lo:Li]], [vc[lo:Li]], L.params.k_scale, L.params.v_scale,
+                                                [Li - lo], D ** -0.5)
+            else:
+                kq, vq = codes[b]
+                r = oracle.decode_attention(qi, [kq[0][lo:Li]], [kq[1][lo:Li]], [vq[0][lo:Li]], [vq[1][lo:Li]],
+                                            [Li - lo], D ** -0.5)
+            ref[b, i] = r[0]
+    return ref
+
+
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128)])
+@pytest.mark.parametrize("window", [1, 17, 64, 100, 1000])
+@pytest.mark.parametrize("S,G,splits", [(1, 8, 0), (4, 4, 1), (2, 2, 3)])
+def test_window_against_oracle(fmt, D, window, S, G, splits):
+    lens = [0, 1, 5, 64, 65, 200, 1000, 3000]
+    Hkv = 2
+    L, cache, table, kv, g = _cache(lens, Hkv, D, fmt, seed=window + S * 13 + D)
+    q = torch.randn(len(lens), S, Hkv * G, D, generator=g).to(torch.bfloat16)
+    _say(f"window attention: {fmt} D {D} window {window} S {S} G {G} splits {splits}")
+    out = fk.decode_window_attention(L, cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(),
+                                     table.cuda(), window, num_splits=splits)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref = _reference(_codes(kv, lens, fmt, L, D, Hkv), lens, q, window, fmt, L, D, Hkv)
+    err = float(hx.row_rel_error(out, ref).max())
+    _say(f"  worst per-row relative error {err:.3e}")
+    assert err <= TOL
+
+
+def test_window_zero_is_unwindowed():
+    lens = [7, 130, 900]
+    L, cache, table, kv, g = _cache(lens, 2, 128, "fp4", seed=4)
+    q = torch.randn(3, 2, 8, 128, generator=g).to(torch.bfloat16)
+    lens_d = torch.tensor(lens, dtype=torch.int32).cuda()
+    a = fk.decode_window_attention(L, cache, q.cuda(), lens_d, table.cuda(), 0)
+    b = fk.decode_multi_attention(L, cache, q.cuda(), lens_d, table.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
