@@ -218,3 +218,52 @@ def bf16_bits(x: torch.Tensor):
     """uint16 numpy view of a bf16 tensor's bit patterns."""
     import numpy as np
     return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------- toy sliding-window network
+
+@dataclass(frozen=True)
+class ToyNet:
+    """A toy multi-layer network of sliding-window attention layers with
+    random weights, for the exact-versus-bounded replay study ("Week 6 -- FP4
+    KV Caches and Bounded Replay", Overview, Core Concepts and Lab)."""
+    name: str
+    layers: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    window: int
+    batch: int
+    tokens: int
+
+    @property
+    def d_model(self) -> int:
+        return self.q_heads * self.head_dim
+
+
+TOY_NETS: Dict[str, ToyNet] = {t.name: t for t in [
+    ToyNet("toy_swa_l4_w32", layers=4, q_heads=4, kv_heads=2, head_dim=128, window=32, batch=8, tokens=160),
+    ToyNet("toy_swa_l1_w32", layers=1, q_heads=4, kv_heads=2, head_dim=128, window=32, batch=4, tokens=80),
+    ToyNet("toy_swa_l2_w16", layers=2, q_heads=2, kv_heads=2, head_dim=128, window=16, batch=4, tokens=64),
+]}
+
+
+def toy_weights(t: ToyNet, seed: int):
+    """Per layer (W_q [d][Hq*D], W_k [d][Hkv*D], W_v [d][Hkv*D], W_o [Hq*D][d]),
+    fp32, N(0, 1/fan_in)."""
+    out = []
+    d = t.d_model
+    for layer in range(t.layers):
+        g = _gen(seed, _name_id(t.name), 100 + layer)
+        wq = torch.randn(d, t.q_heads * t.head_dim, generator=g) / math.sqrt(d)
+        wk = torch.randn(d, t.kv_heads * t.head_dim, generator=g) / math.sqrt(d)
+        wv = torch.randn(d, t.kv_heads * t.head_dim, generator=g) / math.sqrt(d)
+        wo = torch.randn(t.q_heads * t.head_dim, d, generator=g) / math.sqrt(t.q_heads * t.head_dim)
+        out.append((wq, wk, wv, wo))
+    return out
+
+
+def toy_inputs(t: ToyNet, seed: int) -> torch.Tensor:
+    """Token embeddings fp32 [B][tokens][d], N(0, 1)."""
+    g = _gen(seed, _name_id(t.name), 99)
+    return torch.randn(t.batch, t.tokens, t.d_model, generator=g)
