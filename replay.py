@@ -19,7 +19,7 @@ decode_window_attention over its last n_win tokens.  Reports the bounded
 replay's relative error ||y - y_ref|| / ||y_ref||, the tokens each replay
 processes (the compute saved) and their GPU time.
 
-    python replay.py [--net toy_swa_l4_w32] [--format fp8|fp4]
+    python replay.py [--net toy_swa_l4_w32] [--format fp8|fp4] [--curve]
 Prints a table on stderr and one JSON line on stdout.
 """
 import argparse
@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--net", default="toy_swa_l4_w32", choices=sorted(wl.TOY_NETS))
     ap.add_argument("--format", default="fp8", choices=("fp8", "fp4"))
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--curve", action="store_true",
+                    help="also the error after replaying window, 2*window, ... tokens (quality vs compute)")
     args = ap.parse_args()
     if not torch.cuda.is_available():
         sys.exit("replay.py needs a GPU")
@@ -136,6 +138,16 @@ def main():
         "compute_saved": round(r_exact / r_bounded, 3),
         "wall_s": round(time.perf_counter() - t0, 2),
     }
+    if args.curve:
+        gpu = ToySwaGpu(net, wl.toy_weights(net, args.seed), args.format)
+        x = wl.toy_inputs(net, args.seed).to("cuda")
+        points = []
+        for r in list(range(net.window, r_exact, net.window)) + [r_exact]:
+            y = gpu.run(x, net.tokens - r, net.tokens)[:, -1]
+            points.append({"tokens": r, "mean_rel_error": float(relative_errors(y, ref).mean())})
+        result["curve"] = points
+        for pt in points:
+            print(f"  replay {pt['tokens']:5d} tokens: error {pt['mean_rel_error']:.3e}", file=sys.stderr)
     print(f"# {args.net} ({net.layers} layers, window {net.window}, {args.format} K/V), batch {net.batch}",
           file=sys.stderr)
     print(f"  exact replay   {r_exact:5d} tokens  {ms[1]:8.2f} ms  error {float(e_exact.max()):.3e}"
