@@ -143,6 +143,44 @@ def prefill_append(fk, wl, seed, dev, stream, reps=10):
             "algorithmic_bytes": bytes_}
 
 
+def query_extras(fk, gc, w, dev, stream, splits_req, reps=20, window=4096):
+    """On the workload's cache: causal attention of S = 16 / G query tokens
+    per sequence in one pass (speculative verification), and sliding-window
+    attention over the last `window` tokens.  Rates over the bytes each call
+    must move (cache pages read, queries, outputs)."""
+    import torch
+    L, B, Hq, D = gc.layout, w.batch, w.q_heads, w.head_dim
+    S = max(1, 16 // w.group)
+    g = torch.Generator(device=dev).manual_seed(7)
+    q = torch.randn(B, S, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+    lens = [int(x) for x in gc.lens_cpu]
+    out = {}
+    for name, win in (("multi_query", 0), ("window", window)):
+        plan = fk.decode_window_plan(L, B, S if name == "multi_query" else 1, Hq, gc.page_table.shape[1], win,
+                                     splits_req if win == 0 else 0)
+        ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        qq = q if name == "multi_query" else q[:, :1].contiguous()
+        S_ = qq.shape[1]
+        res = torch.empty(B, S_, Hq, D, dtype=torch.float32, device=dev)
+        call = lambda: fk.decode_window_attention(L, gc.cache, qq, gc.seq_lens, gc.page_table, win,
+                                                  num_splits=splits_req if win == 0 else 0, workspace=ws, out=res)
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tokens = [min(n, win + S_ - 1) if win else n for n in lens]
+        bytes_ = sum(tokens) * L.bytes_per_token + B * S_ * Hq * D * (2 + 4) + sum(-(-t // 64) for t in tokens) * 4
+        out[name] = {"q_tokens": S_, "window": win, "ms": round(ms, 5), "gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
+                     "query_tokens_per_s": round(B * S_ / (ms * 1e-3), 1), "algorithmic_bytes": int(bytes_)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +199,8 @@ def main():
                     help="skip the streaming-read probe (the achievable HBM read rate for this access pattern)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill quantise-append measurement (8 x 8192 tokens)")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time several query tokens in one pass and sliding-window attention on the cache")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with one 1 GiB device copy, the known-size kernel for scaling HBM counters")
     args = ap.parse_args()
@@ -349,6 +389,8 @@ def main():
     }
     if not args.no_prefill:
         result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)
+    if args.extras and not paged:
+        result["extras"] = query_extras(fk, gc, w, dev, stream, splits_req)
     if not args.no_read_probe:
         # the achievable read rate: the cache's size in 9216-byte blocks,
         # streamed once by the library's read probe
