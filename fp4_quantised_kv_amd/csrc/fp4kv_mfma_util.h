@@ -302,8 +302,12 @@ __device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, in
 
 // The step's own token (decode with append): the one wave whose chunk holds
 // position len - 1 quantises the sequence's new K and V rows for its KV head
-// and stores them before it copies any page, then waits for the stores, so
-// its own copy of that page reads them.  Only this wave touches that
+// and stores them before it copies any page.  Its copy of that page must be
+// issued after the stores have completed: when the page is the chunk's first
+// one, the wave waits for them here; otherwise the page loop's first wait
+// (which leaves only the first page's copies outstanding, and vector memory
+// operations complete in issue order) already covers them, and the stores'
+// latency overlaps the first pages' copies.  Only this wave touches that
 // (page, KV head) block in the kernel.
 template <int D, bool FP8>
 __device__ __forceinline__ void append_if_last_chunk(const DecodeArgs &a, const Chunk &c, int lane)
@@ -318,7 +322,8 @@ __device__ __forceinline__ void append_if_last_chunk(const DecodeArgs &a, const 
     uint8_t *base = a.cache_w + static_cast<int64_t>(id) * g.page_stride + c.h * g.head_stride;
     const int64_t row = (static_cast<int64_t>(c.b) * g.num_kv_heads + c.h) * D;
     quant::append_token_in_wave<D, FP8>(g, a.k_new + row, a.v_new + row, base, last % kPage, lane);
-    wait_vmem_at_most<0>();
+    if (last / kPage == c.p0)
+        wait_vmem_at_most<0>();
 }
 
 }  // namespace mfma

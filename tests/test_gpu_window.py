@@ -86,3 +86,33 @@ def test_window_zero_is_unwindowed():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
+
+
+def test_full_size_batch_multi_query_and_window():
+    """The 32-sequence, 32768-token cache at its bench launch configuration:
+    two query tokens per sequence in one pass (16 columns per KV head), and a
+    4096-token window; sampled sequences against the oracle."""
+    from test_gpu_decode import _oracle_decode
+    w = wl.WORKLOADS["gqa8_b32_ctx32k"]
+    seqs = [0, 31]
+    gc = hx.build_cache(w, seed=1, keep_seqs=seqs)
+    S = 2
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn(w.batch, S, w.q_heads, w.head_dim, generator=g).to(torch.bfloat16)
+    lens = gc.lens_cpu.tolist()
+    scale = w.head_dim ** -0.5
+    for window, splits in ((0, w.splits), (4096, 0)):
+        _say(f"window attention: {w.name}, S {S}, window {window}, splits {splits}, oracle on {seqs}")
+        out = fk.decode_window_attention(gc.layout, gc.cache, q.cuda(), gc.seq_lens, gc.page_table, window,
+                                         num_splits=splits)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        for i in range(S):
+            li = [n - (S - 1 - i) for n in lens]
+            lo = [max(0, n - window) if window else 0 for n in li]
+            kept = {b: (gc.kept[b][0][lo[b]:li[b]], gc.kept[b][1][lo[b]:li[b]]) for b in seqs}
+            ref = _oracle_decode(q[:, i].contiguous(), kept, [li[b] - lo[b] for b in range(w.batch)], w.head_dim,
+                                 scale)
+            err = max(float(hx.row_rel_error(out[b, i], ref[b]).max()) for b in seqs)
+            _say(f"  query token {i}: worst per-row relative error {err:.3e}")
+            assert err <= TOL
