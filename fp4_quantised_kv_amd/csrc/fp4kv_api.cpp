@@ -39,8 +39,6 @@ int fill_layout(const fp4kv_cache_params &p, fp4kv_cache_layout_t *out)
         return FP4KV_ERR_UNSUPPORTED;
     if (p.head_dim != 64 && p.head_dim != 128)
         return FP4KV_ERR_UNSUPPORTED;
-    if (fp8 && p.head_dim != 128)
-        return FP4KV_ERR_UNSUPPORTED;
     if (p.page_size != kPage)
         return FP4KV_ERR_UNSUPPORTED;
     const int64_t D = p.head_dim;

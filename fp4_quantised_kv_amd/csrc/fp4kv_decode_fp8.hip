@@ -110,8 +110,9 @@ __device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, in
 // 8 tokens then channel c+1's (c = 32u + 2col); codes of tokens at or past
 // `valid` are zeroed so that never-written slots (possibly NaN codes) add
 // exact zeros.
+template <int D = kD>
 __device__ __forceinline__ void values8(uint4 w, int u, int jj, int h, int valid, const half8_t &pf,
-                                        const half8_t &pl, SplitState<kD> &st)
+                                        const half8_t &pl, SplitState<D> &st)
 {
     if (valid < kPage) {
         const int t0 = 16 * jj + 8 * h;
@@ -244,10 +245,95 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
     merge_waves_and_store<kD>(area, a, c.b, c.h, c.part);
 }
 
+// Head dim 64: operands loaded straight into registers (no LDS staging).
+// Score tile t of half page h (t = 2h + i): the lane's token row is
+// tile_token(t, col), and its 16 channels 16jj .. 16jj+15 -- the A operands
+// of the two MFMAs, in the query operand's channel order -- are one 16-byte
+// load.  Values: the lane's two channels 32u + 2col, +1 of the half page's
+// tokens 16jj + 8h .. +7 are one 16-byte row pair, as in the staged kernel.
+template <bool APPEND>
+__global__ __launch_bounds__(kGroupThreads) void decode_split_fp8_d64(DecodeArgs a)
+{
+    constexpr int D = 64;
+    __shared__ __attribute__((aligned(16))) uint8_t areas[kWavesPerGroup][merge_area_bytes<D>()];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15;
+    const int jj = lane >> 4;
+    const CacheGeom &g = a.geom;
+
+    const Chunk c = chunk_of(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
+    uint32_t qbits[D / 8];
+    load_q_bits<D>(a, c.b, c.h, col, jj, qbits);
+    half8_t qf[D / 32];
+    float zscale;
+    make_q_operand<D>(qbits, a.scale_log2e, qf, zscale);
+    if constexpr (APPEND) {
+        append_if_last_chunk<D, true>(a, c, lane);
+        wait_vmem_at_most<0>();                         // the page loads below are issued without a wait
+    }
+    const int shortfall = column_shortfall(a, col);
+    const int first = column_first_token(a, c.len, shortfall);
+
+    SplitState<D> st;
+    init_state(st);
+    for (int pg = c.p0; pg < c.p1; ++pg) {
+        const int id = c.ptab[pg];
+        if (id < 0 || id >= g.num_pages)                // skipped, like the other kernels
+            continue;
+        const uint8_t *blk = a.cache + static_cast<int64_t>(id) * g.page_stride + c.h * g.head_stride;
+        const int valid = min(kPage, c.len - pg * kPage);
+        const int lo = first - pg * kPage, hi = min(kPage, c.len - pg * kPage - shortfall);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            uint4 kx[2], vx[D / 32];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                kx[i] = *reinterpret_cast<const uint4 *>(blk + g.k_codes_off + tile_token(2 * hf + i, col) * D +
+                                                          16 * jj);
+#pragma unroll
+            for (int u = 0; u < D / 32; ++u)
+                vx[u] = *reinterpret_cast<const uint4 *>(blk + g.v_codes_off +
+                                                          ((jj * 2 + hf) * D + 32 * u + 2 * col) * 8);
+            float z[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8(kx[i].x, kx[i].y), qf[0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8(kx[i].z, kx[i].w), qf[1], acc, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = 16 * jj + 8 * hf + 4 * i + e;
+                    z[i][e] = (tok < hi && tok >= lo) ? acc[e] : -INFINITY;
+                }
+            }
+            half8_t pf[1], pl[1];
+            softmax_tiles<D, 2>(z, st, zscale, pf, pl);
+#pragma unroll
+            for (int u = 0; u < D / 32; ++u)
+                values8<D>(vx[u], u, jj, hf, valid, pf[0], pl[0], st);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+        st.acc[t] *= g.v_scale;
+    auto area = [&](int w) { return MergeArea<D>(areas[w]); };
+    state_to_area<D>(area(wave), st, col, jj, query_columns(a));
+    merge_waves_and_store<D>(area, a, c.b, c.h, c.part);
+}
+
 }  // namespace
 
 hipError_t launch_split_fp8(const DecodeArgs &a, hipStream_t stream)
 {
+    if (a.geom.head_dim == 64) {
+        const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
+        if (a.k_new)
+            decode_split_fp8_d64<true><<<grid, kGroupThreads, 0, stream>>>(a);
+        else
+            decode_split_fp8_d64<false><<<grid, kGroupThreads, 0, stream>>>(a);
+        return hipGetLastError();
+    }
     const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
     if (a.k_new)
         decode_split_fp8<true><<<grid, kGroupThreads, 0, stream>>>(a);

@@ -600,7 +600,10 @@ hipError_t launch_quantize_append(const CacheGeom &g, const uint16_t *k, const u
     const int64_t per_token = static_cast<int64_t>(g.num_kv_heads) * (g.head_dim / 16);
     if (g.fp8) {
         const int64_t blocks = (n_tokens * per_token + 255) / 256;
-        append_fp8_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+        if (g.head_dim == 64)
+            append_fp8_kernel<64><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
+        else
+            append_fp8_kernel<128><<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(g, k, v, n_tokens, slots, cache);
     } else if (n_tokens >= kRunKernelMinTokens) {
         const int64_t blocks = ((n_tokens + 15) / 16 * per_token + 255) / 256;
         if (g.head_dim == 64)
@@ -626,7 +629,9 @@ hipError_t launch_append_last(const DecodeArgs &a, hipStream_t stream)
 {
     const int64_t threads = static_cast<int64_t>(a.batch) * a.geom.num_kv_heads * (a.geom.head_dim / 16);
     const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-    if (a.geom.fp8)
+    if (a.geom.fp8 && a.geom.head_dim == 64)
+        append_last_kernel<64, true><<<grid, 256, 0, stream>>>(a);
+    else if (a.geom.fp8)
         append_last_kernel<128, true><<<grid, 256, 0, stream>>>(a);
     else if (a.geom.head_dim == 64)
         append_last_kernel<64, false><<<grid, 256, 0, stream>>>(a);

@@ -83,7 +83,7 @@ enum fp4kv_format {
  * cache per layer, e.g. one buffer per layer or offsets into one buffer.) */
 typedef struct fp4kv_cache_params {
     int32_t num_kv_heads;                 /* H_kv >= 1 */
-    int32_t head_dim;                     /* D: 64 or 128 (FP8: 128) */
+    int32_t head_dim;                     /* D: 64 or 128 */
     int32_t page_size;                    /* tokens per page: FP4KV_PAGE_SIZE */
     int32_t format;                       /* enum fp4kv_format */
     int64_t num_pages;                    /* pages in the pool, >= 1 */
@@ -136,7 +136,7 @@ typedef struct fp4kv_cache_layout_t {
  * Errors: INVALID_ARGUMENT for a null pointer, H_kv < 1, num_pages < 1, an
  * unknown format, FP4 scales not 0 or FP8 scales not finite and positive,
  * or a cache size that overflows int64; UNSUPPORTED for head_dim not in
- * {64, 128} (FP8: not 128), page_size != 64 or FP8 scales outside
+ * {64, 128}, page_size != 64 or FP8 scales outside
  * 2^-64 .. 2^64. */
 FP4KV_API int fp4kv_cache_layout(const fp4kv_cache_params *params, fp4kv_cache_layout_t *out);
 

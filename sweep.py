@@ -90,8 +90,8 @@ class Prepared:
 
 
 def supported(kind, head_dim):
-    """The FP8 cache is built for head_dim 128 only."""
-    return kind != "fp8" or head_dim == 128
+    """Every format is built for head dims 64 and 128."""
+    return head_dim in (64, 128)
 
 
 def row_errors(out, ref):

@@ -62,7 +62,7 @@ def test_layout_sizes(H, D, pages):
     (8, 128, 64, 1, 1, 1.0, float("nan"), fk.ERR_INVALID_ARGUMENT),
     (8, 128, 64, 1, 1, 2.0 ** -70, 1.0, fk.ERR_UNSUPPORTED),        # outside 2^-64 .. 2^64
     (8, 128, 64, 1, 1, 1.0, 2.0 ** 70, fk.ERR_UNSUPPORTED),
-    (8, 64, 64, 1, 1, 1.0, 1.0, fk.ERR_UNSUPPORTED)])               # FP8 is D = 128 only
+    (8, 96, 64, 1, 1, 1.0, 1.0, fk.ERR_UNSUPPORTED)])               # FP8: D 64 or 128 too
 def test_layout_rejects(H, D, P, pages, fmt, ks, vs, code):
     p = fk.CacheParams(H, D, P, fmt, pages, ks, vs)
     out = fk.CacheLayout()
@@ -72,6 +72,8 @@ def test_layout_rejects(H, D, P, pages, fmt, ks, vs, code):
 
 @pytest.mark.parametrize("H,pages", [(1, 1), (8, 512), (3, 1000)])
 def test_fp8_layout_sizes(H, pages):
+    L64 = fk.cache_layout(H, 64, pages, format=fk.FORMAT_FP8_E4M3, k_scale=0.5, v_scale=3.0)
+    assert L64.block_bytes == 64 * 64 * 2 and L64.v_codes_offset == 64 * 64
     L = fk.cache_layout(H, 128, pages, format=fk.FORMAT_FP8_E4M3, k_scale=0.5, v_scale=3.0)
     assert L.block_bytes == 64 * 128 * 2 and L.fp8
     # 8 bits per number, exactly: the oracle's cost model for FP8 with one scale per tensor

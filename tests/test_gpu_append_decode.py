@@ -68,7 +68,7 @@ def _unfused(L, cache, table, lens, kn, vn, q, splits):
                                num_splits=splits)
 
 
-CASES = [("fp4", 128, None), ("fp4", 64, None), ("fp8", 128, None), ("fp4", 128, "valu")]
+CASES = [("fp4", 128, None), ("fp4", 64, None), ("fp8", 128, None), ("fp8", 64, None), ("fp4", 128, "valu")]
 LENS = [0, 1, 2, 63, 64, 65, 128, 129, 1000, 4097]
 
 
@@ -91,7 +91,7 @@ def test_same_as_append_then_decode(fmt, D, kernel, G, splits, monkeypatch):
     assert torch.equal(out, ref)
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp8", 128), ("fp4", 64)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp8", 128), ("fp4", 64), ("fp8", 64)])
 def test_steps_against_oracle(fmt, D):
     """Five consecutive steps (positions of both parities, page crossings);
     the stored bytes and the last step's attention against the oracle."""

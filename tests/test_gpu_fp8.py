@@ -18,8 +18,8 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _layout(H, pages, ks, vs):
-    return fk.cache_layout(H, 128, pages, format=fk.FORMAT_FP8_E4M3, k_scale=ks, v_scale=vs)
+def _layout(H, pages, ks, vs, D=128):
+    return fk.cache_layout(H, D, pages, format=fk.FORMAT_FP8_E4M3, k_scale=ks, v_scale=vs)
 
 
 def _to_rows(bits, H=1, D=128):
@@ -36,21 +36,22 @@ def _append_and_read(k, v, ks, vs, slots=None):
     if slots is None:
         slots = torch.arange(n, dtype=torch.int64)
     pages = int(slots.max()) // 64 + 1 if n else 1
-    L = _layout(H, pages, ks, vs)
+    L = _layout(H, pages, ks, vs, D)
     cache = torch.zeros(L.cache_bytes, dtype=torch.uint8, device="cuda")
     fk.quantize_append(L, k.cuda(), v.cuda(), slots.cuda(), cache)
     torch.cuda.synchronize()
     return L, cache
 
 
-@pytest.mark.parametrize("ks,vs", [(1.0, 0.75), (0.0173, 3.3), (2.0 ** -20, 123.456), (1.0 / 7.0, 2.0 ** 10)])
-def test_every_bf16_value(ks, vs):
+@pytest.mark.parametrize("ks,vs,D", [(1.0, 0.75, 128), (0.0173, 3.3, 128), (2.0 ** -20, 123.456, 128),
+                                     (1.0 / 7.0, 2.0 ** 10, 128), (0.0173, 3.3, 64)])
+def test_every_bf16_value(ks, vs, D):
     """Every finite bf16 pattern as K (in order) and V (reversed), under
     general fp32 scales, power-of-two scales and scales that put quotients
     exactly on E4M3 rounding midpoints."""
     allb = np.array([b for b in range(0x10000) if (b >> 7) & 0xFF != 0xFF], np.uint16)
-    k = _to_rows(allb)
-    v = _to_rows(allb[::-1].copy())
+    k = _to_rows(allb, D=D)
+    v = _to_rows(allb[::-1].copy(), D=D)
     _say(f"fp8 quantize_append: every bf16, scales {ks}, {vs}, {k.shape[0]} tokens")
     L, cache = _append_and_read(k, v, ks, vs)
     kc, vc = hx.read_pages_fp8(cache, L, list(range(L.num_pages)), k.shape[0])
@@ -83,20 +84,21 @@ def test_scattered_slots_and_skips():
             assert (kc[s] == 0x5A).all() and (vc[s] == 0x5A).all()
 
 
-def _decode_ref(q, kept, lens, ks, vs, scale, Hkv):
+def _decode_ref(q, kept, lens, ks, vs, scale, Hkv, D=128):
     kcodes, vcodes = [], []
     for b in range(len(lens)):
         k, v = kept[b]
-        kcodes.append(oracle.quantize_fp8(wl.bf16_bits(k[: lens[b]]), ks).reshape(-1, Hkv, 128)
-                      if lens[b] else np.zeros((0, Hkv, 128), np.uint8))
-        vcodes.append(oracle.quantize_fp8(wl.bf16_bits(v[: lens[b]]), vs).reshape(-1, Hkv, 128)
-                      if lens[b] else np.zeros((0, Hkv, 128), np.uint8))
+        kcodes.append(oracle.quantize_fp8(wl.bf16_bits(k[: lens[b]]), ks).reshape(-1, Hkv, D)
+                      if lens[b] else np.zeros((0, Hkv, D), np.uint8))
+        vcodes.append(oracle.quantize_fp8(wl.bf16_bits(v[: lens[b]]), vs).reshape(-1, Hkv, D)
+                      if lens[b] else np.zeros((0, Hkv, D), np.uint8))
     return oracle.decode_attention_fp8(wl.bf16_bits(q), kcodes, vcodes, ks, vs, lens, scale)
 
 
 @pytest.mark.parametrize("G", [1, 3, 8, 16])
 @pytest.mark.parametrize("splits", [0, 1, 5])
-def test_decode_ragged_lengths(G, splits):
+@pytest.mark.parametrize("D", [128, 64])
+def test_decode_ragged_lengths(G, splits, D):
     """Lengths 0, 1, 31, 32, 33, 63, 64, 65, 1000 (empty rows, both halves of
     a page ragged), random page order, garbage in never-written slots."""
     lens = [0, 1, 31, 32, 33, 63, 64, 65, 1000]
@@ -104,22 +106,22 @@ def test_decode_ragged_lengths(G, splits):
     g = torch.Generator().manual_seed(40 + G)
     maxp = max(-(-l // 64) for l in lens)
     table = torch.randperm(len(lens) * maxp, generator=g).to(torch.int32).reshape(len(lens), maxp)
-    L = _layout(Hkv, len(lens) * maxp, 0.04, 0.015)
+    L = _layout(Hkv, len(lens) * maxp, 0.04, 0.015, D)
     cache = torch.full((L.cache_bytes,), 0x7F, dtype=torch.uint8, device="cuda")   # NaN codes
     kept = {}
     for b, n in enumerate(lens):
-        k = (torch.randn(n, Hkv, 128, generator=g) * 3.0).to(torch.bfloat16)
-        v = torch.randn(n, Hkv, 128, generator=g).to(torch.bfloat16)
+        k = (torch.randn(n, Hkv, D, generator=g) * 3.0).to(torch.bfloat16)
+        v = torch.randn(n, Hkv, D, generator=g).to(torch.bfloat16)
         kept[b] = (k, v)
         if n:
             fk.quantize_append(L, k.cuda(), v.cuda(), wl.slots_for(table, b, 0, n).cuda(), cache)
-    q = torch.randn(len(lens), G * Hkv, 128, generator=g).to(torch.bfloat16)
-    _say(f"fp8 decode: ragged lens {lens}, G={G}, splits={splits}")
+    q = torch.randn(len(lens), G * Hkv, D, generator=g).to(torch.bfloat16)
+    _say(f"fp8 decode: ragged lens {lens}, G={G}, splits={splits}, D={D}")
     out = fk.decode_attention(L, cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(),
                               table.cuda(), num_splits=splits)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
-    ref = _decode_ref(q, kept, lens, L.params.k_scale, L.params.v_scale, 128 ** -0.5, Hkv)
+    ref = _decode_ref(q, kept, lens, L.params.k_scale, L.params.v_scale, D ** -0.5, Hkv, D)
     assert np.array_equal(out[0], np.zeros_like(out[0]))
     err = hx.row_rel_error(out[1:], ref[1:])
     _say(f"  worst per-row relative error {float(err.max()):.3e}")

@@ -66,7 +66,7 @@ def _reference(L, kv, lens, q, fmt, D, Hkv):
     return ref
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64)])
 @pytest.mark.parametrize("S,G", [(2, 8), (4, 4), (16, 1), (3, 5)])
 @pytest.mark.parametrize("splits", [0, 1, 5])
 def test_against_oracle(fmt, D, S, G, splits):
@@ -90,7 +90,7 @@ def test_against_oracle(fmt, D, S, G, splits):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64)])
 def test_one_query_token_is_decode_attention(fmt, D):
     lens = [5, 64, 700]
     L, cache, table, kv, g = _cache(lens, 2, D, fmt, seed=3)

@@ -57,7 +57,7 @@ def _reference(codes, lens, q, window, fmt, L, D, Hkv):
     return ref
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64)])
 @pytest.mark.parametrize("window", [1, 17, 64, 100, 1000])
 @pytest.mark.parametrize("S,G,splits", [(1, 8, 0), (4, 4, 1), (2, 2, 3)])
 def test_window_against_oracle(fmt, D, window, S, G, splits):
