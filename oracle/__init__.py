@@ -1,5 +1,7 @@
 """CPU oracle for the FP4 (E2M1 elements, E4M3 scale per 16 channels) KV cache,
-and for its FP8 E4M3 variant with one scale per tensor.
+for its FP8 E4M3 variant with one scale per tensor, and for the formats of
+the bit-width sweep (integers and FP8 E4M3 with an fp16 scale per token or per
+channel, the unquantised bf16 cache).
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline leg use it; the product library never imports, loads or calls it,
@@ -88,6 +90,10 @@ def lib():
         L.fp4kv_oracle_quantize_int.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                                 ctypes.c_void_p, ctypes.c_void_p]
+        L.fp4kv_oracle_quantize_fp8_groups.restype = ctypes.c_int
+        L.fp4kv_oracle_quantize_fp8_groups.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                                       ctypes.c_void_p]
         L.fp4kv_oracle_attention_values.restype = ctypes.c_int
         L.fp4kv_oracle_attention_values.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -399,6 +405,50 @@ def dequantize_int(codes, scales, granularity: str) -> np.ndarray:
         return c * s[..., None]
     if granularity == "channel":
         return c * s[None]
+    raise ValueError("granularity is 'token' or 'channel'")
+
+
+def _group_args(shape, granularity):
+    T, H, D = shape
+    if granularity == "token":
+        return np.zeros((T, H), np.uint16), (T * H, D, D, 1)
+    if granularity == "channel":
+        return np.zeros((H, D), np.uint16), (H * D, T, 1, H * D)
+    raise ValueError("granularity is 'token' or 'channel'")
+
+
+def quantize_fp8_groups(x_bits, granularity: str):
+    """FP8 E4M3 codes with one fp16 scale per group: the finer FP8 scale
+    granularities ("KV Cache Quantisation", Common questions; groups as in
+    "Quantising the KV cache", Concept section).  Scale = fp16 nearest-even
+    of amax / 448 (zero -> the smallest fp16 subnormal), code = sign bit |
+    E4M3 nearest-even, saturating, of |x| / s.
+
+    x_bits: bf16 [T][H][D] of one sequence; groups as in quantize_int.
+    Returns (codes uint8 [T][H][D], scale codes uint16 (fp16 bit patterns))."""
+    x = as_bf16_bits(x_bits)
+    if x.ndim != 3:
+        raise ValueError("expected [T][H][D]")
+    codes = np.zeros(x.shape, np.uint8)
+    scales, args = _group_args(x.shape, granularity)
+    if x.shape[0] == 0:
+        return codes, scales
+    rc = lib().fp4kv_oracle_quantize_fp8_groups(_ptr(x), *args, _ptr(codes), _ptr(scales))
+    if rc:
+        raise ValueError("bad arguments or non-finite input")
+    return codes, scales
+
+
+def dequantize_fp8_groups(codes, scales, granularity: str) -> np.ndarray:
+    """+-E4M3(code) * fp16(scale) in float64 (exact: 4 + 11 significant bits)."""
+    c = np.asarray(codes, np.uint8)
+    mag = e4m3_table()[np.minimum(c & 0x7F, 126)]
+    val = np.where(c & 0x80, -mag, mag)
+    s = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)
+    if granularity == "token":
+        return val * s[..., None]
+    if granularity == "channel":
+        return val * s[None]
     raise ValueError("granularity is 'token' or 'channel'")
 
 

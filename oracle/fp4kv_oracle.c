@@ -613,6 +613,53 @@ int fp4kv_oracle_quantize_int(const uint16_t *x, int64_t n_groups, int64_t group
     return 0;
 }
 
+/* FP8 E4M3 codes with one fp16 scale per group: the finer FP8 scale
+ * granularities ("KV Cache Quantisation", Common questions: sweep FP8 scale
+ * granularities when checking quality), over the two groupings of "Quantising
+ * the KV cache", Concept section (one token's channels, or one channel across
+ * the tokens).  The pages give no encoder for them; the reading follows the
+ * page's FP4 encoder with E4M3 elements and the integer rows' fp16 scale:
+ *   scale code = fp16 nearest-even, saturating, of amax / 448 (448 the
+ *   largest finite E4M3 magnitude, as the FP4 encoder divides by E2M1's
+ *   largest, 6); a scale that rounds to zero becomes the smallest fp16
+ *   subnormal;
+ *   code = sign bit | E4M3 nearest-even, saturating, of |x| / s (the sign is
+ *   kept for magnitudes that round to zero, as in the per-tensor encoder);
+ *   the stored value is +-E4M3(code) * s.
+ * Groups and strides as in fp4kv_oracle_quantize_int.  Every product below is
+ * exact in double: amax / 448 is decided on fp16 values (11 bits) times 448
+ * (3 bits), |x| / s on E4M3 values (4 bits) times an fp16 s.  Returns -1 on
+ * bad arguments or a non-finite input. */
+int fp4kv_oracle_quantize_fp8_groups(const uint16_t *x, int64_t n_groups, int64_t group_len,
+                                     int64_t group_stride, int64_t elem_stride,
+                                     uint8_t *codes, uint16_t *scale_codes)
+{
+    if (n_groups < 0 || group_len < 1)
+        return -1;
+    const double top = fp4kv_oracle_e4m3_value(E4M3_MAX_CODE);
+    for (int64_t i = 0; i < n_groups; i++) {
+        const int64_t base = i * group_stride;
+        double amax = 0.0;
+        for (int64_t j = 0; j < group_len; j++) {
+            double v = bf16_value(x[base + j * elem_stride]);
+            if (!isfinite(v))
+                return -1;
+            if (fabs(v) > amax)
+                amax = fabs(v);
+        }
+        int sc = fp16_ratio_rne_sat(amax, top);
+        if (sc == 0)
+            sc = 1;
+        scale_codes[i] = (uint16_t)sc;
+        const double s = fp4kv_oracle_fp16_value(sc);
+        for (int64_t j = 0; j < group_len; j++) {
+            double v = bf16_value(x[base + j * elem_stride]);
+            codes[base + j * elem_stride] = (uint8_t)(((signbit(v) ? 1 : 0) << 7) | e4m3_ratio_rne_sat(fabs(v), s));
+        }
+    }
+    return 0;
+}
+
 /* Attention of G bf16 query rows over T tokens whose K and V are given as
  * exact values (fp64, token t's D values at k + t*stride): the same fp64
  * definition as above, for any format once it is dequantised, and for the
