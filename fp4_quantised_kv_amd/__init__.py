@@ -20,7 +20,7 @@ __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", 
            "decode_append_attention", "decode_append_split", "decode_multi_attention",
            "decode_window_plan", "decode_window_attention",
            "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3",
-           "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "int_sizes", "int_quantize", "int_decode_plan",
+           "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "INT_FP8_E4M3", "int_sizes", "int_quantize", "int_decode_plan",
            "int_decode_attention"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +29,7 @@ PAGE_SIZE = 64
 MAX_GROUP = 16
 INT_PER_TOKEN = 0
 INT_PER_CHANNEL = 1
+INT_FP8_E4M3 = 0x108          # the `bits` value of FP8 E4M3 codes with fp16 scales
 
 OK = 0
 ERR_INVALID_ARGUMENT = -1
@@ -469,9 +470,13 @@ def _gran(g):
     return {"token": INT_PER_TOKEN, "channel": INT_PER_CHANNEL}.get(g, g)
 
 
+def _element_bits(bits: int) -> int:
+    return 8 if bits == INT_FP8_E4M3 else int(bits)
+
+
 def int_sizes(batch: int, tokens: int, num_kv_heads: int, head_dim: int, bits: int, granularity="token"):
-    """(code bytes, scale bytes) of one tensor in an integer format (bits 2, 4,
-    8, or 16 for the unquantised bf16 copy)."""
+    """(code bytes, scale bytes) of one tensor in a sweep format (bits 2, 4, 8,
+    INT_FP8_E4M3, or 16 for the unquantised bf16 copy)."""
     d = IntDims(batch, tokens, num_kv_heads, head_dim)
     c, s = ctypes.c_int64(), ctypes.c_int64()
     _check("fp4kv_int_sizes", library().fp4kv_int_sizes(ctypes.byref(d), int(bits), _gran(granularity),
@@ -480,10 +485,11 @@ def int_sizes(batch: int, tokens: int, num_kv_heads: int, head_dim: int, bits: i
 
 
 def int_quantize(x, bits: int, granularity="token", stream=None):
-    """Quantise x (bf16 [B][T][H][D]) to symmetric bits-bit codes with fp16
-    scales per token or per channel.  Returns (codes uint8 [B][H][T][D*bits/8],
-    scales int16 fp16 bit patterns: [B][H][T] per token, [B][H][D] per
-    channel, empty for bits 16)."""
+    """Quantise x (bf16 [B][T][H][D]) to symmetric bits-bit integer codes, or
+    to E4M3 codes for bits = INT_FP8_E4M3, with fp16 scales per token or per
+    channel.  Returns (codes uint8 [B][H][T][D * element bits / 8], scales
+    int16 fp16 bit patterns: [B][H][T] per token, [B][H][D] per channel,
+    empty for bits 16)."""
     import torch
     _need(x, "x", torch.bfloat16)
     if x.dim() != 4:
@@ -496,7 +502,7 @@ def int_quantize(x, bits: int, granularity="token", stream=None):
     _check("fp4kv_int_quantize", library().fp4kv_int_quantize(
         ctypes.byref(d), int(bits), _gran(granularity), x.data_ptr(), codes.data_ptr(),
         scales.data_ptr(), _stream(stream)))
-    codes = codes[:nc].view(B, H, T, D * bits // 8)
+    codes = codes[:nc].view(B, H, T, D * _element_bits(bits) // 8)
     if bits == 16:
         scales = scales[:0]
     elif _gran(granularity) == INT_PER_TOKEN:
@@ -518,8 +524,8 @@ def int_decode_plan(batch: int, tokens: int, num_kv_heads: int, head_dim: int, n
 
 def int_decode_attention(q, bits: int, k, v, tokens: int, k_granularity="token", v_granularity="token",
                          softmax_scale=None, num_splits: int = 0, workspace=None, out=None, stream=None):
-    """Decode attention of q (bf16 [B][Hq][D]) over K and V in an integer
-    format: k and v are the (codes, scales) pairs int_quantize returns for
+    """Decode attention of q (bf16 [B][Hq][D]) over K and V in a sweep format
+    (integer, FP8 with fp16 scales, or bf16): k and v are the (codes, scales) pairs int_quantize returns for
     [B][tokens][H][D] tensors.  Returns fp32 [B][Hq][D]."""
     import torch
     _need(q, "q", torch.bfloat16)

@@ -1,10 +1,13 @@
-// Integer KV formats of the bit-width sweep: quantisers (per token, per
-// channel) and a vector-ALU decode attention over their codes.
+// KV formats of the bit-width sweep: quantisers (per token, per channel) and
+// a vector-ALU decode attention over their codes.
 //
 // ("Quantising the KV cache", Concept section, results table: INT8, INT4 and
 // INT2 with one scale per token, or K per channel and V per token; Maths
-// section: one FP16 scale per group.)  The page gives no integer encoder; the
-// symmetric nearest-even rule used here is spelled out in fp4kv_int.h.
+// section: one FP16 scale per group.  "KV Cache Quantisation", Common
+// questions: FP8 scale granularities.)  The pages give no encoder for these;
+// the symmetric nearest-even integer rule and the FP8 E4M3 rule used here are
+// spelled out in fp4kv_int.h.  A template's FMT is the ABI's element format
+// (2, 4, 8, 16 or FP4KV_INT_FP8_E4M3); BITS is its width in the codes.
 //
 // Exact rounding.  Both roundings (amax / qmax to fp16, |x| / scale to an
 // integer) start from the correctly rounded fp32 quotient.  Every rounding
@@ -16,11 +19,19 @@
 
 #include <hip/hip_runtime.h>
 
+#include "fp4kv_int.h"
 #include "fp4kv_internal.h"
 #include "fp4kv_merge.h"
+#include "fp4kv_quant.h"
 
 namespace fp4kv {
 namespace {
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kE4M3 = FP4KV_INT_FP8_E4M3;
+constexpr int fmt_bits(int fmt) { return fmt == kE4M3 ? 8 : fmt; }
+constexpr int fmt_max(int fmt) { return fmt == kE4M3 ? 448 : (1 << (fmt - 1)) - 1; }   // divisor of amax
 
 __device__ __forceinline__ float bf16_value(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -121,13 +132,14 @@ __device__ __forceinline__ void store_codes(uint8_t *dst, const int c[16])
 // threads of a row are consecutive lanes of one wave; they exchange their
 // block maxima by lane shuffles.  BITS 16 copies the bf16 row to its
 // head-major place.
-template <int D, int BITS>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void int_quantize_token(const uint16_t *__restrict__ x,
                                                           uint8_t *__restrict__ codes,
                                                           uint16_t *__restrict__ scales,
                                                           int64_t n_rows, int64_t T, int H)
 {
     constexpr int NB = D / 16;
+    constexpr int BITS = fmt_bits(FMT);
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const bool valid = idx < n_rows * NB;
     const int blk = static_cast<int>(idx % NB);
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(256) void int_quantize_token(const uint16_t *__rest
         }
         return;
     } else {
-        constexpr int qmax = (1 << (BITS - 1)) - 1;
+        constexpr int qmax = fmt_max(FMT);
         uint32_t am = 0u;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256) void int_quantize_token(const uint16_t *__rest
         int c[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            c[i] = int_code(half16(w, i), s, qmax);
+            c[i] = FMT == kE4M3 ? static_cast<int>(quant::fp8_code(half16(w, i), s)) : int_code(half16(w, i), s, qmax);
         store_codes<BITS>(codes + orow * (D * BITS / 8) + blk * (2 * BITS), c);
         if (blk == 0)
             scales[orow] = static_cast<uint16_t>(sc);
@@ -223,14 +235,15 @@ __global__ __launch_bounds__(256) void int_channel_scales(const uint16_t *__rest
 
 // Codes with per-channel scales: one thread per (sequence, token, KV head,
 // 16-channel block), reading the block's 16 channel scales.
-template <int D, int BITS>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void int_quantize_channel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ scales,
                                                             uint8_t *__restrict__ codes,
                                                             int64_t n_rows, int64_t T, int H)
 {
     constexpr int NB = D / 16;
-    constexpr int qmax = (1 << (BITS - 1)) - 1;
+    constexpr int BITS = fmt_bits(FMT);
+    constexpr int qmax = fmt_max(FMT);
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= n_rows * NB)
         return;
@@ -244,8 +257,10 @@ __global__ __launch_bounds__(256) void int_quantize_channel(const uint16_t *__re
     load_row16(scales + (b * H + h) * D + 16 * blk, sw);
     int c[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        c[i] = int_code(half16(w, i), fp16_value(half16(sw, i)), qmax);
+    for (int i = 0; i < 16; ++i) {
+        const float s = fp16_value(half16(sw, i));
+        c[i] = FMT == kE4M3 ? static_cast<int>(quant::fp8_code(half16(w, i), s)) : int_code(half16(w, i), s, qmax);
+    }
     store_codes<BITS>(codes + ((b * H + h) * T + t) * (D * BITS / 8) + blk * (2 * BITS), c);
 }
 
@@ -273,11 +288,16 @@ constexpr int int_wave_area_bytes()
 // lowered by `off` = 2^(BITS-1).  `off` comes from opaque_offset() so that
 // the compiler keeps the subtraction in floating point: folded back into a
 // sign-extended byte it becomes a conversion that reads negative bytes as
-// large unsigned numbers.
-template <int BITS>
+// large unsigned numbers.  An E4M3 byte converts exactly in hardware (a pair
+// per instruction; scale 1).
+template <int FMT>
 __device__ __forceinline__ float field_value(uint32_t w, int n, float off)
 {
-    if constexpr (BITS == 16) {
+    constexpr int BITS = fmt_bits(FMT);
+    if constexpr (FMT == kE4M3) {
+        const float2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w >> (16 * (n >> 1)), 1.0f, false);
+        return (n & 1) ? p[1] : p[0];
+    } else if constexpr (BITS == 16) {
         return __uint_as_float(n ? (w & 0xFFFF0000u) : (w << 16));
     } else {
         constexpr uint32_t top = BITS == 8 ? 0x80808080u : BITS == 4 ? 0x88888888u : 0xAAAAAAAAu;
@@ -310,9 +330,10 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-template <int D, int BITS, int GM>
+template <int D, int FMT, int GM>
 __global__ __launch_bounds__(256) void int_decode_split(IntDecodeArgs a)
 {
+    constexpr int BITS = fmt_bits(FMT);
     using Tile = IntTile<GM>;
     constexpr int TPL = Tile::TPL;
     constexpr int ROW = D * BITS / 8;                   // bytes per token row
@@ -393,7 +414,7 @@ __global__ __launch_bounds__(256) void int_decode_split(IntDecodeArgs a)
                         const uint32_t w = k == 0 ? piece[j].x : k == 1 ? piece[j].y : k == 2 ? piece[j].z : piece[j].w;
 #pragma unroll
                         for (int n = 0; n < SUB; ++n)
-                            val[j][n] = field_value<BITS>(w, n0 + n, off);
+                            val[j][n] = field_value<FMT>(w, n0 + n, off);
                     }
 #pragma unroll
                     for (int g = 0; g < GM; ++g) {
@@ -469,7 +490,7 @@ __global__ __launch_bounds__(256) void int_decode_split(IntDecodeArgs a)
                 float v[CPL];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
-                    v[c] = field_value<BITS>(BITS == 16 ? w[u] : (w[u] >> shift), BITS == 16 ? (shift >> 4) + c : c, off);
+                    v[c] = field_value<FMT>(BITS == 16 ? w[u] : (w[u] >> shift), BITS == 16 ? (shift >> 4) + c : c, off);
                 const float *pr = pw + (i + u) * GM;
 #pragma unroll
                 for (int g = 0; g < GM; ++g) {
@@ -485,7 +506,7 @@ __global__ __launch_bounds__(256) void int_decode_split(IntDecodeArgs a)
             float v[CPL];
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                v[c] = field_value<BITS>(BITS == 16 ? w : (w >> shift), BITS == 16 ? (shift >> 4) + c : c, off);
+                v[c] = field_value<FMT>(BITS == 16 ? w : (w >> shift), BITS == 16 ? (shift >> 4) + c : c, off);
             const float *pr = pw + i * GM;
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
@@ -533,22 +554,22 @@ __global__ __launch_bounds__(256) void int_decode_split(IntDecodeArgs a)
     merge_waves_and_store<D>([&](int w) { return MergeArea<D>(areas[w]); }, ma, b, h, split);
 }
 
-template <int D, int BITS>
+template <int D, int FMT>
 hipError_t quantize_for(const IntQuantArgs &q, hipStream_t stream)
 {
     const int64_t rows = q.batch * q.tokens * q.num_kv_heads;
     const int64_t threads = rows * (D / 16);
     const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-    if (BITS == 16 || !q.per_channel) {
-        int_quantize_token<D, BITS><<<grid, 256, 0, stream>>>(q.x, q.codes, q.scales, rows, q.tokens,
-                                                              q.num_kv_heads);
+    if (FMT == 16 || !q.per_channel) {
+        int_quantize_token<D, FMT><<<grid, 256, 0, stream>>>(q.x, q.codes, q.scales, rows, q.tokens,
+                                                             q.num_kv_heads);
         return hipGetLastError();
     }
-    if constexpr (BITS != 16) {
+    if constexpr (FMT != 16) {
         const dim3 sgrid(q.num_kv_heads, static_cast<unsigned>(q.batch));
-        int_channel_scales<D><<<sgrid, 256, 0, stream>>>(q.x, q.scales, q.tokens, (1 << (BITS - 1)) - 1);
-        int_quantize_channel<D, BITS><<<grid, 256, 0, stream>>>(q.x, q.scales, q.codes, rows, q.tokens,
-                                                                q.num_kv_heads);
+        int_channel_scales<D><<<sgrid, 256, 0, stream>>>(q.x, q.scales, q.tokens, fmt_max(FMT));
+        int_quantize_channel<D, FMT><<<grid, 256, 0, stream>>>(q.x, q.scales, q.codes, rows, q.tokens,
+                                                               q.num_kv_heads);
     }
     return hipGetLastError();
 }
@@ -560,18 +581,19 @@ hipError_t quantize_d(const IntQuantArgs &q, hipStream_t stream)
     case 2: return quantize_for<D, 2>(q, stream);
     case 4: return quantize_for<D, 4>(q, stream);
     case 8: return quantize_for<D, 8>(q, stream);
+    case kE4M3: return quantize_for<D, kE4M3>(q, stream);
     default: return quantize_for<D, 16>(q, stream);
     }
 }
 
-template <int D, int BITS>
+template <int D, int FMT>
 hipError_t decode_for(const IntDecodeArgs &a, hipStream_t stream)
 {
     const dim3 grid(a.num_kv_heads, a.batch, a.splits);
     if (a.group <= 8)
-        int_decode_split<D, BITS, 8><<<grid, kGroupThreads, 0, stream>>>(a);
+        int_decode_split<D, FMT, 8><<<grid, kGroupThreads, 0, stream>>>(a);
     else
-        int_decode_split<D, BITS, 16><<<grid, kGroupThreads, 0, stream>>>(a);
+        int_decode_split<D, FMT, 16><<<grid, kGroupThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -582,6 +604,7 @@ hipError_t decode_d(const IntDecodeArgs &a, hipStream_t stream)
     case 2: return decode_for<D, 2>(a, stream);
     case 4: return decode_for<D, 4>(a, stream);
     case 8: return decode_for<D, 8>(a, stream);
+    case kE4M3: return decode_for<D, kE4M3>(a, stream);
     default: return decode_for<D, 16>(a, stream);
     }
 }

@@ -20,7 +20,12 @@ constexpr int64_t kMaxSplits = 65535;    // the split kernel's third grid dimens
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
-bool known_bits(int32_t bits) { return bits == 2 || bits == 4 || bits == 8 || bits == 16; }
+bool known_bits(int32_t bits)
+{
+    return bits == 2 || bits == 4 || bits == 8 || bits == 16 || bits == FP4KV_INT_FP8_E4M3;
+}
+// bits per stored element
+int32_t element_bits(int32_t bits) { return bits == FP4KV_INT_FP8_E4M3 ? 8 : bits; }
 bool known_granularity(int32_t g) { return g == FP4KV_INT_PER_TOKEN || g == FP4KV_INT_PER_CHANNEL; }
 
 int check_dims(const fp4kv_int_dims *d)
@@ -41,7 +46,7 @@ int sizes_of(const fp4kv_int_dims &d, int32_t bits, int32_t granularity, IntSize
     if (!known_bits(bits) || !known_granularity(granularity))
         return FP4KV_ERR_INVALID_ARGUMENT;
     const int64_t rows = static_cast<int64_t>(d.batch) * d.tokens * d.num_kv_heads;
-    const int64_t row_bytes = static_cast<int64_t>(d.head_dim) * bits / 8;
+    const int64_t row_bytes = static_cast<int64_t>(d.head_dim) * element_bits(bits) / 8;
     if (rows > std::numeric_limits<int64_t>::max() / 2 / row_bytes)
         return FP4KV_ERR_INVALID_ARGUMENT;
     out->code_bytes = rows * row_bytes;
@@ -122,7 +127,8 @@ int fp4kv_int_quantize(const fp4kv_int_dims *dims, int32_t bits, int32_t granula
         return FP4KV_ERR_INVALID_ARGUMENT;
     if (!aligned(x, 16) || !aligned(codes, 16) || (bits != 16 && !aligned(scales, 16)))
         return FP4KV_ERR_MISALIGNED;
-    const int64_t threads = s.code_bytes / (static_cast<int64_t>(dims->head_dim) * bits / 8) * (dims->head_dim / 16);
+    const int64_t threads =
+        s.code_bytes / (static_cast<int64_t>(dims->head_dim) * element_bits(bits) / 8) * (dims->head_dim / 16);
     if ((threads + 255) / 256 > std::numeric_limits<int32_t>::max())
         return FP4KV_ERR_UNSUPPORTED;
     if (bits != 16 && granularity == FP4KV_INT_PER_CHANNEL && dims->batch > 65535)

@@ -5,13 +5,15 @@ The formats are the rows of the results table in "Quantising the KV cache"
 (numerics-explained, Concept section): bf16 (the unquantised cache), FP8
 E4M3 with one scale per tensor, INT8 per token, FP4 E2M1 with an E4M3 scale
 per 16, INT4 and INT2 per token, and INT4 / INT2 with K per channel and V per
-token.  The sweep itself is the lab of "Week 6 -- FP4 KV Caches and Bounded
+token; plus FP8 E4M3 with an fp16 scale per token, or K per channel and V per
+token (the finer FP8 scale granularities of "KV Cache Quantisation", Common
+questions).  The sweep itself is the lab of "Week 6 -- FP4 KV Caches and Bounded
 Replay" (quantise synthetic KV at several bit widths and measure the
 attention output's error).
 
 Every step runs in the library's kernels: quantise-append and decode for FP4
-and FP8, int_quantize and int_decode_attention for bf16 and the integer
-formats.  For each format:
+and per-tensor FP8, int_quantize and int_decode_attention for bf16, the
+integer formats and FP8 with per-token / per-channel scales.  For each format:
     row error = max_d |o - o_ref| / max_d |o_ref|   per (sequence, query head)
 against the bf16 cache's output o_ref, and bits per number from the bytes
 the format stores.  With --time, each format's decode is also timed on a
@@ -37,6 +39,8 @@ import fp4kv_workloads as wl
 FORMATS = [
     ("BF16, unquantised", "bf16", 16, "token", "token"),
     ("FP8 E4M3, one scale per tensor", "fp8", 8, None, None),
+    ("FP8 E4M3 per token", "int", fk.INT_FP8_E4M3, "token", "token"),
+    ("FP8 E4M3, K per channel, V per token", "int", fk.INT_FP8_E4M3, "channel", "token"),
     ("INT8 per token", "int", 8, "token", "token"),
     ("FP4 E2M1, E4M3 scale per 16", "fp4", 4, None, None),
     ("INT4 per token", "int", 4, "token", "token"),

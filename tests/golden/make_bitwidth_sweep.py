@@ -28,6 +28,8 @@ import oracle  # noqa: E402
 FORMATS = [
     ("BF16, unquantised", "bf16", 16, None, None),
     ("FP8 E4M3, one scale per tensor", "fp8", 8, None, None),
+    ("FP8 E4M3 per token", "fp8g", 8, "token", "token"),
+    ("FP8 E4M3, K per channel, V per token", "fp8g", 8, "channel", "token"),
     ("INT8 per token", "int", 8, "token", "token"),
     ("FP4 E2M1, E4M3 scale per 16", "fp4", 4, None, None),
     ("INT4 per token", "int", 4, "token", "token"),
@@ -57,6 +59,9 @@ def stored_values(kind, bits, gran, x_bits, tensor_scale):
         return oracle.dequantize_fp8(oracle.quantize_fp8(x_bits, tensor_scale), tensor_scale)
     if kind == "fp4":
         return oracle.quantize(x_bits)[2]
+    if kind == "fp8g":
+        c, s = oracle.quantize_fp8_groups(x_bits, gran)
+        return oracle.dequantize_fp8_groups(c, s, gran)
     c, s = oracle.quantize_int(x_bits, bits, gran)
     return oracle.dequantize_int(c, s, gran)
 
@@ -97,7 +102,8 @@ def main():
             f.write(f"# Bit-width sweep on the seeded {name} workload (seed {seed}): {w.description}\n")
             f.write("# Written by tests/golden/make_bitwidth_sweep.py from the oracle alone (fp64 attention\n")
             f.write("#   over each format's stored values against fp64 attention over the bf16 K and V).\n")
-            f.write("# Formats: \"Quantising the KV cache\", Concept section, results table; sweep: \"Week 6 --\n")
+            f.write("# Formats: \"Quantising the KV cache\", Concept section, results table (the FP8 rows with\n")
+            f.write("#   an fp16 scale per token / channel: \"KV Cache Quantisation\", Common questions); sweep: \"Week 6 --\n")
             f.write("#   FP4 KV Caches and Bounded Replay\", Lab section.  Row error = max_d |o - o_ref| /\n")
             f.write("#   max_d |o_ref| per (sequence, query head).\n")
             f.write("# format | bits per number | mean row error | max row error\n")

@@ -184,9 +184,13 @@ def test_read_probe_host_checks():
 # ------------------------------------------------ integer formats (fp4kv_int.h)
 
 @pytest.mark.parametrize("B,T,H,D,bits,gran", [(2, 100, 3, 128, 8, "token"), (1, 7, 1, 64, 4, "channel"),
-                                               (4, 33, 8, 128, 2, "token"), (2, 5, 2, 64, 16, "channel")])
+                                               (4, 33, 8, 128, 2, "token"), (2, 5, 2, 64, 16, "channel"),
+                                               (2, 100, 3, 128, fk.INT_FP8_E4M3, "token"),
+                                               (3, 9, 2, 64, fk.INT_FP8_E4M3, "channel")])
 def test_int_sizes(B, T, H, D, bits, gran):
     nc, ns = fk.int_sizes(B, T, H, D, bits, gran)
+    if bits == fk.INT_FP8_E4M3:
+        bits = 8                                        # one E4M3 byte per number, fp16 scales as INT8
     assert nc == B * T * H * D * bits // 8
     if bits == 16:
         assert ns == 0
@@ -204,7 +208,8 @@ def test_int_sizes(B, T, H, D, bits, gran):
 @pytest.mark.parametrize("args,code", [
     ((1, 4, 1, 128, 3, 0), fk.ERR_INVALID_ARGUMENT), ((1, 4, 1, 128, 8, 2), fk.ERR_INVALID_ARGUMENT),
     ((1, 4, 0, 128, 8, 0), fk.ERR_INVALID_ARGUMENT), ((-1, 4, 1, 128, 8, 0), fk.ERR_INVALID_ARGUMENT),
-    ((1, -4, 1, 128, 8, 0), fk.ERR_INVALID_ARGUMENT), ((1, 4, 1, 96, 8, 0), fk.ERR_UNSUPPORTED)])
+    ((1, -4, 1, 128, 8, 0), fk.ERR_INVALID_ARGUMENT), ((1, 4, 1, 96, 8, 0), fk.ERR_UNSUPPORTED),
+    ((1, 4, 1, 128, 0x109, 0), fk.ERR_INVALID_ARGUMENT), ((1, 4, 1, 128, 0x108, 3), fk.ERR_INVALID_ARGUMENT)])
 def test_int_sizes_rejects(args, code):
     with pytest.raises(fk.Fp4KVError) as e:
         fk.int_sizes(*args)
