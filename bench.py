@@ -36,6 +36,9 @@ KERNEL_SOURCES = {
     "fp4": ["fp4kv_decode_mfma.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h", "fp4kv_quant.h"],
     "fp8": ["fp4kv_decode_fp8.hip", "fp4kv_mfma_util.h", "fp4kv_merge.h", "fp4kv_internal.h", "fp4kv_quant.h"],
 }
+KERNEL_SOURCES["fp8t"] = KERNEL_SOURCES["fp8"]
+FORMAT_NAMES = {"fp4": "fp4_e2m1_e4m3_per16", "fp8": "fp8_e4m3_per_tensor_scale",
+                "fp8t": "fp8_e4m3_per_token_fp16_scale"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -48,7 +51,7 @@ def kernel_source_digest(fmt: str = "fp4") -> str:
 
 
 def _counter_file(workload: str, fmt: str) -> str:
-    prefix = "decode_split" if fmt == "fp4" else "decode_split_fp8"
+    prefix = {"fp4": "decode_split", "fp8": "decode_split_fp8", "fp8t": "decode_split_fp8_token"}[fmt]
     return os.path.join(PROFILES, f"{prefix}_{workload}_hbm_counters.txt")
 
 
@@ -89,7 +92,10 @@ def cpu_baseline(w, seed, threads, fmt="fp4"):
         if b in seqs:
             k = wl.kv_tokens(w, seed, b, "k", 0, sample_lens[b])
             v = wl.kv_tokens(w, seed, b, "v", 0, sample_lens[b])
-            if fmt == "fp8":
+            if fmt == "fp8t":
+                (a, sa), (c, sc) = (oracle.quantize_fp8_groups(wl.bf16_bits(k), "token"),
+                                    oracle.quantize_fp8_groups(wl.bf16_bits(v), "token"))
+            elif fmt == "fp8":
                 a, c = oracle.quantize_fp8(wl.bf16_bits(k), k_scale), oracle.quantize_fp8(wl.bf16_bits(v), v_scale)
                 sa = sc = None
             else:
@@ -101,7 +107,15 @@ def cpu_baseline(w, seed, threads, fmt="fp4"):
         kc.append(a); ks.append(sa); vc.append(c); vs.append(sc)
     heads = [(b, h) for b in seqs for h in range(w.kv_heads)]
     t0 = time.perf_counter()
-    if fmt == "fp8":
+    if fmt == "fp8t":
+        # the stored values (E4M3 codes times each token's fp16 scale), then attention
+        deq = lambda x, s_: (oracle.dequantize_fp8_groups(x, s_, "token") if x.shape[0]
+                             else np.zeros((1, w.kv_heads, w.head_dim)))
+        kv = [deq(x, s_) for x, s_ in zip(kc, ks)]
+        vv = [deq(x, s_) for x, s_ in zip(vc, vs)]
+        oracle.decode_attention_values(wl.bf16_bits(q), kv, vv, sample_lens, w.head_dim ** -0.5,
+                                       heads=heads, n_threads=threads)
+    elif fmt == "fp8":
         oracle.decode_attention_fp8(wl.bf16_bits(q), kc, vc, k_scale, v_scale, sample_lens, w.head_dim ** -0.5,
                                     heads=heads, n_threads=threads)
     else:
@@ -109,7 +123,7 @@ def cpu_baseline(w, seed, threads, fmt="fp4"):
                                 heads=heads, n_threads=threads)
     dt = time.perf_counter() - t0
     tokens = sum(sample_lens[b] for b in seqs)
-    per_number = 1.0 if fmt == "fp8" else 9 / 16
+    per_number = {"fp4": 9 / 16, "fp8": 1.0, "fp8t": 1.0 + 2.0 / w.head_dim}[fmt]
     bytes_ = int(tokens * 2 * w.kv_heads * w.head_dim * per_number) + n_seq * w.q_heads * w.head_dim * 6
     return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_seq} of {w.batch} sequences, {tokens} tokens, all {w.kv_heads} KV heads; "
@@ -189,8 +203,9 @@ def main():
     ap.add_argument("--workload", default="gqa8_b32_ctx32k")
     ap.add_argument("--splits", type=int, default=None, help="context splits (default: the workload's)")
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--format", choices=("fp4", "fp8"), default="fp4",
-                    help="cache format: FP4 E2M1 + E4M3 per 16 (default) or FP8 E4M3 with per-tensor scales")
+    ap.add_argument("--format", choices=("fp4", "fp8", "fp8t"), default="fp4",
+                    help="cache format: FP4 E2M1 + E4M3 per 16 (default), FP8 E4M3 with per-tensor scales, "
+                         "or FP8 E4M3 with an fp16 scale per token (fp8t)")
     ap.add_argument("--unfused", action="store_true",
                     help="paged workload: append with quantize_append, then decode (default: the decode "
                          "kernel stores the new tokens itself)")
@@ -369,7 +384,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": w.kv_heads,
                    "head_dim": D, "context": w.context if not paged else f"{w.min_len}..{w.max_len}",
-                   "format": ("fp8_e4m3_per_tensor_scale" if args.format == "fp8" else "fp4_e2m1_e4m3_per16"),
+                   "format": FORMAT_NAMES[args.format],
                    "splits": splits, "partials": partials, "page_size": 64,
                    "cache_bytes": L.cache_bytes},
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
@@ -382,6 +397,7 @@ def main():
         "host_enqueue_ms_per_step": round(1e3 * host_enqueue / args.steps, 5),
         "roofline": {"bound": "hbm",
                      "kernel": ("decode_split_fp8" if args.format == "fp8" else
+                                "decode_split_fp8 (per-token scales)" if args.format == "fp8t" else
                                 "decode_split_mfma<128, staged>" if D == 128 else "decode_split_mfma<64>"),
                      "achieved": round(split_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),

@@ -19,7 +19,7 @@ __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", 
            "quantize_append", "decode_attention", "decode_split", "decode_combine",
            "decode_append_attention", "decode_append_split", "decode_multi_attention",
            "decode_window_plan", "decode_window_attention",
-           "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3",
+           "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3", "FORMAT_FP8_E4M3_TOKEN",
            "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "INT_FP8_E4M3", "int_sizes", "int_quantize", "int_decode_plan",
            "int_decode_attention"]
 
@@ -47,6 +47,7 @@ class Fp4KVError(RuntimeError):
 
 FORMAT_FP4_E2M1 = 0        # E2M1 elements, one E4M3 scale per 16 channels
 FORMAT_FP8_E4M3 = 1        # E4M3 elements, one fp32 scale per tensor
+FORMAT_FP8_E4M3_TOKEN = 2  # E4M3 elements, one fp16 scale per (token, KV head)
 
 
 class CacheParams(ctypes.Structure):
@@ -81,7 +82,11 @@ class CacheLayout(ctypes.Structure):
 
     @property
     def fp8(self):
-        return self.params.format == FORMAT_FP8_E4M3
+        return self.params.format in (FORMAT_FP8_E4M3, FORMAT_FP8_E4M3_TOKEN)
+
+    @property
+    def token_scales(self):
+        return self.params.format == FORMAT_FP8_E4M3_TOKEN
 
 
 _LIB = None
@@ -179,8 +184,9 @@ def _check(call, rc):
 
 def cache_layout(num_kv_heads: int, head_dim: int, num_pages: int, page_size: int = PAGE_SIZE,
                  format: int = FORMAT_FP4_E2M1, k_scale: float = 0.0, v_scale: float = 0.0) -> CacheLayout:
-    """Layout of a paged cache.  FP8 (format=FORMAT_FP8_E4M3) takes the K and V
-    tensors' scales; FP4 takes none (0)."""
+    """Layout of a paged cache.  FP8 with per-tensor scales
+    (format=FORMAT_FP8_E4M3) takes the K and V tensors' scales; FP4 and FP8
+    with per-token scales (FORMAT_FP8_E4M3_TOKEN) take none (0)."""
     p = CacheParams(num_kv_heads, head_dim, page_size, format, num_pages, k_scale, v_scale)
     out = CacheLayout()
     _check("fp4kv_cache_layout", library().fp4kv_cache_layout(ctypes.byref(p), ctypes.byref(out)))

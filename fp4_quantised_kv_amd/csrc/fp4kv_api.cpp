@@ -30,7 +30,8 @@ int fill_layout(const fp4kv_cache_params &p, fp4kv_cache_layout_t *out)
     if (p.num_kv_heads < 1 || p.num_pages < 1)
         return FP4KV_ERR_INVALID_ARGUMENT;
     const bool fp8 = p.format == FP4KV_FORMAT_FP8_E4M3;
-    if (p.format != FP4KV_FORMAT_FP4_E2M1 && !fp8)
+    const bool fp8_token = p.format == FP4KV_FORMAT_FP8_E4M3_TOKEN;
+    if (p.format != FP4KV_FORMAT_FP4_E2M1 && !fp8 && !fp8_token)
         return FP4KV_ERR_INVALID_ARGUMENT;
     if (fp8 ? !(std::isfinite(p.k_scale) && p.k_scale > 0.0f && std::isfinite(p.v_scale) && p.v_scale > 0.0f)
             : (p.k_scale != 0.0f || p.v_scale != 0.0f))
@@ -42,9 +43,9 @@ int fill_layout(const fp4kv_cache_params &p, fp4kv_cache_layout_t *out)
     if (p.page_size != kPage)
         return FP4KV_ERR_UNSUPPORTED;
     const int64_t D = p.head_dim;
-    const int64_t codes = fp8 ? kPage * D : kPage * D / 2;
-    const int64_t scales = fp8 ? 0 : kPage * D / 16;
-    const int64_t block = 2 * (codes + scales);               // FP4: 64 * D * 9 / 8; FP8: 128 * D
+    const int64_t codes = fp8 || fp8_token ? kPage * D : kPage * D / 2;
+    const int64_t scales = fp8 ? 0 : fp8_token ? kPage * 2 : kPage * D / 16;
+    const int64_t block = 2 * (codes + scales);   // FP4: 64 * D * 9 / 8; FP8: 128 * D; per token: 128 * D + 256
     const int64_t page_stride = block * p.num_kv_heads;
     if (p.num_pages > std::numeric_limits<int64_t>::max() / page_stride)
         return FP4KV_ERR_INVALID_ARGUMENT;
@@ -93,7 +94,8 @@ fp4kv::CacheGeom geom_of(const fp4kv_cache_layout_t &L)
     g.v_scales_off = L.v_scales_offset;
     g.head_stride = L.head_stride;
     g.page_stride = L.page_stride;
-    g.fp8 = L.params.format == FP4KV_FORMAT_FP8_E4M3;
+    g.token_scales = L.params.format == FP4KV_FORMAT_FP8_E4M3_TOKEN;
+    g.fp8 = L.params.format == FP4KV_FORMAT_FP8_E4M3 || g.token_scales;
     g.k_scale = L.params.k_scale;
     g.v_scale = L.params.v_scale;
     return g;

@@ -16,6 +16,15 @@
 //     whole FP4 page does and four workgroups still fit a CU;
 //   - V is stored in [slice][half][channel][8 tokens] rows, so a lane's two
 //     channels of a half page are 16 contiguous bytes.
+// With one fp16 scale per (token, KV head) (template argument TS) a lane's
+// 8 tokens of a half page -- its rows of the two score tiles, and its B
+// operand of the value product -- are 8 consecutive tokens, so their K and V
+// scales are 16 contiguous bytes each: the K scale multiplies the token's
+// score after the product; the V scale multiplies its probability, taken
+// relative to a running reference R (the largest V scale seen, moved up with
+// the accumulators like the softmax max) so that p * s_v / R stays in fp16's
+// range; the partials are multiplied by R at the end.  The softmax
+// denominator still sums the unscaled probabilities.
 #include <cstdint>
 
 #include <hip/hip_runtime.h>
@@ -37,6 +46,7 @@ constexpr int kCopies = 4;                // direct-to-LDS instructions per half
 // token rows (K) or one 8-token row block (V).
 struct Fp8Offsets {
     uint32_t k, v;
+    uint32_t s;          // per-token scales: lanes 0-7 the K plane, 8-15 the V plane, 16 bytes each
 };
 
 // K copies fetch whole 128-byte token rows: in copy (tile i, part p), lane l
@@ -52,13 +62,84 @@ __device__ __forceinline__ Fp8Offsets fp8_offsets(const CacheGeom &g, int lane, 
           (16u * (lane >> 5) + ((lane >> 3) & 3)) * kD + (lane & 7) * 16u;
     // V: channels 2col, 2col+1 of slice jj, 8 tokens each
     o.v = static_cast<uint32_t>(g.v_codes_off) + ((jj * 2u) * kD + 2u * col) * 8u;
+    o.s = static_cast<uint32_t>(lane < 8 ? g.k_scales_off : g.v_scales_off) + 16u * (lane & 7);
     return o;
+}
+
+// Per-token scales: the K slot grows by 128 bytes and holds, past the half
+// page's K codes, the whole page's K scales (kScaleAt) and V scales
+// (kScaleAt + 128), copied once per page with half 0.
+constexpr int kScaleAt = 4096;
+template <bool TS>
+constexpr int k_slot_bytes() { return TS ? kSlotBytes + 128 : kSlotBytes; }
+
+// Fp16 element k of 8 packed in a uint4, as a float.
+__device__ __forceinline__ float fp16_at(const uint4 &w, int k)
+{
+    const uint32_t d = k < 2 ? w.x : k < 4 ? w.y : k < 6 ? w.z : w.w;
+    const uint16_t h = static_cast<uint16_t>((k & 1) ? (d >> 16) : (d & 0xFFFFu));
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Running reference of the V scales (see the file comment).
+struct VRef {
+    float r, rcp;
+};
+
+// Weights s_v / R of the lane's 8 tokens t0 .. t0+7 (0 at or past `valid`:
+// never-written slots may hold any bytes), first moving R up to the largest
+// of the half page's scales if that exceeds it; every lane sees the same
+// maximum (the lanes of one column cover the half page's 32 tokens).
+template <int D>
+__device__ __forceinline__ void v_weights(const uint4 &vs, int t0, int valid, VRef &ref, SplitState<D> &st,
+                                          float (&wv)[8])
+{
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        wv[k] = t0 + k < valid ? fp16_at(vs, k) : 0.0f;
+        mx = fmaxf(mx, wv[k]);
+    }
+    mx = xor_max(mx);
+    if (mx > ref.r) {
+        const float a = ref.r / mx;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+            st.acc[t] *= a;
+        ref.r = mx;
+        ref.rcp = 1.0f / mx;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        wv[k] *= ref.rcp;
+}
+
+// The value product's B operand for per-token V scales: p = pf + pl (exact)
+// times the weights, split again into hi + lo fp16 parts.
+__device__ __forceinline__ void scale_probs(const half8_t &pf, const half8_t &pl, const float (&wv)[8],
+                                            half8_t &vf, half8_t &vl)
+{
+    float minus_one = -1.0f;
+    asm volatile("" : "+s"(minus_one));
+    float p[8], q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        p[e] = (static_cast<float>(pf[e]) + static_cast<float>(pl[e])) * wv[e];
+    vf = cat(pk_rtz(p[0], p[1]), pk_rtz(p[2], p[3]), pk_rtz(p[4], p[5]), pk_rtz(p[6], p[7]));
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        q[e] = __builtin_fmaf(static_cast<float>(vf[e]), minus_one, p[e]);
+    vl = cat(pk_rtz(q[0], q[1]), pk_rtz(q[2], q[3]), pk_rtz(q[4], q[5]), pk_rtz(q[6], q[7]));
 }
 
 // Half page h of K: tiles 2h, 2h+1 (tile t starts 4t token rows past tile
 // 0; part 1 is 32 token rows past part 0).  Slot layout: copy (tile i, part
-// p) at (2i + p) * 1024.
-__device__ __forceinline__ void stage_k8(const uint8_t *blk, const Fp8Offsets &o, int h, uint8_t *slot)
+// p) at (2i + p) * 1024.  With per-token scales, half 0 adds a fifth copy
+// (lanes 0-15): the page's 128-byte K and V scale planes, whole (two copies
+// of half planes would fetch each plane's lines twice under the
+// non-temporal hint).
+template <bool TS>
+__device__ __forceinline__ void stage_k8(const uint8_t *blk, const Fp8Offsets &o, int h, uint8_t *slot, int lane)
 {
     const uint8_t *k = blk + o.k + h * 8 * kD;
 #pragma unroll
@@ -66,6 +147,10 @@ __device__ __forceinline__ void stage_k8(const uint8_t *blk, const Fp8Offsets &o
 #pragma unroll
         for (int p = 0; p < 2; ++p)
             __builtin_amdgcn_global_load_lds(k + (4 * i + 32 * p) * kD, slot + (2 * i + p) * 1024, 16, 0, kStream);
+    if constexpr (TS) {
+        if (h == 0 && lane < 16)
+            __builtin_amdgcn_global_load_lds(blk + o.s, slot + kScaleAt, 16, 0, kStream);
+    }
 }
 
 // Half page h of V: pair block u (32 channels, 256 bytes of rows) at u*1024.
@@ -87,8 +172,9 @@ __device__ __forceinline__ half8_t fp8x8(uint32_t a, uint32_t b)
 // 32jj + 8m .. +7 of the lane's token, the same channel order as the query
 // operand.  Tokens outside lo .. valid-1 (the lane's query column's window
 // in this page) get -inf.
+template <bool TS>
 __device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, int h, int lo, int valid,
-                                        const half8_t (&qf)[kD / 32], float (&z)[2][4])
+                                        const half8_t (&qf)[kD / 32], const uint4 &ks, float (&z)[2][4])
 {
     const int at = (col >> 3) * 1024 + (((col & 7) << 3) + 2 * jj) * 16;
 #pragma unroll
@@ -101,8 +187,10 @@ __device__ __forceinline__ void scores8(const uint8_t *slot, int col, int jj, in
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8(b.x, b.y), qf[2], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8(b.z, b.w), qf[3], acc, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            z[i][e] = (16 * jj + 8 * h + 4 * i + e < valid && 16 * jj + 8 * h + 4 * i + e >= lo) ? acc[e] : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+            const float sc = TS ? acc[e] * fp16_at(ks, 4 * i + e) : acc[e];
+            z[i][e] = (16 * jj + 8 * h + 4 * i + e < valid && 16 * jj + 8 * h + 4 * i + e >= lo) ? sc : -INFINITY;
+        }
     }
 }
 
@@ -135,12 +223,15 @@ __device__ __forceinline__ void values8(uint4 w, int u, int jj, int h, int valid
 // `pid`) have been issued, K then V, if it is live.  Slots are
 // restrict-qualified so that the compiler's LDS-copy wait tracking knows
 // they never alias.
+template <bool TS>
 __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *__restrict__ vslot,
                                           const DecodeArgs &a, const Fp8Offsets &o, int lane, int col, int jj, int h,
                                           int p0, int p1, int len, int shortfall, int first, const int32_t *ptab,
                                           int ids, int pid,
-                                          const half8_t (&qf)[kD / 32], float zscale, SplitState<kD> &st)
+                                          const half8_t (&qf)[kD / 32], float zscale, SplitState<kD> &st,
+                                          VRef &ref)
 {
+    constexpr int kKCopies0 = TS ? kCopies + 1 : kCopies;  // copies of half 0 of K (with the scales)
     const CacheGeom &g = a.geom;
     auto live_page = [&](int id) { return id >= 0 && id < g.num_pages; };
     auto block_of = [&](int id) {
@@ -166,22 +257,38 @@ __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *
             const int nh = hf == 0 ? 1 : 0;
             half8_t pf[1], pl[1];
 
-            // K: outstanding now are this half's K then V copies
+            // K: outstanding now are this half's K (and scale) copies, then V's
             if (cur)
                 wait_vmem_at_most<kCopies>();
+            uint4 ks = {0u, 0u, 0u, 0u}, vs = {0u, 0u, 0u, 0u};
+            if constexpr (TS) {
+                // the lane's tokens 16jj + 8hf .. +7
+                ks = *reinterpret_cast<const uint4 *>(kslot + kScaleAt + 32 * jj + 16 * hf);
+                vs = *reinterpret_cast<const uint4 *>(kslot + kScaleAt + 128 + 32 * jj + 16 * hf);
+            }
             float z[2][4];
-            scores8(kslot, col, jj, hf, first - pg * kPage, min(kPage, len - pg * kPage - shortfall), qf, z);
+            scores8<TS>(kslot, col, jj, hf, first - pg * kPage, min(kPage, len - pg * kPage - shortfall), qf, ks, z);
             __builtin_amdgcn_s_waitcnt(kWaitLds);
             if (next)
-                stage_k8(nblk, o, nh, kslot);
-            if (cur)
+                stage_k8<TS>(nblk, o, nh, kslot, lane);
+            if (cur) {
                 softmax_tiles<kD, 2>(z, st, zscale, pf, pl);
+                if constexpr (TS) {
+                    float wv[8];
+                    v_weights<kD>(vs, 16 * jj + 8 * hf, valid, ref, st, wv);
+                    scale_probs(pf[0], pl[0], wv, pf[0], pl[0]);
+                }
+            }
 
             // V: outstanding now are this half's V then the next half's K
-            if (next)
-                wait_vmem_at_most<kCopies>();
-            else
+            if (next) {
+                if (hf == 1)
+                    wait_vmem_at_most<kKCopies0>();        // the next half is half 0 of the next page
+                else
+                    wait_vmem_at_most<kCopies>();
+            } else {
                 wait_vmem_at_most<0>();
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint4 w = *reinterpret_cast<const uint4 *>(vslot + u * 1024 + lane * 16);
@@ -196,14 +303,16 @@ __device__ __forceinline__ void fp8_pages(uint8_t *__restrict__ kslot, uint8_t *
     }
 }
 
-template <bool APPEND>
+template <bool APPEND, bool TS>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
 {
+    static_assert(kScaleAt + 256 <= k_slot_bytes<true>(), "a page's scales fit the K slot");
+    static_assert(kWavesPerGroup * (k_slot_bytes<TS>() + kSlotBytes) <= 40 * 1024, "four workgroups per CU");
     static_assert(merge_area_bytes<kD>() <= 2 * kSlotBytes, "merge area layout");
     static_assert(8 * kD * 4 + 128 <= kSlotBytes, "merge area must fit the slots");
     static_assert(kWavesPerGroup * 2 * kSlotBytes <= 40 * 1024, "four workgroups per CU");
 
-    __shared__ __attribute__((aligned(16))) uint8_t kslots[kWavesPerGroup][kSlotBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t kslots[kWavesPerGroup][k_slot_bytes<TS>()];
     __shared__ __attribute__((aligned(16))) uint8_t vslots[kWavesPerGroup][kSlotBytes];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,17 +338,20 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
     const int pid = c.p0 < c.p1 ? __builtin_amdgcn_readlane(ids, 0) : -1;
     if (pid >= 0 && pid < g.num_pages) {
         const uint8_t *blk = a.cache + static_cast<int64_t>(pid) * g.page_stride + c.h * g.head_stride;
-        stage_k8(blk, o, 0, kslots[wave]);
+        stage_k8<TS>(blk, o, 0, kslots[wave], lane);
         stage_v8(blk, o, 0, vslots[wave]);
     }
     const int shortfall = column_shortfall(a, col);
-    fp8_pages(kslots[wave], vslots[wave], a, o, lane, col, jj, c.h, c.p0, c.p1, c.len, shortfall,
-              column_first_token(a, c.len, shortfall), c.ptab, ids, pid, qf, zscale, st);
+    VRef ref = {0.0f, 0.0f};
+    fp8_pages<TS>(kslots[wave], vslots[wave], a, o, lane, col, jj, c.h, c.p0, c.p1, c.len, shortfall,
+                  column_first_token(a, c.len, shortfall), c.ptab, ids, pid, qf, zscale, st, ref);
 
-    // the V tensor's scale multiplies every value, so it multiplies o
+    // the V tensor's scale (or the reference the per-token ones were taken
+    // against) multiplies every value, so it multiplies o
+    const float vsc = TS ? ref.r : g.v_scale;
 #pragma unroll
     for (int t = 0; t < kD / 16; ++t)
-        st.acc[t] *= g.v_scale;
+        st.acc[t] *= vsc;
     auto area = [&](int w) { return MergeArea<kD>(kslots[w], vslots[w]); };
     state_to_area<kD>(area(wave), st, col, jj, query_columns(a));
     merge_waves_and_store<kD>(area, a, c.b, c.h, c.part);
@@ -250,8 +362,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
 // tile_token(t, col), and its 16 channels 16jj .. 16jj+15 -- the A operands
 // of the two MFMAs, in the query operand's channel order -- are one 16-byte
 // load.  Values: the lane's two channels 32u + 2col, +1 of the half page's
-// tokens 16jj + 8h .. +7 are one 16-byte row pair, as in the staged kernel.
-template <bool APPEND>
+// tokens 16jj + 8h .. +7 are one 16-byte row pair, as in the staged kernel;
+// with per-token scales, so are the 8 K and the 8 V scales of those tokens.
+template <bool APPEND, bool TS>
 __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8_d64(DecodeArgs a)
 {
     constexpr int D = 64;
@@ -277,6 +390,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8_d64(DecodeArgs
 
     SplitState<D> st;
     init_state(st);
+    VRef ref = {0.0f, 0.0f};
     for (int pg = c.p0; pg < c.p1; ++pg) {
         const int id = c.ptab[pg];
         if (id < 0 || id >= g.num_pages)                // skipped, like the other kernels
@@ -295,6 +409,11 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8_d64(DecodeArgs
             for (int u = 0; u < D / 32; ++u)
                 vx[u] = *reinterpret_cast<const uint4 *>(blk + g.v_codes_off +
                                                           ((jj * 2 + hf) * D + 32 * u + 2 * col) * 8);
+            uint4 ks = {0u, 0u, 0u, 0u}, vs = {0u, 0u, 0u, 0u};
+            if constexpr (TS) {
+                ks = *reinterpret_cast<const uint4 *>(blk + g.k_scales_off + 32 * jj + 16 * hf);
+                vs = *reinterpret_cast<const uint4 *>(blk + g.v_scales_off + 32 * jj + 16 * hf);
+            }
             float z[2][4];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -304,19 +423,26 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8_d64(DecodeArgs
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int tok = 16 * jj + 8 * hf + 4 * i + e;
-                    z[i][e] = (tok < hi && tok >= lo) ? acc[e] : -INFINITY;
+                    const float sc = TS ? acc[e] * fp16_at(ks, 4 * i + e) : acc[e];
+                    z[i][e] = (tok < hi && tok >= lo) ? sc : -INFINITY;
                 }
             }
             half8_t pf[1], pl[1];
             softmax_tiles<D, 2>(z, st, zscale, pf, pl);
+            if constexpr (TS) {
+                float wv[8];
+                v_weights<D>(vs, 16 * jj + 8 * hf, valid, ref, st, wv);
+                scale_probs(pf[0], pl[0], wv, pf[0], pl[0]);
+            }
 #pragma unroll
             for (int u = 0; u < D / 32; ++u)
                 values8<D>(vx[u], u, jj, hf, valid, pf[0], pl[0], st);
         }
     }
+    const float vsc = TS ? ref.r : g.v_scale;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-        st.acc[t] *= g.v_scale;
+        st.acc[t] *= vsc;
     auto area = [&](int w) { return MergeArea<D>(areas[w]); };
     state_to_area<D>(area(wave), st, col, jj, query_columns(a));
     merge_waves_and_store<D>(area, a, c.b, c.h, c.part);
@@ -324,21 +450,27 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8_d64(DecodeArgs
 
 }  // namespace
 
+namespace {
+
+template <bool APPEND, bool TS>
+void launch_fp8(const DecodeArgs &a, hipStream_t stream)
+{
+    const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
+    if (a.geom.head_dim == 64)
+        decode_split_fp8_d64<APPEND, TS><<<grid, kGroupThreads, 0, stream>>>(a);
+    else
+        decode_split_fp8<APPEND, TS><<<grid, kGroupThreads, 0, stream>>>(a);
+}
+
+}  // namespace
+
 hipError_t launch_split_fp8(const DecodeArgs &a, hipStream_t stream)
 {
-    if (a.geom.head_dim == 64) {
-        const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
-        if (a.k_new)
-            decode_split_fp8_d64<true><<<grid, kGroupThreads, 0, stream>>>(a);
-        else
-            decode_split_fp8_d64<false><<<grid, kGroupThreads, 0, stream>>>(a);
-        return hipGetLastError();
-    }
-    const dim3 grid(a.geom.num_kv_heads, a.batch, a.partials);
-    if (a.k_new)
-        decode_split_fp8<true><<<grid, kGroupThreads, 0, stream>>>(a);
+    const bool append = a.k_new != nullptr;
+    if (a.geom.token_scales)
+        append ? launch_fp8<true, true>(a, stream) : launch_fp8<false, true>(a, stream);
     else
-        decode_split_fp8<false><<<grid, kGroupThreads, 0, stream>>>(a);
+        append ? launch_fp8<true, false>(a, stream) : launch_fp8<false, false>(a, stream);
     return hipGetLastError();
 }
 

@@ -35,36 +35,13 @@ constexpr int fmt_max(int fmt) { return fmt == kE4M3 ? 448 : (1 << (fmt - 1)) - 
 
 __device__ __forceinline__ float bf16_value(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-__device__ __forceinline__ float fp16_value(uint32_t code)
-{
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(code)));
-}
+using quant::fp16_value;
 
-// fp16 code of amax / qmax: nearest even, saturating at 65504, and the
-// smallest subnormal (code 1) in place of zero.
+// fp16 code of amax / qmax (qmax = 127, 7, 1 or 448): nearest even,
+// saturating at 65504, and the smallest subnormal in place of zero.
 __device__ __forceinline__ uint32_t int_scale_code(float amax, int qmax)
 {
-    const float fq = static_cast<float>(qmax);
-    const float q = amax / fq;
-    uint32_t code;
-    if (!(q < 65504.0f)) {
-        code = 0x7BFFu;
-    } else {
-        code = __builtin_bit_cast(uint16_t, static_cast<_Float16>(q));
-        const float f = fp16_value(code);
-        if (f != q) {
-            const uint32_t other = q > f ? code + 1u : code - 1u;   // the neighbour on q's side
-            const float mid = 0.5f * (f + fp16_value(other));
-            if (q == mid) {
-                const float r = fmaf(mid, fq, -amax);              // sign of mid * qmax - amax
-                if (r > 0.0f)
-                    code = code < other ? code : other;
-                else if (r < 0.0f)
-                    code = code > other ? code : other;
-            }
-        }
-    }
-    return code == 0u ? 1u : code;
+    return quant::fp16_scale_code(amax, static_cast<float>(qmax));
 }
 
 // sign(x) * nearest-even integer of |x| / s, capped at qmax.

@@ -15,7 +15,8 @@ struct CacheGeom {
     int64_t num_pages;
     int64_t k_codes_off, k_scales_off, v_codes_off, v_scales_off;
     int64_t head_stride, page_stride;
-    bool fp8;                    // FP8 E4M3 elements with per-tensor scales (else FP4)
+    bool fp8;                    // FP8 E4M3 elements (else FP4)
+    bool token_scales;           // FP8 with an fp16 scale per (token, KV head) (else per tensor)
     float k_scale, v_scale;      // FP8 per-tensor scales
 };
 

@@ -219,7 +219,9 @@ __global__ __launch_bounds__(256) void append_slices_kernel(
 }
 
 // One token's block `blk` of KV head `head` at `slot` in an FP8 cache; slots
-// outside the pool are skipped.
+// outside the pool are skipped.  With per-token scales the D/16 lanes of a
+// (token, head) -- consecutive and aligned, and all skipped or all not --
+// find the row's scale together, and the first stores it.
 template <int D>
 __device__ __forceinline__ void append_token_fp8(const CacheGeom &g, const uint16_t *ksrc, const uint16_t *vsrc,
                                                  int64_t slot, int head, int blk, uint8_t *cache)
@@ -230,19 +232,33 @@ __device__ __forceinline__ void append_token_fp8(const CacheGeom &g, const uint1
     const int off = static_cast<int>(slot % kPage);
     uint32_t w[8];
     load_block16(ksrc, w);
+    float s = g.k_scale;
+    if (g.token_scales) {
+        const uint32_t sc = row_scale_code_e4m3<D / 16>(w);
+        s = fp16_value(sc);
+        if (blk == 0)
+            *reinterpret_cast<uint16_t *>(base + g.k_scales_off + 2 * off) = static_cast<uint16_t>(sc);
+    }
     uint32_t kc[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
-        kc[c >> 2] |= fp8_code(bits, g.k_scale) << (8 * (c & 3));
+        kc[c >> 2] |= fp8_code(bits, s) << (8 * (c & 3));
     }
     *reinterpret_cast<uint4 *>(base + g.k_codes_off + off * D + 16 * blk) = make_uint4(kc[0], kc[1], kc[2], kc[3]);
     load_block16(vsrc, w);
+    s = g.v_scale;
+    if (g.token_scales) {
+        const uint32_t sc = row_scale_code_e4m3<D / 16>(w);
+        s = fp16_value(sc);
+        if (blk == 0)
+            *reinterpret_cast<uint16_t *>(base + g.v_scales_off + 2 * off) = static_cast<uint16_t>(sc);
+    }
     uint8_t *vrow = base + g.v_codes_off + ((((off >> 4) * 2 + ((off >> 3) & 1)) * D + 16 * blk) * 8) + (off & 7);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
-        vrow[8 * c] = static_cast<uint8_t>(fp8_code(bits, g.v_scale));
+        vrow[8 * c] = static_cast<uint8_t>(fp8_code(bits, s));
     }
 }
 

@@ -168,12 +168,72 @@ __device__ __forceinline__ uint32_t fp8_code(uint32_t bits16, float s)
     return c | ((bits16 >> 8) & 0x80u);
 }
 
+// ---- fp16 scales (FP8 with a scale per token; the sweep's formats)
+
+__device__ __forceinline__ float fp16_value(uint32_t code)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(code)));
+}
+
+// fp16 code of amax / div (div a positive integer of at most 9 significant
+// bits: an integer format's qmax, or 448 for E4M3 elements): nearest even,
+// saturating at 65504, and the smallest subnormal (code 1) in place of zero.
+// The correctly rounded fp32 quotient lies on the same side of every fp16
+// midpoint (an fp32 number) as the exact one, or on it; then the sign of
+// mid * div - amax, exact in one FMA, decides.
+__device__ __forceinline__ uint32_t fp16_scale_code(float amax, float div)
+{
+    const float q = amax / div;
+    uint32_t code;
+    if (!(q < 65504.0f)) {
+        code = 0x7BFFu;
+    } else {
+        code = __builtin_bit_cast(uint16_t, static_cast<_Float16>(q));
+        const float f = fp16_value(code);
+        if (f != q) {
+            const uint32_t other = q > f ? code + 1u : code - 1u;   // the neighbour on q's side
+            const float mid = 0.5f * (f + fp16_value(other));
+            if (q == mid) {
+                const float r = __builtin_fmaf(mid, div, -amax);   // sign of mid * div - amax
+                if (r > 0.0f)
+                    code = code < other ? code : other;
+                else if (r < 0.0f)
+                    code = code > other ? code : other;
+            }
+        }
+    }
+    return code == 0u ? 1u : code;
+}
+
+// The fp16 scale code of one token's row of one KV head (E4M3 elements:
+// amax / 448) from its 16-channel blocks, one block per lane in NB
+// consecutive, NB-aligned lanes that all take part: the block maxima (as
+// bf16 magnitude bits, which order like the values) meet by lane shuffles.
+template <int NB>
+__device__ __forceinline__ uint32_t row_scale_code_e4m3(const uint32_t w[8])
+{
+    uint32_t am = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+        am = lo > am ? lo : am;
+        am = hi > am ? hi : am;
+    }
+#pragma unroll
+    for (int o = 1; o < NB; o <<= 1) {
+        const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), o));
+        am = other > am ? other : am;
+    }
+    return fp16_scale_code(__uint_as_float(am << 16), 448.0f);
+}
+
 // ---- the decode step's own token, appended inside the decode kernel
 
 // Quantise one token's K and V rows of one KV head (bf16, D channels each)
 // and store them at page offset `off` of the (page, KV head) block at `base`,
 // with one wave: lanes 0 .. D/16-1 take the K blocks, the next D/16 lanes the
-// V blocks.  The caller guarantees that no other thread writes this block
+// V blocks (FP8 with per-token scales: each group also finds its row's
+// scale and its first lane stores it).  The caller guarantees that no other thread writes this block
 // during the kernel, so the FP4 V nibbles (two tokens per byte) are placed
 // by a plain read-modify-write of their dwords.
 template <int D, bool FP8>
@@ -188,7 +248,15 @@ __device__ __forceinline__ void append_token_in_wave(const CacheGeom &g, const u
     uint32_t w[8];
     load_block16((is_v ? v_row : k_row) + 16 * blk, w);
     if constexpr (FP8) {
-        const float s = is_v ? g.v_scale : g.k_scale;
+        float s = is_v ? g.v_scale : g.k_scale;
+        if (g.token_scales) {
+            // the K lanes and the V lanes are two NB-lane groups
+            const uint32_t sc = row_scale_code_e4m3<NB>(w);
+            s = fp16_value(sc);
+            if (blk == 0)
+                *reinterpret_cast<uint16_t *>(base + (is_v ? g.v_scales_off : g.k_scales_off) + 2 * off) =
+                    static_cast<uint16_t>(sc);
+        }
         uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {

@@ -46,7 +46,7 @@ def build_cache(w: wl.Workload, seed: int, device="cuda", keep_seqs=(), extra_to
     `extra_tokens` more tokens per sequence.  `seqs` limits which sequences
     are filled (others stay zero); `keep_seqs` keeps their bf16 rows on the
     CPU for the oracle.  fmt "fp8" builds an FP8 E4M3 cache with the
-    workload's per-tensor scales."""
+    workload's per-tensor scales, "fp8t" one with per-token scales."""
     lens = wl.seq_lengths(w, seed)
     if w.kind == "paged":
         pt = wl.random_page_table(lens, extra_tokens, seed, w.name)
@@ -56,6 +56,8 @@ def build_cache(w: wl.Workload, seed: int, device="cuda", keep_seqs=(), extra_to
         ks, vs = wl.fp8_tensor_scales(w, seed)
         layout = fk.cache_layout(w.kv_heads, w.head_dim, pt.num_pages, format=fk.FORMAT_FP8_E4M3,
                                  k_scale=ks, v_scale=vs)
+    elif fmt == "fp8t":
+        layout = fk.cache_layout(w.kv_heads, w.head_dim, pt.num_pages, format=fk.FORMAT_FP8_E4M3_TOKEN)
     else:
         layout = fk.cache_layout(w.kv_heads, w.head_dim, pt.num_pages)
     cache = (torch.zeros if zero else torch.empty)(layout.cache_bytes, dtype=torch.uint8, device=device)
@@ -136,6 +138,21 @@ def read_pages_fp8(cache: torch.Tensor, layout: fk.CacheLayout, pages, n_tokens:
         return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(P * 64, H, D)[:n_tokens])
 
     return tok(kc), tok(vc)
+
+
+def read_token_scales(cache: torch.Tensor, layout: fk.CacheLayout, pages, n_tokens: int):
+    """fp16 scale patterns of the first n_tokens slots of a list of pages of
+    an FP8 cache with per-token scales, token-major: K [n][H], V [n][H]."""
+    H = layout.num_kv_heads
+    idx = torch.as_tensor(np.asarray(pages, np.int64), device=cache.device)
+    blocks = cache[: layout.cache_bytes].view(-1, H, layout.block_bytes)[idx].cpu().numpy()
+    P = len(pages)
+
+    def plane(off):
+        s = np.ascontiguousarray(blocks[:, :, off:off + 128]).view(np.uint16).reshape(P, H, 64)
+        return np.ascontiguousarray(s.transpose(0, 2, 1).reshape(P * 64, H)[:n_tokens])
+
+    return plane(layout.k_scales_offset), plane(layout.v_scales_offset)
 
 
 def row_rel_error(out: np.ndarray, ref: np.ndarray) -> np.ndarray:

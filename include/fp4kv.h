@@ -72,10 +72,13 @@ enum fp4kv_status {
 
 /* Number formats of a cache.  ("Quantising the KV cache", Concept section,
  * results table: "FP4 E2M1, E4M3 scale per 16" at 4.5 bits per number and
- * "FP8 E4M3, one scale per tensor" at 8.) */
+ * "FP8 E4M3, one scale per tensor" at 8; "KV Cache Quantisation", Common
+ * questions: FP8 at finer scale granularities, here one fp16 scale per
+ * token and KV head, 8 + 16/D bits per number.) */
 enum fp4kv_format {
     FP4KV_FORMAT_FP4_E2M1 = 0,            /* E2M1 elements, one E4M3 scale per 16 channels */
-    FP4KV_FORMAT_FP8_E4M3 = 1             /* E4M3 elements, one fp32 scale per tensor (K, V) */
+    FP4KV_FORMAT_FP8_E4M3 = 1,            /* E4M3 elements, one fp32 scale per tensor (K, V) */
+    FP4KV_FORMAT_FP8_E4M3_TOKEN = 2       /* E4M3 elements, one fp16 scale per (token, KV head) */
 };
 
 /* Shape of one layer's cache.  ("Quantising the KV cache", Maths section:
@@ -87,8 +90,8 @@ typedef struct fp4kv_cache_params {
     int32_t page_size;                    /* tokens per page: FP4KV_PAGE_SIZE */
     int32_t format;                       /* enum fp4kv_format */
     int64_t num_pages;                    /* pages in the pool, >= 1 */
-    float k_scale;                        /* FP8: the K tensor's scale, 2^-64 .. 2^64; FP4: 0 */
-    float v_scale;                        /* FP8: the V tensor's scale, 2^-64 .. 2^64; FP4: 0 */
+    float k_scale;                        /* FP8: the K tensor's scale, 2^-64 .. 2^64; others: 0 */
+    float v_scale;                        /* FP8: the V tensor's scale, 2^-64 .. 2^64; others: 0 */
 } fp4kv_cache_params;
 
 /* Byte layout of the cache, filled by fp4kv_cache_layout.  Plain data: it
@@ -118,23 +121,36 @@ typedef struct fp4kv_cache_params {
  *             (j, h, c) holds channel c of tokens 16j+8h .. 16j+8h+7
  * and no scale planes (k_scales_offset = 64*D and v_scales_offset = 128*D
  * mark empty planes).  A code byte is sign << 7 | E4M3 magnitude code; the
- * stored value is E4M3(code) times the tensor's scale from the params. */
+ * stored value is E4M3(code) times the tensor's scale from the params.
+ *
+ * FP8 format with per-token scales: a block holds
+ *   K codes   [64 tokens][D] bytes         at k_codes_offset (0)
+ *   K scales  [64 tokens] fp16             at k_scales_offset (64*D)
+ *   V codes   as in the FP8 format         at v_codes_offset (64*D + 128)
+ *   V scales  [64 tokens] fp16             at v_scales_offset (128*D + 128)
+ * The scale of a token's K (or V) row of one KV head is the fp16
+ * round-to-nearest-even of amax / 448 over its D channels, saturating at
+ * 65504, with 0 replaced by 2^-24; the stored value is E4M3(code) times
+ * it. */
 typedef struct fp4kv_cache_layout_t {
     fp4kv_cache_params params;
-    int64_t block_bytes;                  /* FP4: 64 * D * 9 / 8; FP8: 128 * D */
+    int64_t block_bytes;                  /* FP4: 64 * D * 9 / 8; FP8: 128 * D; FP8 per token: 128 * D + 256 */
     int64_t k_codes_offset;               /* offsets inside a block */
     int64_t k_scales_offset;
     int64_t v_codes_offset;
     int64_t v_scales_offset;
     int64_t head_stride;                  /* = block_bytes */
     int64_t page_stride;                  /* = num_kv_heads * block_bytes */
-    int64_t cache_bytes;                  /* = num_pages * page_stride: exactly 9/16 B (FP8: 1 B) per number */
-    int64_t bytes_per_token;              /* = 2 * H_kv * D * 9 / 16 (FP8: 2 * H_kv * D) */
+    int64_t cache_bytes;                  /* = num_pages * page_stride: exactly 9/16 B (FP8: 1 B; FP8
+                                             per token: 1 + 2/D B) per number */
+    int64_t bytes_per_token;              /* = 2 * H_kv * D * 9 / 16 (FP8: 2 * H_kv * D; per token:
+                                             2 * H_kv * (D + 2)) */
 } fp4kv_cache_layout_t;
 
 /* Fill *out from *params.  Host only, no HIP call, pure.
  * Errors: INVALID_ARGUMENT for a null pointer, H_kv < 1, num_pages < 1, an
- * unknown format, FP4 scales not 0 or FP8 scales not finite and positive,
+ * unknown format, FP8 scales not finite and positive or other formats'
+ * scales not 0,
  * or a cache size that overflows int64; UNSUPPORTED for head_dim not in
  * {64, 128}, page_size != 64 or FP8 scales outside
  * 2^-64 .. 2^64. */
@@ -152,7 +168,9 @@ FP4KV_API int fp4kv_cache_layout(const fp4kv_cache_params *params, fp4kv_cache_l
  * nibble-wise with atomics unless one call covers both).
  * FP8 format ("Quantising the KV cache", Concept section, results table):
  * code = sign << 7 | E4M3 round-to-nearest-even of |x| / scale with the
- * tensor's scale from the layout, saturating at 448, sign kept.
+ * tensor's scale from the layout, saturating at 448, sign kept.  FP8 with
+ * per-token scales: the same code under the token's own fp16 scale (see the
+ * layout), which is stored beside it.
  *   layout        host, from fp4kv_cache_layout (re-checked).
  *   k, v          device bf16 [n_tokens][H_kv][D], contiguous, 16-B aligned.
  *   n_tokens      >= 0; 0 is a no-op (pointers may then be NULL).
@@ -195,7 +213,7 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  * For sequence b and query head h, with G = num_q_heads / H_kv and KV head
  * h / G, over its tokens t < seq_lens[b]:
  *   out[b][h] = sum_t softmax_t(softmax_scale * q[b][h] . K^[t]) * V^[t]
- * where K^, V^ are the stored E2M1 values times their scales.  The context
+ * where K^, V^ are the stored E2M1 (or E4M3) values times their scales.  The context
  * is cut into splits; each split keeps a running max and sum (online
  * softmax) and a second kernel merges the splits.  Accumulation is fp32.
  *   layout, cache      as above (device cache, 256-B aligned).

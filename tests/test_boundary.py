@@ -52,7 +52,7 @@ def test_layout_sizes(H, D, pages):
 
 @pytest.mark.parametrize("H,D,P,pages,fmt,ks,vs,code", [
     (0, 128, 64, 1, 0, 0, 0, fk.ERR_INVALID_ARGUMENT), (8, 128, 64, 0, 0, 0, 0, fk.ERR_INVALID_ARGUMENT),
-    (8, 128, 64, 1, 2, 0, 0, fk.ERR_INVALID_ARGUMENT), (8, 96, 64, 1, 0, 0, 0, fk.ERR_UNSUPPORTED),
+    (8, 128, 64, 1, 3, 0, 0, fk.ERR_INVALID_ARGUMENT), (8, 96, 64, 1, 0, 0, 0, fk.ERR_UNSUPPORTED),
     (8, 100, 64, 1, 0, 0, 0, fk.ERR_UNSUPPORTED), (8, 256, 64, 1, 0, 0, 0, fk.ERR_UNSUPPORTED),
     (8, 128, 32, 1, 0, 0, 0, fk.ERR_UNSUPPORTED), (8, 128, 64, 1 << 60, 0, 0, 0, fk.ERR_INVALID_ARGUMENT),
     (8, 128, 64, 1, 0, 1.0, 0, fk.ERR_INVALID_ARGUMENT),            # FP4 takes no scales
@@ -62,7 +62,8 @@ def test_layout_sizes(H, D, pages):
     (8, 128, 64, 1, 1, 1.0, float("nan"), fk.ERR_INVALID_ARGUMENT),
     (8, 128, 64, 1, 1, 2.0 ** -70, 1.0, fk.ERR_UNSUPPORTED),        # outside 2^-64 .. 2^64
     (8, 128, 64, 1, 1, 1.0, 2.0 ** 70, fk.ERR_UNSUPPORTED),
-    (8, 96, 64, 1, 1, 1.0, 1.0, fk.ERR_UNSUPPORTED)])               # FP8: D 64 or 128 too
+    (8, 96, 64, 1, 1, 1.0, 1.0, fk.ERR_UNSUPPORTED),                # FP8: D 64 or 128 too
+    (8, 96, 64, 1, 2, 0.0, 0.0, fk.ERR_UNSUPPORTED)])
 def test_layout_rejects(H, D, P, pages, fmt, ks, vs, code):
     p = fk.CacheParams(H, D, P, fmt, pages, ks, vs)
     out = fk.CacheLayout()
@@ -81,6 +82,26 @@ def test_fp8_layout_sizes(H, pages):
     assert [L.k_codes_offset, L.k_scales_offset, L.v_codes_offset, L.v_scales_offset] == [0, 8192, 8192, 16384]
     assert L.bytes_per_token * 64 == L.page_stride == H * L.block_bytes
     assert (L.params.k_scale, L.params.v_scale) == (0.5, 3.0)
+
+
+@pytest.mark.parametrize("H,D,pages", [(1, 64, 1), (8, 128, 512), (3, 128, 1000)])
+def test_fp8_token_layout_sizes(H, D, pages):
+    """FP8 with an fp16 scale per (token, KV head): K codes, K scales, V
+    codes, V scales per block; 8 + 16/D bits per number, the page's cost
+    formula b + s/g with s = 16 and g = D."""
+    L = fk.cache_layout(H, D, pages, format=fk.FORMAT_FP8_E4M3_TOKEN)
+    assert L.block_bytes == 128 * D + 256 and L.fp8 and L.token_scales
+    assert [L.k_codes_offset, L.k_scales_offset, L.v_codes_offset, L.v_scales_offset] == \
+        [0, 64 * D, 64 * D + 128, 128 * D + 128]
+    assert 8 * L.cache_bytes / (pages * 64 * 2 * H * D) == pytest.approx(oracle.bits_per_number(8, 16, D))
+    assert L.bytes_per_token * 64 == L.page_stride == H * L.block_bytes
+    for ks, vs in ((0.5, 0.0), (0.0, 1.0)):                       # it takes no tensor scales
+        p = fk.CacheParams(H, D, 64, fk.FORMAT_FP8_E4M3_TOKEN, pages, ks, vs)
+        assert fk.library().fp4kv_cache_layout(ctypes.byref(p), ctypes.byref(fk.CacheLayout())) == \
+            fk.ERR_INVALID_ARGUMENT
+    p = fk.CacheParams(H, D, 64, 3, pages, 0.0, 0.0)                # unknown format
+    assert fk.library().fp4kv_cache_layout(ctypes.byref(p), ctypes.byref(fk.CacheLayout())) == \
+        fk.ERR_INVALID_ARGUMENT
 
 
 def test_plan():

@@ -11,6 +11,7 @@ import torch
 import fp4_quantised_kv_amd as fk
 import fp4kv_harness as hx
 import fp4kv_workloads as wl
+import kv_formats as kf
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -28,10 +29,7 @@ def _setup(lens, Hkv, G, D, fmt, seed, extra=1):
     B = len(lens)
     maxp = max(1, max(-(-(n + extra) // 64) for n in lens))
     table = torch.randperm(B * maxp, generator=g).to(torch.int32).reshape(B, maxp)
-    if fmt == "fp8":
-        L = fk.cache_layout(Hkv, D, B * maxp, format=fk.FORMAT_FP8_E4M3, k_scale=0.03, v_scale=0.02)
-    else:
-        L = fk.cache_layout(Hkv, D, B * maxp)
+    L = kf.layout(fmt, Hkv, D, B * maxp)
     cache = torch.full((L.cache_bytes,), 0x5A, dtype=torch.uint8, device="cuda")
     kv = {}
     for b, n in enumerate(lens):
@@ -68,7 +66,8 @@ def _unfused(L, cache, table, lens, kn, vn, q, splits):
                                num_splits=splits)
 
 
-CASES = [("fp4", 128, None), ("fp4", 64, None), ("fp8", 128, None), ("fp8", 64, None), ("fp4", 128, "valu")]
+CASES = [("fp4", 128, None), ("fp4", 64, None), ("fp8", 128, None), ("fp8", 64, None), ("fp8t", 128, None),
+         ("fp8t", 64, None), ("fp4", 128, "valu")]
 LENS = [0, 1, 2, 63, 64, 65, 128, 129, 1000, 4097]
 
 
@@ -91,7 +90,8 @@ def test_same_as_append_then_decode(fmt, D, kernel, G, splits, monkeypatch):
     assert torch.equal(out, ref)
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp8", 128), ("fp4", 64), ("fp8", 64)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp8", 128), ("fp4", 64), ("fp8", 64), ("fp8t", 128),
+                                   ("fp8t", 64)])
 def test_steps_against_oracle(fmt, D):
     """Five consecutive steps (positions of both parities, page crossings);
     the stored bytes and the last step's attention against the oracle."""
@@ -108,7 +108,18 @@ def test_steps_against_oracle(fmt, D):
     out = out.cpu().numpy()
     lens = [n + 4 for n in lens0]
     pages = [table[b, : -(-n // 64)].tolist() for b, n in enumerate(lens)]
-    if fmt == "fp8":
+    if fmt == "fp8t":
+        for b, n in enumerate(lens):
+            gk, gv = hx.read_pages_fp8(cache, L, pages[b], n)
+            gks, gvs = hx.read_token_scales(cache, L, pages[b], n)
+            ek, eks = oracle.quantize_fp8_groups(wl.bf16_bits(kv[b][0][:n]), "token")
+            ev, evs = oracle.quantize_fp8_groups(wl.bf16_bits(kv[b][1][:n]), "token")
+            assert np.array_equal(gk, ek) and np.array_equal(gks, eks)
+            assert np.array_equal(gv, ev) and np.array_equal(gvs, evs)
+        kvals = [kf.stored_values(fmt, L, kv[b][0][:n]) for b, n in enumerate(lens)]
+        vvals = [kf.stored_values(fmt, L, kv[b][1][:n]) for b, n in enumerate(lens)]
+        ref = oracle.decode_attention_values(wl.bf16_bits(q), kvals, vvals, lens, D ** -0.5)
+    elif fmt == "fp8":
         ks, vs = L.params.k_scale, L.params.v_scale
         kc = [oracle.quantize_fp8(wl.bf16_bits(kv[b][0][:n]), ks) for b, n in enumerate(lens)]
         vc = [oracle.quantize_fp8(wl.bf16_bits(kv[b][1][:n]), vs) for b, n in enumerate(lens)]

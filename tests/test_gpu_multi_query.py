@@ -10,6 +10,7 @@ import torch
 import fp4_quantised_kv_amd as fk
 import fp4kv_harness as hx
 import fp4kv_workloads as wl
+import kv_formats as kf
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -25,10 +26,7 @@ def _cache(lens, Hkv, D, fmt, seed):
     B = len(lens)
     maxp = max(1, max(-(-n // 64) for n in lens))
     table = torch.randperm(B * maxp, generator=g).to(torch.int32).reshape(B, maxp)
-    if fmt == "fp8":
-        L = fk.cache_layout(Hkv, D, B * maxp, format=fk.FORMAT_FP8_E4M3, k_scale=0.03, v_scale=0.02)
-    else:
-        L = fk.cache_layout(Hkv, D, B * maxp)
+    L = kf.layout(fmt, Hkv, D, B * maxp)
     cache = torch.full((L.cache_bytes,), 0x7F, dtype=torch.uint8, device="cuda")
     kv = {}
     for b, n in enumerate(lens):
@@ -49,7 +47,11 @@ def _reference(L, kv, lens, q, fmt, D, Hkv):
     for i in range(S):
         li = [max(0, n - (S - 1 - i)) for n in lens]
         qi = wl.bf16_bits(q[:, i].contiguous())
-        if fmt == "fp8":
+        if fmt == "fp8t":
+            kv_ = [kf.stored_values(fmt, L, kv[b][0]) if lens[b] else np.zeros((1, Hkv, D)) for b in range(B)]
+            vv_ = [kf.stored_values(fmt, L, kv[b][1]) if lens[b] else np.zeros((1, Hkv, D)) for b in range(B)]
+            ref[:, i] = oracle.decode_attention_values(qi, kv_, vv_, li, D ** -0.5)
+        elif fmt == "fp8":
             ks, vs = L.params.k_scale, L.params.v_scale
             kc = [oracle.quantize_fp8(wl.bf16_bits(kv[b][0]), ks) if lens[b] else np.zeros((1, Hkv, D), np.uint8)
                   for b in range(B)]
@@ -66,7 +68,8 @@ def _reference(L, kv, lens, q, fmt, D, Hkv):
     return ref
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64), ("fp8t", 128),
+                                   ("fp8t", 64)])
 @pytest.mark.parametrize("S,G", [(2, 8), (4, 4), (16, 1), (3, 5)])
 @pytest.mark.parametrize("splits", [0, 1, 5])
 def test_against_oracle(fmt, D, S, G, splits):
@@ -90,7 +93,8 @@ def test_against_oracle(fmt, D, S, G, splits):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64), ("fp8t", 128),
+                                   ("fp8t", 64)])
 def test_one_query_token_is_decode_attention(fmt, D):
     lens = [5, 64, 700]
     L, cache, table, kv, g = _cache(lens, 2, D, fmt, seed=3)

@@ -9,6 +9,7 @@ import torch
 import fp4_quantised_kv_amd as fk
 import fp4kv_harness as hx
 import fp4kv_workloads as wl
+import kv_formats as kf
 import oracle
 from test_gpu_multi_query import _cache
 
@@ -23,7 +24,9 @@ def _say(msg):
 def _codes(kv, lens, fmt, L, D, Hkv):
     out = []
     for b, n in enumerate(lens):
-        if fmt == "fp8":
+        if fmt == "fp8t":
+            out.append((kf.stored_values(fmt, L, kv[b][0]), kf.stored_values(fmt, L, kv[b][1])))
+        elif fmt == "fp8":
             kc = oracle.quantize_fp8(wl.bf16_bits(kv[b][0]), L.params.k_scale) if n else np.zeros((1, Hkv, D), np.uint8)
             vc = oracle.quantize_fp8(wl.bf16_bits(kv[b][1]), L.params.v_scale) if n else np.zeros((1, Hkv, D), np.uint8)
             out.append((kc, vc))
@@ -45,7 +48,10 @@ def _reference(codes, lens, q, window, fmt, L, D, Hkv):
                 continue
             lo = max(0, Li - window) if window > 0 else 0
             qi = wl.bf16_bits(q[b:b + 1, i].contiguous())
-            if fmt == "fp8":
+            if fmt == "fp8t":
+                kvals, vvals = codes[b]
+                r = oracle.decode_attention_values(qi, [kvals[lo:Li]], [vvals[lo:Li]], [Li - lo], D ** -0.5)
+            elif fmt == "fp8":
                 kc, vc = codes[b]
                 r = oracle.decode_attention_fp8(qi, [kc[lo:Li]], [vc[lo:Li]], L.params.k_scale, L.params.v_scale,
                                                 [Li - lo], D ** -0.5)
@@ -57,7 +63,8 @@ def _reference(codes, lens, q, window, fmt, L, D, Hkv):
     return ref
 
 
-@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64)])
+@pytest.mark.parametrize("fmt,D", [("fp4", 128), ("fp4", 64), ("fp8", 128), ("fp8", 64), ("fp8t", 128),
+                                   ("fp8t", 64)])
 @pytest.mark.parametrize("window", [1, 17, 64, 100, 1000])
 @pytest.mark.parametrize("S,G,splits", [(1, 8, 0), (4, 4, 1), (2, 2, 3)])
 def test_window_against_oracle(fmt, D, window, S, G, splits):
