@@ -81,7 +81,9 @@ def cpu_baseline(w, seed, threads, fmt="fp4"):
     import fp4kv_workloads as wl
     import oracle
     lens = wl.seq_lengths(w, seed)
-    n_seq = min(w.batch, max(1, threads // 2))
+    # every sequence (about 10-15 s of oracle time at the 32K batch); the
+    # per-token FP8 oracle holds float64 values, so a quarter of them there
+    n_seq = w.batch if fmt != "fp8t" else min(w.batch, max(1, threads // 2))
     seqs = list(range(n_seq))
     q = wl.queries(w, seed)
     kc, ks, vc, vs = [], [], [], []
@@ -155,6 +157,76 @@ def prefill_append(fk, wl, seed, dev, stream, reps=10):
     bytes_ = 2 * k.numel() * 2 + layout.cache_bytes + n * 8
     return {"workload": w.name, "tokens": n, "ms": round(ms, 5), "gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
             "algorithmic_bytes": bytes_}
+
+
+def cold_and_warm(fk, gc, w, seed, dev, stream, splits_req, step_bytes, reps=20):
+    """For a cache smaller than the 256 MB last-level cache: decode step
+    (split + combine) time warm (back to back: the cache stays in the
+    last-level cache) and cold (1 GiB of unrelated data read and written
+    between calls, outside the timed events, so every call reads the cache
+    from HBM).  Steps this small take less GPU time than the host needs to
+    enqueue them, so both measurements queue their calls behind GPU work
+    that is still running (a spin kernel that touches no memory, or the
+    scrub) and time the GPU, not the host."""
+    import torch
+    B, Hq, D = w.batch, w.q_heads, w.head_dim
+    splits, partials, ws_bytes = fk.decode_plan(gc.layout, B, Hq, gc.page_table.shape[1], splits_req)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    import fp4kv_workloads as wl
+    q = wl.queries(w, seed).to(dev)
+    scrub = torch.zeros(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
+
+    def call():
+        fk.decode_split(gc.layout, gc.cache, q, gc.seq_lens, gc.page_table, num_splits=splits_req, workspace=ws)
+        fk.decode_combine(ws, B, Hq, D, partials, out=out)
+
+    for _ in range(5):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(2_000_000)                  # ~1 ms of GPU clock cycles while the calls are enqueued
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) / reps
+    cold = []
+    for _ in range(reps):
+        scrub.add_(1)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        call()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    cold_ms = sorted(cold)[len(cold) // 2]
+    del scrub
+    return {"cache_bytes": gc.layout.cache_bytes, "step_bytes": int(step_bytes),
+            "warm_ms": round(warm, 5), "warm_gbs": round(step_bytes / (warm * 1e-3) / 1e9, 1),
+            "cold_ms_median": round(cold_ms, 5), "cold_ms_min": round(min(cold), 5),
+            "cold_gbs": round(step_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "note": "warm: back-to-back steps; cold: 1 GiB scrubbed through the caches before each step"}
+
+
+def copy_ceiling(dev, stream, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy (read + write) of nbytes: the rate a
+    kernel that reads and writes HBM in equal measure can expect."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_read_and_written": 2 * nbytes, "ms": round(ms, 5), "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def query_extras(fk, gc, w, dev, stream, splits_req, reps=20, window=4096):
@@ -405,6 +477,9 @@ def main():
     }
     if not args.no_prefill:
         result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)
+        result["prefill_append"]["device_copy"] = copy_ceiling(dev, stream)
+    if L.cache_bytes < (256 << 20) and not paged:
+        result["cold_warm"] = cold_and_warm(fk, gc, w, args.seed, dev, stream, splits_req, step_bytes)
     if args.extras and not paged:
         result["extras"] = query_extras(fk, gc, w, dev, stream, splits_req)
     if not args.no_read_probe:
