@@ -3,7 +3,9 @@
 //   quantize_append_kernel   bf16 K/V rows -> E2M1 codes + E4M3 scales at slots
 //   decode_split_valu        split-K decode attention, one wave per
 //                            (context split, KV head, sequence)
-//   decode_combine           merges the splits' (max, sum, output) partials
+//   decode_combine_few       merges the splits' (max, sum, output) partials,
+//                            one wave per row (up to 32 partials)
+//   decode_combine           the same merge, one workgroup per row (more partials)
 //
 // Number formats ("Quantising the KV cache", numerics-explained, Code
 // section): E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with the sign in bit 3
@@ -565,6 +567,69 @@ __global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ 
     }
 }
 
+// The same merge for rows with at most PM partials: one wave per row, four
+// rows per workgroup, lane l covering channels CL*l .. CL*l + CL - 1.  Every
+// load of the row is issued before any result is used (partials past the
+// last re-read the last one and get weight zero), and the (m, l) pairs are
+// the same for the whole wave, so the merge needs no LDS and no barrier.
+template <int D, int PM>
+__global__ __launch_bounds__(256) void decode_combine_few(const float *__restrict__ ws_o,
+                                                          const float *__restrict__ ws_ml, int64_t rows,
+                                                          int num_q_heads, int partials, float *__restrict__ out)
+{
+    constexpr int CL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int64_t b = row / num_q_heads, hq = row % num_q_heads;
+    // partial j of this row: index (b * partials + j) * num_q_heads + hq
+    const int64_t first = b * partials * num_q_heads + hq;
+    const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + first;
+    const float *o = ws_o + first * D + lane * CL;
+    const int64_t stride = static_cast<int64_t>(num_q_heads) * D;
+    float2 mj[PM];
+    float x[PM][CL];
+#pragma unroll
+    for (int j = 0; j < PM; ++j) {
+        const int jc = j < partials ? j : partials - 1;
+        mj[j] = ml[static_cast<int64_t>(jc) * num_q_heads];
+        if constexpr (CL == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(o + jc * stride);
+            x[j][0] = v.x;
+            x[j][1] = v.y;
+        } else {
+            x[j][0] = o[jc * stride];
+        }
+    }
+    // keep the scheduler from placing the maximum (which needs the (m, l)
+    // loads) before the channel loads are issued
+    __builtin_amdgcn_sched_barrier(0);
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PM; ++j)
+        M = j < partials ? fmaxf(M, mj[j].x) : M;
+    float L = 0.0f, O[CL];
+#pragma unroll
+    for (int i = 0; i < CL; ++i)
+        O[i] = 0.0f;
+    // no branch on M: every weight is zero when all partials are empty
+#pragma unroll
+    for (int j = 0; j < PM; ++j) {
+        const float w = (j < partials && mj[j].x != -INFINITY) ? exp2f(mj[j].x - M) : 0.0f;
+        L = fmaf(mj[j].y, w, L);
+#pragma unroll
+        for (int i = 0; i < CL; ++i)
+            O[i] = fmaf(x[j][i], w, O[i]);
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if constexpr (CL == 2) {
+        *reinterpret_cast<float2 *>(out + row * D + lane * CL) = make_float2(O[0] * inv, O[1] * inv);
+    } else {
+        out[row * D + lane] = O[0] * inv;
+    }
+}
+
 // Each wave reads one 9216-byte block per iteration: nine 1 KB rows, lane l
 // taking bytes 16l .. 16l+15 of each, all nine loads in flight together.
 __global__ __launch_bounds__(256) void read_probe(const uint8_t *__restrict__ buf, int64_t blocks,
@@ -706,7 +771,24 @@ hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,
                                  int32_t partials, int32_t head_dim, float *out, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(batch) * num_q_heads));   // one workgroup per row
+    const int64_t rows = static_cast<int64_t>(batch) * num_q_heads;
+    if (partials <= 32) {
+        // one wave per row, four rows per workgroup
+        const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+        if (head_dim == 64) {
+            if (partials <= 16)
+                decode_combine_few<64, 16><<<grid, 256, 0, stream>>>(ws_o, ws_ml, rows, num_q_heads, partials, out);
+            else
+                decode_combine_few<64, 32><<<grid, 256, 0, stream>>>(ws_o, ws_ml, rows, num_q_heads, partials, out);
+        } else {
+            if (partials <= 16)
+                decode_combine_few<128, 16><<<grid, 256, 0, stream>>>(ws_o, ws_ml, rows, num_q_heads, partials, out);
+            else
+                decode_combine_few<128, 32><<<grid, 256, 0, stream>>>(ws_o, ws_ml, rows, num_q_heads, partials, out);
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid(static_cast<unsigned>(rows));   // one workgroup per row
     if (head_dim == 64)
         decode_combine<64><<<grid, 256, 0, stream>>>(ws_o, ws_ml, num_q_heads, partials, out);
     else
