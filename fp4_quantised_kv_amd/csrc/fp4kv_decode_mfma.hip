@@ -192,15 +192,25 @@ __device__ __forceinline__ void load_v_direct(const uint8_t *blk, const CacheGeo
 // copies are 16 bytes per lane; the two scale planes of a page travel in one
 // instruction with the K codes.
 //   K slot [0, 4096): tile t at t*1024, lane l's 16 code bytes at l*16;
-//          [4096, 4608): the page's K scale plane [64 tokens][8];
+//          [4096, 4608): the page's K scale plane [64 tokens][8] in 16-byte
+//          pieces of two tokens, piece p stored at k_scale_piece(p);
 //          [4608, 5120): its V scale plane [4 slices][8 blocks][16].
 //   V slot [0, 4096): pair block u at u*1024, lane l at l*16;
 //          [4096, 5120): the page's V scales in fp16, converted once per page
-//          during the K phase (each lane converts 8).
+//          during the K phase (each lane converts 8), 32-byte block b (slice
+//          b/8, channel block b%8, 16 tokens) stored at v_scale_block(b).
+// The two permutations keep the scale reads free of LDS bank conflicts: the
+// lanes reading one score tile's K scales (two tokens per piece, pieces
+// 8q + 2t + {0, 1} for q = 0..3) and the lanes reading one pair block's V
+// scales (blocks 8*slice + 2u + {0, 1}) land on distinct banks instead of
+// on blocks 128 or 256 bytes apart.
 constexpr int kKSlotBytes = 5120;
 constexpr int kVSlotBytes = 5120;
 constexpr int kCopiesK = 5;               // direct-to-LDS instructions per K copy
 constexpr int kCopiesV = 4;               // ... per V copy
+
+__device__ __forceinline__ uint32_t k_scale_piece(uint32_t p) { return p ^ (2u * ((p >> 3) & 3u)); }
+__device__ __forceinline__ uint32_t v_scale_block(uint32_t b) { return b ^ (2u * ((b >> 3) & 3u)); }
 
 struct StageOffsets {
     uint32_t k, s, v;                     // per-lane byte offsets inside a block: tile/block 0, scales
@@ -211,8 +221,11 @@ __device__ __forceinline__ StageOffsets stage_offsets(const CacheGeom &g, int la
     StageOffsets o;
     const uint32_t tok0 = static_cast<uint32_t>(tile_token(0, col));
     o.k = static_cast<uint32_t>(g.k_codes_off) + tok0 * 64u + jj * 16u;
-    // lanes 0..31: the K scale plane, lanes 32..63: the V scale plane
-    o.s = static_cast<uint32_t>(lane < 32 ? g.k_scales_off : g.v_scales_off) + (lane & 31) * 16u;
+    // lanes 0..31: the K scale plane (lane l fetches the piece stored at
+    // position l; k_scale_piece is its own inverse), lanes 32..63: the V
+    // scale plane
+    o.s = lane < 32 ? static_cast<uint32_t>(g.k_scales_off) + k_scale_piece(static_cast<uint32_t>(lane)) * 16u
+                    : static_cast<uint32_t>(g.v_scales_off) + (lane & 31) * 16u;
     o.v = static_cast<uint32_t>(g.v_codes_off) + (jj * 128u + 2u * col) * 8u;
     return o;
 }
@@ -242,7 +255,9 @@ __device__ __forceinline__ void read_k(const uint8_t *slot, int lane, int col, i
     for (int t = 0; t < 4; ++t) {
         const uint4 x = *reinterpret_cast<const uint4 *>(slot + t * 1024 + lane * 16);
         r.kw[t][0] = x.x; r.kw[t][1] = x.y; r.kw[t][2] = x.z; r.kw[t][3] = x.w;
-        r.ks[t] = *reinterpret_cast<const uint16_t *>(slot + 4096 + tile_token(t, col) * 8 + 2 * jj);
+        const uint32_t tok = static_cast<uint32_t>(tile_token(t, col));
+        r.ks[t] = *reinterpret_cast<const uint16_t *>(slot + 4096 + k_scale_piece(tok >> 1) * 16 + (tok & 1) * 8 +
+                                                      2 * jj);
     }
 }
 
@@ -259,7 +274,7 @@ __device__ __forceinline__ void convert_v_scales(const uint8_t *kslot, uint8_t *
         raw.y = keep_valid_bytes(raw.y, t0 + 4, valid);
     }
     const half8_t h = cat(fp8x2<false>(raw.x), fp8x2<true>(raw.x), fp8x2<false>(raw.y), fp8x2<true>(raw.y));
-    *reinterpret_cast<half8_t *>(vslot + 4096 + lane * 16) = h;
+    *reinterpret_cast<half8_t *>(vslot + 4096 + v_scale_block(lane >> 1) * 32 + (lane & 1) * 16) = h;
 }
 
 template <int N>
@@ -269,7 +284,8 @@ __device__ __forceinline__ void read_v(const uint8_t *slot, int u0, int lane, in
 #pragma unroll
     for (int u = 0; u < N; ++u) {
         vw[u] = *reinterpret_cast<const uint4 *>(slot + (u0 + u) * 1024 + lane * 16);
-        const half8_t *sp = reinterpret_cast<const half8_t *>(slot + 4096 + (jj * 8 + 2 * (u0 + u) + (col >> 3)) * 32);
+        const half8_t *sp = reinterpret_cast<const half8_t *>(
+            slot + 4096 + v_scale_block(static_cast<uint32_t>(jj * 8 + 2 * (u0 + u) + (col >> 3))) * 32);
         sv[u][0] = sp[0];
         sv[u][1] = sp[1];
     }
