@@ -15,6 +15,8 @@ namespace {
 
 constexpr int32_t kPage = FP4KV_PAGE_SIZE;
 constexpr int32_t kTargetWaves = 16384;   // context chunks (one wave each): 4x the waves 256 CUs hold at once, so ragged lengths balance
+constexpr int64_t kMinAutoChunkPages = 2;  // automatic plans: pages per chunk at least ...
+constexpr int64_t kMinAutoChunks = 1024;   // ... unless that leaves fewer chunks than this
 constexpr int32_t kChunksPerGroup = 4;   // chunks merged inside one workgroup
 constexpr int64_t kMaxPartials = 65535;  // partials per row: the split kernel's third grid dimension
 
@@ -125,6 +127,12 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
     if (s == 0) {
         const int64_t units = static_cast<int64_t>(batch > 0 ? batch : 1) * hkv;
         s = (kTargetWaves + units - 1) / units;
+        // chunks of one page are mostly fixed cost: at least two pages each,
+        // as long as that still leaves enough chunks to spread over the GPU
+        // (a tiny batch is faster with one page per wave, in parallel)
+        const int64_t most = max_pages / kMinAutoChunkPages;
+        if (most > 0 && units * most >= kMinAutoChunks)
+            s = s > most ? most : s;
     }
     if (s > max_pages)
         s = max_pages;

@@ -194,7 +194,8 @@ FP4KV_API int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout,
  * to 4 * 65535, then trimmed so that no chunk starts past page
  * max_pages_per_seq); 0 lets the library choose S, about 16384 chunks in
  * total over batch x H_kv, so that the GPU stays full even when sequence
- * lengths differ.  Each chunk pays a fixed start (its first page's
+ * lengths differ, but no more than max_pages_per_seq / 2 (chunks of at
+ * least two pages) when that still gives batch x H_kv x S >= 1024.  Each chunk pays a fixed start (its first page's
  * latency, the merge): when every sequence is long and about equally so,
  * chunks of about 32 pages (S = max_pages_per_seq / 32) stream faster than
  * the automatic choice.  *splits_out gets S, *partials_out P and

@@ -115,6 +115,12 @@ def test_plan():
     assert fk.decode_plan(L, 1, 32, 9, 4)[0] == 3                   # 3 pages per split: 3 splits
     s, p, ws = fk.decode_plan(L, 64, 32, 258, 0)
     assert 1 <= s <= 258 and p == -(-s // 4) and ws > 0
+    # the automatic choice keeps chunks of at least two pages while 1024 chunks remain
+    assert fk.decode_plan(L, 8, 32, 64, 0)[:2] == (32, 8)           # 8 x 8 x 32 = 2048 chunks
+    assert fk.decode_plan(L, 1, 32, 64, 0)[0] == 64                 # 8 x 32 < 1024: one page each
+    assert fk.decode_plan(L, 1, 32, 3, 0)[0] == 3
+    assert fk.decode_plan(L, 1, 32, 1, 0)[0] == 1
+    assert fk.decode_plan(L, 64, 32, 258, 0)[0] == 29               # the ragged paged batch: 9 pages a chunk
     for args, code in [((32, 65, 512, 64), fk.ERR_INVALID_ARGUMENT),      # Hq % Hkv
                        ((32, 8 * 17, 512, 64), fk.ERR_UNSUPPORTED),       # group 17
                        ((-1, 64, 512, 64), fk.ERR_INVALID_ARGUMENT),
