@@ -4,10 +4,13 @@
 Default workload: 32 sequences of 32768 tokens, 64 query heads over 8 KV heads
 (group 8), head dim 128, 64 context splits -- 1.2 GB of packed cache, larger
 than the GPU's last-level cache, so every step streams it from HBM.  A step
-is one decode-attention call (split kernel + combine kernel); for the paged
-workload a step also appends one token per sequence first, inside the split
-kernel (--unfused: with a separate quantize_append call).  The cache, the
-queries and every argument are resident on the device before timing starts.
+is one fp4kv_decode_attention call (split kernel + combine kernel; the split
+kernel alone when there is one partial per row); for the paged workload it is
+one fp4kv_decode_append_attention call, whose split kernel first stores each
+sequence's new token (--unfused: a separate quantize_append call, then
+decode_attention).  The per-kernel breakdown runs the same steps as their
+halves with events between launches.  The cache, the queries and every
+argument are resident on the device before timing starts.
 
 Prints one JSON line: achieved HBM GB/s over the step's algorithmic bytes
 (packed K/V read, queries read, outputs written, page-table and length
@@ -161,7 +164,7 @@ def prefill_append(fk, wl, seed, dev, stream, reps=10):
 
 def cold_and_warm(fk, gc, w, seed, dev, stream, splits_req, step_bytes, reps=20):
     """For a cache smaller than the 256 MB last-level cache: decode step
-    (split + combine) time warm (back to back: the cache stays in the
+    (one fp4kv_decode_attention call) time warm (back to back: the cache stays in the
     last-level cache) and cold (1 GiB of unrelated data read and written
     between calls, outside the timed events, so every call reads the cache
     from HBM).  Steps this small take less GPU time than the host needs to
@@ -178,8 +181,8 @@ def cold_and_warm(fk, gc, w, seed, dev, stream, splits_req, step_bytes, reps=20)
     scrub = torch.zeros(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
 
     def call():
-        fk.decode_split(gc.layout, gc.cache, q, gc.seq_lens, gc.page_table, num_splits=splits_req, workspace=ws)
-        fk.decode_combine(ws, B, Hq, D, partials, out=out)
+        fk.decode_attention(gc.layout, gc.cache, q, gc.seq_lens, gc.page_table, num_splits=splits_req,
+                            workspace=ws, out=out)
 
     for _ in range(5):
         call()
@@ -349,7 +352,21 @@ def main():
 
     fused = paged and not args.unfused
 
+    def step_call(s):
+        # one step through the library's entry point, as a caller makes it
+        if paged and fused:
+            fk.decode_append_attention(L, gc.cache, news[s][0], news[s][1], qs[s % len(qs)], lens_dev[s],
+                                       gc.page_table, softmax_scale=scale, num_splits=splits_req, workspace=ws,
+                                       out=out)
+            return
+        if paged:
+            fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
+        fk.decode_attention(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
+                            softmax_scale=scale, num_splits=splits_req, workspace=ws, out=out)
+
     def step(s, e=None):
+        """The same step as its halves (split kernel, then combine), with
+        events between the launches for the per-kernel breakdown."""
         if e is not None:
             e[0].record(stream)
         if paged and not fused:
@@ -379,7 +396,7 @@ def main():
         fk.decode_combine(ws, B, Hq, D, partials, out=out)
     torch.cuda.synchronize()
     for s in range(args.warmup):
-        step(s)
+        step_call(s)
     torch.cuda.synchronize()
     # the timed region: K steps with no event between their launches
     t0 = time.perf_counter()
@@ -387,7 +404,7 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for s in range(args.warmup, total_steps):
-        step(s)
+        step_call(s)
     stop.record(stream)
     host_enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()

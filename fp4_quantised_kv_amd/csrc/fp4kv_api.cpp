@@ -5,6 +5,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 #include <limits>
 
 #include <hip/hip_runtime.h>
@@ -298,6 +300,18 @@ int prepare_append(void *cache, const void *k_new, const void *v_new, fp4kv::Dec
     return FP4KV_OK;
 }
 
+// With one partial per row the split kernel writes the final output itself
+// and no combine is launched (FP4KV_DECODE_COMBINE=separate keeps the
+// combine; the results are the same).
+bool direct_output(fp4kv::DecodeArgs *a, float *out)
+{
+    const char *v = std::getenv("FP4KV_DECODE_COMBINE");
+    if (a->partials != 1 || (v && std::strcmp(v, "separate") == 0))
+        return false;
+    a->out = out;
+    return true;
+}
+
 int64_t partial_o_bytes(int32_t batch, int32_t num_q_heads, int32_t partials, int32_t head_dim)
 {
     return round_up(static_cast<int64_t>(batch) * num_q_heads * partials * head_dim * 4, 256);
@@ -365,9 +379,12 @@ int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache
     if (!aligned(out, 16))
         return FP4KV_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool direct = direct_output(&a, out);
     hipError_t e = fp4kv::launch_decode_split(a, st);
     if (e != hipSuccess)
         return FP4KV_ERR_HIP;
+    if (direct)
+        return FP4KV_OK;
     e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
                                      out, st);
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
@@ -410,9 +427,12 @@ int fp4kv_decode_append_attention(const fp4kv_cache_layout_t *layout, void *cach
     if (!aligned(out, 16))
         return FP4KV_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool direct = direct_output(&a, out);
     hipError_t e = fp4kv::launch_decode_split(a, st);
     if (e != hipSuccess)
         return FP4KV_ERR_HIP;
+    if (direct)
+        return FP4KV_OK;
     e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
                                      out, st);
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
@@ -434,9 +454,12 @@ int fp4kv_decode_multi_attention(const fp4kv_cache_layout_t *layout, const void 
     if (!aligned(out, 16))
         return FP4KV_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool direct = direct_output(&a, out);
     hipError_t e = fp4kv::launch_decode_split(a, st);
     if (e != hipSuccess)
         return FP4KV_ERR_HIP;
+    if (direct)
+        return FP4KV_OK;
     e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, q_tokens * num_q_heads, a.partials,
                                      layout->params.head_dim, out, st);
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
@@ -479,9 +502,12 @@ int fp4kv_decode_window_attention(const fp4kv_cache_layout_t *layout, const void
     if (!aligned(out, 16))
         return FP4KV_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool direct = direct_output(&a, out);
     hipError_t e = fp4kv::launch_decode_split(a, st);
     if (e != hipSuccess)
         return FP4KV_ERR_HIP;
+    if (direct)
+        return FP4KV_OK;
     e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, q_tokens * num_q_heads, a.partials,
                                      layout->params.head_dim, out, st);
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;

@@ -34,7 +34,8 @@ struct DecodeArgs {
     float scale_log2e;           // softmax scale times log2(e): scores kept in base 2
     float *ws_o;                 // [batch][partials][q_tokens * num_q_heads][D] unnormalised outputs
     float *ws_ml;                // [batch][partials][q_tokens * num_q_heads][2] running max (base 2), sum
-    float *out;                  // [batch][q_tokens * num_q_heads][D]
+    float *out;                  // [batch][q_tokens * num_q_heads][D]; set only with one partial per
+                                 // row: the split kernel then writes the final rows, no combine
     bool staged;                 // matrix-core kernel: stage pages through LDS (D = 128)
     // The step's own token, appended before attending (all null: no append):
     // bf16 K and V rows [batch][H_kv][D] of one token per sequence, placed at

@@ -37,7 +37,8 @@ struct MergeArea {
 };
 
 // Call with every thread of the workgroup, after each wave has filled its
-// area; area(w) gives wave w's area.  Area row q is query token q / G, head
+// area; area(w) gives wave w's area.  With a.out set (one partial per row)
+// the rows are written to a.out as final outputs instead of partials.  Area row q is query token q / G, head
 // h*G + q % G of the group; its partial goes to row
 // (q / G) * num_q_heads + h*G + q % G of ws_o[b][part] and ws_ml[b][part],
 // so with one query token a workgroup's G rows are one contiguous block of
@@ -76,9 +77,16 @@ __device__ __forceinline__ void merge_waves_and_store(AreaOf area, const DecodeA
                 L = fmaf(ar.ml[2 * q + 1], wt, L);
             }
         }
-        *reinterpret_cast<float4 *>(a.ws_o + row * D + c) = O;
-        if (c == 0)
-            *reinterpret_cast<float2 *>(a.ws_ml + row * 2) = make_float2(M, L);
+        if (a.out) {
+            // the only partial of its rows: the final output, normalised as
+            // the combine would (with one partial its weight is exactly 1)
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            *reinterpret_cast<float4 *>(a.out + row * D + c) = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
+        } else {
+            *reinterpret_cast<float4 *>(a.ws_o + row * D + c) = O;
+            if (c == 0)
+                *reinterpret_cast<float2 *>(a.ws_ml + row * 2) = make_float2(M, L);
+        }
     }
 }
 
