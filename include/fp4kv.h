@@ -238,7 +238,9 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, MISALIGNED, WORKSPACE_TOO_SMALL,
  * HIP.  Equivalent to fp4kv_decode_split followed by fp4kv_decode_combine
  * on the same stream; with one partial per row (at most four chunks) the
- * split kernel writes `out` itself and no combine is launched. */
+ * split kernel writes `out` itself and no combine is launched (the
+ * environment variable FP4KV_DECODE_COMBINE=separate launches the combine
+ * anyway, for tests; the results are the same). */
 FP4KV_API int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache,
                            const void *q, int32_t batch, int32_t num_q_heads,
                            const int32_t *seq_lens, const int32_t *page_table,
