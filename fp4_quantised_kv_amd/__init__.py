@@ -16,7 +16,7 @@ import math
 import os
 
 __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
-           "quantize_append", "decode_attention", "decode_split", "decode_combine",
+           "quantize_append", "decode_attention", "decode_attention_noalloc", "decode_split", "decode_combine",
            "decode_append_attention", "decode_append_split", "decode_multi_attention",
            "decode_window_plan", "decode_window_attention",
            "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3", "FORMAT_FP8_E4M3_TOKEN",
@@ -27,6 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(HERE, "libfp4kv.so")
 PAGE_SIZE = 64
 MAX_GROUP = 16
+NOALLOC_WORKSPACE_BYTES = 32 << 20   # the static workspace of decode_attention_noalloc
 INT_PER_TOKEN = 0
 INT_PER_CHANNEL = 1
 INT_FP8_E4M3 = 0x108          # the `bits` value of FP8 E4M3 codes with fp16 scales
@@ -120,6 +121,10 @@ def library():
                                              ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_float,
                                              ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
         L.fp4kv_decode_attention.restype = ctypes.c_int
+        L.fp4kv_decode_attention_noalloc.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int32,
+                                                     ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_float,
+                                                     ctypes.c_int32, _P, _P]
+        L.fp4kv_decode_attention_noalloc.restype = ctypes.c_int
         L.fp4kv_decode_split.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_float,
                                          ctypes.c_int32, _P, ctypes.c_int64, _P]
@@ -299,6 +304,34 @@ def decode_attention(layout: CacheLayout, cache, q, seq_lens, page_table, softma
         ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, Hq, seq_lens.data_ptr(),
         page_table.data_ptr(), max_pages, float(softmax_scale), num_splits,
         workspace.data_ptr(), workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def decode_attention_noalloc(layout: CacheLayout, cache, q, seq_lens, page_table, softmax_scale=None,
+                             num_splits: int = 0, out=None, stream=None):
+    """decode_attention with the library's static workspace
+    (NOALLOC_WORKSPACE_BYTES per GPU) instead of a caller's: the C call
+    allocates nothing.  `out` (fp32 [B][Hq][D]) should be given by callers
+    that must not allocate; without it this binding allocates the result."""
+    import torch
+    _need(cache, "cache", torch.uint8)
+    _need(q, "q", torch.bfloat16)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_table, "page_table", torch.int32)
+    B, Hq, D = q.shape
+    if D != layout.head_dim:
+        raise ValueError("q's last dimension must equal the cache head_dim")
+    if tuple(seq_lens.shape) != (B,) or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("seq_lens must be [B] and page_table [B][max_pages]")
+    if cache.numel() < layout.cache_bytes:
+        raise ValueError("cache is smaller than layout.cache_bytes")
+    out = _out_tensor(out, B, Hq, D, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _check("fp4kv_decode_attention_noalloc", library().fp4kv_decode_attention_noalloc(
+        ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, Hq, seq_lens.data_ptr(),
+        page_table.data_ptr(), page_table.shape[1], float(softmax_scale), num_splits, out.data_ptr(),
+        _stream(stream)))
     return out
 
 

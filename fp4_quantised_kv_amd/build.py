@@ -15,7 +15,8 @@ SOURCES = [os.path.join(HERE, "csrc", "fp4kv_api.cpp"),
            os.path.join(HERE, "csrc", "fp4kv_decode_mfma.hip"),
            os.path.join(HERE, "csrc", "fp4kv_decode_fp8.hip"),
            os.path.join(HERE, "csrc", "fp4kv_int_api.cpp"),
-           os.path.join(HERE, "csrc", "fp4kv_int.hip")]
+           os.path.join(HERE, "csrc", "fp4kv_int.hip"),
+           os.path.join(HERE, "csrc", "fp4kv_scratch.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

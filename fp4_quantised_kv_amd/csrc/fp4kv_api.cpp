@@ -4,6 +4,7 @@
 #include "fp4kv.h"
 
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -378,6 +379,42 @@ int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache
         return FP4KV_ERR_INVALID_ARGUMENT;
     if (!aligned(out, 16))
         return FP4KV_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool direct = direct_output(&a, out);
+    hipError_t e = fp4kv::launch_decode_split(a, st);
+    if (e != hipSuccess)
+        return FP4KV_ERR_HIP;
+    if (direct)
+        return FP4KV_OK;
+    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
+                                     out, st);
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+int fp4kv_decode_attention_noalloc(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
+                                   int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
+                                   const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
+                                   int32_t num_splits, float *out, void *stream)
+{
+    // Every host-visible check runs first, against a stand-in workspace
+    // address that is replaced by the static workspace's before any launch;
+    // a plan that needs more than the static workspace is rejected here.
+    void *const stand_in = reinterpret_cast<void *>(static_cast<uintptr_t>(256));
+    fp4kv::DecodeArgs a;
+    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
+                           softmax_scale, num_splits, stand_in, fp4kv::kScratchBytes, &a);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    if (!out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(out, 16))
+        return FP4KV_ERR_MISALIGNED;
+    void *ws = nullptr;
+    if (fp4kv::scratch_for_current_device(&ws) != hipSuccess)
+        return FP4KV_ERR_HIP;
+    const ptrdiff_t ml_offset = reinterpret_cast<uint8_t *>(a.ws_ml) - static_cast<uint8_t *>(stand_in);
+    a.ws_o = static_cast<float *>(ws);
+    a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + ml_offset);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool direct = direct_output(&a, out);
     hipError_t e = fp4kv::launch_decode_split(a, st);

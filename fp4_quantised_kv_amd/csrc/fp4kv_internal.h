@@ -71,6 +71,12 @@ bool split_appends_itself(const DecodeArgs &a);
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,
                                  int32_t partials, int32_t head_dim, float *out, hipStream_t stream);
 
+// The device address of the library's static decode workspace
+// (kScratchBytes, 256-byte aligned) on the current device, looked up once
+// per device; for the entry point that allocates nothing.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+hipError_t scratch_for_current_device(void **out);
+
 // Streaming read of `blocks` 9216-byte blocks (measurement utility).
 hipError_t launch_read_probe(const uint8_t *buf, int64_t blocks, uint32_t *sink, hipStream_t stream);
 

@@ -14,6 +14,9 @@
  *   fp4kv_decode_plan       chooses the split count and workspace size.
  *   fp4kv_decode_attention  split-K decode attention over the packed cache,
  *                           dequantising on the fly.
+ *   fp4kv_decode_attention_noalloc
+ *                           the same with a static workspace, for callers
+ *                           that cannot allocate.
  *   fp4kv_decode_split,     its two halves: per-split partial results, and
  *   fp4kv_decode_combine    their merge.
  *   fp4kv_decode_append_attention, fp4kv_decode_append_split
@@ -29,9 +32,10 @@
  *   - Pointers marked "device" are HIP device memory; all others are host.
  *   - The caller owns every buffer.  The library allocates nothing, keeps no
  *     pointer after returning and holds no mutable global state, so calls
- *     are re-entrant.  Calls on one stream run in order; calls that write the
- *     same cache bytes, or use the same decode workspace, from different
- *     streams race.
+ *     are re-entrant; the one exception is the static workspace of
+ *     fp4kv_decode_attention_noalloc (see there).  Calls on one stream run in
+ *     order; calls that write the same cache bytes, or use the same decode
+ *     workspace, from different streams race.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
  *     stream) and the call returns without waiting.  Results are valid once
  *     the stream reaches them.
@@ -275,6 +279,31 @@ FP4KV_API int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void 
 
 FP4KV_API int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t partials,
                                    const void *workspace, int64_t workspace_bytes, float *out, void *stream);
+
+/* fp4kv_decode_attention without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc).  The partial results go to a static
+ * device array of FP4KV_NOALLOC_WORKSPACE_BYTES (32 MiB) that the library
+ * holds on every GPU it runs on until the process ends; the call itself
+ * allocates nothing.  The array's device address is looked up once per
+ * device, on the first call with that device current.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (different
+ * streams, or different threads without ordering) race; calls on one stream
+ * run in order.  Nothing in the array has to start at zero: each call
+ * overwrites what it reads.
+ *   stream       must belong to the current device (or be NULL).
+ *   other arguments and results as for fp4kv_decode_attention.
+ * Errors: as for fp4kv_decode_attention; WORKSPACE_TOO_SMALL (before any HIP
+ * call) when the plan for these arguments needs more than
+ * FP4KV_NOALLOC_WORKSPACE_BYTES, i.e. when fp4kv_decode_plan's
+ * *workspace_bytes_out exceeds it; HIP if the array's address cannot be
+ * looked up. */
+#define FP4KV_NOALLOC_WORKSPACE_BYTES (32ll << 20)
+FP4KV_API int fp4kv_decode_attention_noalloc(const fp4kv_cache_layout_t *layout, const void *cache,
+                                             const void *q, int32_t batch, int32_t num_q_heads,
+                                             const int32_t *seq_lens, const int32_t *page_table,
+                                             int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
+                                             float *out, void *stream);
 
 /* One decode step with its own token: for every sequence b with
  * seq_lens[b] >= 1, quantise the new K and V rows k_new[b], v_new[b] (as
