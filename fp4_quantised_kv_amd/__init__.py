@@ -18,7 +18,7 @@ import os
 __all__ = ["Fp4KVError", "CacheParams", "CacheLayout", "DecodePlan", "library", "cache_layout", "decode_plan",
            "quantize_append", "decode_attention", "decode_attention_noalloc", "decode_split", "decode_combine",
            "decode_append_attention", "decode_append_split", "decode_multi_attention",
-           "decode_window_plan", "decode_window_attention",
+           "decode_window_plan", "decode_window_attention", "DecodeOptions", "decode_with_options",
            "status_string", "PAGE_SIZE", "MAX_GROUP", "FORMAT_FP4_E2M1", "FORMAT_FP8_E4M3", "FORMAT_FP8_E4M3_TOKEN",
            "IntDims", "INT_PER_TOKEN", "INT_PER_CHANNEL", "INT_FP8_E4M3", "int_sizes", "int_quantize", "int_decode_plan",
            "int_decode_attention"]
@@ -90,6 +90,14 @@ class CacheLayout(ctypes.Structure):
         return self.params.format == FORMAT_FP8_E4M3_TOKEN
 
 
+class DecodeOptions(ctypes.Structure):
+    """fp4kv_decode_options: the split kernel and how partials are merged."""
+    _fields_ = [("kernel", ctypes.c_int32), ("merge", ctypes.c_int32)]
+
+
+DECODE_KERNELS = {"auto": 0, "mfma_staged": 1, "mfma_direct": 2, "valu": 3}
+DECODE_MERGES = {"auto": 0, "combine_kernel": 1}
+
 _LIB = None
 _P = ctypes.c_void_p
 
@@ -154,6 +162,11 @@ def library():
                                                     ctypes.c_int32, ctypes.c_float, ctypes.c_int32, _P,
                                                     ctypes.c_int64, _P, _P]
         L.fp4kv_decode_window_attention.restype = ctypes.c_int
+        L.fp4kv_decode_with_options.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, _P, _P, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_float, ctypes.c_int32, _P,
+                                                ctypes.c_int64, _P, ctypes.POINTER(DecodeOptions), _P]
+        L.fp4kv_decode_with_options.restype = ctypes.c_int
         L.fp4kv_read_probe.argtypes = [_P, ctypes.c_int64, _P, _P]
         L.fp4kv_read_probe.restype = ctypes.c_int
         L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
@@ -210,10 +223,22 @@ class DecodePlan(tuple):
     workspace_bytes = property(lambda self: self[2])
 
 
+_PLANS = {}
+
+
 def decode_plan(layout: CacheLayout, batch: int, num_q_heads: int, max_pages_per_seq: int,
                 num_splits: int = 0) -> DecodePlan:
     """Context chunks, partials per row and workspace bytes that
-    decode_attention uses for these arguments."""
+    decode_attention uses for these arguments (the library's answer, kept per
+    argument set: the plan is a pure function of them)."""
+    key = (bytes(layout), batch, num_q_heads, max_pages_per_seq, num_splits)
+    plan = _PLANS.get(key)
+    if plan is None:
+        plan = _PLANS[key] = _decode_plan(layout, batch, num_q_heads, max_pages_per_seq, num_splits)
+    return plan
+
+
+def _decode_plan(layout, batch, num_q_heads, max_pages_per_seq, num_splits):
     s = ctypes.c_int32()
     p = ctypes.c_int32()
     ws = ctypes.c_int64()
@@ -391,6 +416,16 @@ def decode_multi_attention(layout: CacheLayout, cache, q, seq_lens, page_table, 
 
 def decode_window_plan(layout: CacheLayout, batch: int, q_tokens: int, num_q_heads: int, max_pages_per_seq: int,
                        window: int, num_splits: int = 0) -> "DecodePlan":
+    """Plan of a multi-query / sliding-window call (kept per argument set)."""
+    key = ("window", bytes(layout), batch, q_tokens, num_q_heads, max_pages_per_seq, window, num_splits)
+    plan = _PLANS.get(key)
+    if plan is None:
+        plan = _PLANS[key] = _decode_window_plan(layout, batch, q_tokens, num_q_heads, max_pages_per_seq, window,
+                                                 num_splits)
+    return plan
+
+
+def _decode_window_plan(layout, batch, q_tokens, num_q_heads, max_pages_per_seq, window, num_splits):
     s, p, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
     _check("fp4kv_decode_window_plan", library().fp4kv_decode_window_plan(
         ctypes.byref(layout), batch, q_tokens, num_q_heads, max_pages_per_seq, window, num_splits,
@@ -433,6 +468,55 @@ def decode_window_attention(layout: CacheLayout, cache, q, seq_lens, page_table,
         ctypes.byref(layout), cache.data_ptr(), q.data_ptr(), B, S, Hq, seq_lens.data_ptr(),
         page_table.data_ptr(), max_pages, int(window), float(softmax_scale), num_splits, workspace.data_ptr(),
         workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def decode_with_options(layout: CacheLayout, cache, q, seq_lens, page_table, k_new=None, v_new=None, window=0,
+                        softmax_scale=None, num_splits: int = 0, workspace=None, out=None, kernel="auto",
+                        merge="auto", stream=None):
+    """fp4kv_decode_with_options: any decode call with an explicit split
+    kernel ("auto", "mfma_staged", "mfma_direct", "valu") and merge ("auto",
+    "combine_kernel").  q is bf16 [B][Hq][D] (one query token; the result is
+    [B][Hq][D]) or [B][S][Hq][D]; k_new, v_new (bf16 [B][H_kv][D]) append the
+    step's token first (one query token, no window)."""
+    import torch
+    _need(cache, "cache", torch.uint8)
+    _need(q, "q", torch.bfloat16)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_table, "page_table", torch.int32)
+    one = q.dim() == 3
+    B, S, Hq, D = (q.shape[0], 1, q.shape[1], q.shape[2]) if one else tuple(q.shape)
+    if D != layout.head_dim:
+        raise ValueError("q's last dimension must equal the cache head_dim")
+    if tuple(seq_lens.shape) != (B,) or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("seq_lens must be [B] and page_table [B][max_pages]")
+    if cache.numel() < layout.cache_bytes:
+        raise ValueError("cache is smaller than layout.cache_bytes")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _new_token_rows(layout, k_new, v_new, B)
+    max_pages = page_table.shape[1]
+    plan = decode_window_plan(layout, B, S, Hq, max_pages, window, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    shape = (B, Hq, D) if one else (B, S, Hq, D)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", torch.float32)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {list(shape)}")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    opts = DecodeOptions(DECODE_KERNELS[kernel], DECODE_MERGES[merge])
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check("fp4kv_decode_with_options", library().fp4kv_decode_with_options(
+        ctypes.byref(layout), cache.data_ptr(), ptr(k_new), ptr(v_new), q.data_ptr(), B, S, Hq,
+        seq_lens.data_ptr(), page_table.data_ptr(), max_pages, int(window), float(softmax_scale), num_splits,
+        workspace.data_ptr(), workspace.numel(), out.data_ptr(), ctypes.byref(opts), _stream(stream)))
     return out
 
 

@@ -6,8 +6,6 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 #include <limits>
 
 #include <hip/hip_runtime.h>
@@ -301,21 +299,130 @@ int prepare_append(void *cache, const void *k_new, const void *v_new, fp4kv::Dec
     return FP4KV_OK;
 }
 
-// With one partial per row the split kernel writes the final output itself
-// and no combine is launched (FP4KV_DECODE_COMBINE=separate keeps the
-// combine; the results are the same).
-bool direct_output(fp4kv::DecodeArgs *a, float *out)
-{
-    const char *v = std::getenv("FP4KV_DECODE_COMBINE");
-    if (a->partials != 1 || (v && std::strcmp(v, "separate") == 0))
-        return false;
-    a->out = out;
-    return true;
-}
-
 int64_t partial_o_bytes(int32_t batch, int32_t num_q_heads, int32_t partials, int32_t head_dim)
 {
     return round_up(static_cast<int64_t>(batch) * num_q_heads * partials * head_dim * 4, 256);
+}
+
+// The split kernel a call asks for (FP4KV_DECODE_KERNEL_AUTO: the default
+// for the cache), if it serves these arguments.
+int choose_kernel(const fp4kv::DecodeArgs &a, int32_t requested, fp4kv::SplitKernel *out)
+{
+    using fp4kv::SplitKernel;
+    const bool fp8 = a.geom.fp8;
+    switch (requested) {
+    case FP4KV_DECODE_KERNEL_AUTO:
+        *out = fp8 ? SplitKernel::fp8 : a.geom.head_dim == 128 ? SplitKernel::mfma_staged : SplitKernel::mfma_direct;
+        return FP4KV_OK;
+    case FP4KV_DECODE_KERNEL_MFMA_STAGED:
+        if (fp8 || a.geom.head_dim != 128)
+            return FP4KV_ERR_UNSUPPORTED;
+        *out = SplitKernel::mfma_staged;
+        return FP4KV_OK;
+    case FP4KV_DECODE_KERNEL_MFMA_DIRECT:
+        if (fp8)
+            return FP4KV_ERR_UNSUPPORTED;
+        *out = SplitKernel::mfma_direct;
+        return FP4KV_OK;
+    case FP4KV_DECODE_KERNEL_VALU:
+        if (fp8 || a.q_tokens > 1 || a.window > 0)
+            return FP4KV_ERR_UNSUPPORTED;
+        *out = SplitKernel::valu;
+        return FP4KV_OK;
+    default:
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    }
+}
+
+// How a call ends, fixed by its checks before any launch.
+struct Finish {
+    fp4kv::SplitKernel kernel;
+    bool combine;                // a combine kernel after the split kernel (else the split kernel writes out)
+};
+
+
+// Checks of `out` and of the options (null: defaults) for a call whose
+// split arguments are in `a`.
+int check_finish(const fp4kv::DecodeArgs &a, const float *out, const fp4kv_decode_options *opts, Finish *f)
+{
+    if (!out)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(out, 16))
+        return FP4KV_ERR_MISALIGNED;
+    const int32_t kernel = opts ? opts->kernel : FP4KV_DECODE_KERNEL_AUTO;
+    const int32_t merge = opts ? opts->merge : FP4KV_DECODE_MERGE_AUTO;
+    if (merge != FP4KV_DECODE_MERGE_AUTO && merge != FP4KV_DECODE_MERGE_COMBINE_KERNEL)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    const int rc = choose_kernel(a, kernel, &f->kernel);
+    if (rc != FP4KV_OK)
+        return rc;
+    // With one partial per row the split kernel writes the final rows itself
+    // (the combine's weight would be exactly 1) and no combine is launched.
+    f->combine = a.partials != 1 || merge == FP4KV_DECODE_MERGE_COMBINE_KERNEL;
+    return FP4KV_OK;
+}
+
+// The launches of a checked call.
+int run_decode(fp4kv::DecodeArgs &a, const Finish &f, float *out, hipStream_t st)
+{
+    a.out = f.combine ? nullptr : out;
+    hipError_t e = fp4kv::launch_decode_split(a, f.kernel, st);
+    if (e != hipSuccess)
+        return FP4KV_ERR_HIP;
+    if (!f.combine)
+        return FP4KV_OK;
+    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, a.batch, a.q_tokens * a.num_q_heads, a.partials,
+                                     a.geom.head_dim, out, st);
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
+// Every attention entry point: split arguments, the optional appended token,
+// then the finish.
+int decode_call(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new, const void *v_new, bool append,
+                const void *q, int32_t batch, int32_t q_tokens, int32_t num_q_heads, const int32_t *seq_lens,
+                const int32_t *page_table, int32_t max_pages_per_seq, int32_t window, float softmax_scale,
+                int32_t num_splits, void *workspace, int64_t workspace_bytes, float *out,
+                const fp4kv_decode_options *opts, void *stream)
+{
+    fp4kv::DecodeArgs a;
+    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
+                           softmax_scale, num_splits, workspace, workspace_bytes, &a, q_tokens, window);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    if (append) {
+        rc = prepare_append(cache, k_new, v_new, &a);
+        if (rc != FP4KV_OK)
+            return rc;
+    }
+    Finish f;
+    rc = check_finish(a, out, opts, &f);
+    if (rc != FP4KV_OK)
+        return rc;
+    return run_decode(a, f, out, static_cast<hipStream_t>(stream));
+}
+
+// The split kernel alone (partials left in the workspace).
+int split_call(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new, const void *v_new, bool append,
+               const void *q, int32_t batch, int32_t num_q_heads, const int32_t *seq_lens, const int32_t *page_table,
+               int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits, void *workspace,
+               int64_t workspace_bytes, void *stream)
+{
+    fp4kv::DecodeArgs a;
+    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
+                           softmax_scale, num_splits, workspace, workspace_bytes, &a);
+    if (rc != FP4KV_OK || batch == 0)
+        return rc;
+    if (append) {
+        rc = prepare_append(cache, k_new, v_new, &a);
+        if (rc != FP4KV_OK)
+            return rc;
+    }
+    fp4kv::SplitKernel kernel;
+    rc = choose_kernel(a, FP4KV_DECODE_KERNEL_AUTO, &kernel);
+    if (rc != FP4KV_OK)
+        return rc;
+    const hipError_t e = fp4kv::launch_decode_split(a, kernel, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
 
 }  // namespace
@@ -327,14 +434,8 @@ int fp4kv_decode_split(const fp4kv_cache_layout_t *layout, const void *cache, co
                        const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
                        int32_t num_splits, void *workspace, int64_t workspace_bytes, void *stream)
 {
-    fp4kv::DecodeArgs a;
-    const int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table,
-                                 max_pages_per_seq, softmax_scale, num_splits, workspace,
-                                 workspace_bytes, &a);
-    if (rc != FP4KV_OK || batch == 0)
-        return rc;
-    const hipError_t e = fp4kv::launch_decode_split(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+    return split_call(layout, const_cast<void *>(cache), nullptr, nullptr, false, q, batch, num_q_heads, seq_lens,
+                      page_table, max_pages_per_seq, softmax_scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 int fp4kv_decode_combine(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t partials,
@@ -369,26 +470,9 @@ int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache
                            float softmax_scale, int32_t num_splits, void *workspace,
                            int64_t workspace_bytes, float *out, void *stream)
 {
-    fp4kv::DecodeArgs a;
-    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table,
-                           max_pages_per_seq, softmax_scale, num_splits, workspace,
-                           workspace_bytes, &a);
-    if (rc != FP4KV_OK || batch == 0)
-        return rc;
-    if (!out)
-        return FP4KV_ERR_INVALID_ARGUMENT;
-    if (!aligned(out, 16))
-        return FP4KV_ERR_MISALIGNED;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool direct = direct_output(&a, out);
-    hipError_t e = fp4kv::launch_decode_split(a, st);
-    if (e != hipSuccess)
-        return FP4KV_ERR_HIP;
-    if (direct)
-        return FP4KV_OK;
-    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
-                                     out, st);
-    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+    return decode_call(layout, const_cast<void *>(cache), nullptr, nullptr, false, q, batch, 1, num_q_heads, seq_lens,
+                       page_table, max_pages_per_seq, 0, softmax_scale, num_splits, workspace, workspace_bytes, out,
+                       nullptr, stream);
 }
 
 int fp4kv_decode_attention_noalloc(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
@@ -405,26 +489,17 @@ int fp4kv_decode_attention_noalloc(const fp4kv_cache_layout_t *layout, const voi
                            softmax_scale, num_splits, stand_in, fp4kv::kScratchBytes, &a);
     if (rc != FP4KV_OK || batch == 0)
         return rc;
-    if (!out)
-        return FP4KV_ERR_INVALID_ARGUMENT;
-    if (!aligned(out, 16))
-        return FP4KV_ERR_MISALIGNED;
+    Finish f;
+    rc = check_finish(a, out, nullptr, &f);
+    if (rc != FP4KV_OK)
+        return rc;
     void *ws = nullptr;
     if (fp4kv::scratch_for_current_device(&ws) != hipSuccess)
         return FP4KV_ERR_HIP;
     const ptrdiff_t ml_offset = reinterpret_cast<uint8_t *>(a.ws_ml) - static_cast<uint8_t *>(stand_in);
     a.ws_o = static_cast<float *>(ws);
     a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + ml_offset);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool direct = direct_output(&a, out);
-    hipError_t e = fp4kv::launch_decode_split(a, st);
-    if (e != hipSuccess)
-        return FP4KV_ERR_HIP;
-    if (direct)
-        return FP4KV_OK;
-    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
-                                     out, st);
-    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+    return run_decode(a, f, out, static_cast<hipStream_t>(stream));
 }
 
 int fp4kv_decode_append_split(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,
@@ -433,16 +508,8 @@ int fp4kv_decode_append_split(const fp4kv_cache_layout_t *layout, void *cache, c
                               float softmax_scale, int32_t num_splits, void *workspace, int64_t workspace_bytes,
                               void *stream)
 {
-    fp4kv::DecodeArgs a;
-    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
-                           softmax_scale, num_splits, workspace, workspace_bytes, &a);
-    if (rc != FP4KV_OK || batch == 0)
-        return rc;
-    rc = prepare_append(cache, k_new, v_new, &a);
-    if (rc != FP4KV_OK)
-        return rc;
-    const hipError_t e = fp4kv::launch_decode_split(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+    return split_call(layout, cache, k_new, v_new, true, q, batch, num_q_heads, seq_lens, page_table,
+                      max_pages_per_seq, softmax_scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 int fp4kv_decode_append_attention(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,
@@ -451,28 +518,9 @@ int fp4kv_decode_append_attention(const fp4kv_cache_layout_t *layout, void *cach
                                   int32_t max_pages_per_seq, float softmax_scale, int32_t num_splits,
                                   void *workspace, int64_t workspace_bytes, float *out, void *stream)
 {
-    fp4kv::DecodeArgs a;
-    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
-                           softmax_scale, num_splits, workspace, workspace_bytes, &a);
-    if (rc != FP4KV_OK || batch == 0)
-        return rc;
-    rc = prepare_append(cache, k_new, v_new, &a);
-    if (rc != FP4KV_OK)
-        return rc;
-    if (!out)
-        return FP4KV_ERR_INVALID_ARGUMENT;
-    if (!aligned(out, 16))
-        return FP4KV_ERR_MISALIGNED;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool direct = direct_output(&a, out);
-    hipError_t e = fp4kv::launch_decode_split(a, st);
-    if (e != hipSuccess)
-        return FP4KV_ERR_HIP;
-    if (direct)
-        return FP4KV_OK;
-    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, num_q_heads, a.partials, layout->params.head_dim,
-                                     out, st);
-    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+    return decode_call(layout, cache, k_new, v_new, true, q, batch, 1, num_q_heads, seq_lens, page_table,
+                       max_pages_per_seq, 0, softmax_scale, num_splits, workspace, workspace_bytes, out, nullptr,
+                       stream);
 }
 
 int fp4kv_decode_multi_attention(const fp4kv_cache_layout_t *layout, const void *cache, const void *q,
@@ -481,25 +529,9 @@ int fp4kv_decode_multi_attention(const fp4kv_cache_layout_t *layout, const void 
                                  int32_t num_splits, void *workspace, int64_t workspace_bytes, float *out,
                                  void *stream)
 {
-    fp4kv::DecodeArgs a;
-    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
-                           softmax_scale, num_splits, workspace, workspace_bytes, &a, q_tokens);
-    if (rc != FP4KV_OK || batch == 0)
-        return rc;
-    if (!out)
-        return FP4KV_ERR_INVALID_ARGUMENT;
-    if (!aligned(out, 16))
-        return FP4KV_ERR_MISALIGNED;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool direct = direct_output(&a, out);
-    hipError_t e = fp4kv::launch_decode_split(a, st);
-    if (e != hipSuccess)
-        return FP4KV_ERR_HIP;
-    if (direct)
-        return FP4KV_OK;
-    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, q_tokens * num_q_heads, a.partials,
-                                     layout->params.head_dim, out, st);
-    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+    return decode_call(layout, const_cast<void *>(cache), nullptr, nullptr, false, q, batch, q_tokens, num_q_heads,
+                       seq_lens, page_table, max_pages_per_seq, 0, softmax_scale, num_splits, workspace,
+                       workspace_bytes, out, nullptr, stream);
 }
 
 int fp4kv_decode_window_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t q_tokens,
@@ -529,25 +561,24 @@ int fp4kv_decode_window_attention(const fp4kv_cache_layout_t *layout, const void
                                   float softmax_scale, int32_t num_splits, void *workspace,
                                   int64_t workspace_bytes, float *out, void *stream)
 {
-    fp4kv::DecodeArgs a;
-    int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
-                           softmax_scale, num_splits, workspace, workspace_bytes, &a, q_tokens, window);
-    if (rc != FP4KV_OK || batch == 0)
-        return rc;
-    if (!out)
-        return FP4KV_ERR_INVALID_ARGUMENT;
-    if (!aligned(out, 16))
-        return FP4KV_ERR_MISALIGNED;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool direct = direct_output(&a, out);
-    hipError_t e = fp4kv::launch_decode_split(a, st);
-    if (e != hipSuccess)
-        return FP4KV_ERR_HIP;
-    if (direct)
-        return FP4KV_OK;
-    e = fp4kv::launch_decode_combine(a.ws_o, a.ws_ml, batch, q_tokens * num_q_heads, a.partials,
-                                     layout->params.head_dim, out, st);
-    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+    return decode_call(layout, const_cast<void *>(cache), nullptr, nullptr, false, q, batch, q_tokens, num_q_heads,
+                       seq_lens, page_table, max_pages_per_seq, window, softmax_scale, num_splits, workspace,
+                       workspace_bytes, out, nullptr, stream);
+}
+
+int fp4kv_decode_with_options(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,
+                              const void *v_new, const void *q, int32_t batch, int32_t q_tokens,
+                              int32_t num_q_heads, const int32_t *seq_lens, const int32_t *page_table,
+                              int32_t max_pages_per_seq, int32_t window, float softmax_scale, int32_t num_splits,
+                              void *workspace, int64_t workspace_bytes, float *out,
+                              const fp4kv_decode_options *options, void *stream)
+{
+    const bool append = k_new || v_new;
+    if (append && (q_tokens != 1 || window != 0))
+        return FP4KV_ERR_UNSUPPORTED;
+    return decode_call(layout, cache, k_new, v_new, append, q, batch, q_tokens, num_q_heads, seq_lens, page_table,
+                       max_pages_per_seq, window, softmax_scale, num_splits, workspace, workspace_bytes, out, options,
+                       stream);
 }
 
 const char *fp4kv_status_string(int status)

@@ -404,6 +404,10 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
             const uint8_t *blk = a.cache + static_cast<int64_t>(pid) * g.page_stride + c.h * g.head_stride;
             stage_k(blk, so, kslots[wave]);
             stage_v(blk, so, vslots[wave]);
+        } else if (APPEND) {
+            // no first page: the page loop issues the next page's copy before
+            // its first wait, so the token's stores must complete here
+            wait_vmem_at_most<0>();
         }
         staged_pages<D>(kslots[wave], vslots[wave], a, so, lane, col, jj, c.h, c.p0, c.p1, c.len, shortfall, first,
                         c.ptab, ids, pid, qf, zscale, st);

@@ -55,18 +55,23 @@ hipError_t launch_split_mfma(const DecodeArgs &a, hipStream_t stream);
 // The FP8 cache's kernel (D = 128).
 hipError_t launch_split_fp8(const DecodeArgs &a, hipStream_t stream);
 
-// Chooses the kernel: the FP8 kernel for an FP8 cache; for FP4, matrix
-// cores with LDS staging for D = 128, unless
-// FP4KV_DECODE_KERNEL names another (valu: vector ALU; mfma_direct: matrix
-// cores with operands loaded straight into registers).
-hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
+// The split kernel of a decode call, chosen once per call by the host API:
+// the FP8 kernel for an FP8 cache; for FP4 the matrix-core kernel with LDS
+// staging (D = 128), the matrix-core kernel with operands loaded straight
+// into registers (any D; the D = 64 kernel), or the vector-ALU kernel (one
+// query token, no window).
+enum class SplitKernel { fp8, mfma_staged, mfma_direct, valu };
+
+// Launches the chosen split kernel, preceded by the append kernel when the
+// call appends the step's token (a.k_new set) and that kernel does not store
+// it itself.
+hipError_t launch_decode_split(const DecodeArgs &a, SplitKernel kernel, hipStream_t stream);
 
 // Places each sequence's k_new / v_new row at position seq_lens[b] - 1 (a
 // kernel of its own, for the decode kernels that do not append themselves).
 hipError_t launch_append_last(const DecodeArgs &a, hipStream_t stream);
-// True when launch_decode_split appends the step's token inside the split
-// kernel for these arguments.
-bool split_appends_itself(const DecodeArgs &a);
+// True when that split kernel appends the step's token itself.
+bool split_appends_itself(SplitKernel kernel);
 
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,
                                  int32_t partials, int32_t head_dim, float *out, hipStream_t stream);

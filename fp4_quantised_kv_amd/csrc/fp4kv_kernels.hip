@@ -12,8 +12,6 @@
 // of the nibble; E4M3 (OCP FN) scales, bias 7, largest finite 448, smallest
 // subnormal 2^-9.
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include <hip/hip_runtime.h>
 
@@ -287,7 +285,8 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(
 // The decode step's own token, for the split kernels that do not append it
 // themselves: one thread per (sequence, KV head, 16-channel block) places
 // k_new / v_new of sequence b at position seq_lens[b] - 1 through the page
-// table.  Empty sequences and out-of-range page ids are skipped.
+// table.  Empty sequences, lengths past the page table and out-of-range page
+// ids are skipped.
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) void append_last_kernel(DecodeArgs a)
 {
@@ -300,9 +299,8 @@ __global__ __launch_bounds__(256) void append_last_kernel(DecodeArgs a)
     const int64_t bh = idx / NB;                        // sequence * H_kv + head
     const int head = static_cast<int>(bh % g.num_kv_heads);
     const int b = static_cast<int>(bh / g.num_kv_heads);
-    int len = a.seq_lens[b];
-    len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
-    if (len == 0)
+    const int len = a.seq_lens[b];
+    if (len < 1 || len > a.max_pages * kPage)            // nothing to place, or a position past the table
         return;
     const int id = a.page_table[static_cast<int64_t>(b) * a.max_pages + (len - 1) / kPage];
     const int64_t slot = (id >= 0 && id < g.num_pages) ? static_cast<int64_t>(id) * kPage + (len - 1) % kPage : -1;
@@ -721,40 +719,22 @@ hipError_t launch_append_last(const DecodeArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-namespace {
-enum class SplitKernel { fp8, valu, mfma_staged, mfma_direct };
-
-SplitKernel split_kernel_for(const DecodeArgs &a)
+bool split_appends_itself(SplitKernel kernel)
 {
-    if (a.geom.fp8)
-        return SplitKernel::fp8;
-    const char *v = std::getenv("FP4KV_DECODE_KERNEL");
-    // the vector-ALU kernel takes one query token and no window
-    if (v && std::strcmp(v, "valu") == 0 && a.q_tokens <= 1 && a.window <= 0)
-        return SplitKernel::valu;
-    if (a.geom.head_dim == 64 || (v && std::strcmp(v, "mfma_direct") == 0))
-        return SplitKernel::mfma_direct;
-    return SplitKernel::mfma_staged;
-}
-}  // namespace
-
-bool split_appends_itself(const DecodeArgs &a)
-{
-    const SplitKernel k = split_kernel_for(a);
-    return k == SplitKernel::fp8 || k == SplitKernel::mfma_staged;
+    return kernel == SplitKernel::fp8 || kernel == SplitKernel::mfma_staged;
 }
 
-hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
+hipError_t launch_decode_split(const DecodeArgs &a, SplitKernel kernel, hipStream_t stream)
 {
     DecodeArgs m = a;
-    if (a.k_new && !split_appends_itself(a)) {
+    if (a.k_new && !split_appends_itself(kernel)) {
         const hipError_t e = launch_append_last(a, stream);
         if (e != hipSuccess)
             return e;
         m.k_new = m.v_new = nullptr;
         m.cache_w = nullptr;
     }
-    switch (split_kernel_for(m)) {
+    switch (kernel) {
     case SplitKernel::fp8:
         return launch_split_fp8(m, stream);
     case SplitKernel::valu:
@@ -762,10 +742,11 @@ hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream)
     case SplitKernel::mfma_direct:
         m.staged = false;
         return launch_split_mfma(m, stream);
-    default:
+    case SplitKernel::mfma_staged:
         m.staged = true;
         return launch_split_mfma(m, stream);
     }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_ml, int32_t batch, int32_t num_q_heads,

@@ -309,12 +309,16 @@ __device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, in
 // operations complete in issue order) already covers them, and the stores'
 // latency overlaps the first pages' copies.  Only this wave touches that
 // (page, KV head) block in the kernel.
+// A length past the page table (max_pages * 64) appends nothing: the
+// attention clamps it, but the token's position is not in the table.
 template <int D, bool FP8>
 __device__ __forceinline__ void append_if_last_chunk(const DecodeArgs &a, const Chunk &c, int lane)
 {
     const CacheGeom &g = a.geom;
     const int last = c.len - 1;
     if (last < 0 || last / kPage < c.p0 || last / kPage >= c.p1)
+        return;
+    if (a.seq_lens[c.b] > a.max_pages * kPage)
         return;
     const int id = c.ptab[last / kPage];
     if (id < 0 || id >= g.num_pages)

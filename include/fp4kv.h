@@ -26,6 +26,9 @@
  *                           several query tokens per sequence, causal.
  *   fp4kv_decode_window_plan, fp4kv_decode_window_attention
  *                           the same with a sliding window.
+ *   fp4kv_decode_with_options
+ *                           any of the above with an explicit kernel and
+ *                           merge choice (tests, measurements).
  *   fp4kv_status_string     text of a status code.
  *
  * Conventions for every call:
@@ -242,9 +245,8 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, MISALIGNED, WORKSPACE_TOO_SMALL,
  * HIP.  Equivalent to fp4kv_decode_split followed by fp4kv_decode_combine
  * on the same stream; with one partial per row (at most four chunks) the
- * split kernel writes `out` itself and no combine is launched (the
- * environment variable FP4KV_DECODE_COMBINE=separate launches the combine
- * anyway, for tests; the results are the same). */
+ * split kernel writes `out` itself and no combine is launched (the results
+ * are the same; fp4kv_decode_with_options can launch the combine anyway). */
 FP4KV_API int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const void *cache,
                            const void *q, int32_t batch, int32_t num_q_heads,
                            const int32_t *seq_lens, const int32_t *page_table,
@@ -322,7 +324,9 @@ FP4KV_API int fp4kv_decode_attention_noalloc(const fp4kv_cache_layout_t *layout,
  *   cache          device, as for the other calls, and written.
  *   k_new, v_new   device bf16 [batch][H_kv][D], 16-B aligned.
  *   other arguments as for fp4kv_decode_attention; seq_lens are the lengths
- *                  including the new token.  A sequence of length 0 appends
+ *                  including the new token.  A sequence of length 0, or of
+ *                  a length above max_pages_per_seq * 64 (whose position is
+ *                  not in the table; attention still clamps it), appends
  *                  nothing; an out-of-range page id skips the append (and,
  *                  as always, the page's tokens).  The page that receives a
  *                  sequence's token must not be shared with another
@@ -395,6 +399,45 @@ FP4KV_API int fp4kv_decode_window_attention(const fp4kv_cache_layout_t *layout, 
                                             const int32_t *page_table, int32_t max_pages_per_seq,
                                             int32_t window, float softmax_scale, int32_t num_splits,
                                             void *workspace, int64_t workspace_bytes, float *out, void *stream);
+
+/* Choices inside a decode call, for tests and measurements; the other
+ * entry points use FP4KV_DECODE_KERNEL_AUTO and FP4KV_DECODE_MERGE_AUTO.
+ * Every choice gives the same results within the attention tolerance, and
+ * the same split kernel gives the same bits whatever the merge. */
+enum fp4kv_decode_kernel {
+    FP4KV_DECODE_KERNEL_AUTO = 0,         /* FP8 cache: its kernel; FP4: MFMA_STAGED at D = 128, else MFMA_DIRECT */
+    FP4KV_DECODE_KERNEL_MFMA_STAGED = 1,  /* FP4, D = 128: matrix cores, pages staged through LDS */
+    FP4KV_DECODE_KERNEL_MFMA_DIRECT = 2,  /* FP4: matrix cores, operands loaded straight into registers */
+    FP4KV_DECODE_KERNEL_VALU = 3          /* FP4, one query token, no window: vector ALU only */
+};
+enum fp4kv_decode_merge {
+    FP4KV_DECODE_MERGE_AUTO = 0,          /* one partial per row: the split kernel writes out; else a combine */
+    FP4KV_DECODE_MERGE_COMBINE_KERNEL = 1 /* always a separate combine kernel */
+};
+typedef struct fp4kv_decode_options {
+    int32_t kernel;                       /* enum fp4kv_decode_kernel */
+    int32_t merge;                        /* enum fp4kv_decode_merge */
+} fp4kv_decode_options;
+
+/* Every decode entry point in one call, with explicit choices: append the
+ * step's token when k_new and v_new are given (both or neither; then
+ * q_tokens must be 1 and window 0), q_tokens query tokens per sequence,
+ * sliding window `window` (0: none), as fp4kv_decode_append_attention,
+ * fp4kv_decode_multi_attention and fp4kv_decode_window_attention describe.
+ * `options` (host; NULL: both AUTO) chooses the split kernel and whether a
+ * separate combine kernel merges the partials.  The workspace is sized by
+ * fp4kv_decode_window_plan for the same arguments (fp4kv_decode_plan when
+ * q_tokens = 1 and window = 0).
+ * Errors: as for those calls; INVALID_ARGUMENT for an unknown option value
+ * or only one of k_new, v_new; UNSUPPORTED for a kernel that does not serve
+ * the cache format, head size, query tokens or window, or an append with
+ * q_tokens > 1 or a window. */
+FP4KV_API int fp4kv_decode_with_options(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,
+                                        const void *v_new, const void *q, int32_t batch, int32_t q_tokens,
+                                        int32_t num_q_heads, const int32_t *seq_lens, const int32_t *page_table,
+                                        int32_t max_pages_per_seq, int32_t window, float softmax_scale,
+                                        int32_t num_splits, void *workspace, int64_t workspace_bytes, float *out,
+                                        const fp4kv_decode_options *options, void *stream);
 
 /* Measurement utility, not a step of the method: reads `bytes` of device
  * memory at `buf` (device) once with 16-byte loads and discards the data.

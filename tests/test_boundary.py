@@ -303,3 +303,33 @@ def test_window_rejects_negative_window():
     full = fk.decode_plan(big, 4, 32, 512, 0)
     win = fk.decode_window_plan(big, 4, 1, 32, 512, 256, 0)
     assert win.splits <= 6 < full.splits
+
+
+def test_decode_with_options_host_checks():
+    """fp4kv_decode_with_options refuses unknown option values, one of
+    k_new / v_new alone, an append with several query tokens or a window,
+    and kernels that do not serve the cache, before any HIP call."""
+    L = fk.cache_layout(2, 128, 64)
+    L8 = fk.cache_layout(2, 128, 64, format=fk.FORMAT_FP8_E4M3, k_scale=1.0, v_scale=1.0)
+    L64 = fk.cache_layout(2, 64, 64)
+    lib = fk.library()
+    ok = 0x10000
+    ws = fk.decode_window_plan(L, 2, 2, 8, 8, 0).workspace_bytes
+
+    def call(layout=L, kn=None, vn=None, qt=1, window=0, kernel=0, merge=0, opts=True):
+        o = fk.DecodeOptions(kernel, merge)
+        return lib.fp4kv_decode_with_options(ctypes.byref(layout), ok, kn, vn, ok, 2, qt, 8, ok, ok, 8, window,
+                                             ctypes.c_float(0.1), 0, ok, ws, ok,
+                                             ctypes.byref(o) if opts else None, None)
+
+    assert call(kernel=99) == fk.ERR_INVALID_ARGUMENT
+    assert call(kernel=-1) == fk.ERR_INVALID_ARGUMENT
+    assert call(merge=7) == fk.ERR_INVALID_ARGUMENT
+    assert call(kn=ok) == fk.ERR_INVALID_ARGUMENT                 # v_new missing
+    assert call(kn=ok, vn=ok, qt=2) == fk.ERR_UNSUPPORTED
+    assert call(kn=ok, vn=ok, window=64) == fk.ERR_UNSUPPORTED
+    assert call(kernel=3, qt=2) == fk.ERR_UNSUPPORTED             # vector-ALU kernel: one query token
+    assert call(kernel=3, window=64) == fk.ERR_UNSUPPORTED        # ... and no window
+    assert call(layout=L8, kernel=2) == fk.ERR_UNSUPPORTED        # FP8 has its own kernel only
+    assert call(layout=L64, kernel=1) == fk.ERR_UNSUPPORTED       # staged kernel: D = 128
+    assert call(kn=ok + 8, vn=ok) == fk.ERR_MISALIGNED

@@ -57,13 +57,13 @@ def _new_rows(kv, lens, Hkv, D, step=0):
     return torch.stack(rows_k), torch.stack(rows_v)
 
 
-def _unfused(L, cache, table, lens, kn, vn, q, splits):
+def _unfused(L, cache, table, lens, kn, vn, q, splits, kernel="auto"):
     slots = []
     for b, n in enumerate(lens):
         slots.append(int(wl.slots_for(table, b, n - 1, n)[0]) if n >= 1 else -1)
     fk.quantize_append(L, kn.cuda(), vn.cuda(), torch.tensor(slots, dtype=torch.int64).cuda(), cache)
-    return fk.decode_attention(L, cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), table.cuda(),
-                               num_splits=splits)
+    return fk.decode_with_options(L, cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), table.cuda(),
+                                  num_splits=splits, kernel=kernel)
 
 
 CASES = [("fp4", 128, None), ("fp4", 64, None), ("fp8", 128, None), ("fp8", 64, None), ("fp8t", 128, None),
@@ -73,18 +73,21 @@ LENS = [0, 1, 2, 63, 64, 65, 128, 129, 1000, 4097]
 
 @pytest.mark.parametrize("fmt,D,kernel", CASES)
 @pytest.mark.parametrize("G,splits", [(1, 0), (4, 1), (8, 3), (16, 0), (3, 1000)])
-def test_same_as_append_then_decode(fmt, D, kernel, G, splits, monkeypatch):
-    if kernel:
-        monkeypatch.setenv("FP4KV_DECODE_KERNEL", kernel)
+def test_same_as_append_then_decode(fmt, D, kernel, G, splits):
     Hkv = 2
     L, cache, table, kv, q = _setup(LENS, Hkv, G, D, fmt, seed=G * 7 + D + splits)
     kn, vn = _new_rows(kv, LENS, Hkv, D)
     ref_cache = cache.clone()
     _say(f"append+decode: {fmt} D {D} kernel {kernel or 'default'} G {G} splits {splits}")
     lens_d = torch.tensor(LENS, dtype=torch.int32).cuda()
-    out = fk.decode_append_attention(L, cache, kn.cuda(), vn.cuda(), q.cuda(), lens_d, table.cuda(),
-                                     num_splits=splits)
-    ref = _unfused(L, ref_cache, table, LENS, kn, vn, q, splits)
+    if kernel:
+        out = fk.decode_with_options(L, cache, q.cuda(), lens_d, table.cuda(), k_new=kn.cuda(), v_new=vn.cuda(),
+                                     num_splits=splits, kernel=kernel)
+        ref = _unfused(L, ref_cache, table, LENS, kn, vn, q, splits, kernel)
+    else:
+        out = fk.decode_append_attention(L, cache, kn.cuda(), vn.cuda(), q.cuda(), lens_d, table.cuda(),
+                                         num_splits=splits)
+        ref = _unfused(L, ref_cache, table, LENS, kn, vn, q, splits)
     torch.cuda.synchronize()
     assert torch.equal(cache, ref_cache)
     assert torch.equal(out, ref)
@@ -163,3 +166,56 @@ def test_skipped_page_and_empty_sequences():
     assert torch.equal(out, ref)
     assert not out[0].any()
 
+
+
+@pytest.mark.parametrize("fmt,kernel", [("fp4", "auto"), ("fp4", "valu"), ("fp8", "auto")])
+def test_dead_first_page_then_token_page(fmt, kernel):
+    """The chunk's first page id is out of range and the token's page is the
+    next one: the token's stores must land before that page is read.  One
+    chunk covers both pages (one split), so the page loop starts at the dead
+    page.  Bytes and output equal quantize_append + decode_attention."""
+    lens = [100, 90, 128]                               # positions 99, 89, 127: page 1 of each
+    Hkv, G, D = 2, 8, 128
+    L, cache, table, kv, q = _setup(lens, Hkv, G, D, fmt, seed=17)
+    table = table.clone()
+    table[:, 0] = -1                                    # every sequence's first page is skipped
+    kn, vn = _new_rows(kv, lens, Hkv, D)
+    ref_cache = cache.clone()
+    lens_d = torch.tensor(lens, dtype=torch.int32).cuda()
+    _say(f"append+decode with a dead first page: {fmt} kernel {kernel}")
+    out = fk.decode_with_options(L, cache, q.cuda(), lens_d, table.cuda(), k_new=kn.cuda(), v_new=vn.cuda(),
+                                 num_splits=1, kernel=kernel)
+    ref = _unfused(L, ref_cache, table, lens, kn, vn, q, 1, kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, ref_cache)
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("fmt,kernel", [("fp4", "auto"), ("fp4", "valu"), ("fp8", "auto"), ("fp8t", "auto")])
+def test_length_past_the_table_appends_nothing(fmt, kernel):
+    """seq_lens[b] above max_pages * 64: the token's position is not in the
+    table, so nothing is stored (the last valid token is not overwritten);
+    attention clamps the length, as decode_attention does."""
+    lens = [128, 70]
+    Hkv, G, D = 1, 4, 128
+    L, cache, table, kv, q = _setup(lens, Hkv, G, D, fmt, seed=23, extra=0)
+    assert table.shape[1] == 2                          # room for 128 tokens per sequence
+    # sequence 0 holds 127 tokens; fill its last slot so that an overwrite would show
+    fk.quantize_append(L, kv[0][0][127:128].cuda(), kv[0][1][127:128].cuda(),
+                       wl.slots_for(table, 0, 127, 128).cuda(), cache)
+    torch.cuda.synchronize()
+    kn = torch.randn(2, Hkv, D).to(torch.bfloat16) * 5
+    vn = torch.randn(2, Hkv, D).to(torch.bfloat16) * 5
+    before = cache.clone()
+    over = [129, 70]                                    # 129 > 2 * 64
+    _say(f"append+decode with a length past the table: {fmt} kernel {kernel}")
+    out = fk.decode_with_options(L, cache, q.cuda(), torch.tensor(over, dtype=torch.int32).cuda(), table.cuda(),
+                                 k_new=kn.cuda(), v_new=vn.cuda(), kernel=kernel)
+    ref_cache = before.clone()
+    slots = [-1, int(wl.slots_for(table, 1, 69, 70)[0])]
+    fk.quantize_append(L, kn.cuda(), vn.cuda(), torch.tensor(slots, dtype=torch.int64).cuda(), ref_cache)
+    ref = fk.decode_with_options(L, ref_cache, q.cuda(), torch.tensor([128, 70], dtype=torch.int32).cuda(),
+                                 table.cuda(), kernel=kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, ref_cache)
+    assert torch.equal(out, ref)

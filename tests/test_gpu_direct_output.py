@@ -4,7 +4,8 @@ When the plan gives one partial per row (contexts of at most four chunks),
 the decode entry points let the split kernel write the final output rows
 itself and launch no combine.  With one partial the combine's weight is
 exactly 1, so the rows must equal those of the split + combine path
-(FP4KV_DECODE_COMBINE=separate) for every kernel and entry point."""
+(fp4kv_decode_with_options with a separate combine kernel) for every kernel
+and entry point."""
 
 import pytest
 import torch
@@ -36,13 +37,12 @@ def _cache(fmt, lens, Hkv, D, seed):
     return L, cache, table.cuda()
 
 
-def _both(monkeypatch, fn):
-    monkeypatch.setenv("FP4KV_DECODE_COMBINE", "separate")
-    ref = fn()
+def _both(call, **kw):
+    """(default finish, split + combine kernel) of the same call."""
+    ref = fk.decode_with_options(*call, merge="combine_kernel", **kw)
     torch.cuda.synchronize()
     ref = ref.cpu()
-    monkeypatch.delenv("FP4KV_DECODE_COMBINE", raising=False)
-    got = fn()
+    got = fk.decode_with_options(*call, **kw)
     torch.cuda.synchronize()
     return got.cpu(), ref
 
@@ -62,11 +62,9 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_direct_output_equals_combine(monkeypatch, case):
+def test_direct_output_equals_combine(case):
     fmt, D, lens, Hkv, G, splits, kernel = CASES[case]
     _say(f"single partial: {CASES[case]}")
-    if kernel:
-        monkeypatch.setenv("FP4KV_DECODE_KERNEL", kernel)
     L, cache, pt = _cache(fmt, lens, Hkv, D, seed=400 + case)
     assert fk.decode_plan(L, len(lens), Hkv * G, pt.shape[1], splits).partials == 1
     g = torch.Generator().manual_seed(500 + case)
@@ -74,14 +72,18 @@ def test_direct_output_equals_combine(monkeypatch, case):
     sl = torch.tensor(lens, dtype=torch.int32).cuda()
     ws = torch.full((fk.decode_plan(L, len(lens), Hkv * G, pt.shape[1], splits).workspace_bytes,), 0xC3,
                     dtype=torch.uint8, device="cuda")
-    got, ref = _both(monkeypatch, lambda: fk.decode_attention(L, cache, q, sl, pt, num_splits=splits, workspace=ws))
+    got, ref = _both((L, cache, q, sl, pt), num_splits=splits, workspace=ws, kernel=kernel or "auto")
     assert torch.equal(got, ref)
+    if kernel is None:
+        plain = fk.decode_attention(L, cache, q, sl, pt, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(plain.cpu(), got)
     for b, n in enumerate(lens):
         if n == 0:
             assert torch.equal(got[b], torch.zeros_like(got[b]))     # an empty sequence gives zero rows
 
 
-def test_direct_output_multi_window_append(monkeypatch):
+def test_direct_output_multi_window_append():
     lens, Hkv, G, D = [3000, 65, 1500, 4096], 2, 4, 128
     L, cache, pt = _cache("fp4", lens, Hkv, D, seed=77)
     g = torch.Generator().manual_seed(78)
@@ -91,11 +93,29 @@ def test_direct_output_multi_window_append(monkeypatch):
     vn = torch.randn(len(lens), Hkv, D, generator=g).to(torch.bfloat16).cuda()
     sl = torch.tensor(lens, dtype=torch.int32).cuda()
     for splits in (1, 4):
-        got, ref = _both(monkeypatch, lambda: fk.decode_multi_attention(L, cache, q2, sl, pt, num_splits=splits))
+        got, ref = _both((L, cache, q2, sl, pt), num_splits=splits)
         assert torch.equal(got, ref), ("multi", splits)
-        got, ref = _both(monkeypatch, lambda: fk.decode_window_attention(L, cache, q2, sl, pt, 700,
-                                                                          num_splits=splits))
+        assert torch.equal(fk.decode_multi_attention(L, cache, q2, sl, pt, num_splits=splits).cpu(), got)
+        got, ref = _both((L, cache, q2, sl, pt), window=700, num_splits=splits)
         assert torch.equal(got, ref), ("window", splits)
-        got, ref = _both(monkeypatch, lambda: fk.decode_append_attention(L, cache, kn, vn, q1, sl, pt,
-                                                                          num_splits=splits))
+        assert torch.equal(fk.decode_window_attention(L, cache, q2, sl, pt, 700, num_splits=splits).cpu(), got)
+        got, ref = _both((L, cache, q1, sl, pt), k_new=kn, v_new=vn, num_splits=splits)
         assert torch.equal(got, ref), ("append", splits)
+        assert torch.equal(fk.decode_append_attention(L, cache, kn, vn, q1, sl, pt, num_splits=splits).cpu(), got)
+
+
+def test_options_are_checked():
+    """Kernels that do not serve the arguments are refused, before any launch."""
+    lens, Hkv, G, D = [300, 65], 2, 4, 128
+    L, cache, pt = _cache("fp4", lens, Hkv, D, seed=79)
+    L8, cache8, pt8 = _cache("fp8", lens, Hkv, D, seed=79)
+    q1 = torch.zeros(2, Hkv * G, D, dtype=torch.bfloat16, device="cuda")
+    q2 = torch.zeros(2, 2, Hkv * G, D, dtype=torch.bfloat16, device="cuda")
+    sl = torch.tensor(lens, dtype=torch.int32).cuda()
+    for args, kw in [((L, cache, q2, sl, pt), dict(kernel="valu")),              # several query tokens
+                     ((L, cache, q1, sl, pt), dict(kernel="valu", window=64)),    # a window
+                     ((L8, cache8, q1, sl, pt8), dict(kernel="mfma_direct")),    # an FP8 cache
+                     ((L8, cache8, q1, sl, pt8), dict(kernel="valu"))]:
+        with pytest.raises(fk.Fp4KVError) as e:
+            fk.decode_with_options(*args, **kw)
+        assert e.value.status == fk.ERR_UNSUPPORTED
