@@ -284,6 +284,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="paged workload: append with quantize_append, then decode (default: the decode "
                          "kernel stores the new tokens itself)")
+    ap.add_argument("--kernel", choices=("auto", "mfma_staged", "mfma_direct", "valu"),
+                    default="auto", help="split kernel of the timed steps (through fp4kv_decode_with_options "
+                                         "unless auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the streaming-read probe (the achievable HBM read rate for this access pattern)")
@@ -354,6 +357,14 @@ def main():
 
     def step_call(s):
         # one step through the library's entry point, as a caller makes it
+        if args.kernel != "auto":
+            if paged and not fused:
+                fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
+            kv = dict(k_new=news[s][0], v_new=news[s][1]) if paged and fused else {}
+            fk.decode_with_options(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
+                                   softmax_scale=scale, num_splits=splits_req, workspace=ws, out=out,
+                                   kernel=args.kernel, **kv)
+            return
         if paged and fused:
             fk.decode_append_attention(L, gc.cache, news[s][0], news[s][1], qs[s % len(qs)], lens_dev[s],
                                        gc.page_table, softmax_scale=scale, num_splits=splits_req, workspace=ws,
@@ -479,6 +490,7 @@ def main():
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "append": (None if not paged else "fused into the split kernel" if fused else "quantize_append"),
+        "kernel": args.kernel,
         "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
                       "decode_combine": round(t_comb, 5), "decode_split_back_to_back": round(t_split_b2b, 5)},
         "settle_decode_calls": SETTLE_CALLS,
