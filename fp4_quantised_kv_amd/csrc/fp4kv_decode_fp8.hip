@@ -325,6 +325,10 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
     const int ids = chunk_ids(a, c, lane);
     uint32_t qbits[kD / 8];
     load_q_bits<kD>(a, c.b, c.h, col, jj, qbits);
+    if (!a.out && group_chunks_empty(a, c, wave)) {     // every chunk of the workgroup past the context
+        mark_partial_empty(a, c.b, c.h, c.part);
+        return;
+    }
     half8_t qf[kD / 32];
     float zscale;
     make_q_operand<kD>(qbits, a.scale_log2e, qf, zscale);   // scale_log2e includes the K tensor's scale
@@ -378,6 +382,10 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8_d64(DecodeArgs
     const Chunk c = chunk_of(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
     uint32_t qbits[D / 8];
     load_q_bits<D>(a, c.b, c.h, col, jj, qbits);
+    if (!a.out && group_chunks_empty(a, c, wave)) {     // every chunk of the workgroup past the context
+        mark_partial_empty(a, c.b, c.h, c.part);
+        return;
+    }
     half8_t qf[D / 32];
     float zscale;
     make_q_operand<D>(qbits, a.scale_log2e, qf, zscale);

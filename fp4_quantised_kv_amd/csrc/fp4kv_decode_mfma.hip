@@ -384,6 +384,12 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     const int ids = STAGED ? chunk_ids(a, c, lane) : -1;
     uint32_t qbits[D / 8];
     load_q_bits<D>(a, c.b, c.h, col, jj, qbits);
+    // (the loads above are issued first so that they need not wait for the
+    // length; an empty workgroup leaves them unused)
+    if (!a.out && group_chunks_empty(a, c, wave)) {
+        mark_partial_empty(a, c.b, c.h, c.part);
+        return;
+    }
     half8_t qf[D / 32];
     float zscale;
     make_q_operand<D>(qbits, a.scale_log2e, qf, zscale);

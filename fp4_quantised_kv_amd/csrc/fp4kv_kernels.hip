@@ -539,12 +539,14 @@ __global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ 
             const float2 mj = ml[static_cast<int64_t>(j) * num_q_heads];
             const float w = mj.x == -INFINITY ? 0.0f : exp2f(mj.x - M);
             L = fmaf(mj.y, w, L);
+            // an empty partial's outputs are not meaningful (not written):
+            // a zero weight leaves the sums as they are
             if constexpr (CL == 2) {
                 const float2 x = *reinterpret_cast<const float2 *>(o + j * stride);
-                O[0] = fmaf(x.x, w, O[0]);
-                O[1] = fmaf(x.y, w, O[1]);
+                O[0] = w != 0.0f ? fmaf(x.x, w, O[0]) : O[0];
+                O[1] = w != 0.0f ? fmaf(x.y, w, O[1]) : O[1];
             } else {
-                O[0] = fmaf(o[j * stride], w, O[0]);
+                O[0] = w != 0.0f ? fmaf(o[j * stride], w, O[0]) : O[0];
             }
         }
     }
@@ -616,9 +618,11 @@ __global__ __launch_bounds__(256) void decode_combine_few(const float *__restric
     for (int j = 0; j < PM; ++j) {
         const float w = (j < partials && mj[j].x != -INFINITY) ? exp2f(mj[j].x - M) : 0.0f;
         L = fmaf(mj[j].y, w, L);
+        // an empty partial's outputs are not meaningful (not written): a
+        // zero weight leaves the sums as they are
 #pragma unroll
         for (int i = 0; i < CL; ++i)
-            O[i] = fmaf(x[j][i], w, O[i]);
+            O[i] = w != 0.0f ? fmaf(x[j][i], w, O[i]) : O[i];
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     if constexpr (CL == 2) {

@@ -286,6 +286,28 @@ __device__ __forceinline__ Chunk chunk_of(const DecodeArgs &a, int h, int b, int
     return c;
 }
 
+// True when all of the workgroup's chunks lie past the end of the context
+// (wave 0's chunk, the first of them, has no page): common in ragged batches,
+// where the split count follows the longest sequence.
+__device__ __forceinline__ bool group_chunks_empty(const DecodeArgs &a, const Chunk &c, int wave)
+{
+    return c.p0 - wave * a.pages_per_split >= (c.len + kPage - 1) / kPage;
+}
+
+// The partial of such a workgroup: its rows are marked empty (m = -inf,
+// l = 0), and their outputs are neither written nor read by the combine.
+// Call with every thread of the workgroup.
+__device__ __forceinline__ void mark_partial_empty(const DecodeArgs &a, int b, int h, int part)
+{
+    const int G = a.group;
+    const int S = a.q_tokens > 1 ? a.q_tokens : 1;
+    const int64_t row0 = (static_cast<int64_t>(b) * a.partials + part) * S * a.num_q_heads + static_cast<int64_t>(h) * G;
+    for (int q = threadIdx.x; q < S * G; q += kGroupThreads) {
+        const int64_t row = row0 + static_cast<int64_t>(q / G) * a.num_q_heads + q % G;
+        *reinterpret_cast<float2 *>(a.ws_ml + row * 2) = make_float2(-INFINITY, 0.0f);
+    }
+}
+
 // First token of the context the lane's query column sees (0 without a
 // window), for a column whose prefix ends `shortfall` tokens before len.
 __device__ __forceinline__ int column_first_token(const DecodeArgs &a, int len, int shortfall)

@@ -264,8 +264,10 @@ FP4KV_API int fp4kv_decode_attention(const fp4kv_cache_layout_t *layout, const v
  *   ml  fp32 [batch][P][num_q_heads][2]   at byte round_up(batch*P*num_q_heads*D*4, 256)
  * where P is the plan's partial count, m = max_t z_t over the partial's
  * tokens with z_t = log2(e) * softmax_scale * q.k_t, l = sum_t 2^(z_t - m)
- * and o = sum_t 2^(z_t - m) v_t.  A partial without tokens has m = -inf,
- * l = 0, o = 0.
+ * and o = sum_t 2^(z_t - m) v_t.  A partial without tokens has m = -inf and
+ * l = 0, and its o is unspecified (a workgroup whose chunks all lie past the
+ * end of its sequence writes only m and l); the combine gives such a partial
+ * weight 0 and never uses its o.
  *
  * fp4kv_decode_combine merges P such partials per (sequence, query head):
  *   out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M),  M = max_j m_j,

@@ -2,7 +2,8 @@
 
 The merge of split partials is the definition in include/fp4kv.h: with
 M = max_j m_j, out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M), zero where
-every partial is empty (m = -inf, l = 0, o = 0).  The library picks one of two
+every partial is empty (m = -inf, l = 0; an empty partial's o is not
+meaningful and must not reach the result, even when it holds NaN).  The library picks one of two
 kernels by the partial count (one wave per row up to 32 partials, a
 workgroup per row above), so the counts below straddle that boundary.  The
 reference is the same formula in float64.
@@ -43,7 +44,7 @@ def _reference(o, ml):
     return np.where(L[..., None] > 0, O / np.where(L > 0, L, 1.0)[..., None], 0.0)
 
 
-def _partials(rng, B, P, H, D, empty_frac):
+def _partials(rng, B, P, H, D, empty_frac, empty_o=0.0):
     m = rng.normal(0.0, 6.0, (B, P, H)).astype(np.float32)
     l = rng.uniform(0.5, 200.0, (B, P, H)).astype(np.float32)
     o = rng.normal(0.0, 30.0, (B, P, H, D)).astype(np.float32)
@@ -51,21 +52,24 @@ def _partials(rng, B, P, H, D, empty_frac):
     empty[0, :, 0] = True                                    # one row with no tokens at all
     m[empty] = -np.inf
     l[empty] = 0.0
-    o[empty] = 0.0
+    o[empty] = empty_o
     return o, np.stack([m, l], axis=-1)
 
 
+@pytest.mark.parametrize("empty_o", [0.0, float("nan"), float("inf")])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("P", [1, 2, 5, 16, 17, 31, 32, 33, 70])
-def test_combine_matches_definition(P, D):
+def test_combine_matches_definition(P, D, empty_o):
+    """Empty partials' outputs hold zeros, NaN or infinity (what an
+    unwritten workspace may hold): the result is the same."""
     rng = np.random.default_rng(1000 * P + D)
     B, H = 3, 5
-    o, ml = _partials(rng, B, P, H, D, empty_frac=0.3)
+    o, ml = _partials(rng, B, P, H, D, empty_frac=0.3, empty_o=empty_o)
     ws = _workspace(o, ml)
     out = fk.decode_combine(ws, B, H, D, P)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    ref = _reference(o, ml)
+    ref = _reference(np.where(np.isfinite(o), o, 0.0), ml)
     assert np.array_equal(got[0, 0], np.zeros(D))             # every partial empty -> zero row
     scale = np.abs(ref).max(axis=-1, keepdims=True)
     err = np.abs(got - ref) / np.where(scale > 0, scale, 1.0)
