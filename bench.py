@@ -1,28 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the FP4 KV-cache decode path on one MI355X.
 
-Default workload: 32 sequences of 32768 tokens, 64 query heads over 8 KV heads
-(group 8), head dim 128, 64 context splits -- 1.2 GB of packed cache, larger
-than the GPU's last-level cache, so every step streams it from HBM.  A step
-is one fp4kv_decode_attention call (split kernel + combine kernel; the split
-kernel alone when there is one partial per row); for the paged workload it is
-one fp4kv_decode_append_attention call, whose split kernel first stores each
-sequence's new token (--unfused: a separate quantize_append call, then
-decode_attention).  The per-kernel breakdown runs the same steps as their
-halves with events between launches.  The cache, the queries and every
-argument are resident on the device before timing starts.
+Headline workload: 32 sequences of 32768 tokens, 64 query heads over 8 KV
+heads (group 8), head dim 128, 64 context splits -- 1.2 GB of packed cache,
+larger than the GPU's last-level cache, so every step streams it from HBM.  A
+step is one fp4kv_decode_attention call (split kernel + combine kernel; the
+split kernel alone when there is one partial per row); for the paged
+workload it is one fp4kv_decode_append_attention call, whose split kernel
+first stores each sequence's new token (--unfused: a separate
+quantize_append call, then decode_attention).  The per-kernel breakdown runs
+the same steps as their halves with events between launches.  The cache, the
+queries and every argument are resident on the device before timing starts.
 
 Prints one JSON line: achieved HBM GB/s over the step's algorithmic bytes
 (packed K/V read, queries read, outputs written, page-table and length
-entries read), decode steps/s, the split kernel's roofline figures, and the
-CPU oracle's rate on a bounded sample of the same workload.
+entries read), decode steps/s, the split kernel's roofline figures, the
+achievable read rate (a sweep of streaming-read probes), the CPU oracle's
+rate on a bounded sample of the same workload, and under "configs" the same
+figures for the other workloads: the 256-token and 4096-token batches (cold
+and warm: their caches fit the last-level cache), the 512K-token sequence,
+the paged batch and the prefill quantise-append.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--splits S]
 """
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -33,6 +36,11 @@ sys.path.insert(0, ROOT)
 METRIC = "FP4-KV decode attention: achieved HBM GB/s (% of peak) and decode steps/s"
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E peak, GB/s
 SETTLE_CALLS = 100                          # untimed decode calls before the warm-up steps
+# The arithmetic of the decode path: dequantised K and V (exact in fp16) and
+# the query (times a power of two, exact) as fp16 matrix-core operands,
+# probabilities as two fp16 parts, fp32 accumulation and softmax.
+DTYPE = "f16 MFMA operands, f32 accumulate"
+LLC_BYTES = 256 << 20                       # MI355X last-level (Infinity) cache
 # sources of the split kernel (per cache format) whose HBM counters profiles/ may hold
 _CSRC = os.path.join(ROOT, "fp4_quantised_kv_amd", "csrc")
 KERNEL_SOURCES = {
@@ -43,6 +51,8 @@ KERNEL_SOURCES["fp8t"] = KERNEL_SOURCES["fp8"]
 FORMAT_NAMES = {"fp4": "fp4_e2m1_e4m3_per16", "fp8": "fp8_e4m3_per_tensor_scale",
                 "fp8t": "fp8_e4m3_per_token_fp16_scale"}
 PROFILES = os.path.join(ROOT, "profiles")
+# the other workloads reported under "configs"
+SUB_CONFIGS = ("tiny_d64_ctx256", "gqa4_b8_ctx4k", "gqa4_b1_ctx512k", "paged_b64_len1k_16k")
 
 
 def kernel_source_digest(fmt: str = "fp4") -> str:
@@ -75,6 +85,20 @@ def measured_traffic(workload: str, fmt: str = "fp4"):
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def oracle_threads() -> int:
+    """Threads for the oracle: the CPUs this process may run on, capped by the
+    per-GPU CPU share the environment states in OMP_NUM_THREADS, if set."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return max(1, min(avail, share) if share > 0 else avail)
 
 
 def cpu_baseline(w, seed, threads, fmt="fp4"):
@@ -130,15 +154,37 @@ def cpu_baseline(w, seed, threads, fmt="fp4"):
     tokens = sum(sample_lens[b] for b in seqs)
     per_number = {"fp4": 9 / 16, "fp8": 1.0, "fp8t": 1.0 + 2.0 / w.head_dim}[fmt]
     bytes_ = int(tokens * 2 * w.kv_heads * w.head_dim * per_number) + n_seq * w.q_heads * w.head_dim * 6
-    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    host = os.cpu_count()
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "threads": threads,
+            "host_cpus": host, "kind": "oracle",
             "sample": f"{n_seq} of {w.batch} sequences, {tokens} tokens, all {w.kv_heads} KV heads; "
-                      f"decode attention from the oracle's own codes in fp64, {dt:.2f} s wall"}
+                      f"decode attention from the oracle's own codes in fp64 on {threads} threads "
+                      f"(the CPUs given to this process; the host shows {host}), {dt:.2f} s wall"}
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _time(torch, stream, call, reps, warm=3):
+    """Average ms of `reps` back-to-back calls after `warm` untimed ones."""
+    for _ in range(warm):
+        call()
+    e0, e1 = _events(torch)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def prefill_append(fk, wl, seed, dev, stream, reps=10):
     """quantize_append of the prefill workload (8 sequences x 8192 tokens,
     H_kv 8, D 128, contiguous slots) as one call; bf16 K, V read + packed
-    bytes written, per call."""
+    bytes written + slots read, per call.  The kernel reads and writes HBM,
+    so its ceiling is a device copy, timed beside it."""
     import torch
     w = wl.WORKLOADS["prefill_b8_8k"]
     fkk, fvv = wl.channel_factors(w, seed, "k"), wl.channel_factors(w, seed, "v")
@@ -148,69 +194,17 @@ def prefill_append(fk, wl, seed, dev, stream, reps=10):
     layout = fk.cache_layout(w.kv_heads, w.head_dim, -(-n // 64))
     cache = torch.empty(layout.cache_bytes, dtype=torch.uint8, device=dev)
     slots = torch.arange(n, dtype=torch.int64, device=dev)
-    fk.quantize_append(layout, k, v, slots, cache)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        fk.quantize_append(layout, k, v, slots, cache)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ms = _time(torch, stream, lambda: fk.quantize_append(layout, k, v, slots, cache), reps)
     bytes_ = 2 * k.numel() * 2 + layout.cache_bytes + n * 8
-    return {"workload": w.name, "tokens": n, "ms": round(ms, 5), "gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
-            "algorithmic_bytes": bytes_}
-
-
-def cold_and_warm(fk, gc, w, seed, dev, stream, splits_req, step_bytes, reps=20):
-    """For a cache smaller than the 256 MB last-level cache: decode step
-    (one fp4kv_decode_attention call) time warm (back to back: the cache stays in the
-    last-level cache) and cold (1 GiB of unrelated data read and written
-    between calls, outside the timed events, so every call reads the cache
-    from HBM).  Steps this small take less GPU time than the host needs to
-    enqueue them, so both measurements queue their calls behind GPU work
-    that is still running (a spin kernel that touches no memory, or the
-    scrub) and time the GPU, not the host."""
-    import torch
-    B, Hq, D = w.batch, w.q_heads, w.head_dim
-    splits, partials, ws_bytes = fk.decode_plan(gc.layout, B, Hq, gc.page_table.shape[1], splits_req)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
-    import fp4kv_workloads as wl
-    q = wl.queries(w, seed).to(dev)
-    scrub = torch.zeros(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
-
-    def call():
-        fk.decode_attention(gc.layout, gc.cache, q, gc.seq_lens, gc.page_table, num_splits=splits_req,
-                            workspace=ws, out=out)
-
-    for _ in range(5):
-        call()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(2_000_000)                  # ~1 ms of GPU clock cycles while the calls are enqueued
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    warm = e0.elapsed_time(e1) / reps
-    cold = []
-    for _ in range(reps):
-        scrub.add_(1)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        call()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cold.append(c0.elapsed_time(c1))
-    cold_ms = sorted(cold)[len(cold) // 2]
-    del scrub
-    return {"cache_bytes": gc.layout.cache_bytes, "step_bytes": int(step_bytes),
-            "warm_ms": round(warm, 5), "warm_gbs": round(step_bytes / (warm * 1e-3) / 1e9, 1),
-            "cold_ms_median": round(cold_ms, 5), "cold_ms_min": round(min(cold), 5),
-            "cold_gbs": round(step_bytes / (cold_ms * 1e-3) / 1e9, 1),
-            "note": "warm: back-to-back steps; cold: 1 GiB scrubbed through the caches before each step"}
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    copy = copy_ceiling(dev, stream)
+    return {"workload": w.name, "tokens": n, "ms": round(ms, 5), "gbs": round(gbs, 1),
+            "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2), "algorithmic_bytes": bytes_,
+            "roofline": {"bound": "hbm", "kernel": "append_slices_kernel<128>", "achieved": round(gbs, 2),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": None, "algorithmic_bytes_per_launch": bytes_,
+                         "frac_of_device_copy": round(gbs / copy["gbs"], 4)},
+            "device_copy": copy}
 
 
 def copy_ceiling(dev, stream, nbytes=1 << 30, reps=10):
@@ -219,17 +213,277 @@ def copy_ceiling(dev, stream, nbytes=1 << 30, reps=10):
     import torch
     src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = _time(torch, stream, lambda: dst.copy_(src), reps)
+    return {"bytes_read_and_written": 2 * nbytes, "ms": round(ms, 5), "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def read_ceiling(fk, dev, stream, nbytes, reps=10):
+    """The achievable HBM read rate: streaming-read probes over a buffer of
+    about nbytes (larger than the last-level cache, read once per call),
+    swept over loads in flight per lane, workgroups and destination
+    (registers, or LDS as the decode kernels copy pages); the fastest is the
+    ceiling.  Also the library's fixed-shape read probe."""
+    import torch
+    nbytes = max(nbytes, 2 * LLC_BYTES) // 16384 * 16384
+    buf = torch.full((nbytes,), 1, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sweep = []
+    for to_lds in (False, True):
+        for loads in ((4, 8, 16) if not to_lds else (4, 8)):
+            for groups in (512, 1024, 2048, 4096):
+                ms = _time(torch, stream, lambda: fk.read_probe_config(buf, sink, loads, groups, to_lds), reps)
+                sweep.append({"dest": "lds" if to_lds else "regs", "loads_per_lane": loads, "workgroups": groups,
+                              "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+    fixed = buf[: nbytes // 9216 * 9216]
+    ms = _time(torch, stream, lambda: fk.read_probe(fixed, sink), reps)
+    fixed_gbs = round(fixed.numel() / (ms * 1e-3) / 1e9, 1)
+    best = max(sweep, key=lambda r: r["gbs"])
+    del buf, fixed
+    return {"kernel": "read_probe_regs / read_probe_lds: 16-byte non-temporal loads, one pass, grid-stride",
+            "bytes": nbytes, "gbs": best["gbs"], "pct_of_peak_hbm": round(100.0 * best["gbs"] / PEAK_HBM_GBS, 2),
+            "best": best, "fixed_shape_read_probe_gbs": fixed_gbs, "sweep": sweep}
+
+
+class DecodeRun:
+    """One decode workload's cache on the device, its per-step inputs and the
+    calls that make a step."""
+
+    def __init__(self, fk, hx, wl, w, seed, fmt, dev, n_steps, splits=None, unfused=False, kernel="auto"):
+        import torch
+        self.fk, self.w, self.fmt, self.dev = fk, w, fmt, dev
+        self.paged = w.kind == "paged"
+        self.fused = self.paged and not unfused
+        self.kernel = kernel
+        self.splits_req = w.splits if splits is None else splits
+        t_setup = time.perf_counter()
+        print(f"# building cache for {w.name}: {w.description}", file=sys.stderr, flush=True)
+        self.gc = gc = hx.build_cache(w, seed, extra_tokens=n_steps if self.paged else 0, zero=False, fmt=fmt)
+        print(f"# cache built in {time.perf_counter() - t_setup:.1f} s "
+              f"({gc.layout.cache_bytes / 1e9:.3f} GB)", file=sys.stderr, flush=True)
+        L = gc.layout
+        B, Hq, D = w.batch, w.q_heads, w.head_dim
+        self.splits, self.partials, ws_bytes = fk.decode_plan(L, B, Hq, gc.page_table.shape[1], self.splits_req)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+        self.lens0 = gc.lens_cpu.clone()
+        self.scale = D ** -0.5
+        # per-step inputs, all on the device before timing
+        self.qs = [wl.queries(w, seed, step=s if self.paged else 0).to(dev) for s in range(n_steps if self.paged else 1)]
+        if self.paged:
+            self.news, self.slots, self.lens_dev = [], [], []
+            for s in range(n_steps):
+                kn, vn = wl.new_tokens(w, seed, s)
+                sl = torch.stack([wl.slots_for(gc.pt_cpu.table, b, int(self.lens0[b]) + s,
+                                               int(self.lens0[b]) + s + 1)[0] for b in range(B)])
+                self.news.append((kn.to(dev), vn.to(dev)))
+                self.slots.append(sl.to(dev))
+                self.lens_dev.append((self.lens0 + s + 1).to(torch.int32).to(dev))
+        else:
+            self.lens_dev = [gc.seq_lens]
+
+    def q(self, s):
+        return self.qs[s % len(self.qs)]
+
+    def lens(self, s):
+        return self.lens_dev[s % len(self.lens_dev)]
+
+    def step(self, s):
+        """One step through the library's entry point, as a caller makes it."""
+        fk, gc, L = self.fk, self.gc, self.gc.layout
+        if self.paged and not self.fused:
+            fk.quantize_append(L, self.news[s][0], self.news[s][1], self.slots[s], gc.cache)
+        if self.kernel != "auto":
+            kv = dict(k_new=self.news[s][0], v_new=self.news[s][1]) if self.fused else {}
+            fk.decode_with_options(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
+                                   num_splits=self.splits_req, workspace=self.ws, out=self.out, kernel=self.kernel,
+                                   **kv)
+        elif self.fused:
+            fk.decode_append_attention(L, gc.cache, self.news[s][0], self.news[s][1], self.q(s), self.lens(s),
+                                       gc.page_table, softmax_scale=self.scale, num_splits=self.splits_req,
+                                       workspace=self.ws, out=self.out)
+        else:
+            fk.decode_attention(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
+                                num_splits=self.splits_req, workspace=self.ws, out=self.out)
+
+    def append(self, s):
+        if self.paged and not self.fused:
+            self.fk.quantize_append(self.gc.layout, self.news[s][0], self.news[s][1], self.slots[s], self.gc.cache)
+
+    def split(self, s, append=True):
+        """The split kernel of step s (storing the step's new tokens itself
+        when the step is fused and `append`)."""
+        fk, gc, L = self.fk, self.gc, self.gc.layout
+        if self.fused and append:
+            fk.decode_append_split(L, gc.cache, self.news[s][0], self.news[s][1], self.q(s), self.lens(s),
+                                   gc.page_table, softmax_scale=self.scale, num_splits=self.splits_req,
+                                   workspace=self.ws)
+        else:
+            fk.decode_split(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
+                            num_splits=self.splits_req, workspace=self.ws)
+
+    def combine(self):
+        w = self.w
+        self.fk.decode_combine(self.ws, w.batch, w.q_heads, w.head_dim, self.partials, out=self.out)
+
+    def split_bytes(self, ctx):
+        """Algorithmic bytes of one split-kernel launch over context lengths
+        `ctx`: packed K/V of every token, the queries, one page-table entry
+        per page and one length per sequence."""
+        L, w = self.gc.layout, self.w
+        return (sum(ctx) * L.bytes_per_token + w.batch * w.q_heads * w.head_dim * 2
+                + sum(-(-c // 64) for c in ctx) * 4 + w.batch * 4)
+
+    def split_kernel_name(self):
+        if self.fmt == "fp8":
+            return "decode_split_fp8"
+        if self.fmt == "fp8t":
+            return "decode_split_fp8 (per-token scales)"
+        return "decode_split_mfma<128, staged>" if self.w.head_dim == 128 else "decode_split_mfma<64>"
+
+
+def decode_record(torch, run, stream, steps, warmup):
+    """Time `steps` steps launched back to back (after a clock settle and
+    `warmup` untimed steps), then the same steps as their halves with events
+    between launches, then the split kernel alone back to back; returns the
+    step's rate, the breakdown and the split kernel's roofline block.  For a
+    cache larger than the last-level cache, so every step reads it from HBM."""
+    w = run.w
+    B, Hq, D = w.batch, w.q_heads, w.head_dim
+    # Clock settle, before the warm-up steps: the GPU reaches its steady
+    # clocks only after tens of milliseconds of load (100 decode calls take
+    # ~20 ms here; with 5 warm-up steps alone the first timed steps run ~8 %
+    # slower).  Decode only, so the paged cache is not changed.
+    for _ in range(SETTLE_CALLS):
+        run.split(0, append=False)
+        run.combine()
     torch.cuda.synchronize()
+    for s in range(warmup):
+        run.step(s)
+    torch.cuda.synchronize()
+    # the timed region: K steps with no event between their launches
+    t0 = time.perf_counter()
+    start, stop = _events(torch)
+    start.record(stream)
+    for s in range(warmup, warmup + steps):
+        run.step(s)
+    stop.record(stream)
+    host_enqueue = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / steps
+    # per-kernel breakdown: the same steps again (appends rewrite the same
+    # slots with the same bytes), with an event between launches
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i, s in enumerate(range(warmup, warmup + steps)):
+        ev[i][0].record(stream)
+        run.append(s)
+        ev[i][1].record(stream)
+        run.split(s)
+        ev[i][2].record(stream)
+        run.combine()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    t_append = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    t_split = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    t_comb = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    # the split kernel alone, launched back to back with no event between
+    # launches (over the last step's lengths): its average duration for the
+    # roofline figure
+    last = warmup + steps - 1
+    e0, e1 = _events(torch)
     e0.record(stream)
-    for _ in range(reps):
-        dst.copy_(src)
+    for _ in range(steps):
+        run.split(last, append=False)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return {"bytes_read_and_written": 2 * nbytes, "ms": round(ms, 5), "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+    t_split_b2b = e0.elapsed_time(e1) / steps
+
+    if run.paged:
+        ctx = [int(run.lens0[b]) + warmup + 1 for b in range(B)]   # mid-run lengths, +1 per step
+        step_split = run.split_bytes(ctx) + B * (steps - 1) / 2.0 * run.gc.layout.bytes_per_token
+        ctx_last = [int(run.lens0[b]) + warmup + steps for b in range(B)]
+    else:
+        ctx = ctx_last = [int(x) for x in run.lens0]
+        step_split = run.split_bytes(ctx)
+    step_bytes = step_split + B * Hq * D * 4
+    if run.paged:
+        step_bytes += B * w.kv_heads * D * 2 * 2 + B * run.gc.layout.bytes_per_token + B * 8
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    split_bytes_b2b = run.split_bytes(ctx_last)
+    split_gbs = split_bytes_b2b / (t_split_b2b * 1e-3) / 1e9
+    return {
+        "workload": w.name, "ms_per_step": round(ms_per_step, 5), "gbs": round(gbs, 2),
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2), "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+        "step_bytes": int(step_bytes), "splits": run.splits, "partials": run.partials,
+        "append": (None if not run.paged else "fused into the split kernel" if run.fused else "quantize_append"),
+        "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
+                      "decode_combine": round(t_comb, 5), "decode_split_back_to_back": round(t_split_b2b, 5)},
+        "host_enqueue_ms_per_step": round(1e3 * host_enqueue / steps, 5), "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": run.split_kernel_name(), "achieved": round(split_gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(w.name, run.fmt), "algorithmic_bytes_per_launch": int(split_bytes_b2b)},
+    }
+
+
+def cold_warm(torch, run, stream, reps=20):
+    """For a cache smaller than the last-level cache: the step (one
+    fp4kv_decode_attention call) cold (1 GiB of unrelated data read and
+    written between calls, outside the timed events, so every call reads the
+    cache from HBM; median of `reps`) and warm (back to back: the cache stays
+    in the last-level cache), and the split kernel alone cold for the
+    roofline block.  Steps this small take less GPU time than the host needs
+    to enqueue them, so the warm calls queue behind a spin kernel that
+    touches no memory and the cold ones behind the scrub: both time the GPU,
+    not the host."""
+    w = run.w
+    B, Hq, D = w.batch, w.q_heads, w.head_dim
+    ctx = [int(x) for x in run.lens0]
+    split_bytes = run.split_bytes(ctx)
+    step_bytes = split_bytes + B * Hq * D * 4
+    scrub = torch.zeros(1 << 28, dtype=torch.int32, device=run.dev)     # 1 GiB
+    for s in range(5):
+        run.step(s)
+    e0, e1 = _events(torch)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(2_000_000)                  # ~1 ms of GPU clock cycles while the calls are enqueued
+    e0.record(stream)
+    for s in range(reps):
+        run.step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) / reps
+
+    def cold(call):
+        times = []
+        for s in range(reps):
+            scrub.add_(1)
+            c0, c1 = _events(torch)
+            c0.record(stream)
+            call(s)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        return sorted(times)[len(times) // 2], min(times)
+
+    cold_ms, cold_min = cold(run.step)
+    split_ms, _ = cold(run.split)
+    del scrub
+    gbs = step_bytes / (cold_ms * 1e-3) / 1e9
+    split_gbs = split_bytes / (split_ms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "cache_bytes": run.gc.layout.cache_bytes, "step_bytes": int(step_bytes),
+        "splits": run.splits, "partials": run.partials,
+        "ms_per_step": round(cold_ms, 5), "gbs": round(gbs, 1), "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "decode_steps_per_s": round(1e3 / cold_ms, 2), "cold_ms_min": round(cold_min, 5),
+        "warm_ms": round(warm, 5), "warm_gbs": round(step_bytes / (warm * 1e-3) / 1e9, 1),
+        "warm_decode_steps_per_s": round(1e3 / warm, 2),
+        "roofline": {"bound": "hbm", "kernel": run.split_kernel_name(), "achieved": round(split_gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(w.name), "algorithmic_bytes_per_launch": int(split_bytes),
+                     "split_cold_ms_median": round(split_ms, 5)},
+        "note": "ms_per_step, gbs: cold (1 GiB scrubbed through the caches before each step, median of "
+                f"{reps}); warm_*: back-to-back steps with the cache in the last-level cache",
+    }
 
 
 def query_extras(fk, gc, w, dev, stream, splits_req, reps=20, window=4096):
@@ -253,16 +507,7 @@ def query_extras(fk, gc, w, dev, stream, splits_req, reps=20, window=4096):
         res = torch.empty(B, S_, Hq, D, dtype=torch.float32, device=dev)
         call = lambda: fk.decode_window_attention(L, gc.cache, qq, gc.seq_lens, gc.page_table, win,
                                                   num_splits=splits_req if win == 0 else 0, workspace=ws, out=res)
-        for _ in range(3):
-            call()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = _time(torch, stream, call, reps)
         tokens = [min(n, win + S_ - 1) if win else n for n in lens]
         bytes_ = sum(tokens) * L.bytes_per_token + B * S_ * Hq * D * (2 + 4) + sum(-(-t // 64) for t in tokens) * 4
         out[name] = {"q_tokens": S_, "window": win, "ms": round(ms, 5), "gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
@@ -276,7 +521,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa8_b32_ctx32k")
-    ap.add_argument("--splits", type=int, default=None, help="context splits (default: the workload's)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="context splits of the headline workload (default: the workload's)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--format", choices=("fp4", "fp8", "fp8t"), default="fp4",
                     help="cache format: FP4 E2M1 + E4M3 per 16 (default), FP8 E4M3 with per-tensor scales, "
@@ -289,9 +535,14 @@ def main():
                                          "unless auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true",
-                    help="skip the streaming-read probe (the achievable HBM read rate for this access pattern)")
+                    help="skip the streaming-read probe sweep (the achievable HBM read rate)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill quantise-append measurement (8 x 8192 tokens)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only, not the other workloads")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps of each other workload")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill quantise-append measurement (for profiling its kernel)")
     ap.add_argument("--extras", action="store_true",
                     help="also time several query tokens in one pass and sliding-window attention on the cache")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -316,218 +567,75 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.prefill_only:
+        print(json.dumps({"prefill_append": prefill_append(fk, wl, args.seed, dev, stream)}), flush=True)
+        return
 
     w = wl.WORKLOADS[args.workload]
     if w.kind == "prefill":
-        raise SystemExit("the prefill workload is timed by its own test, not as a decode step")
-    splits_req = w.splits if args.splits is None else args.splits
-    paged = w.kind == "paged"
-    total_steps = args.warmup + args.steps
-    t_setup = time.perf_counter()
-    print(f"# building cache for {w.name}: {w.description}", file=sys.stderr, flush=True)
-    gc = hx.build_cache(w, args.seed, extra_tokens=total_steps if paged else 0, zero=False, fmt=args.format)
-    print(f"# cache built in {time.perf_counter() - t_setup:.1f} s "
-          f"({gc.layout.cache_bytes / 1e9:.3f} GB)", file=sys.stderr, flush=True)
-    L = gc.layout
-    B, Hq, D = w.batch, w.q_heads, w.head_dim
-    max_pages = gc.page_table.shape[1]
-    splits, partials, ws_bytes = fk.decode_plan(L, B, Hq, max_pages, splits_req)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
-    lens0 = gc.lens_cpu.clone()
-
-    # per-step inputs, all on the device before timing
-    qs = [wl.queries(w, args.seed, step=s if paged else 0).to(dev) for s in range(total_steps if paged else 1)]
-    if paged:
-        news, slots, lens_dev = [], [], []
-        for s in range(total_steps):
-            kn, vn = wl.new_tokens(w, args.seed, s)
-            sl = torch.stack([wl.slots_for(gc.pt_cpu.table, b, int(lens0[b]) + s, int(lens0[b]) + s + 1)[0]
-                              for b in range(B)])
-            news.append((kn.to(dev), vn.to(dev)))
-            slots.append(sl.to(dev))
-            lens_dev.append((lens0 + s + 1).to(torch.int32).to(dev))
-    else:
-        lens_dev = [gc.seq_lens]
-    scale = D ** -0.5
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total_steps)]
-
-    fused = paged and not args.unfused
-
-    def step_call(s):
-        # one step through the library's entry point, as a caller makes it
-        if args.kernel != "auto":
-            if paged and not fused:
-                fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
-            kv = dict(k_new=news[s][0], v_new=news[s][1]) if paged and fused else {}
-            fk.decode_with_options(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
-                                   softmax_scale=scale, num_splits=splits_req, workspace=ws, out=out,
-                                   kernel=args.kernel, **kv)
-            return
-        if paged and fused:
-            fk.decode_append_attention(L, gc.cache, news[s][0], news[s][1], qs[s % len(qs)], lens_dev[s],
-                                       gc.page_table, softmax_scale=scale, num_splits=splits_req, workspace=ws,
-                                       out=out)
-            return
-        if paged:
-            fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
-        fk.decode_attention(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
-                            softmax_scale=scale, num_splits=splits_req, workspace=ws, out=out)
-
-    def step(s, e=None):
-        """The same step as its halves (split kernel, then combine), with
-        events between the launches for the per-kernel breakdown."""
-        if e is not None:
-            e[0].record(stream)
-        if paged and not fused:
-            fk.quantize_append(L, news[s][0], news[s][1], slots[s], gc.cache)
-        if e is not None:
-            e[1].record(stream)
-        if fused:
-            # the split kernel stores each sequence's new token itself
-            fk.decode_append_split(L, gc.cache, news[s][0], news[s][1], qs[s % len(qs)], lens_dev[s],
-                                   gc.page_table, softmax_scale=scale, num_splits=splits_req, workspace=ws)
-        else:
-            fk.decode_split(L, gc.cache, qs[s % len(qs)], lens_dev[s % len(lens_dev)], gc.page_table,
-                            softmax_scale=scale, num_splits=splits_req, workspace=ws)
-        if e is not None:
-            e[2].record(stream)
-        fk.decode_combine(ws, B, Hq, D, partials, out=out)
-        if e is not None:
-            e[3].record(stream)
-
-    # Clock settle, before the warm-up steps: the GPU reaches its steady
-    # clocks only after tens of milliseconds of load (100 decode calls take
-    # ~20 ms here; with 5 warm-up steps alone the first timed steps run ~8 %
-    # slower).  Decode only, so the paged cache is not changed.
-    for _ in range(SETTLE_CALLS):
-        fk.decode_split(L, gc.cache, qs[0], gc.seq_lens, gc.page_table, softmax_scale=scale,
-                        num_splits=splits_req, workspace=ws)
-        fk.decode_combine(ws, B, Hq, D, partials, out=out)
-    torch.cuda.synchronize()
-    for s in range(args.warmup):
-        step_call(s)
-    torch.cuda.synchronize()
-    # the timed region: K steps with no event between their launches
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for s in range(args.warmup, total_steps):
-        step_call(s)
-    stop.record(stream)
-    host_enqueue = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-
-    # per-kernel breakdown: the same steps again (appends rewrite the same
-    # slots with the same bytes), with an event between launches
-    for s in range(args.warmup, total_steps):
-        step(s, ev[s])
-    torch.cuda.synchronize()
-    timed = ev[args.warmup:]
-    t_append = sum(e[0].elapsed_time(e[1]) for e in timed) / args.steps
-    t_split = sum(e[1].elapsed_time(e[2]) for e in timed) / args.steps
-    t_comb = sum(e[2].elapsed_time(e[3]) for e in timed) / args.steps
-
-    # the split kernel alone, launched back to back with no event between
-    # launches: its average duration for the roofline figure
-    last = total_steps - 1
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        fk.decode_split(L, gc.cache, qs[last % len(qs)], lens_dev[last % len(lens_dev)], gc.page_table,
-                        softmax_scale=scale, num_splits=splits_req, workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_split_b2b = e0.elapsed_time(e1) / args.steps
-
-    # algorithmic bytes
-    if paged:
-        ctx = [int(lens0[b]) + args.warmup + 1 for b in range(B)]   # mid-run lengths, +1 per step
-        ctx_tokens = sum(ctx) + B * (args.steps - 1) / 2.0
-    else:
-        ctx = [int(x) for x in lens0]
-        ctx_tokens = float(sum(ctx))
-    pages_read = sum(-(-c // 64) for c in ctx)
-    cache_read = ctx_tokens * L.bytes_per_token
-    split_bytes = cache_read + B * Hq * D * 2 + pages_read * 4 + B * 4
-    step_bytes = split_bytes + B * Hq * D * 4
-    if paged:
-        step_bytes += B * w.kv_heads * D * 2 * 2 + B * L.bytes_per_token + B * 8
-    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # the back-to-back launches all attend over the last step's lengths
-    if paged:
-        ctx_last = [int(lens0[b]) + total_steps for b in range(B)]
-        split_bytes_b2b = (sum(ctx_last) * L.bytes_per_token + B * Hq * D * 2
-                           + sum(-(-c // 64) for c in ctx_last) * 4 + B * 4)
-    else:
-        split_bytes_b2b = split_bytes
-    split_gbs = split_bytes_b2b / (t_split_b2b * 1e-3) / 1e9
-    traffic = measured_traffic(w.name, args.format)
-
+        raise SystemExit("the prefill workload is timed under configs (or alone with --prefill-only), "
+                         "not as a decode step")
+    run = DecodeRun(fk, hx, wl, w, args.seed, args.format, dev, args.warmup + args.steps, splits=args.splits,
+                    unfused=args.unfused, kernel=args.kernel)
+    head = decode_record(torch, run, stream, args.steps, args.warmup)
+    L = run.gc.layout
     result = {
         "metric": METRIC,
-        "value": round(gbs, 2),
+        "value": head["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": w.kv_heads,
-                   "head_dim": D, "context": w.context if not paged else f"{w.min_len}..{w.max_len}",
-                   "format": FORMAT_NAMES[args.format],
-                   "splits": splits, "partials": partials, "page_size": 64,
-                   "cache_bytes": L.cache_bytes},
-        "decode_steps_per_s": round(1e3 / ms_per_step, 2),
-        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "append": (None if not paged else "fused into the split kernel" if fused else "quantize_append"),
-        "kernel": args.kernel,
-        "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
-                      "decode_combine": round(t_comb, 5), "decode_split_back_to_back": round(t_split_b2b, 5)},
-        "settle_decode_calls": SETTLE_CALLS,
-        "wall_s_timed": round(wall, 4),
-        "host_enqueue_ms_per_step": round(1e3 * host_enqueue / args.steps, 5),
-        "roofline": {"bound": "hbm",
-                     "kernel": ("decode_split_fp8" if args.format == "fp8" else
-                                "decode_split_fp8 (per-token scales)" if args.format == "fp8t" else
-                                "decode_split_mfma<128, staged>" if D == 128 else "decode_split_mfma<64>"),
-                     "achieved": round(split_gbs, 2),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(split_bytes_b2b)},
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "context": w.context if not run.paged else f"{w.min_len}..{w.max_len}",
+                   "format": FORMAT_NAMES[args.format], "splits": run.splits, "partials": run.partials,
+                   "page_size": 64, "cache_bytes": L.cache_bytes},
     }
-    if not args.no_prefill:
-        result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)
-        result["prefill_append"]["device_copy"] = copy_ceiling(dev, stream)
-    if L.cache_bytes < (256 << 20) and not paged:
-        result["cold_warm"] = cold_and_warm(fk, gc, w, args.seed, dev, stream, splits_req, step_bytes)
-    if args.extras and not paged:
-        result["extras"] = query_extras(fk, gc, w, dev, stream, splits_req)
+    result.update({k: head[k] for k in ("decode_steps_per_s", "pct_of_peak_hbm", "append")})
+    result["kernel"] = args.kernel
+    result.update({k: head[k] for k in ("kernel_ms", "wall_s_timed", "host_enqueue_ms_per_step")})
+    result["settle_decode_calls"] = SETTLE_CALLS
+    result["roofline"] = head["roofline"]
+    if args.extras and not run.paged:
+        result["extras"] = query_extras(fk, run.gc, w, dev, stream, run.splits_req)
+    if L.cache_bytes < LLC_BYTES and not run.paged:
+        result["cold_warm"] = cold_warm(torch, run, stream)
+    cache_bytes = L.cache_bytes
+    del run
+    torch.cuda.empty_cache()
     if not args.no_read_probe:
-        # the achievable read rate: the cache's size in 9216-byte blocks,
-        # streamed once by the library's read probe
-        buf = torch.full((L.cache_bytes // 9216 * 9216,), 1, dtype=torch.uint8, device=dev)
-        sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        for _ in range(3):
-            fk.read_probe(buf, sink)
-        e0.record(stream)
-        for _ in range(10):
-            fk.read_probe(buf, sink)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        result["hbm_read_probe"] = {"kernel": "read_probe: 16-byte loads, one 9216-byte block per wave",
-                                    "bytes": buf.numel(),
-                                    "gbs": round(buf.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
-        result["roofline"]["frac_of_read_probe"] = round(split_gbs / result["hbm_read_probe"]["gbs"], 4)
-        del buf
+        ceiling = read_ceiling(fk, dev, stream, cache_bytes)
+        result["hbm_read_probe"] = ceiling
+        result["roofline"]["frac_of_read_probe"] = round(result["roofline"]["achieved"] / ceiling["gbs"], 4)
+        result["frac_of_read_probe"] = round(head["gbs"] / ceiling["gbs"], 4)
+        torch.cuda.empty_cache()
+    if not args.no_configs:
+        configs = {}
+        for name in SUB_CONFIGS:
+            if name == w.name:
+                continue
+            cw = wl.WORKLOADS[name]
+            r = DecodeRun(fk, hx, wl, cw, args.seed, "fp4", dev, args.warmup + args.config_steps)
+            if r.gc.layout.cache_bytes < LLC_BYTES and not r.paged:
+                configs[name] = cold_warm(torch, r, stream)
+            else:
+                configs[name] = decode_record(torch, r, stream, args.config_steps, args.warmup)
+            del r
+            torch.cuda.empty_cache()
+        if not args.no_prefill:
+            configs["prefill_b8_8k"] = prefill_append(fk, wl, args.seed, dev, stream)
+            torch.cuda.empty_cache()
+        result["configs"] = configs
+    elif not args.no_prefill:
+        result["prefill_append"] = prefill_append(fk, wl, args.seed, dev, stream)
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -537,8 +645,7 @@ def main():
         result["calibration_copy_bytes"] = src.numel()
         del src, dst
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        result["cpu_baseline"] = cpu_baseline(w, args.seed, threads, args.format)
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, oracle_threads(), args.format)
     print(json.dumps(result), flush=True)
 
 

@@ -169,6 +169,9 @@ def library():
         L.fp4kv_decode_with_options.restype = ctypes.c_int
         L.fp4kv_read_probe.argtypes = [_P, ctypes.c_int64, _P, _P]
         L.fp4kv_read_probe.restype = ctypes.c_int
+        L.fp4kv_read_probe_config.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              _P, _P]
+        L.fp4kv_read_probe_config.restype = ctypes.c_int
         L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         L.fp4kv_int_sizes.restype = ctypes.c_int
@@ -585,6 +588,18 @@ def read_probe(buf, sink, stream=None):
     _need(sink, "sink", torch.int32)
     _check("fp4kv_read_probe", library().fp4kv_read_probe(buf.data_ptr(), buf.numel(), sink.data_ptr(),
                                                           _stream(stream)))
+
+
+def read_probe_config(buf, sink, loads_per_lane: int, workgroups: int, to_lds: bool = False, stream=None):
+    """Measurement utility: the read probe with a chosen shape (see
+    fp4kv_read_probe_config); `buf` uint8, a multiple of 1024 * loads_per_lane
+    bytes."""
+    import torch
+    _need(buf, "buf", torch.uint8)
+    _need(sink, "sink", torch.int32)
+    _check("fp4kv_read_probe_config", library().fp4kv_read_probe_config(
+        buf.data_ptr(), buf.numel(), int(loads_per_lane), int(workgroups), int(bool(to_lds)), sink.data_ptr(),
+        _stream(stream)))
 
 
 # ------------------------------------------- integer formats (include/fp4kv_int.h)

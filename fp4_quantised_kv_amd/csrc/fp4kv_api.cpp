@@ -606,6 +606,24 @@ int fp4kv_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *strea
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
 
+int fp4kv_read_probe_config(const void *buf, int64_t bytes, int32_t loads_per_lane, int32_t workgroups,
+                            int32_t to_lds, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink || bytes <= 0 || workgroups < 1 || (to_lds != 0 && to_lds != 1))
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8 &&
+        loads_per_lane != 16)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (bytes % (1024 * static_cast<int64_t>(loads_per_lane)) != 0)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(buf, 1024) || !aligned(sink, 4))
+        return FP4KV_ERR_MISALIGNED;
+    const hipError_t e = fp4kv::launch_read_probe_config(static_cast<const uint8_t *>(buf), bytes, loads_per_lane,
+                                                         workgroups, to_lds != 0, sink,
+                                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
 int fp4kv_version(void) { return 100; }
 
 }  // extern "C"

@@ -84,6 +84,10 @@ hipError_t scratch_for_current_device(void **out);
 
 // Streaming read of `blocks` 9216-byte blocks (measurement utility).
 hipError_t launch_read_probe(const uint8_t *buf, int64_t blocks, uint32_t *sink, hipStream_t stream);
+// The configurable read probes (loads_per_lane 1, 2, 4, 8 or 16; bytes a
+// multiple of 1024 * loads_per_lane).
+hipError_t launch_read_probe_config(const uint8_t *buf, int64_t bytes, int loads_per_lane, int workgroups,
+                                    bool to_lds, uint32_t *sink, hipStream_t stream);
 
 // Integer formats of the bit-width sweep (fp4kv_int.hip).
 struct IntQuantArgs {

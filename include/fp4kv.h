@@ -452,6 +452,19 @@ FP4KV_API int fp4kv_decode_with_options(const fp4kv_cache_layout_t *layout, void
  * MISALIGNED before any HIP call, or FP4KV_ERR_HIP. */
 FP4KV_API int fp4kv_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
 
+/* Measurement utility, not a step of the method: the same one-pass read of
+ * `bytes` at `buf` with a chosen shape, to find the achievable read rate.
+ * Each wave reads whole stretches of 64 * 16 * loads_per_lane bytes (16-byte
+ * non-temporal loads, loads_per_lane of them per lane in flight together)
+ * in a grid-stride loop over `workgroups` workgroups of four waves, into
+ * registers (to_lds = 0) or straight into LDS (to_lds = 1, as the decode
+ * kernels copy pages).  loads_per_lane is 1, 2, 4, 8 or 16; `bytes` a
+ * positive multiple of 1024 * loads_per_lane; `buf` 1024-byte aligned; `sink`
+ * as for fp4kv_read_probe.  Returns FP4KV_OK, or INVALID_ARGUMENT /
+ * MISALIGNED before any HIP call, or FP4KV_ERR_HIP. */
+FP4KV_API int fp4kv_read_probe_config(const void *buf, int64_t bytes, int32_t loads_per_lane, int32_t workgroups,
+                                      int32_t to_lds, uint32_t *sink, void *stream);
+
 /* Static text for a status code (never NULL). */
 FP4KV_API const char *fp4kv_status_string(int status);
 

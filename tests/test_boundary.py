@@ -206,6 +206,14 @@ def test_read_probe_host_checks():
     assert lib.fp4kv_read_probe(ok, 9216, None, None) == fk.ERR_INVALID_ARGUMENT
     assert lib.fp4kv_read_probe(ok + 16, 9216, ok, None) == fk.ERR_MISALIGNED
     assert lib.fp4kv_read_probe(ok, 9216, ok + 2, None) == fk.ERR_MISALIGNED
+    cfg = lib.fp4kv_read_probe_config
+    assert cfg(None, 16384, 16, 256, 0, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert cfg(ok, 16384, 3, 256, 0, ok, None) == fk.ERR_INVALID_ARGUMENT      # loads per lane 1, 2, 4, 8, 16
+    assert cfg(ok, 16384 + 1024, 16, 256, 0, ok, None) == fk.ERR_INVALID_ARGUMENT   # whole stretches
+    assert cfg(ok, 16384, 16, 0, 0, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert cfg(ok, 16384, 16, 256, 2, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert cfg(ok + 512, 16384, 16, 256, 0, ok, None) == fk.ERR_MISALIGNED
+    assert cfg(ok, 16384, 16, 256, 1, ok + 1, None) == fk.ERR_MISALIGNED
 
 
 # ------------------------------------------------ integer formats (fp4kv_int.h)
