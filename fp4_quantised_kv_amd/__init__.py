@@ -172,6 +172,11 @@ def library():
         L.fp4kv_read_probe_config.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               _P, _P]
         L.fp4kv_read_probe_config.restype = ctypes.c_int
+        L.fp4kv_decode_chunks.argtypes = [ctypes.POINTER(CacheLayout), ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32)]
+        L.fp4kv_decode_chunks.restype = ctypes.c_int
         L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         L.fp4kv_int_sizes.restype = ctypes.c_int
@@ -249,6 +254,37 @@ def _decode_plan(layout, batch, num_q_heads, max_pages_per_seq, num_splits):
         ctypes.byref(layout), batch, num_q_heads, max_pages_per_seq, num_splits,
         ctypes.byref(s), ctypes.byref(p), ctypes.byref(ws)))
     return DecodePlan(s.value, p.value, ws.value)
+
+
+class DecodeChunks(tuple):
+    """(lead_chunks, lead_pages, tail_pages) of fp4kv_decode_chunks: chunks
+    0 .. lead_chunks - 1 hold lead_pages pages each, the later ones
+    tail_pages each."""
+    __slots__ = ()
+
+    def __new__(cls, lead_chunks, lead_pages, tail_pages):
+        return tuple.__new__(cls, (lead_chunks, lead_pages, tail_pages))
+
+    lead_chunks = property(lambda self: self[0])
+    lead_pages = property(lambda self: self[1])
+    tail_pages = property(lambda self: self[2])
+
+    def first_page(self, k: int) -> int:
+        """First page (from the span's start) of chunk k."""
+        if k < self.lead_chunks:
+            return k * self.lead_pages
+        return self.lead_chunks * self.lead_pages + (k - self.lead_chunks) * self.tail_pages
+
+
+def decode_chunks(layout: CacheLayout, batch: int, num_q_heads: int, max_pages_per_seq: int,
+                  num_splits: int = 0, q_tokens: int = 1, window: int = 0) -> DecodeChunks:
+    """Chunk page counts a decode call with these arguments uses
+    (fp4kv_decode_chunks)."""
+    lc, lp, tp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check("fp4kv_decode_chunks", library().fp4kv_decode_chunks(
+        ctypes.byref(layout), batch, q_tokens, num_q_heads, max_pages_per_seq, window, num_splits,
+        ctypes.byref(lc), ctypes.byref(lp), ctypes.byref(tp)))
+    return DecodeChunks(lc.value, lp.value, tp.value)
 
 
 def _stream(stream):

@@ -3,6 +3,7 @@
 // call, so a rejected call has no effect on the device.
 #include "fp4kv.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -20,6 +21,7 @@ constexpr int64_t kMinAutoChunkPages = 2;  // automatic plans: pages per chunk a
 constexpr int64_t kMinAutoChunks = 1024;   // ... unless that leaves fewer chunks than this
 constexpr int32_t kChunksPerGroup = 4;   // chunks merged inside one workgroup
 constexpr int64_t kMaxPartials = 65535;  // partials per row: the split kernel's third grid dimension
+constexpr int64_t kResidentGroups = 768;  // split-kernel workgroups resident at once: 256 CUs x 3
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -152,6 +154,39 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
     return FP4KV_OK;
 }
 
+// Chunk page counts of a plan (chunk_first_page in the kernels): the first
+// lead_chunks chunks hold lead_pages pages, the rest tail_pages.  Even
+// chunks of pages_per_split, except in a grid of at least twice the
+// workgroups the GPU runs at once: there the last half of the partials take
+// chunks of 3/8 of that size and the other partials share out their pages,
+// so that the workgroups the grid starts last are short and few slots idle
+// while it drains.  (Measured on the 32 x 32K batch at 64 chunks and the
+// paged 64-sequence batch: larger shares or shorter tails gain more on the
+// first and lose on the second, whose long lead chunks then hold its few
+// long sequences in few workgroups.)
+struct ChunkSizes {
+    int32_t lead_chunks, lead_pages, tail_pages;
+};
+
+ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan &plan, int64_t span)
+{
+    const int64_t chunks = static_cast<int64_t>(plan.partials) * kChunksPerGroup;
+    ChunkSizes cs{static_cast<int32_t>(chunks), plan.pages_per_split, plan.pages_per_split};
+    const int64_t groups = static_cast<int64_t>(L.params.num_kv_heads) * batch * plan.partials;
+    const int64_t tail_parts = plan.partials / 2;
+    if (groups < 2 * kResidentGroups || tail_parts < 1)
+        return cs;
+    const int64_t tail = std::max<int64_t>(1, plan.pages_per_split * 3 / 8);
+    const int64_t lead_chunks = chunks - tail_parts * kChunksPerGroup;
+    const int64_t lead = (span - tail_parts * kChunksPerGroup * tail + lead_chunks - 1) / lead_chunks;
+    if (tail < plan.pages_per_split && lead >= plan.pages_per_split) {
+        cs.lead_chunks = static_cast<int32_t>(lead_chunks);
+        cs.lead_pages = static_cast<int32_t>(lead);
+        cs.tail_pages = static_cast<int32_t>(tail);
+    }
+    return cs;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +237,40 @@ int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t
     *splits_out = plan.splits;
     *partials_out = plan.partials;
     *workspace_bytes_out = plan.ws_bytes;
+    return FP4KV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t window_span_pages(int32_t max_pages, int32_t q_tokens, int32_t window);
+
+}  // namespace
+
+extern "C" {
+
+int fp4kv_decode_chunks(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t q_tokens, int32_t num_q_heads,
+                        int32_t max_pages_per_seq, int32_t window, int32_t num_splits, int32_t *lead_chunks_out,
+                        int32_t *lead_pages_out, int32_t *tail_pages_out)
+{
+    int rc = check_layout(layout);
+    if (rc != FP4KV_OK)
+        return rc;
+    if (!lead_chunks_out || !lead_pages_out || !tail_pages_out || q_tokens < 1 || window < 0 || num_q_heads < 1 ||
+        static_cast<int64_t>(q_tokens) * num_q_heads > std::numeric_limits<int32_t>::max())
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (max_pages_per_seq < 1)
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    const int32_t span = window_span_pages(max_pages_per_seq, q_tokens, window);
+    Plan plan;
+    rc = make_plan(*layout, batch, q_tokens * num_q_heads, span, num_splits, &plan);
+    if (rc != FP4KV_OK)
+        return rc;
+    const ChunkSizes cs = chunk_sizes(*layout, batch, plan, span);
+    *lead_chunks_out = cs.lead_chunks;
+    *lead_pages_out = cs.lead_pages;
+    *tail_pages_out = cs.tail_pages;
     return FP4KV_OK;
 }
 
@@ -273,6 +342,10 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     a->splits = plan.splits;
     a->pages_per_split = plan.pages_per_split;
     a->partials = plan.partials;
+    const ChunkSizes cs = chunk_sizes(*layout, batch, plan, window_span_pages(max_pages_per_seq, q_tokens, window));
+    a->lead_chunks = cs.lead_chunks;
+    a->lead_pages = cs.lead_pages;
+    a->tail_pages = cs.tail_pages;
     a->staged = true;
     // scores are kept in base 2; an FP8 cache's K tensor scale multiplies every score
     const double k_scale = layout->params.format == FP4KV_FORMAT_FP8_E4M3 ? layout->params.k_scale : 1.0;

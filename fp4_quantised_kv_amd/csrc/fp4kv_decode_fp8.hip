@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
 
     // grid (KV head, sequence, partial), as for the FP4 kernel
     const Chunk c = chunk_of(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
-    const int ids = chunk_ids(a, c, lane);
+    const int ids = chunk_ids(a, c, wave, lane);
     uint32_t qbits[kD / 8];
     load_q_bits<kD>(a, c.b, c.h, col, jj, qbits);
     if (!a.out && group_chunks_empty(a, c, wave)) {     // every chunk of the workgroup past the context

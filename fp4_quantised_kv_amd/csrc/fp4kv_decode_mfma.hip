@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     // deals round-robin to the XCDs -- belong to different KV heads.  Every
     // independent load is issued before any is waited on.
     const Chunk c = chunk_of(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
-    const int ids = STAGED ? chunk_ids(a, c, lane) : -1;
+    const int ids = STAGED ? chunk_ids(a, c, wave, lane) : -1;
     uint32_t qbits[D / 8];
     load_q_bits<D>(a, c.b, c.h, col, jj, qbits);
     // (the loads above are issued first so that they need not wait for the

@@ -31,6 +31,9 @@ struct DecodeArgs {
     int32_t window;              // > 0: a query sees only the last `window` tokens of its prefix (sliding window)
     int32_t splits, pages_per_split;   // context chunks and pages per chunk (from the window's first page)
     int32_t partials;            // partial slots per row: ceil(splits / 4), one per workgroup
+    // Chunk sizes (pages): the first lead_chunks chunks hold lead_pages
+    // each, the rest tail_pages each (all pages_per_split: even chunks)
+    int32_t lead_chunks, lead_pages, tail_pages;
     float scale_log2e;           // softmax scale times log2(e): scores kept in base 2
     float *ws_o;                 // [batch][partials][q_tokens * num_q_heads][D] unnormalised outputs
     float *ws_ml;                // [batch][partials][q_tokens * num_q_heads][2] running max (base 2), sum

@@ -377,8 +377,8 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
     const int n_pages = (len + kPage - 1) / kPage;
-    const int p0 = sp * a.pages_per_split;
-    const int p1 = min(p0 + a.pages_per_split, n_pages);
+    const int p0 = chunk_first_page(a, sp);
+    const int p1 = min(p0 + chunk_pages(a, sp), n_pages);
 
     float m[GM], l[GM], o0[GM], o1[GM];
 #pragma unroll

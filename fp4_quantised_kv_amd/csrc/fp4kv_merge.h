@@ -21,6 +21,24 @@ namespace fp4kv {
 constexpr int kWavesPerGroup = 4;
 constexpr int kGroupThreads = 64 * kWavesPerGroup;
 
+// Context chunk k (wave k % 4 of partial k / 4) holds chunk_pages(a, k)
+// pages from chunk_first_page(a, k); the chunks tile the context in order:
+// lead_chunks chunks of lead_pages, then chunks of tail_pages.  The grid's
+// partial index varies slowest, so the long chunks are dispatched first and
+// the workgroups that start last -- in a grid of many more workgroups than
+// the GPU holds at once -- are short ones: fewer slots idle while the grid
+// drains.
+__device__ __forceinline__ int chunk_first_page(const DecodeArgs &a, int k)
+{
+    return k < a.lead_chunks ? k * a.lead_pages
+                             : a.lead_chunks * a.lead_pages + (k - a.lead_chunks) * a.tail_pages;
+}
+
+__device__ __forceinline__ int chunk_pages(const DecodeArgs &a, int k)
+{
+    return k < a.lead_chunks ? a.lead_pages : a.tail_pages;
+}
+
 template <int D>
 constexpr int merge_area_bytes() { return 16 * D * 4 + 16 * 2 * 4; }
 

@@ -272,17 +272,18 @@ __device__ __forceinline__ Chunk chunk_of(const DecodeArgs &a, int h, int b, int
     Chunk c;
     c.h = h; c.b = b; c.part = part;
     c.ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-    c.p0 = (part * kWavesPerGroup + wave) * a.pages_per_split;
+    const int k = part * kWavesPerGroup + wave;
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
     c.len = len;
+    c.p0 = chunk_first_page(a, k);
     if (a.window > 0) {
         // chunks start at the page of the earliest token any query column
         // sees: the first query token's prefix end minus the window
         const int first = len - ((a.q_tokens > 1 ? a.q_tokens : 1) - 1) - a.window;
         c.p0 += first > 0 ? first / kPage : 0;
     }
-    c.p1 = min(c.p0 + a.pages_per_split, (len + kPage - 1) / kPage);
+    c.p1 = min(c.p0 + chunk_pages(a, k), (len + kPage - 1) / kPage);
     return c;
 }
 
@@ -291,7 +292,8 @@ __device__ __forceinline__ Chunk chunk_of(const DecodeArgs &a, int h, int b, int
 // where the split count follows the longest sequence.
 __device__ __forceinline__ bool group_chunks_empty(const DecodeArgs &a, const Chunk &c, int wave)
 {
-    return c.p0 - wave * a.pages_per_split >= (c.len + kPage - 1) / kPage;
+    const int k0 = c.part * kWavesPerGroup;
+    return c.p0 - (chunk_first_page(a, k0 + wave) - chunk_first_page(a, k0)) >= (c.len + kPage - 1) / kPage;
 }
 
 // The partial of such a workgroup: its rows are marked empty (m = -inf,
@@ -316,10 +318,25 @@ __device__ __forceinline__ int column_first_token(const DecodeArgs &a, int len, 
     return (a.window > 0 && first > 0) ? first : 0;
 }
 
-__device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, int lane)
+__device__ __forceinline__ int ids_from(const DecodeArgs &a, const int32_t *ptab, int p0, int pages, int lane)
 {
-    const int end = min(c.p0 + a.pages_per_split, a.max_pages);
-    return c.p0 + lane < end ? c.ptab[c.p0 + lane] : -1;
+    const int end = min(p0 + pages, a.max_pages);
+    return p0 + lane < end ? ptab[p0 + lane] : -1;
+}
+
+// The chunk's page ids, loaded from its unshifted start so that the load
+// waits for nothing but the kernel arguments: only a window moves the start
+// (by an amount that depends on the length), and then the ids are loaded
+// again from the moved start.  Written as one address computed from the
+// length, the load would wait a further memory round trip for it.
+__device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, int wave, int lane)
+{
+    const int k = c.part * kWavesPerGroup + wave;
+    const int base = chunk_first_page(a, k), pages = chunk_pages(a, k);
+    int ids = ids_from(a, c.ptab, base, pages, lane);
+    if (a.window > 0 && c.p0 != base)
+        ids = ids_from(a, c.ptab, c.p0, pages, lane);
+    return ids;
 }
 
 // The step's own token (decode with append): the one wave whose chunk holds

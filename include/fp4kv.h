@@ -193,10 +193,11 @@ FP4KV_API int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout,
                           const int64_t *slot_mapping, void *cache, void *stream);
 
 /* Split count and workspace bytes for fp4kv_decode_attention.  Host only.
- * The context of every sequence is cut into S chunks of equal page counts;
- * one wave attends over each chunk, and workgroups of four waves merge their
- * four chunks into one partial result, so the workspace holds
- * P = ceil(S / 4) partials per (sequence, query head).
+ * The context of every sequence is cut into S chunks of about equal page
+ * counts (exact sizes: fp4kv_decode_chunks); one wave attends over each
+ * chunk, and workgroups of four waves merge their four chunks into one
+ * partial result, so the workspace holds P = ceil(S / 4) partials per
+ * (sequence, query head).
  * num_splits > 0 asks for S = num_splits (clamped to max_pages_per_seq and
  * to 4 * 65535, then trimmed so that no chunk starts past page
  * max_pages_per_seq); 0 lets the library choose S, about 16384 chunks in
@@ -214,6 +215,28 @@ FP4KV_API int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout,
 FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t num_q_heads,
                                 int32_t max_pages_per_seq, int32_t num_splits,
                                 int32_t *splits_out, int32_t *partials_out, int64_t *workspace_bytes_out);
+
+/* The chunk page counts a decode call with these arguments uses.  Host only;
+ * for callers that want to know how the work is cut, and for tests.  With
+ * P partials there are 4P chunk slots (chunk 4p + w is wave w of partial
+ * p); they tile each sequence's context in order from its first page (with
+ * a window: the page of its first query token's window start):
+ *   chunk k < *lead_chunks_out  pages [k * LP, (k + 1) * LP)
+ *   chunk k >= *lead_chunks_out pages [L + (k - lc) * TP, L + (k - lc + 1) * TP)
+ * where lc = *lead_chunks_out, LP = *lead_pages_out, TP = *tail_pages_out and
+ * L = lc * LP, each cut at the end of the context.  Usually LP = TP =
+ * ceil(span / S) (even chunks).  In a grid of at least 1536 workgroups
+ * (H_kv x batch x P: twice what 256 CUs hold at once) the last floor(P / 2)
+ * partials take chunks of TP = max(1, 3 * ceil(span / S) / 8) pages and the
+ * others LP >= ceil(span / S): the workgroups dispatched last are then short
+ * ones, so fewer CUs idle while the grid drains.  Arguments as for
+ * fp4kv_decode_plan, plus q_tokens >= 1 and window >= 0 as for
+ * fp4kv_decode_window_attention (batch x q_tokens x num_q_heads query rows).
+ * Errors: as fp4kv_decode_plan, and INVALID_ARGUMENT for a null output,
+ * q_tokens < 1 or window < 0. */
+FP4KV_API int fp4kv_decode_chunks(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t q_tokens,
+                                  int32_t num_q_heads, int32_t max_pages_per_seq, int32_t window, int32_t num_splits,
+                                  int32_t *lead_chunks_out, int32_t *lead_pages_out, int32_t *tail_pages_out);
 
 /* One decode step of attention for `batch` sequences, one query token each,
  * over the packed cache.  ("Quantising the KV cache", Concept and Code

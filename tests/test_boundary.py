@@ -131,6 +131,50 @@ def test_plan():
         assert e.value.status == code
 
 
+def test_chunks():
+    L = fk.cache_layout(8, 128, 32 * 512)
+    # 8 x 32 x 16 = 4096 workgroups: the last 8 partials take chunks of
+    # 3 pages (3/8 of 8), the first 32 chunks share out the other 416 pages
+    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64)) == (32, 13, 3)
+    # the paged batch: 29 chunks of 9 pages in 8 partials, 4096 workgroups
+    assert tuple(fk.decode_chunks(L, 64, 32, 258, 0)) == (16, 14, 3)
+    # fewer than 1536 workgroups: even chunks
+    assert tuple(fk.decode_chunks(L, 1, 32, 8192, 256)) == (256, 32, 32)
+    assert tuple(fk.decode_chunks(L, 8, 32, 64, 0)) == (32, 2, 2)
+    assert tuple(fk.decode_chunks(L, 8, 32, 64, 0, q_tokens=2, window=0)) == (32, 2, 2)
+    for B, Hq, maxp, S, qt, win in [(32, 64, 512, 64, 1, 0), (64, 32, 258, 0, 1, 0), (48, 32, 48, 16, 1, 0),
+                                    (64, 32, 48, 16, 1, 0), (96, 32, 32, 7, 2, 700), (96, 32, 32, 0, 2, 700),
+                                    (200, 8, 100, 3, 1, 0), (6, 8, 5000, 0, 1, 0), (512, 64, 40, 40, 1, 0),
+                                    (33, 16, 77, 29, 4, 300), (1024, 8, 2, 0, 1, 0)]:
+        span = maxp if win == 0 else min(maxp, -(-(win + qt - 1) // 64) + 1)
+        plan = (fk.decode_plan(L, B, Hq, maxp, S) if win == 0 and qt == 1
+                else fk.decode_window_plan(L, B, qt, Hq, maxp, win, S))
+        ch = fk.decode_chunks(L, B, Hq, maxp, S, q_tokens=qt, window=win)
+        pps = -(-span // plan.splits)
+        chunks = 4 * plan.partials
+        assert ch.first_page(chunks) >= span                          # the chunks tile the span
+        if ch.lead_chunks == chunks:
+            assert ch.lead_pages == ch.tail_pages == pps
+        else:
+            assert 8 * B * plan.partials >= 1536
+            assert ch.lead_chunks == 4 * (plan.partials - plan.partials // 2)
+            assert ch.tail_pages == max(1, 3 * pps // 8) < pps <= ch.lead_pages
+            # the lead chunks hold no more than they must: a page fewer each leaves pages uncovered
+            assert ch.lead_chunks * (ch.lead_pages - 1) + (chunks - ch.lead_chunks) * ch.tail_pages < span
+    for kw, code in [(dict(q_tokens=0), fk.ERR_INVALID_ARGUMENT), (dict(window=-1), fk.ERR_INVALID_ARGUMENT)]:
+        with pytest.raises(fk.Fp4KVError) as e:
+            fk.decode_chunks(L, 4, 32, 16, 0, **kw)
+        assert e.value.status == code
+    for args, code in [((32, 65, 512, 64), fk.ERR_INVALID_ARGUMENT), ((1, 64, 0, 64), fk.ERR_INVALID_ARGUMENT),
+                       ((32, 8 * 17, 512, 64), fk.ERR_UNSUPPORTED)]:
+        with pytest.raises(fk.Fp4KVError) as e:
+            fk.decode_chunks(L, *args)
+        assert e.value.status == code
+    lc = ctypes.c_int32()
+    assert fk.library().fp4kv_decode_chunks(ctypes.byref(L), 4, 1, 32, 16, 0, 0, ctypes.byref(lc), None,
+                                            ctypes.byref(lc)) == fk.ERR_INVALID_ARGUMENT
+
+
 def _lib():
     return fk.library()
 
