@@ -166,50 +166,76 @@ __global__ __launch_bounds__(256) void append_slices_kernel(
     }
     uint8_t *base = cache + (s0 / kPage) * g.page_stride + head * g.head_stride;
     const int off0 = static_cast<int>(s0 % kPage);
-    // K: eight tokens' blocks loaded together (256 bytes in flight per
-    // thread), then quantised and stored token by token
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t w[8][8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            load_block16(ksrc + (8 * h + i) * row_stride, w[i]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t lo, hi, sc;
-            quantize_block16(w[i], lo, hi, sc);
-            const int off = off0 + 8 * h + i;
-            *reinterpret_cast<uint2 *>(base + g.k_codes_off + off * (D / 2) + 8 * blk) = make_uint2(lo, hi);
-            base[g.k_scales_off + off * (D / 16) + blk] = static_cast<uint8_t>(sc);
-        }
-        asm volatile("" ::: "memory");
-    }
+    // the head's NB threads are consecutive lanes (NB divides 64), all on
+    // this path together (`whole` is a property of the slice)
+    const int lane_head0 = (threadIdx.x & 63) - blk;
+    // Eight rounds of four tokens' rows: K of tokens 0-15 (rounds 0-3), then
+    // V (rounds 4-7).  Each round's loads are issued before the previous
+    // round's arithmetic, so that a wave has rows in flight while it
+    // computes: a prefill's waves all fit on the GPU at once, and with one
+    // round at a time they would all load, then all compute, in lockstep.
     // V: nibble rows of channels 16*blk + c, tokens off0 .. off0 + 15.  Per
     // 8 tokens the codes come out token-major (dword i = token i, nibble c =
     // channel c); an 8 x 8 nibble transpose makes them channel-major (dword
     // c = channel c, nibble i = token i), which is a V code row's half.
+    uint32_t w[2][4][8];                                // rows of two rounds
     uint32_t vd[2][16];                                 // [token half][channel]
     uint32_t vs[4] = {0u, 0u, 0u, 0u};
+    auto load_round = [&](int r, uint32_t (&rows)[4][8]) {
+        const uint16_t *src = (r < 4 ? ksrc : vsrc) + 4 * (r & 3) * row_stride;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+        for (int i = 0; i < 4; ++i)
+            load_block16(src + i * row_stride, rows[i]);
+    };
+    load_round(0, w[0]);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {               // four tokens' rows in flight at a time
-            uint32_t w[4][8];
+    for (int r = 0; r < 8; ++r) {
+        if (r + 1 < 8)
+            load_round(r + 1, w[(r + 1) & 1]);
+        asm volatile("" ::: "memory");
+        uint32_t (&rows)[4][8] = w[r & 1];
+        if (r < 4) {
+            uint32_t ks = 0;                            // this block's scale codes of the round's 4 tokens
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                load_block16(vsrc + (8 * h + 4 * q + i) * row_stride, w[i]);
+            for (int i = 0; i < 4; ++i) {
+                uint32_t lo, hi, sc;
+                quantize_block16(rows[i], lo, hi, sc);
+                const int off = off0 + 4 * r + i;
+                *reinterpret_cast<uint2 *>(base + g.k_codes_off + off * (D / 2) + 8 * blk) = make_uint2(lo, hi);
+                ks |= sc << (8 * i);
+            }
+            // The 4 tokens' K scale rows (NB bytes each, consecutive) are
+            // 4 * NB contiguous bytes: lane blk of the head stores their
+            // dword blk, gathering byte m from lane (4 blk + m) % NB, the
+            // block of that byte, whose codes hold it at token (4 blk + m) / NB.
+            uint32_t dw = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int b = 4 * blk + m;
+                const uint32_t from = __shfl(ks, lane_head0 + b % NB);
+                dw |= ((from >> (8 * (b / NB))) & 0xFFu) << (8 * m);
+            }
+            *reinterpret_cast<uint32_t *>(base + g.k_scales_off + (off0 + 4 * r) * NB + 4 * blk) = dw;
+        } else {
+            const int h = (r - 4) >> 1, q = (r - 4) & 1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t sc;
-                quantize_block16(w[i], vd[h][4 * q + i], vd[h][8 + 4 * q + i], sc);
+                quantize_block16(rows[i], vd[h][4 * q + i], vd[h][8 + 4 * q + i], sc);
                 vs[2 * h + q] |= sc << (8 * i);
+                // the codes are wanted here, not at the stores: without this
+                // the compiler defers the arithmetic past later loads and
+                // holds several rounds of rows at once
+                asm volatile("" : "+v"(vd[h][4 * q + i]), "+v"(vd[h][8 + 4 * q + i]));
             }
-            // the next rows' loads stay after this arithmetic, so that only
-            // four rows are held at once
-            asm volatile("" ::: "memory");
+            asm volatile("" : "+v"(vs[2 * h + q]));
+            if (q == 1) {
+                transpose_nibbles8(&vd[h][0]);
+                transpose_nibbles8(&vd[h][8]);
+            }
         }
-        transpose_nibbles8(&vd[h][0]);
-        transpose_nibbles8(&vd[h][8]);
+        // the round after next loads into these rows: not before this arithmetic
+        asm volatile("" ::: "memory");
     }
     uint4 *vrow = reinterpret_cast<uint4 *>(base + g.v_codes_off + v_code_row<D>(off0, 16 * blk));
 #pragma unroll

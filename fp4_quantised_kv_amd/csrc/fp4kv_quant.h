@@ -54,9 +54,11 @@ __device__ __forceinline__ float e2m1_value(uint32_t nib)
 }
 
 // The quotient x / s rounded once to fp32, without a division per element:
-// q = x * r with r = 1/s (correctly rounded, once per block), then one
-// Newton step with the exact residual, q - (q*s - x)*r, in two FMAs.  The
-// result is within 2^-46 (relative) of the exact quotient.  A bf16 x over an
+// q = x * r with r ~ 1/s (the hardware reciprocal, within 1 ulp, once per
+// block), then one Newton step with the exact residual, q - (q*s - x)*r, in
+// two FMAs.  The residual is exact (q*s has at most 28 significant bits and
+// lies within a few ulps of x), so the result is within about 2^-44
+// (relative) of the exact quotient.  A bf16 x over an
 // E4M3 s is either exactly an E2M1 rounding midpoint (0.25, 0.75, 1.25,
 // 1.75, 2.5, 3.5, 5) or at least 2^-8 (relative) away from every one, so the
 // corrected quotient rounds to the same E2M1 code as the exact one, ties
@@ -88,20 +90,27 @@ __device__ __forceinline__ uint32_t pack_pair(uint32_t d, uint32_t w, float s, f
 __device__ __forceinline__ void quantize_block16(const uint32_t w[8], uint32_t &lo, uint32_t &hi,
                                                  uint32_t &scale_code)
 {
-    uint32_t amax = 0;
+    // bf16 magnitudes as unsigned 16-bit integers order like the values:
+    // two channels per packed max
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m2 = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        amax = max(amax, w[i] & 0x7FFFu);
-        amax = max(amax, (w[i] >> 16) & 0x7FFFu);
-    }
+    for (int i = 1; i < 8; ++i)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    const uint32_t amax = max(static_cast<uint32_t>(m2.x), static_cast<uint32_t>(m2.y));
     // amax / 6 in correctly rounded fp32 gives the same E4M3 code as the exact
     // quotient for every bf16 amax (checked exhaustively against the oracle).
+    // It is formed without a division: q = amax * RN(1/6), then one Newton
+    // step with the exact residual, which rounds correctly (Markstein's
+    // condition: a correctly rounded reciprocal; also checked for every bf16).
     const float a = __uint_as_float(amax << 16);
-    uint32_t sc = e4m3_code_rne_sat(a / 6.0f);
+    constexpr float kSixth = 0x1.555556p-3f;            // RN(1/6)
+    const float q6 = a * kSixth;
+    uint32_t sc = e4m3_code_rne_sat(__builtin_fmaf(__builtin_fmaf(-q6, 6.0f, a), kSixth, q6));
     sc = sc ? sc : 1u;                                  // zero scale -> smallest subnormal
     scale_code = sc;
     const float s = e4m3_value(sc);
-    const float r = 1.0f / s;
+    const float r = __builtin_amdgcn_rcpf(s);
     lo = pack_pair<0>(0u, w[0], s, r);
     lo = pack_pair<1>(lo, w[1], s, r);
     lo = pack_pair<2>(lo, w[2], s, r);
