@@ -197,14 +197,72 @@ def prefill_append(fk, wl, seed, dev, stream, reps=10):
     ms = _time(torch, stream, lambda: fk.quantize_append(layout, k, v, slots, cache), reps)
     bytes_ = 2 * k.numel() * 2 + layout.cache_bytes + n * 8
     gbs = bytes_ / (ms * 1e-3) / 1e9
+    del k, v, cache
     copy = copy_ceiling(dev, stream)
+    ceil = stream_ceiling(fk, dev, stream, 2 * n * w.kv_heads * w.head_dim * 2, layout.cache_bytes)
     return {"workload": w.name, "tokens": n, "ms": round(ms, 5), "gbs": round(gbs, 1),
             "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2), "algorithmic_bytes": bytes_,
             "roofline": {"bound": "hbm", "kernel": "append_slices_kernel<128>", "achieved": round(gbs, 2),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": None, "algorithmic_bytes_per_launch": bytes_,
-                         "frac_of_device_copy": round(gbs / copy["gbs"], 4)},
-            "device_copy": copy}
+                         "traffic": prefill_traffic(), "algorithmic_bytes_per_launch": bytes_,
+                         "frac_of_stream_ceiling": round(gbs / ceil["coalesced"]["gbs"], 4),
+                         "frac_of_paired_load_ceiling": round(gbs / ceil["paired"]["gbs"], 4)},
+            "stream_ceiling": ceil, "device_copy": copy}
+
+
+def stream_ceiling(fk, dev, stream, read_total, write_total, reps=10):
+    """The achievable rate of the prefill's traffic: streaming probes that
+    read and write in its proportion, one wave per 16-token slice's worth
+    (64 KB of bf16 K and V in, a quarter of that plus the scales out), with
+    whole-kilobyte loads (coalesced) and with the quantiser's own pattern (a
+    16-channel block's 32 bytes per lane as two 16-byte loads: paired); the
+    fastest grid of each."""
+    import torch
+    unit_r = 65536
+    units = read_total // unit_r
+    unit_w = -(-write_total // units // 1024) * 1024
+    src = torch.full((units * unit_r,), 1, dtype=torch.uint8, device=dev)
+    dst = torch.empty(units * unit_w, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, paired in (("coalesced", False), ("paired", True)):
+        best = None
+        for groups in (1024, 2048, 4096):
+            ms = _time(torch, stream, lambda: fk.stream_probe(src, dst, unit_r, unit_w, paired, groups, sink), reps)
+            g = units * (unit_r + unit_w) / (ms * 1e-3) / 1e9
+            if best is None or g > best["gbs"]:
+                best = {"gbs": round(g, 1), "ms": round(ms, 5), "workgroups": groups}
+        out[name] = best
+    out["per_wave_unit"] = {"read_bytes": unit_r, "write_bytes": unit_w, "units": units}
+    del src, dst
+    return out
+
+
+def prefill_traffic():
+    """Per-launch HBM bytes of the prefill quantiser from the committed
+    counter summary, if taken from the current source; else None."""
+    path = os.path.join(PROFILES, "append_prefill_b8_8k_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != quantiser_source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def quantiser_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("fp4kv_kernels.hip", "fp4kv_quant.h", "fp4kv_internal.h"):
+        with open(os.path.join(_CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def copy_ceiling(dev, stream, nbytes=1 << 30, reps=10):

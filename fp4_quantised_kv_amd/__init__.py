@@ -177,6 +177,9 @@ def library():
                                           ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]
         L.fp4kv_decode_chunks.restype = ctypes.c_int
+        L.fp4kv_stream_probe.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, _P, _P]
+        L.fp4kv_stream_probe.restype = ctypes.c_int
         L.fp4kv_int_sizes.argtypes = [ctypes.POINTER(IntDims), ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         L.fp4kv_int_sizes.restype = ctypes.c_int
@@ -636,6 +639,22 @@ def read_probe_config(buf, sink, loads_per_lane: int, workgroups: int, to_lds: b
     _check("fp4kv_read_probe_config", library().fp4kv_read_probe_config(
         buf.data_ptr(), buf.numel(), int(loads_per_lane), int(workgroups), int(bool(to_lds)), sink.data_ptr(),
         _stream(stream)))
+
+
+def stream_probe(src, dst, read_bytes: int, write_bytes: int, paired: bool, workgroups: int, sink, stream=None):
+    """Measurement utility: streaming reads and writes in a given proportion
+    (fp4kv_stream_probe); units = src.numel() // read_bytes, and dst must
+    hold units * write_bytes bytes."""
+    import torch
+    _need(src, "src", torch.uint8)
+    _need(dst, "dst", torch.uint8)
+    _need(sink, "sink", torch.int32)
+    units = src.numel() // read_bytes
+    if units < 1 or dst.numel() < units * write_bytes:
+        raise ValueError("stream_probe: src must hold a unit and dst units * write_bytes bytes")
+    _check("fp4kv_stream_probe", library().fp4kv_stream_probe(
+        src.data_ptr(), dst.data_ptr(), units, int(read_bytes), int(write_bytes), int(bool(paired)), int(workgroups),
+        sink.data_ptr(), _stream(stream)))
 
 
 # ------------------------------------------- integer formats (include/fp4kv_int.h)

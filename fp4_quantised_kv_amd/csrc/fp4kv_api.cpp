@@ -697,6 +697,20 @@ int fp4kv_read_probe_config(const void *buf, int64_t bytes, int32_t loads_per_la
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
 
+int fp4kv_stream_probe(const void *src, void *dst, int64_t units, int32_t read_bytes, int32_t write_bytes,
+                       int32_t paired, int32_t workgroups, uint32_t *sink, void *stream)
+{
+    if (!src || !sink || units < 1 || read_bytes < 8192 || read_bytes % 8192 != 0 || write_bytes < 0 ||
+        write_bytes % 1024 != 0 || (write_bytes > 0 && !dst) || workgroups < 1 || (paired != 0 && paired != 1))
+        return FP4KV_ERR_INVALID_ARGUMENT;
+    if (!aligned(src, 1024) || (dst && !aligned(dst, 1024)) || !aligned(sink, 4))
+        return FP4KV_ERR_MISALIGNED;
+    const hipError_t e = fp4kv::launch_stream_probe(static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), units,
+                                                    read_bytes, write_bytes, paired != 0, workgroups, sink,
+                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
+}
+
 int fp4kv_version(void) { return 100; }
 
 }  // extern "C"

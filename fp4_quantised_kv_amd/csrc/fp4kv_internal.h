@@ -89,6 +89,8 @@ hipError_t scratch_for_current_device(void **out);
 hipError_t launch_read_probe(const uint8_t *buf, int64_t blocks, uint32_t *sink, hipStream_t stream);
 // The configurable read probes (loads_per_lane 1, 2, 4, 8 or 16; bytes a
 // multiple of 1024 * loads_per_lane).
+hipError_t launch_stream_probe(const uint8_t *src, uint8_t *dst, int64_t units, int read_bytes, int write_bytes,
+                               bool paired, int workgroups, uint32_t *sink, hipStream_t stream);
 hipError_t launch_read_probe_config(const uint8_t *buf, int64_t bytes, int loads_per_lane, int workgroups,
                                     bool to_lds, uint32_t *sink, hipStream_t stream);
 

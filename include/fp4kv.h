@@ -488,6 +488,24 @@ FP4KV_API int fp4kv_read_probe(const void *buf, int64_t bytes, uint32_t *sink, v
 FP4KV_API int fp4kv_read_probe_config(const void *buf, int64_t bytes, int32_t loads_per_lane, int32_t workgroups,
                                       int32_t to_lds, uint32_t *sink, void *stream);
 
+/* Measurement utility, not a step of the method: the achievable rate of a
+ * kernel that streams reads and writes in a given proportion.  `units`
+ * waves' worth of work, in a grid-stride loop over `workgroups` workgroups of
+ * four waves: unit u reads read_bytes contiguous bytes at src + u *
+ * read_bytes (128 bytes per lane in flight) and then writes write_bytes
+ * contiguous bytes at dst + u * write_bytes.  paired = 0: each load
+ * instruction reads a whole kilobyte (16 bytes per lane); paired = 1: lane l
+ * reads bytes [32 l, 32 l + 32) of each 2 KB row in two 16-byte loads, the
+ * pattern of the quantiser, which holds a 16-channel bf16 block per lane.
+ * read_bytes a positive multiple of 8192, write_bytes a multiple of 1024
+ * (0: no writes, dst may be NULL); src and dst 1024-byte aligned and at
+ * least units * read_bytes and units * write_bytes long (not checkable:
+ * the caller's obligation); sink as for fp4kv_read_probe.  Returns
+ * FP4KV_OK, or INVALID_ARGUMENT / MISALIGNED before any HIP call, or
+ * FP4KV_ERR_HIP. */
+FP4KV_API int fp4kv_stream_probe(const void *src, void *dst, int64_t units, int32_t read_bytes, int32_t write_bytes,
+                                 int32_t paired, int32_t workgroups, uint32_t *sink, void *stream);
+
 /* Static text for a status code (never NULL). */
 FP4KV_API const char *fp4kv_status_string(int status);
 

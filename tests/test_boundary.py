@@ -258,6 +258,18 @@ def test_read_probe_host_checks():
     assert cfg(ok, 16384, 16, 256, 2, ok, None) == fk.ERR_INVALID_ARGUMENT
     assert cfg(ok + 512, 16384, 16, 256, 0, ok, None) == fk.ERR_MISALIGNED
     assert cfg(ok, 16384, 16, 256, 1, ok + 1, None) == fk.ERR_MISALIGNED
+    sp = lib.fp4kv_stream_probe
+    assert sp(None, ok, 4, 8192, 1024, 0, 256, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert sp(ok, ok, 0, 8192, 1024, 0, 256, ok, None) == fk.ERR_INVALID_ARGUMENT      # no units
+    assert sp(ok, ok, 4, 4096, 1024, 0, 256, ok, None) == fk.ERR_INVALID_ARGUMENT      # reads in 8 KB steps
+    assert sp(ok, ok, 4, 8192, 1000, 0, 256, ok, None) == fk.ERR_INVALID_ARGUMENT      # writes in 1 KB steps
+    assert sp(ok, None, 4, 8192, 1024, 0, 256, ok, None) == fk.ERR_INVALID_ARGUMENT    # writes need dst
+    assert sp(ok, ok, 4, 8192, 1024, 2, 256, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert sp(ok, ok, 4, 8192, 1024, 0, 0, ok, None) == fk.ERR_INVALID_ARGUMENT
+    assert sp(ok, ok, 4, 8192, 1024, 0, 256, None, None) == fk.ERR_INVALID_ARGUMENT
+    assert sp(ok + 16, ok, 4, 8192, 1024, 0, 256, ok, None) == fk.ERR_MISALIGNED
+    assert sp(ok, ok + 16, 4, 8192, 1024, 1, 256, ok, None) == fk.ERR_MISALIGNED
+    assert sp(ok, ok, 4, 8192, 1024, 1, 256, ok + 2, None) == fk.ERR_MISALIGNED
 
 
 # ------------------------------------------------ integer formats (fp4kv_int.h)

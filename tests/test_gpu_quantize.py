@@ -57,20 +57,28 @@ def _to_rows(blocks_u16, H=1, D=128):
     return torch.from_numpy(pad.view(np.int16).reshape(n_tok, H, D)).view(torch.bfloat16)
 
 
-def test_scale_rule_every_bf16_amax():
-    """Blocks [a, 0, ..., 0] and [-a, ...] for every finite bf16 magnitude a."""
+# token rows of 256 B to 2 KB: one KV head up to several per wave of the
+# 16-token slice kernel, at D = 128 and 64
+SHAPES = [(1, 128), (4, 128), (8, 128), (8, 64), (16, 64)]
+
+
+@pytest.mark.parametrize("H,D", SHAPES)
+def test_scale_rule_every_bf16_amax(H, D):
+    """Blocks [a, 0, ..., 0] and [-a, ...] for every finite bf16 magnitude a
+    (the maximum in either half of the block)."""
     a = np.arange(0, 0x7F80, dtype=np.uint16)
     blocks = np.zeros((2 * a.size, 16), np.uint16)
     blocks[0::2, 0] = a
-    blocks[1::2, 5] = a | 0x8000
-    k = _to_rows(blocks)
-    v = _to_rows(blocks[::-1].copy())
-    _say(f"quantize_append: every bf16 amax, {k.shape[0]} tokens")
+    blocks[1::2, 13] = a | 0x8000
+    k = _to_rows(blocks, H, D)
+    v = _to_rows(blocks[::-1].copy(), H, D)
+    _say(f"quantize_append: every bf16 amax, H {H} D {D}, {k.shape[0]} tokens")
     layout, cache = _quantize_on_gpu(k, v)
     _check_tokens(layout, cache, k, v, k.shape[0])
 
 
-def test_element_rule_every_scale_and_magnitude():
+@pytest.mark.parametrize("H,D", SHAPES)
+def test_element_rule_every_scale_and_magnitude(H, D):
     """For each of the 126 scale codes, every bf16 magnitude up to the largest
     block maximum that yields it, both signs, 15 per block behind that
     maximum."""
@@ -93,9 +101,9 @@ def test_element_rule_every_scale_and_magnitude():
         blk[:, 1:] = flat.reshape(nb, 15)
         chunks.append(blk)
     blocks = np.concatenate(chunks)
-    k = _to_rows(blocks)
-    v = _to_rows(np.roll(blocks, 7, axis=0))
-    _say(f"quantize_append: element rule, {blocks.shape[0]} blocks, {k.shape[0]} tokens")
+    k = _to_rows(blocks, H, D)
+    v = _to_rows(np.roll(blocks, 7, axis=0), H, D)
+    _say(f"quantize_append: element rule, H {H} D {D}, {blocks.shape[0]} blocks, {k.shape[0]} tokens")
     layout, cache = _quantize_on_gpu(k, v)
     _check_tokens(layout, cache, k, v, k.shape[0])
 
