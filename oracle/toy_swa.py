@@ -68,9 +68,11 @@ def _store(x64, fmt):
     raise ValueError("format is bf16, fp8 or fp4")
 
 
-def run(net, weights, x, start: int, end: int, fmt: str = "fp8") -> np.ndarray:
+def run(net, weights, x, start: int, end: int, fmt: str = "fp8", record=None) -> np.ndarray:
     """Final hidden states of tokens start .. end-1 ([B][end-start][d],
-    float64), processing them one at a time from empty windows."""
+    float64), processing them one at a time from empty windows.  With a list
+    `record`, appends for every token the (q, k, v) bf16 rows of each layer
+    (the input run_with_rows takes)."""
     B = x.shape[0]
     Hq, Hkv, D, W = net.q_heads, net.kv_heads, net.head_dim, net.window
     G = Hq // Hkv
@@ -85,21 +87,65 @@ def run(net, weights, x, start: int, end: int, fmt: str = "fp8") -> np.ndarray:
         for layer, (wq, wk, wv, wo) in enumerate(ws):
             u = h / np.sqrt(np.mean(h * h, axis=1, keepdims=True))
             q = bf16_round(u @ wq).reshape(B, Hq, D)
-            k = _store(bf16_round(u @ wk).reshape(B, Hkv, D), fmt)
-            v = _store(bf16_round(u @ wv).reshape(B, Hkv, D), fmt)
-            attn = np.zeros((B, Hq, D))
-            for b in range(B):
-                kwin[layer][b].append(k[b])
-                vwin[layer][b].append(v[b])
-                kk = np.stack(kwin[layer][b][-W:])          # [n][Hkv][D]
-                vv = np.stack(vwin[layer][b][-W:])
-                for j in range(Hq):
-                    z = scale * (kk[:, j // G] @ q[b, j])
-                    p = np.exp(z - z.max())
-                    attn[b, j] = (p @ vv[:, j // G]) / p.sum()
+            k_row = bf16_round(u @ wk).reshape(B, Hkv, D)
+            v_row = bf16_round(u @ wv).reshape(B, Hkv, D)
+            if record is not None:
+                if layer == 0:
+                    record.append([])
+                record[-1].append((q, k_row, v_row))
+            attn = _window_attention(q, _store(k_row, fmt), _store(v_row, fmt), kwin[layer], vwin[layer], W, G,
+                                     scale)
             h = h + attn.reshape(B, Hq * D) @ wo
         out[:, t - start] = h
     return out
+
+
+def _window_attention(q, k, v, kwin, vwin, W, G, scale):
+    """One token's attention in one layer: appends the stored k, v rows
+    [B][Hkv][D] to the per-sequence windows kwin, vwin and attends q
+    [B][Hq][D] over their last W rows (query head j reads KV head j // G)."""
+    B, Hq, D = q.shape
+    attn = np.zeros((B, Hq, D))
+    for b in range(B):
+        kwin[b].append(k[b])
+        vwin[b].append(v[b])
+        kk = np.stack(kwin[b][-W:])                         # [n][Hkv][D]
+        vv = np.stack(vwin[b][-W:])
+        for j in range(Hq):
+            z = scale * (kk[:, j // G] @ q[b, j])
+            p = np.exp(z - z.max())
+            attn[b, j] = (p @ vv[:, j // G]) / p.sum()
+    return attn
+
+
+def run_with_rows(net, weights, x, start: int, end: int, rows, fmt: str = "fp8"):
+    """As run(), but with the bf16 q, k and v rows of every (token, layer)
+    given instead of projected here: rows[t - start][layer] = (q [B][Hq][D],
+    k [B][Hkv][D], v [B][Hkv][D]), values exactly bf16.  Compares another
+    implementation's attention and residual stream with the oracle's on
+    identical inputs to the cache, so that no rounding of a projection can
+    flip a stored code.  Returns the final hidden states [B][end-start][d]
+    and the attention outputs [end-start][L][B][Hq][D]."""
+    B = x.shape[0]
+    Hq, Hkv, D, W = net.q_heads, net.kv_heads, net.head_dim, net.window
+    G = Hq // Hkv
+    ws = [tuple(np.asarray(m, np.float64) for m in layer) for layer in weights]
+    xs = np.asarray(x, np.float64)
+    kwin = [[[] for _ in range(B)] for _ in range(net.layers)]
+    vwin = [[[] for _ in range(B)] for _ in range(net.layers)]
+    out = np.zeros((B, end - start, net.d_model))
+    attns = np.zeros((end - start, net.layers, B, Hq, D))
+    scale = D ** -0.5
+    for t in range(start, end):
+        h = xs[:, t].copy()
+        for layer, (_, _, _, wo) in enumerate(ws):
+            q, k, v = (np.asarray(r, np.float64) for r in rows[t - start][layer])
+            assert np.array_equal(bf16_round(q), q) and np.array_equal(bf16_round(k), k), "rows must be bf16"
+            attn = _window_attention(q, _store(k, fmt), _store(v, fmt), kwin[layer], vwin[layer], W, G, scale)
+            attns[t - start, layer] = attn
+            h = h + attn.reshape(B, Hq * D) @ wo
+        out[:, t - start] = h
+    return out, attns
 
 
 def replay_lengths(net):

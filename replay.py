@@ -55,9 +55,11 @@ class ToySwaGpu:
         # that a replay lays its tokens out exactly as the full run does
         self.seq_base = torch.arange(net.batch, dtype=torch.int64, device=device) * self.pages_per_seq * fk.PAGE_SIZE
 
-    def run(self, x: torch.Tensor, start: int, end: int) -> torch.Tensor:
+    def run(self, x: torch.Tensor, start: int, end: int, record=None) -> torch.Tensor:
         """Final hidden states of tokens start .. end-1 ([B][end-start][d],
-        fp32), from empty windows."""
+        fp32), from empty windows.  With a list `record`, appends for every
+        token the (q, k, v) bf16 rows and the attention output of each layer
+        (CPU copies), then the layers' caches."""
         net = self.net
         B, Hq, Hkv, D = net.batch, net.q_heads, net.kv_heads, net.head_dim
         caches = [torch.zeros(self.layout.cache_bytes, dtype=torch.uint8, device=self.device)
@@ -75,8 +77,14 @@ class ToySwaGpu:
                 v = (u @ wv).to(torch.bfloat16).view(B, Hkv, D)
                 fk.quantize_append(self.layout, k, v, slots, caches[layer])
                 attn = fk.decode_window_attention(self.layout, caches[layer], q, lens, self.table, window)
+                if record is not None:
+                    if layer == 0:
+                        record.append([])
+                    record[-1].append((q.view(B, Hq, D).cpu(), k.cpu(), v.cpu(), attn.view(B, Hq, D).cpu()))
                 h = h + attn.view(B, Hq * D) @ wo
             out[:, t - start] = h
+        if record is not None:
+            record.append([c.cpu() for c in caches])
         return out
 
 

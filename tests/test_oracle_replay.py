@@ -76,3 +76,21 @@ def test_error_grows_with_depth():
         assert np.array_equal(exact, ref)
         errs.append(float(ts.relative_errors(bounded, ref).mean()))
     assert errs[0] < errs[1]
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "bf16"])
+def test_run_with_given_rows_reproduces_run(fmt):
+    """Fed the rows run() projects, run_with_rows() reproduces its hidden
+    states bit for bit (the two share the attention arithmetic, not the
+    projections); rows that are not bf16 are refused."""
+    net = wl.ToyNet("rows", layers=2, q_heads=4, kv_heads=2, head_dim=128, window=6, batch=2, tokens=20)
+    w, x = wl.toy_weights(net, 4), wl.toy_inputs(net, 4)
+    rows = []
+    ref = ts.run(net, w, x, 3, 20, fmt, record=rows)
+    assert len(rows) == 17 and len(rows[0]) == 2
+    out, attns = ts.run_with_rows(net, w, x, 3, 20, rows, fmt)
+    assert np.array_equal(out, ref)
+    assert attns.shape == (17, 2, 2, 4, 128) and np.isfinite(attns).all()
+    bad = [[(q + 1e-9, k, v) for q, k, v in layer] for layer in rows]
+    with pytest.raises(AssertionError):
+        ts.run_with_rows(net, w, x, 3, 20, bad, fmt)
