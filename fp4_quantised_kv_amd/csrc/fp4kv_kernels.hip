@@ -522,17 +522,23 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_valu(DecodeArgs a)
 
 // Merge the partials of one (sequence, query head): M = max_j m_j,
 // L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L.  Partials with
-// no tokens carry m = -inf and l = 0 and are skipped; a row with no tokens at
-// all is written as zeros.  One workgroup per row: each of its four waves
-// sums a quarter of the partials (lane c covering D/64 consecutive channels),
-// and the four sums are added in LDS.
+// no tokens carry m = -inf and l = 0 and are skipped (their outputs are not
+// read into the sums); a row with no tokens at all is written as zeros.  One
+// workgroup per row (rows with many partials are few: a small batch over a
+// long context).  Wave w takes every fourth batch of 16 partials, issues all
+// of a batch's loads -- the (m, l) pairs and lane c's D/64 channels of each
+// output -- before using any, and folds the batch into a running (M_w, L_w,
+// O_w) relative to its own maximum, so the row costs one memory round trip
+// per batch instead of a first pass for M; the four waves' states are then
+// merged once in LDS: out = sum_w O_w 2^(M_w - M) / sum_w L_w 2^(M_w - M).
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ ws_o,
                                                       const float *__restrict__ ws_ml, int num_q_heads,
                                                       int partials, float *__restrict__ out)
 {
     constexpr int CL = D / 64;                          // consecutive channels per lane
-    __shared__ float part[4][D + 1];                    // per wave: its output sum, then its weight sum
+    constexpr int NBT = 16;                             // partials a wave loads together
+    __shared__ float part[4][D + 2];                    // per wave: O_w, then L_w and M_w
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = blockIdx.x;                     // b * num_q_heads + query head
@@ -540,55 +546,92 @@ __global__ __launch_bounds__(256) void decode_combine(const float *__restrict__ 
     // partial j of this row: index (b * partials + j) * num_q_heads + hq
     const int64_t first = b * partials * num_q_heads + hq;
     const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + first;
+    const float *o = ws_o + first * D + lane * CL;
+    const int64_t stride = static_cast<int64_t>(num_q_heads) * D;
 
-    // the largest partial maximum, in every wave
-    float M = -INFINITY;
-    for (int j = lane; j < partials; j += 64)
-        M = fmaxf(M, ml[static_cast<int64_t>(j) * num_q_heads].x);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        M = fmaxf(M, __shfl_xor(M, o));
-
-    // wave w sums partials [w*per, (w+1)*per); the loads of one batch of
-    // partials are all in flight together
-    const int per = (partials + 3) / 4;
-    const int j0 = wave * per, j1 = min(partials, j0 + per);
-    float L = 0.0f, O[CL];
+    float Mw = -INFINITY, Lw = 0.0f, O[CL];
 #pragma unroll
     for (int i = 0; i < CL; ++i)
         O[i] = 0.0f;
-    if (M != -INFINITY) {
-        const float *o = ws_o + first * D + lane * CL;
-        const int64_t stride = static_cast<int64_t>(num_q_heads) * D;
-#pragma unroll 8
-        for (int j = j0; j < j1; ++j) {
-            const float2 mj = ml[static_cast<int64_t>(j) * num_q_heads];
-            const float w = mj.x == -INFINITY ? 0.0f : exp2f(mj.x - M);
-            L = fmaf(mj.y, w, L);
+    for (int j0 = wave * NBT; j0 < partials; j0 += 4 * NBT) {
+        const int n = min(NBT, partials - j0);
+        float2 mj[NBT];
+        float x[NBT][CL];
+        // the outputs' loads, then lane i < 16 loads pair i: one vector load
+        // for the batch's pairs, issued last, so that waiting for it (the
+        // counter is in order) waits for the whole batch, one round trip; as
+        // 16 scalar loads the pairs went out ahead of the outputs with a wait
+        // between.  Every lane then takes the 16 pairs with readlane.
+#pragma unroll
+        for (int i = 0; i < NBT; ++i) {
+            const int64_t jj = j0 + (i < n ? i : n - 1);     // past the last: re-read it, weight zero below
+#pragma unroll
+            for (int c = 0; c < CL; ++c)
+                x[i][c] = o[jj * stride + c];
+        }
+        const int li = lane < n ? lane : n - 1;
+        const float2 my = ml[static_cast<int64_t>(j0 + (li < NBT ? li : NBT - 1)) * num_q_heads];
+        // the scheduler would otherwise hoist the pair load and its readlanes
+        // above most of the output loads (one more round trip)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NBT; ++i) {
+            mj[i].x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my.x), i));
+            mj[i].y = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my.y), i));
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NBT; ++i)
+            mb = i < n ? fmaxf(mb, mj[i].x) : mb;
+        // no branch on an empty batch (it would let the compiler sink the
+        // output loads below a wait for the pairs): with Mn = -inf every
+        // weight below is 0 and the state stays as it is
+        const float Mn = fmaxf(Mw, mb);
+        const float alpha = Mw == -INFINITY ? 0.0f : exp2f(Mw - Mn);
+        Lw *= alpha;
+#pragma unroll
+        for (int c = 0; c < CL; ++c)
+            O[c] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NBT; ++i) {
+            const float w = (i < n && mj[i].x != -INFINITY) ? exp2f(mj[i].x - Mn) : 0.0f;
+            Lw = fmaf(mj[i].y, w, Lw);
             // an empty partial's outputs are not meaningful (not written):
             // a zero weight leaves the sums as they are
-            if constexpr (CL == 2) {
-                const float2 x = *reinterpret_cast<const float2 *>(o + j * stride);
-                O[0] = w != 0.0f ? fmaf(x.x, w, O[0]) : O[0];
-                O[1] = w != 0.0f ? fmaf(x.y, w, O[1]) : O[1];
-            } else {
-                O[0] = w != 0.0f ? fmaf(o[j * stride], w, O[0]) : O[0];
-            }
+#pragma unroll
+            for (int c = 0; c < CL; ++c)
+                O[c] = w != 0.0f ? fmaf(x[i][c], w, O[c]) : O[c];
         }
+        Mw = Mn;
     }
 #pragma unroll
-    for (int i = 0; i < CL; ++i)
-        part[wave][lane * CL + i] = O[i];
-    if (lane == 0)
-        part[wave][D] = L;
+    for (int c = 0; c < CL; ++c)
+        part[wave][lane * CL + c] = O[c];
+    if (lane == 0) {
+        part[wave][D] = Lw;
+        part[wave][D + 1] = Mw;
+    }
     __syncthreads();
     if (wave == 0) {
-        const float Lt = part[0][D] + part[1][D] + part[2][D] + part[3][D];
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            M = fmaxf(M, part[w][D + 1]);
+        float sc[4], Lt = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            sc[w] = part[w][D + 1] == -INFINITY ? 0.0f : exp2f(part[w][D + 1] - M);
+            Lt = fmaf(part[w][D], sc[w], Lt);
+        }
         const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
 #pragma unroll
         for (int i = 0; i < CL; ++i) {
             const int c = lane * CL + i;
-            out[row * D + c] = (part[0][c] + part[1][c] + part[2][c] + part[3][c]) * inv;
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                acc = sc[w] != 0.0f ? fmaf(part[w][c], sc[w], acc) : acc;
+            out[row * D + c] = acc * inv;
         }
     }
 }
