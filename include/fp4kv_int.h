@@ -116,7 +116,10 @@ FP4KV_API int fp4kv_int_decode_plan(const fp4kv_int_dims *dims, int32_t num_q_he
  * scales are applied where they factor out: a per-token K scale multiplies
  * the token's score, a per-channel K scale multiplies q, a per-token V scale
  * multiplies the token's weight, a per-channel V scale multiplies the
- * output.  Accumulation is fp32; the splits are merged by the combine
+ * output.  Both products run on the matrix cores with bf16 operands that
+ * hold the stored values exactly (the query exactly too; times per-channel
+ * K scales, as three bf16 terms) and the weights as two bf16 terms (~2^-15
+ * relative); accumulation is fp32.  The splits are merged by the combine
  * kernel of fp4kv_decode_combine.
  *   q           device bf16 [B][num_q_heads][D], 16-B aligned.
  *   k_*, v_*    as written by fp4kv_int_quantize with these dims.

@@ -18,13 +18,15 @@ integer formats and FP8 with per-token / per-channel scales.  For each format:
 against the bf16 cache's output o_ref, and bits per number from the bytes
 the format stores.  With --time, each format's decode is also timed on a
 larger workload (inputs drawn on the GPU with the same distributions) and
-its cache bytes per second reported, with the kind of kernel that decodes
-it: FP4 and per-tensor FP8 run on the matrix-core split-K kernels (the
-product path, 70-80 % of the HBM peak); bf16, the integer formats and FP8
-with per-token / per-channel scales on a vector-ALU split-K kernel built for
-the sweep, which is ALU-bound (10-25 % of peak).  The times therefore
-compare kernel designs as much as formats: only the error and bits columns
-compare the formats themselves.
+its cache bytes per second reported, with the kernel that decodes it.
+Every format decodes on the matrix cores: FP4 and per-tensor FP8 on the
+product path's split-K kernels (paged cache), bf16, the integer formats and
+FP8 with per-token / per-channel scales on the sweep's own split-K kernel
+(contiguous rows), which turns each stored code into an exact bf16 operand
+on the vector ALUs.  That conversion costs about the same per number at
+every width, so the narrow formats (INT4, INT2) are bound by it rather than
+by their few bytes: their rates fall below the 8-bit formats' while their
+times stay close.
 
     python sweep.py                       # error table, 4096-token workload
     python sweep.py --workload tiny_d64_ctx256
@@ -175,7 +177,7 @@ def timing_table(name, seed, reps, device="cuda"):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         nbytes = p.stored_bytes + q.numel() * 2 + out.numel() * 4
-        kernel = "matrix-core split-K" if kind in ("fp4", "fp8") else "vector-ALU split-K (sweep)"
+        kernel = "matrix-core split-K, paged" if kind in ("fp4", "fp8") else "matrix-core split-K, sweep formats"
         rows.append((fname, p.bits_per_number, ms, nbytes / (ms * 1e-3) / 1e9, kernel))
         print(f"# timed {fname}: {ms:.4f} ms", file=sys.stderr, flush=True)
         del p, ws, out
@@ -210,12 +212,13 @@ def main():
     if args.time:
         t = timing_table(args.time, args.seed, args.reps)
         result["timing"] = {"workload": args.time, "reps": args.reps,
-                            "note": "the formats decode on different kernels (see 'kernel'): the times "
-                                    "compare kernel designs as much as formats",
+                            "note": "every format decodes on the matrix cores ('kernel': the paged "
+                                    "product kernels or the sweep formats' kernel); the narrow integer "
+                                    "formats are bound by converting codes to operands, not by bytes",
                             "rows": [{"format": r[0], "bits_per_number": round(r[1], 6), "kernel": r[4],
                                       "decode_ms": round(r[2], 5), "gbs": round(r[3], 1),
                                       "pct_of_peak_hbm": round(100.0 * r[3] / 8000.0, 1)} for r in t]}
-        print(f"# decode on {args.time} (the kernel column: the times compare kernel designs as much as formats)",
+        print(f"# decode on {args.time} (INT4 / INT2: bound by converting codes to matrix-core operands)",
               file=sys.stderr)
         for r in t:
             print(f"  {r[0]:36s} {r[1]:8.4f} bits  {r[2]:9.4f} ms  {r[3]:8.1f} GB/s  {100.0 * r[3] / 8000.0:5.1f} %  "

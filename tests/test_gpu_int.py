@@ -110,6 +110,9 @@ def _oracle_values(x, bits, gran):
     bits_ = wl.bf16_bits(x)
     if bits == 16:
         return oracle.bf16_values(bits_)
+    if bits == fk.INT_FP8_E4M3:
+        c, s = oracle.quantize_fp8_groups(bits_, gran)
+        return oracle.dequantize_fp8_groups(c, s, gran)
     c, s = oracle.quantize_int(bits_, bits, gran)
     return oracle.dequantize_int(c, s, gran)
 
@@ -173,5 +176,33 @@ def test_decode_workload_shape():
           for b in range(w.batch)]
     ref = oracle.decode_attention_values(wl.bf16_bits(q), kv, vv, [T] * w.batch, 128 ** -0.5, heads=heads)
     err = max(float(hx.row_rel_error(out[b], ref[b]).max()) for b in (0, 5))
+    _say(f"  worst per-row relative error {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("bits,kg", [(16, "token"), (8, "token"), (4, "channel"), (2, "token"),
+                                     (fk.INT_FP8_E4M3, "token")])
+def test_decode_rising_scores_long_split(bits, kg):
+    """Scores that grow along the sequence, so each wave's running maximum
+    moves block after block, over one split per (sequence, head) of 5,000
+    tokens (every wave takes many blocks, the last one partial)."""
+    B, T, H, G, D = 2, 5000, 2, 8, 128
+    g = torch.Generator().manual_seed(bits)
+    q = torch.randn(B, H * G, D, generator=g)
+    direction = q.view(B, H, G, D).mean(2)                      # [B][H][D]
+    ramp = torch.linspace(0, 6, T).view(1, T, 1, 1)
+    k = (torch.randn(B, T, H, D, generator=g) + ramp * direction.view(B, 1, H, D)).to(torch.bfloat16)
+    v = torch.randn(B, T, H, D, generator=g).to(torch.bfloat16)
+    q = q.to(torch.bfloat16)
+    _say(f"int decode, rising scores: bits {bits}, K per {kg}, T {T}, one split")
+    kq = fk.int_quantize(k.cuda(), bits, kg)
+    vq = fk.int_quantize(v.cuda(), bits, "token")
+    out = fk.int_decode_attention(q.cuda(), bits, kq, vq, T, kg, "token", num_splits=1)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    kv = [_oracle_values(k[b], bits, kg) for b in range(B)]
+    vv = [_oracle_values(v[b], bits, "token") for b in range(B)]
+    ref = oracle.decode_attention_values(wl.bf16_bits(q), kv, vv, [T] * B, D ** -0.5)
+    err = float(hx.row_rel_error(out, ref).max())
     _say(f"  worst per-row relative error {err:.3e}")
     assert err <= TOL
