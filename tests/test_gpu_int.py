@@ -206,3 +206,29 @@ def test_decode_rising_scores_long_split(bits, kg):
     err = float(hx.row_rel_error(out, ref).max())
     _say(f"  worst per-row relative error {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("bits,kg,vg", [(16, "token", "token")] +
+                         [(b, g, g) for b in (8, 4, 2, fk.INT_FP8_E4M3) for g in ("token", "channel")])
+def test_decode_single_token_returns_stored_values_exactly(bits, kg, vg):
+    """With one token of context every head's softmax weight is exactly 1,
+    so each output row must be the stored V row itself, bit for bit: this
+    pins the value path's channel order, the code conversion and the removal
+    of the INT4 / INT2 offset (all exact by construction)."""
+    for G, D in ((4, 128), (16, 64)):
+        B, H = 3, 2
+        g = torch.Generator().manual_seed(bits + G)
+        k = torch.randn(B, 1, H, D, generator=g).to(torch.bfloat16)
+        v = (torch.randn(B, 1, H, D, generator=g) * torch.exp(torch.empty(H, D).uniform_(-2, 2, generator=g))
+             ).to(torch.bfloat16)
+        q = torch.randn(B, H * G, D, generator=g).to(torch.bfloat16)
+        _say(f"int decode, one token: bits {bits}, K per {kg}, V per {vg}, G {G}, D {D}")
+        kq = fk.int_quantize(k.cuda(), bits, kg)
+        vq = fk.int_quantize(v.cuda(), bits, vg)
+        out = fk.int_decode_attention(q.cuda(), bits, kq, vq, 1, kg, vg)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        for b in range(B):
+            vv = _oracle_values(v[b], bits, vg)[0]                    # [H][D], float64, exact in fp32
+            want = np.repeat(vv, G, axis=0).astype(np.float32)
+            assert np.array_equal(out[b], want), (b, np.abs(out[b] - want).max())
