@@ -321,10 +321,14 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_fp8(DecodeArgs a)
     const CacheGeom &g = a.geom;
 
     // grid (KV head, sequence, partial), as for the FP4 kernel
-    const Chunk c = chunk_of(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
-    const int ids = chunk_ids(a, c, wave, lane);
+    Chunk c = chunk_start(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
+    int ids = chunk_ids(a, c, wave, lane);
     uint32_t qbits[kD / 8];
     load_q_bits<kD>(a, c.b, c.h, col, jj, qbits);
+    // the length only now, so that its load overlaps the ones above
+    __builtin_amdgcn_sched_barrier(0);
+    chunk_clamp(a, c);
+    ids = chunk_ids_moved(a, c, wave, lane, ids);
     if (!a.out && group_chunks_empty(a, c, wave)) {     // every chunk of the workgroup past the context
         mark_partial_empty(a, c.b, c.h, c.part);
         return;

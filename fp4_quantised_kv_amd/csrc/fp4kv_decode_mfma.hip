@@ -380,12 +380,18 @@ __global__ __launch_bounds__(kGroupThreads) void decode_split_mfma(DecodeArgs a)
     // dispatched first, and consecutive workgroups -- which the hardware
     // deals round-robin to the XCDs -- belong to different KV heads.  Every
     // independent load is issued before any is waited on.
-    const Chunk c = chunk_of(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
-    const int ids = STAGED ? chunk_ids(a, c, wave, lane) : -1;
+    Chunk c = chunk_start(a, blockIdx.x, blockIdx.y, blockIdx.z, wave);
+    int ids = STAGED ? chunk_ids(a, c, wave, lane) : -1;
     uint32_t qbits[D / 8];
     load_q_bits<D>(a, c.b, c.h, col, jj, qbits);
-    // (the loads above are issued first so that they need not wait for the
-    // length; an empty workgroup leaves them unused)
+    // the length is read only now: issued earlier, its scalar load would
+    // join the wait for the kernel arguments the loads above need, and
+    // delay them by a memory round trip (an empty workgroup leaves them
+    // unused)
+    __builtin_amdgcn_sched_barrier(0);
+    chunk_clamp(a, c);
+    if constexpr (STAGED)
+        ids = chunk_ids_moved(a, c, wave, lane, ids);
     if (!a.out && group_chunks_empty(a, c, wave)) {
         mark_partial_empty(a, c.b, c.h, c.part);
         return;

@@ -267,23 +267,43 @@ struct Chunk {
     const int32_t *ptab;
 };
 
-__device__ __forceinline__ Chunk chunk_of(const DecodeArgs &a, int h, int b, int part, int wave)
+// The part of a wave's chunk that needs no memory read: its unshifted first
+// page and page count.  The page ids load from here.
+__device__ __forceinline__ Chunk chunk_start(const DecodeArgs &a, int h, int b, int part, int wave)
 {
     Chunk c;
     c.h = h; c.b = b; c.part = part;
     c.ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages;
     const int k = part * kWavesPerGroup + wave;
-    int len = a.seq_lens[b];
+    c.p0 = chunk_first_page(a, k);
+    c.p1 = c.p0 + chunk_pages(a, k);
+    c.len = 0;
+    return c;
+}
+
+// The part that needs the context length: the length itself, the window's
+// shift of the start and the end clamped to the context.  Kernels read it
+// after issuing the loads that do not need it, so that its load overlaps
+// theirs instead of preceding them.
+__device__ __forceinline__ void chunk_clamp(const DecodeArgs &a, Chunk &c)
+{
+    int len = a.seq_lens[c.b];
     len = len < 0 ? 0 : (len > a.max_pages * kPage ? a.max_pages * kPage : len);
     c.len = len;
-    c.p0 = chunk_first_page(a, k);
+    const int pages = c.p1 - c.p0;
     if (a.window > 0) {
         // chunks start at the page of the earliest token any query column
         // sees: the first query token's prefix end minus the window
         const int first = len - ((a.q_tokens > 1 ? a.q_tokens : 1) - 1) - a.window;
         c.p0 += first > 0 ? first / kPage : 0;
     }
-    c.p1 = min(c.p0 + chunk_pages(a, k), (len + kPage - 1) / kPage);
+    c.p1 = min(c.p0 + pages, (len + kPage - 1) / kPage);
+}
+
+__device__ __forceinline__ Chunk chunk_of(const DecodeArgs &a, int h, int b, int part, int wave)
+{
+    Chunk c = chunk_start(a, h, b, part, wave);
+    chunk_clamp(a, c);
     return c;
 }
 
@@ -324,18 +344,22 @@ __device__ __forceinline__ int ids_from(const DecodeArgs &a, const int32_t *ptab
     return p0 + lane < end ? ptab[p0 + lane] : -1;
 }
 
-// The chunk's page ids, loaded from its unshifted start so that the load
-// waits for nothing but the kernel arguments: only a window moves the start
-// (by an amount that depends on the length), and then the ids are loaded
-// again from the moved start.  Written as one address computed from the
-// length, the load would wait a further memory round trip for it.
+// The chunk's page ids, loaded from its unshifted start (a chunk_start
+// value) so that the load waits for nothing but the kernel arguments.
 __device__ __forceinline__ int chunk_ids(const DecodeArgs &a, const Chunk &c, int wave, int lane)
 {
     const int k = c.part * kWavesPerGroup + wave;
-    const int base = chunk_first_page(a, k), pages = chunk_pages(a, k);
-    int ids = ids_from(a, c.ptab, base, pages, lane);
-    if (a.window > 0 && c.p0 != base)
-        ids = ids_from(a, c.ptab, c.p0, pages, lane);
+    return ids_from(a, c.ptab, chunk_first_page(a, k), chunk_pages(a, k), lane);
+}
+
+// After chunk_clamp: only a window moves the start (by an amount that
+// depends on the length), and then the ids are loaded again from the moved
+// start.
+__device__ __forceinline__ int chunk_ids_moved(const DecodeArgs &a, const Chunk &c, int wave, int lane, int ids)
+{
+    const int k = c.part * kWavesPerGroup + wave;
+    if (a.window > 0 && c.p0 != chunk_first_page(a, k))
+        ids = ids_from(a, c.ptab, c.p0, chunk_pages(a, k), lane);
     return ids;
 }
 
