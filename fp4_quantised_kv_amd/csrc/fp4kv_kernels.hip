@@ -151,14 +151,34 @@ __global__ __launch_bounds__(256) void append_slices_kernel(
     const int head = static_cast<int>(sh % g.num_kv_heads);
     const int64_t t0 = (sh / g.num_kv_heads) * 16;
     const int n = static_cast<int>(n_tokens - t0 < 16 ? n_tokens - t0 : 16);
-    const int64_t s0 = slots[t0];
-    bool whole = n == 16 && s0 >= 0 && s0 % 16 == 0 && s0 + 16 <= g.num_pages * kPage;
-    for (int i = 1; i < n && whole; ++i)
-        whole = slots[t0 + i] == s0 + i;
-
     const int64_t row_stride = static_cast<int64_t>(g.num_kv_heads) * D;   // one input token
     const uint16_t *ksrc = k + t0 * row_stride + head * D + 16 * blk;
     const uint16_t *vsrc = v + t0 * row_stride + head * D + 16 * blk;
+
+    uint32_t w[2][4][8];                                // rows of two rounds
+    auto load_round = [&](int r, uint32_t (&rows)[4][8]) {
+        const uint16_t *src = (r < 4 ? ksrc : vsrc) + 4 * (r & 3) * row_stride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            load_block16(src + i * row_stride, rows[i]);
+    };
+    // The slice's 16 slots with all their loads in flight at once (a loop
+    // that stops at the first break issues them one at a time, each after
+    // the last has arrived), and the first round of K rows beside them:
+    // neither needs the other, so the check costs no round trip of its own.
+    // (When the slice is not whole the rows go unused.)
+    int64_t sl[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        sl[i] = i < n ? slots[t0 + i] : -1;
+    if (n == 16)
+        load_round(0, w[0]);
+    asm volatile("" ::: "memory");
+    const int64_t s0 = sl[0];
+    bool whole = n == 16 && s0 >= 0 && s0 % 16 == 0 && s0 + 16 <= g.num_pages * kPage;
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+        whole = whole & (sl[i] == s0 + i);
     if (!whole) {
         for (int i = 0; i < n; ++i)
             append_token_fp4<D>(g, ksrc + i * row_stride, vsrc + i * row_stride, slots[t0 + i], head, blk, cache);
@@ -178,16 +198,8 @@ __global__ __launch_bounds__(256) void append_slices_kernel(
     // 8 tokens the codes come out token-major (dword i = token i, nibble c =
     // channel c); an 8 x 8 nibble transpose makes them channel-major (dword
     // c = channel c, nibble i = token i), which is a V code row's half.
-    uint32_t w[2][4][8];                                // rows of two rounds
     uint32_t vd[2][16];                                 // [token half][channel]
     uint32_t vs[4] = {0u, 0u, 0u, 0u};
-    auto load_round = [&](int r, uint32_t (&rows)[4][8]) {
-        const uint16_t *src = (r < 4 ? ksrc : vsrc) + 4 * (r & 3) * row_stride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            load_block16(src + i * row_stride, rows[i]);
-    };
-    load_round(0, w[0]);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         if (r + 1 < 8)
