@@ -203,6 +203,32 @@ def test_contiguous_runs_aligned_or_not(first_slot, n):
             assert (vc[s] == (nib | nib << 4)).all()
 
 
+@pytest.mark.parametrize("H,D,first_slot,n", [(16, 128, 0, 1024), (16, 128, 5, 700), (32, 64, 16, 640),
+                                              (2, 128, 0, 512), (16, 64, 32, 544)])
+def test_slices_at_other_row_widths(H, D, first_slot, n):
+    """The slice kernel where a wave's 64 blocks are part of a token row
+    (H_kv 16 at D 128, H_kv 32 at D 64), exactly one row (H_kv 16 at D 64)
+    or several tokens' rows (H_kv 2): the oracle's bytes at every slot,
+    whole and misaligned slices alike."""
+    g = torch.Generator().manual_seed(H * 1000 + D + first_slot)
+    f = torch.exp(torch.empty(H, D).uniform_(-2.0, 2.0, generator=g))
+    k = (torch.randn(n, H, D, generator=g) * f).to(torch.bfloat16)
+    v = (torch.randn(n, H, D, generator=g) * f.flip(1)).to(torch.bfloat16)
+    pages = -(-(first_slot + n) // 64)
+    layout = fk.cache_layout(H, D, pages)
+    cache = torch.zeros(layout.cache_bytes, dtype=torch.uint8, device="cuda")
+    slots = torch.arange(first_slot, first_slot + n, dtype=torch.int64)
+    _say(f"quantize_append: H_kv {H}, D {D}, {n} tokens from slot {first_slot}")
+    fk.quantize_append(layout, k.cuda(), v.cuda(), slots.cuda(), cache)
+    torch.cuda.synchronize()
+    kc, ks, vc, vs = hx.read_pages(cache, layout, list(range(pages)), pages * 64)
+    ek, eks = _expect(k)
+    ev, evs = _expect(v)
+    sl = slice(first_slot, first_slot + n)
+    assert np.array_equal(kc[sl], ek) and np.array_equal(ks[sl], eks)
+    assert np.array_equal(vc[sl], ev) and np.array_equal(vs[sl], evs)
+
+
 def test_skipped_slots_leave_bytes_untouched():
     w = wl.WORKLOADS["gqa4_b8_ctx4k"]
     k = wl.kv_tokens(w, 6, 0, "k", 0, 6)
