@@ -4,13 +4,19 @@
 Headline workload: 32 sequences of 32768 tokens, 64 query heads over 8 KV
 heads (group 8), head dim 128, 64 context splits -- 1.2 GB of packed cache,
 larger than the GPU's last-level cache, so every step streams it from HBM.  A
-step is one fp4kv_decode_attention call (split kernel + combine kernel; the
-split kernel alone when there is one partial per row); for the paged
-workload it is one fp4kv_decode_append_attention call, whose split kernel
-first stores each sequence's new token (--unfused: a separate
-quantize_append call, then decode_attention).  The per-kernel breakdown runs
-the same steps as their halves with events between launches.  The cache, the
-queries and every argument are resident on the device before timing starts.
+step is one decode-attention call (split kernel + combine kernel; the split
+kernel alone when there is one partial per row) through
+fp4kv_decode_with_options, given the batch's shortest length (min_seq_len:
+host knowledge a serving caller has; it only sizes the context chunks, and
+sends a uniform batch's last workgroups one-page chunks).  For the paged
+workload the call appends: its split kernel first stores each sequence's new
+token (--unfused: a separate quantize_append call, then the decode).  The
+same step through the plain entry point (fp4kv_decode_attention or
+fp4kv_decode_append_attention, which know no lengths) is timed beside it and
+reported as "plain_entry_point"; --no-length-hint times the plain calls'
+chunking throughout.  The per-kernel breakdown runs the same steps as their
+halves with events between launches.  The cache, the queries and every
+argument are resident on the device before timing starts.
 
 Prints one JSON line: achieved HBM GB/s over the step's algorithmic bytes
 (packed K/V read, queries read, outputs written, page-table and length
@@ -306,12 +312,14 @@ class DecodeRun:
     """One decode workload's cache on the device, its per-step inputs and the
     calls that make a step."""
 
-    def __init__(self, fk, hx, wl, w, seed, fmt, dev, n_steps, splits=None, unfused=False, kernel="auto"):
+    def __init__(self, fk, hx, wl, w, seed, fmt, dev, n_steps, splits=None, unfused=False, kernel="auto",
+                 length_hint=True):
         import torch
         self.fk, self.w, self.fmt, self.dev = fk, w, fmt, dev
         self.paged = w.kind == "paged"
         self.fused = self.paged and not unfused
         self.kernel = kernel
+        self.length_hint = length_hint
         self.splits_req = w.splits if splits is None else splits
         t_setup = time.perf_counter()
         print(f"# building cache for {w.name}: {w.description}", file=sys.stderr, flush=True)
@@ -324,6 +332,8 @@ class DecodeRun:
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         self.out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
         self.lens0 = gc.lens_cpu.clone()
+        # the shortest length of every step (a paged step adds one token per sequence first)
+        self.min_len = int(self.lens0.min()) + (1 if self.paged else 0) if length_hint else 0
         self.scale = D ** -0.5
         # per-step inputs, all on the device before timing
         self.qs = [wl.queries(w, seed, step=s if self.paged else 0).to(dev) for s in range(n_steps if self.paged else 1)]
@@ -345,17 +355,29 @@ class DecodeRun:
     def lens(self, s):
         return self.lens_dev[s % len(self.lens_dev)]
 
+    def chunks(self):
+        """The chunk cut the steps use (fp4kv_decode_chunks)."""
+        w = self.w
+        return self.fk.decode_chunks(self.gc.layout, w.batch, w.q_heads, self.gc.page_table.shape[1],
+                                     self.splits_req, min_seq_len=self.min_len)
+
     def step(self, s):
-        """One step through the library's entry point, as a caller makes it."""
+        """One step through the library's entry point, as a caller makes it:
+        with the batch's shortest length (and the kernel asked for)."""
         fk, gc, L = self.fk, self.gc, self.gc.layout
         if self.paged and not self.fused:
             fk.quantize_append(L, self.news[s][0], self.news[s][1], self.slots[s], gc.cache)
-        if self.kernel != "auto":
-            kv = dict(k_new=self.news[s][0], v_new=self.news[s][1]) if self.fused else {}
-            fk.decode_with_options(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
-                                   num_splits=self.splits_req, workspace=self.ws, out=self.out, kernel=self.kernel,
-                                   **kv)
-        elif self.fused:
+        kv = dict(k_new=self.news[s][0], v_new=self.news[s][1]) if self.fused else {}
+        fk.decode_with_options(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
+                               num_splits=self.splits_req, workspace=self.ws, out=self.out, kernel=self.kernel,
+                               min_seq_len=self.min_len, **kv)
+
+    def step_plain(self, s):
+        """The same step through the entry point that knows no lengths."""
+        fk, gc, L = self.fk, self.gc, self.gc.layout
+        if self.paged and not self.fused:
+            fk.quantize_append(L, self.news[s][0], self.news[s][1], self.slots[s], gc.cache)
+        if self.fused:
             fk.decode_append_attention(L, gc.cache, self.news[s][0], self.news[s][1], self.q(s), self.lens(s),
                                        gc.page_table, softmax_scale=self.scale, num_splits=self.splits_req,
                                        workspace=self.ws, out=self.out)
@@ -368,16 +390,13 @@ class DecodeRun:
             self.fk.quantize_append(self.gc.layout, self.news[s][0], self.news[s][1], self.slots[s], self.gc.cache)
 
     def split(self, s, append=True):
-        """The split kernel of step s (storing the step's new tokens itself
-        when the step is fused and `append`)."""
+        """The split kernel of step s as the step launches it (storing the
+        step's new tokens itself when the step is fused and `append`)."""
         fk, gc, L = self.fk, self.gc, self.gc.layout
-        if self.fused and append:
-            fk.decode_append_split(L, gc.cache, self.news[s][0], self.news[s][1], self.q(s), self.lens(s),
-                                   gc.page_table, softmax_scale=self.scale, num_splits=self.splits_req,
-                                   workspace=self.ws)
-        else:
-            fk.decode_split(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
-                            num_splits=self.splits_req, workspace=self.ws)
+        kv = dict(k_new=self.news[s][0], v_new=self.news[s][1]) if self.fused and append else {}
+        fk.decode_with_options(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
+                               num_splits=self.splits_req, workspace=self.ws, kernel=self.kernel, merge="none",
+                               min_seq_len=self.min_len, **kv)
 
     def combine(self):
         w = self.w
@@ -429,6 +448,15 @@ def decode_record(torch, run, stream, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / steps
+    # the same steps through the plain entry point (no length known), back to
+    # back; the paged appends rewrite the same slots with the same bytes
+    e0, e1 = _events(torch)
+    e0.record(stream)
+    for s in range(warmup, warmup + steps):
+        run.step_plain(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_plain = e0.elapsed_time(e1) / steps
     # per-kernel breakdown: the same steps again (appends rewrite the same
     # slots with the same bytes), with an event between launches
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -469,10 +497,19 @@ def decode_record(torch, run, stream, steps, warmup):
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     split_bytes_b2b = run.split_bytes(ctx_last)
     split_gbs = split_bytes_b2b / (t_split_b2b * 1e-3) / 1e9
+    plain_gbs = step_bytes / (t_plain * 1e-3) / 1e9
+    plain_call = "fp4kv_decode_append_attention" if run.fused else "fp4kv_decode_attention"
     return {
         "workload": w.name, "ms_per_step": round(ms_per_step, 5), "gbs": round(gbs, 2),
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2), "decode_steps_per_s": round(1e3 / ms_per_step, 2),
         "step_bytes": int(step_bytes), "splits": run.splits, "partials": run.partials,
+        "min_seq_len": run.min_len, "chunks": dict(zip(("lead_chunks", "lead_pages", "tail_pages"), run.chunks())),
+        "plain_entry_point": {"call": plain_call, "chunks": dict(zip(("lead_chunks", "lead_pages", "tail_pages"),
+                                                                     run.fk.decode_chunks(run.gc.layout, B, Hq,
+                                                                                          run.gc.page_table.shape[1],
+                                                                                          run.splits_req))),
+                              "ms_per_step": round(t_plain, 5), "gbs": round(plain_gbs, 2),
+                              "pct_of_peak_hbm": round(100.0 * plain_gbs / PEAK_HBM_GBS, 2)},
         "append": (None if not run.paged else "fused into the split kernel" if run.fused else "quantize_append"),
         "kernel_ms": {"append": round(t_append, 5), "decode_split": round(t_split, 5),
                       "decode_combine": round(t_comb, 5), "decode_split_back_to_back": round(t_split_b2b, 5)},
@@ -588,6 +625,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="paged workload: append with quantize_append, then decode (default: the decode "
                          "kernel stores the new tokens itself)")
+    ap.add_argument("--no-length-hint", action="store_true",
+                    help="time the steps without the batch's shortest length (the plain entry points' chunking)")
     ap.add_argument("--kernel", choices=("auto", "mfma_staged", "mfma_direct", "valu"),
                     default="auto", help="split kernel of the timed steps (through fp4kv_decode_with_options "
                                          "unless auto)")
@@ -636,7 +675,7 @@ def main():
         raise SystemExit("the prefill workload is timed under configs (or alone with --prefill-only), "
                          "not as a decode step")
     run = DecodeRun(fk, hx, wl, w, args.seed, args.format, dev, args.warmup + args.steps, splits=args.splits,
-                    unfused=args.unfused, kernel=args.kernel)
+                    unfused=args.unfused, kernel=args.kernel, length_hint=not args.no_length_hint)
     head = decode_record(torch, run, stream, args.steps, args.warmup)
     L = run.gc.layout
     result = {
@@ -655,9 +694,10 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "head_dim": w.head_dim, "context": w.context if not run.paged else f"{w.min_len}..{w.max_len}",
                    "format": FORMAT_NAMES[args.format], "splits": run.splits, "partials": run.partials,
-                   "page_size": 64, "cache_bytes": L.cache_bytes},
+                   "page_size": 64, "cache_bytes": L.cache_bytes, "min_seq_len": head["min_seq_len"],
+                   "chunks": head["chunks"]},
     }
-    result.update({k: head[k] for k in ("decode_steps_per_s", "pct_of_peak_hbm", "append")})
+    result.update({k: head[k] for k in ("decode_steps_per_s", "pct_of_peak_hbm", "append", "plain_entry_point")})
     result["kernel"] = args.kernel
     result.update({k: head[k] for k in ("kernel_ms", "wall_s_timed", "host_enqueue_ms_per_step")})
     result["settle_decode_calls"] = SETTLE_CALLS
@@ -681,7 +721,8 @@ def main():
             if name == w.name:
                 continue
             cw = wl.WORKLOADS[name]
-            r = DecodeRun(fk, hx, wl, cw, args.seed, "fp4", dev, args.warmup + args.config_steps)
+            r = DecodeRun(fk, hx, wl, cw, args.seed, "fp4", dev, args.warmup + args.config_steps,
+                          length_hint=not args.no_length_hint)
             if r.gc.layout.cache_bytes < LLC_BYTES and not r.paged:
                 configs[name] = cold_warm(torch, r, stream)
             else:

@@ -92,11 +92,11 @@ class CacheLayout(ctypes.Structure):
 
 class DecodeOptions(ctypes.Structure):
     """fp4kv_decode_options: the split kernel and how partials are merged."""
-    _fields_ = [("kernel", ctypes.c_int32), ("merge", ctypes.c_int32)]
+    _fields_ = [("kernel", ctypes.c_int32), ("merge", ctypes.c_int32), ("min_seq_len", ctypes.c_int32)]
 
 
 DECODE_KERNELS = {"auto": 0, "mfma_staged": 1, "mfma_direct": 2, "valu": 3}
-DECODE_MERGES = {"auto": 0, "combine_kernel": 1}
+DECODE_MERGES = {"auto": 0, "combine_kernel": 1, "none": 2}
 
 _LIB = None
 _P = ctypes.c_void_p
@@ -174,7 +174,7 @@ def library():
         L.fp4kv_read_probe_config.restype = ctypes.c_int
         L.fp4kv_decode_chunks.argtypes = [ctypes.POINTER(CacheLayout), ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]
         L.fp4kv_decode_chunks.restype = ctypes.c_int
         L.fp4kv_stream_probe.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -280,12 +280,12 @@ class DecodeChunks(tuple):
 
 
 def decode_chunks(layout: CacheLayout, batch: int, num_q_heads: int, max_pages_per_seq: int,
-                  num_splits: int = 0, q_tokens: int = 1, window: int = 0) -> DecodeChunks:
+                  num_splits: int = 0, q_tokens: int = 1, window: int = 0, min_seq_len: int = 0) -> DecodeChunks:
     """Chunk page counts a decode call with these arguments uses
-    (fp4kv_decode_chunks)."""
+    (fp4kv_decode_chunks); min_seq_len as decode_with_options takes it."""
     lc, lp, tp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check("fp4kv_decode_chunks", library().fp4kv_decode_chunks(
-        ctypes.byref(layout), batch, q_tokens, num_q_heads, max_pages_per_seq, window, num_splits,
+        ctypes.byref(layout), batch, q_tokens, num_q_heads, max_pages_per_seq, window, num_splits, min_seq_len,
         ctypes.byref(lc), ctypes.byref(lp), ctypes.byref(tp)))
     return DecodeChunks(lc.value, lp.value, tp.value)
 
@@ -515,12 +515,15 @@ def decode_window_attention(layout: CacheLayout, cache, q, seq_lens, page_table,
 
 def decode_with_options(layout: CacheLayout, cache, q, seq_lens, page_table, k_new=None, v_new=None, window=0,
                         softmax_scale=None, num_splits: int = 0, workspace=None, out=None, kernel="auto",
-                        merge="auto", stream=None):
+                        merge="auto", min_seq_len: int = 0, stream=None):
     """fp4kv_decode_with_options: any decode call with an explicit split
-    kernel ("auto", "mfma_staged", "mfma_direct", "valu") and merge ("auto",
-    "combine_kernel").  q is bf16 [B][Hq][D] (one query token; the result is
-    [B][Hq][D]) or [B][S][Hq][D]; k_new, v_new (bf16 [B][H_kv][D]) append the
-    step's token first (one query token, no window)."""
+    kernel ("auto", "mfma_staged", "mfma_direct", "valu"), merge ("auto",
+    "combine_kernel", or "none": the split kernel alone, returning
+    (workspace, plan) as decode_split does) and min_seq_len (the host's lower
+    bound on every seq_lens[b], 0 if unknown: it sizes the chunks only).  q
+    is bf16 [B][Hq][D] (one query token; the result is [B][Hq][D]) or
+    [B][S][Hq][D]; k_new, v_new (bf16 [B][H_kv][D]) append the step's token
+    first (one query token, no window)."""
     import torch
     _need(cache, "cache", torch.uint8)
     _need(q, "q", torch.bfloat16)
@@ -545,7 +548,11 @@ def decode_with_options(layout: CacheLayout, cache, q, seq_lens, page_table, k_n
     else:
         _need(workspace, "workspace", torch.uint8)
     shape = (B, Hq, D) if one else (B, S, Hq, D)
-    if out is None:
+    partials_only = merge == "none"
+    if partials_only:
+        if out is not None:
+            raise ValueError("merge='none' writes no output rows: pass no out")
+    elif out is None:
         out = torch.empty(shape, dtype=torch.float32, device=q.device)
     else:
         _need(out, "out", torch.float32)
@@ -553,13 +560,13 @@ def decode_with_options(layout: CacheLayout, cache, q, seq_lens, page_table, k_n
             raise ValueError(f"out must be {list(shape)}")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
-    opts = DecodeOptions(DECODE_KERNELS[kernel], DECODE_MERGES[merge])
+    opts = DecodeOptions(DECODE_KERNELS[kernel], DECODE_MERGES[merge], int(min_seq_len))
     ptr = lambda t: None if t is None else t.data_ptr()
     _check("fp4kv_decode_with_options", library().fp4kv_decode_with_options(
         ctypes.byref(layout), cache.data_ptr(), ptr(k_new), ptr(v_new), q.data_ptr(), B, S, Hq,
         seq_lens.data_ptr(), page_table.data_ptr(), max_pages, int(window), float(softmax_scale), num_splits,
-        workspace.data_ptr(), workspace.numel(), out.data_ptr(), ctypes.byref(opts), _stream(stream)))
-    return out
+        workspace.data_ptr(), workspace.numel(), ptr(out), ctypes.byref(opts), _stream(stream)))
+    return (workspace, plan) if partials_only else out
 
 
 def _new_token_rows(layout, k_new, v_new, B):

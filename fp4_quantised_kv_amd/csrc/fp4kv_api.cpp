@@ -157,26 +157,35 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
 // Chunk page counts of a plan (chunk_first_page in the kernels): the first
 // lead_chunks chunks hold lead_pages pages, the rest tail_pages.  Even
 // chunks of pages_per_split, except in a grid of at least twice the
-// workgroups the GPU runs at once: there the last half of the partials take
-// chunks of 3/8 of that size and the other partials share out their pages,
-// so that the workgroups the grid starts last are short and few slots idle
-// while it drains.  (Measured on the 32 x 32K batch at 64 chunks and the
-// paged 64-sequence batch: larger shares or shorter tails gain more on the
-// first and lose on the second, whose long lead chunks then hold its few
-// long sequences in few workgroups.)
+// workgroups the GPU runs at once: there the workgroups the grid starts last
+// are given short chunks (longest first), so that few slots idle while it
+// drains, and the earlier partials share out the remaining pages.  How far
+// that can go depends on the lengths, which only the caller knows:
+//   - by default the last half of the partials take chunks of 3/8 of the
+//     even size;
+//   - when the caller promises that every sequence covers at least 7/8 of
+//     the span (min_span: pages each sequence is known to cover, 0 when
+//     nothing is known), the last 3/4 of the partials take chunks of 1/8 of
+//     the even size (at least one page).
+// (Measured on the 32 x 32K batch at 64 chunks and the paged 64-sequence
+// batch: the second cut gains 4.5 % on the first, but on the second it packs
+// a short sequence's pages into one long lead chunk whose workgroup's other
+// waves idle, and it holds the long sequences in few long workgroups.)
 struct ChunkSizes {
     int32_t lead_chunks, lead_pages, tail_pages;
 };
 
-ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan &plan, int64_t span)
+ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan &plan, int64_t span,
+                       int64_t min_span)
 {
     const int64_t chunks = static_cast<int64_t>(plan.partials) * kChunksPerGroup;
     ChunkSizes cs{static_cast<int32_t>(chunks), plan.pages_per_split, plan.pages_per_split};
     const int64_t groups = static_cast<int64_t>(L.params.num_kv_heads) * batch * plan.partials;
-    const int64_t tail_parts = plan.partials / 2;
+    const bool uniform = min_span > 0 && 8 * min_span >= 7 * span;
+    const int64_t tail_parts = uniform ? plan.partials * 3 / 4 : plan.partials / 2;
     if (groups < 2 * kResidentGroups || tail_parts < 1)
         return cs;
-    const int64_t tail = std::max<int64_t>(1, plan.pages_per_split * 3 / 8);
+    const int64_t tail = std::max<int64_t>(1, plan.pages_per_split * (uniform ? 1 : 3) / 8);
     const int64_t lead_chunks = chunks - tail_parts * kChunksPerGroup;
     const int64_t lead = (span - tail_parts * kChunksPerGroup * tail + lead_chunks - 1) / lead_chunks;
     if (tail < plan.pages_per_split && lead >= plan.pages_per_split) {
@@ -185,6 +194,14 @@ ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan 
         cs.tail_pages = static_cast<int32_t>(tail);
     }
     return cs;
+}
+
+// Pages of the span every sequence covers when each is at least min_seq_len
+// tokens long (0: nothing known).
+int64_t promised_span(int64_t span, int32_t min_seq_len)
+{
+    const int64_t pages = (static_cast<int64_t>(min_seq_len) + kPage - 1) / kPage;
+    return pages < span ? pages : span;
 }
 
 }  // namespace
@@ -251,14 +268,14 @@ int32_t window_span_pages(int32_t max_pages, int32_t q_tokens, int32_t window);
 extern "C" {
 
 int fp4kv_decode_chunks(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t q_tokens, int32_t num_q_heads,
-                        int32_t max_pages_per_seq, int32_t window, int32_t num_splits, int32_t *lead_chunks_out,
-                        int32_t *lead_pages_out, int32_t *tail_pages_out)
+                        int32_t max_pages_per_seq, int32_t window, int32_t num_splits, int32_t min_seq_len,
+                        int32_t *lead_chunks_out, int32_t *lead_pages_out, int32_t *tail_pages_out)
 {
     int rc = check_layout(layout);
     if (rc != FP4KV_OK)
         return rc;
     if (!lead_chunks_out || !lead_pages_out || !tail_pages_out || q_tokens < 1 || window < 0 || num_q_heads < 1 ||
-        static_cast<int64_t>(q_tokens) * num_q_heads > std::numeric_limits<int32_t>::max())
+        min_seq_len < 0 || static_cast<int64_t>(q_tokens) * num_q_heads > std::numeric_limits<int32_t>::max())
         return FP4KV_ERR_INVALID_ARGUMENT;
     if (max_pages_per_seq < 1)
         return FP4KV_ERR_INVALID_ARGUMENT;
@@ -267,7 +284,7 @@ int fp4kv_decode_chunks(const fp4kv_cache_layout_t *layout, int32_t batch, int32
     rc = make_plan(*layout, batch, q_tokens * num_q_heads, span, num_splits, &plan);
     if (rc != FP4KV_OK)
         return rc;
-    const ChunkSizes cs = chunk_sizes(*layout, batch, plan, span);
+    const ChunkSizes cs = chunk_sizes(*layout, batch, plan, span, promised_span(span, min_seq_len));
     *lead_chunks_out = cs.lead_chunks;
     *lead_pages_out = cs.lead_pages;
     *tail_pages_out = cs.tail_pages;
@@ -295,12 +312,12 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
                   int32_t batch, int32_t num_q_heads, const int32_t *seq_lens,
                   const int32_t *page_table, int32_t max_pages_per_seq, float softmax_scale,
                   int32_t num_splits, void *workspace, int64_t workspace_bytes,
-                  fp4kv::DecodeArgs *a, int32_t q_tokens = 1, int32_t window = 0)
+                  fp4kv::DecodeArgs *a, int32_t q_tokens = 1, int32_t window = 0, int32_t min_seq_len = 0)
 {
     int rc = check_layout(layout);
     if (rc != FP4KV_OK)
         return rc;
-    if (window < 0)
+    if (window < 0 || min_seq_len < 0)
         return FP4KV_ERR_INVALID_ARGUMENT;
     if (q_tokens < 1 || num_q_heads < 1 || num_q_heads % layout->params.num_kv_heads ||
         static_cast<int64_t>(q_tokens) * num_q_heads > std::numeric_limits<int32_t>::max())
@@ -342,7 +359,8 @@ int prepare_split(const fp4kv_cache_layout_t *layout, const void *cache, const v
     a->splits = plan.splits;
     a->pages_per_split = plan.pages_per_split;
     a->partials = plan.partials;
-    const ChunkSizes cs = chunk_sizes(*layout, batch, plan, window_span_pages(max_pages_per_seq, q_tokens, window));
+    const int32_t span = window_span_pages(max_pages_per_seq, q_tokens, window);
+    const ChunkSizes cs = chunk_sizes(*layout, batch, plan, span, promised_span(span, min_seq_len));
     a->lead_chunks = cs.lead_chunks;
     a->lead_pages = cs.lead_pages;
     a->tail_pages = cs.tail_pages;
@@ -411,6 +429,7 @@ int choose_kernel(const fp4kv::DecodeArgs &a, int32_t requested, fp4kv::SplitKer
 struct Finish {
     fp4kv::SplitKernel kernel;
     bool combine;                // a combine kernel after the split kernel (else the split kernel writes out)
+    bool partials_only;          // the split kernel alone, partials left in the workspace
 };
 
 
@@ -418,27 +437,31 @@ struct Finish {
 // split arguments are in `a`.
 int check_finish(const fp4kv::DecodeArgs &a, const float *out, const fp4kv_decode_options *opts, Finish *f)
 {
-    if (!out)
-        return FP4KV_ERR_INVALID_ARGUMENT;
-    if (!aligned(out, 16))
-        return FP4KV_ERR_MISALIGNED;
     const int32_t kernel = opts ? opts->kernel : FP4KV_DECODE_KERNEL_AUTO;
     const int32_t merge = opts ? opts->merge : FP4KV_DECODE_MERGE_AUTO;
-    if (merge != FP4KV_DECODE_MERGE_AUTO && merge != FP4KV_DECODE_MERGE_COMBINE_KERNEL)
+    if (merge != FP4KV_DECODE_MERGE_AUTO && merge != FP4KV_DECODE_MERGE_COMBINE_KERNEL &&
+        merge != FP4KV_DECODE_MERGE_NONE)
         return FP4KV_ERR_INVALID_ARGUMENT;
+    f->partials_only = merge == FP4KV_DECODE_MERGE_NONE;
+    if (!f->partials_only) {
+        if (!out)
+            return FP4KV_ERR_INVALID_ARGUMENT;
+        if (!aligned(out, 16))
+            return FP4KV_ERR_MISALIGNED;
+    }
     const int rc = choose_kernel(a, kernel, &f->kernel);
     if (rc != FP4KV_OK)
         return rc;
     // With one partial per row the split kernel writes the final rows itself
     // (the combine's weight would be exactly 1) and no combine is launched.
-    f->combine = a.partials != 1 || merge == FP4KV_DECODE_MERGE_COMBINE_KERNEL;
+    f->combine = !f->partials_only && (a.partials != 1 || merge == FP4KV_DECODE_MERGE_COMBINE_KERNEL);
     return FP4KV_OK;
 }
 
 // The launches of a checked call.
 int run_decode(fp4kv::DecodeArgs &a, const Finish &f, float *out, hipStream_t st)
 {
-    a.out = f.combine ? nullptr : out;
+    a.out = f.combine || f.partials_only ? nullptr : out;
     hipError_t e = fp4kv::launch_decode_split(a, f.kernel, st);
     if (e != hipSuccess)
         return FP4KV_ERR_HIP;
@@ -459,7 +482,8 @@ int decode_call(const fp4kv_cache_layout_t *layout, void *cache, const void *k_n
 {
     fp4kv::DecodeArgs a;
     int rc = prepare_split(layout, cache, q, batch, num_q_heads, seq_lens, page_table, max_pages_per_seq,
-                           softmax_scale, num_splits, workspace, workspace_bytes, &a, q_tokens, window);
+                           softmax_scale, num_splits, workspace, workspace_bytes, &a, q_tokens, window,
+                           opts ? opts->min_seq_len : 0);
     if (rc != FP4KV_OK || batch == 0)
         return rc;
     if (append) {

@@ -225,18 +225,24 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  *   chunk k >= *lead_chunks_out pages [L + (k - lc) * TP, L + (k - lc + 1) * TP)
  * where lc = *lead_chunks_out, LP = *lead_pages_out, TP = *tail_pages_out and
  * L = lc * LP, each cut at the end of the context.  Usually LP = TP =
- * ceil(span / S) (even chunks).  In a grid of at least 1536 workgroups
- * (H_kv x batch x P: twice what 256 CUs hold at once) the last floor(P / 2)
- * partials take chunks of TP = max(1, 3 * ceil(span / S) / 8) pages and the
- * others LP >= ceil(span / S): the workgroups dispatched last are then short
- * ones, so fewer CUs idle while the grid drains.  Arguments as for
- * fp4kv_decode_plan, plus q_tokens >= 1 and window >= 0 as for
- * fp4kv_decode_window_attention (batch x q_tokens x num_q_heads query rows).
+ * E = ceil(span / S) (even chunks).  In a grid of at least 1536 workgroups
+ * (H_kv x batch x P: twice what 256 CUs hold at once) the last partials take
+ * short chunks and the others LP >= E: the workgroups dispatched last are
+ * then short ones, so fewer CUs idle while the grid drains.  By default the
+ * last floor(P / 2) partials take TP = max(1, 3E / 8) pages.  When
+ * min_seq_len (fp4kv_decode_options; 0 here and in the calls without
+ * options) says that every sequence covers at least 7/8 of the span
+ * (ceil(min_seq_len / 64) >= 7/8 of it), the last floor(3P / 4) partials
+ * take TP = max(1, E / 8) pages.  Either cut is used only where it leaves
+ * TP < E <= LP.  Arguments as for fp4kv_decode_plan, plus q_tokens >= 1 and
+ * window >= 0 as for fp4kv_decode_window_attention (batch x q_tokens x
+ * num_q_heads query rows) and min_seq_len >= 0.
  * Errors: as fp4kv_decode_plan, and INVALID_ARGUMENT for a null output,
- * q_tokens < 1 or window < 0. */
+ * q_tokens < 1, window < 0 or min_seq_len < 0. */
 FP4KV_API int fp4kv_decode_chunks(const fp4kv_cache_layout_t *layout, int32_t batch, int32_t q_tokens,
                                   int32_t num_q_heads, int32_t max_pages_per_seq, int32_t window, int32_t num_splits,
-                                  int32_t *lead_chunks_out, int32_t *lead_pages_out, int32_t *tail_pages_out);
+                                  int32_t min_seq_len, int32_t *lead_chunks_out, int32_t *lead_pages_out,
+                                  int32_t *tail_pages_out);
 
 /* One decode step of attention for `batch` sequences, one query token each,
  * over the packed cache.  ("Quantising the KV cache", Concept and Code
@@ -425,10 +431,11 @@ FP4KV_API int fp4kv_decode_window_attention(const fp4kv_cache_layout_t *layout, 
                                             int32_t window, float softmax_scale, int32_t num_splits,
                                             void *workspace, int64_t workspace_bytes, float *out, void *stream);
 
-/* Choices inside a decode call, for tests and measurements; the other
- * entry points use FP4KV_DECODE_KERNEL_AUTO and FP4KV_DECODE_MERGE_AUTO.
- * Every choice gives the same results within the attention tolerance, and
- * the same split kernel gives the same bits whatever the merge. */
+/* Choices inside a decode call, and what the caller knows of the batch;
+ * the other entry points use FP4KV_DECODE_KERNEL_AUTO,
+ * FP4KV_DECODE_MERGE_AUTO and min_seq_len 0.  Every choice gives the same
+ * results within the attention tolerance, and the same split kernel over
+ * the same chunks gives the same bits whatever the merge. */
 enum fp4kv_decode_kernel {
     FP4KV_DECODE_KERNEL_AUTO = 0,         /* FP8 cache: its kernel; FP4: MFMA_STAGED at D = 128, else MFMA_DIRECT */
     FP4KV_DECODE_KERNEL_MFMA_STAGED = 1,  /* FP4, D = 128: matrix cores, pages staged through LDS */
@@ -437,11 +444,20 @@ enum fp4kv_decode_kernel {
 };
 enum fp4kv_decode_merge {
     FP4KV_DECODE_MERGE_AUTO = 0,          /* one partial per row: the split kernel writes out; else a combine */
-    FP4KV_DECODE_MERGE_COMBINE_KERNEL = 1 /* always a separate combine kernel */
+    FP4KV_DECODE_MERGE_COMBINE_KERNEL = 1, /* always a separate combine kernel */
+    FP4KV_DECODE_MERGE_NONE = 2           /* the split kernel alone: partials left in the workspace as
+                                             fp4kv_decode_split leaves them; `out` is not used (may be NULL) */
 };
 typedef struct fp4kv_decode_options {
     int32_t kernel;                       /* enum fp4kv_decode_kernel */
     int32_t merge;                        /* enum fp4kv_decode_merge */
+    int32_t min_seq_len;                  /* host knowledge: every seq_lens[b] is at least this (0: nothing
+                                             known; negative: INVALID_ARGUMENT).  It only decides how the
+                                             context is cut into chunks (fp4kv_decode_chunks): when every
+                                             sequence covers at least 7/8 of the span, the last chunks are
+                                             made shorter than for a ragged batch.  Every cut covers the same
+                                             tokens, so a wrong value costs time, never correctness (results
+                                             differ from the unhinted call's by rounding only). */
 } fp4kv_decode_options;
 
 /* Every decode entry point in one call, with explicit choices: append the
@@ -449,12 +465,14 @@ typedef struct fp4kv_decode_options {
  * q_tokens must be 1 and window 0), q_tokens query tokens per sequence,
  * sliding window `window` (0: none), as fp4kv_decode_append_attention,
  * fp4kv_decode_multi_attention and fp4kv_decode_window_attention describe.
- * `options` (host; NULL: both AUTO) chooses the split kernel and whether a
- * separate combine kernel merges the partials.  The workspace is sized by
- * fp4kv_decode_window_plan for the same arguments (fp4kv_decode_plan when
- * q_tokens = 1 and window = 0).
- * Errors: as for those calls; INVALID_ARGUMENT for an unknown option value
- * or only one of k_new, v_new; UNSUPPORTED for a kernel that does not serve
+ * `options` (host; NULL: AUTO, AUTO, 0) chooses the split kernel, whether a
+ * separate combine kernel merges the partials (or none: the split kernel
+ * alone, as fp4kv_decode_split; then `out` may be NULL) and gives the
+ * shortest length's lower bound that sizes the chunks.  The workspace is
+ * sized by fp4kv_decode_window_plan for the same arguments
+ * (fp4kv_decode_plan when q_tokens = 1 and window = 0).
+ * Errors: as for those calls; INVALID_ARGUMENT for an unknown option value,
+ * a negative min_seq_len or only one of k_new, v_new; UNSUPPORTED for a kernel that does not serve
  * the cache format, head size, query tokens or window, or an append with
  * q_tokens > 1 or a window. */
 FP4KV_API int fp4kv_decode_with_options(const fp4kv_cache_layout_t *layout, void *cache, const void *k_new,

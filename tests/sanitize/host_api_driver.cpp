@@ -74,26 +74,30 @@ static void plans()
         for (int32_t maxp : {1, 2, 9, 257, 512, 8192, 1 << 20})
             for (int32_t S : {0, 1, 3, 64, 256, 1000, 1 << 20})
                 for (int32_t qt : {1, 2, 16})
-                    for (int32_t win : {0, 1, 700, 1 << 20}) {
-                        const int rc = fp4kv_decode_chunks(&L, B, qt, 32 * (qt == 16 ? 1 : 8 / qt), maxp, win, S, &lc,
-                                                           &lp, &tp);
-                        if (rc != FP4KV_OK)
-                            continue;
-                        EXPECT(lc >= 1 && lp >= 1 && tp >= 1 && tp <= lp);
-                        if (win == 0 && qt == 1) {
-                            EXPECT(fp4kv_decode_plan(&L, B, 64, maxp, S, &s, &p, &ws) == FP4KV_OK);
-                            EXPECT(int64_t(lc) * lp + int64_t(4 * p - lc) * tp >= maxp);
+                    for (int32_t win : {0, 1, 700, 1 << 20})
+                        for (int32_t min_len : {0, 1, maxp * 32, maxp * 64}) {
+                            const int rc = fp4kv_decode_chunks(&L, B, qt, 32 * (qt == 16 ? 1 : 8 / qt), maxp, win, S,
+                                                               min_len, &lc, &lp, &tp);
+                            if (rc != FP4KV_OK)
+                                continue;
+                            EXPECT(lc >= 1 && lp >= 1 && tp >= 1 && tp <= lp);
+                            if (win == 0 && qt == 1) {
+                                EXPECT(fp4kv_decode_plan(&L, B, 64, maxp, S, &s, &p, &ws) == FP4KV_OK);
+                                EXPECT(int64_t(lc) * lp + int64_t(4 * p - lc) * tp >= maxp);
+                            }
                         }
-                    }
     EXPECT(fp4kv_decode_plan(&L, 32, 64, 512, 64, &s, &p, &ws) == FP4KV_OK && s == 64 && p == 16);
-    EXPECT(fp4kv_decode_chunks(&L, 32, 1, 64, 512, 0, 64, &lc, &lp, &tp) == FP4KV_OK && lc == 32 && lp == 13 &&
+    EXPECT(fp4kv_decode_chunks(&L, 32, 1, 64, 512, 0, 64, 0, &lc, &lp, &tp) == FP4KV_OK && lc == 32 && lp == 13 &&
            tp == 3);
+    EXPECT(fp4kv_decode_chunks(&L, 32, 1, 64, 512, 0, 64, 32768, &lc, &lp, &tp) == FP4KV_OK && lc == 16 &&
+           lp == 29 && tp == 1);
     EXPECT(fp4kv_decode_plan(&L, -1, 64, 512, 64, &s, &p, &ws) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_plan(&L, 1, 65, 512, 64, &s, &p, &ws) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_plan(&L, 1, 64, 512, 64, nullptr, &p, &ws) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_plan(nullptr, 1, 64, 512, 64, &s, &p, &ws) == FP4KV_ERR_INVALID_ARGUMENT);
-    EXPECT(fp4kv_decode_chunks(&L, 1, 0, 64, 512, 0, 64, &lc, &lp, &tp) == FP4KV_ERR_INVALID_ARGUMENT);
-    EXPECT(fp4kv_decode_chunks(&L, 1, 1, 64, 512, -1, 64, &lc, &lp, &tp) == FP4KV_ERR_INVALID_ARGUMENT);
+    EXPECT(fp4kv_decode_chunks(&L, 1, 0, 64, 512, 0, 64, 0, &lc, &lp, &tp) == FP4KV_ERR_INVALID_ARGUMENT);
+    EXPECT(fp4kv_decode_chunks(&L, 1, 1, 64, 512, -1, 64, 0, &lc, &lp, &tp) == FP4KV_ERR_INVALID_ARGUMENT);
+    EXPECT(fp4kv_decode_chunks(&L, 1, 1, 64, 512, 0, 64, -1, &lc, &lp, &tp) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_window_plan(&L, 4, 2, 64, 100, 700, 0, &s, &p, &ws) == FP4KV_OK);
     EXPECT(fp4kv_decode_window_plan(&L, 4, 0, 64, 100, 700, 0, &s, &p, &ws) != FP4KV_OK);
 }
@@ -128,12 +132,23 @@ static void decode_calls()
     EXPECT(fp4kv_decode_window_attention(&L, dev(1), dev(2), 32, 2, 32, lens, table, 512, 700, 0.088f, 0, dev(6),
                                          wsm, out, nullptr) == FP4KV_OK);
     for (int32_t k : {0, 1, 2, 3})
-        for (int32_t m : {0, 1}) {
-            const fp4kv_decode_options o{k, m};
-            EXPECT(fp4kv_decode_with_options(&L, dev(1), nullptr, nullptr, dev(2), 32, 1, 64, lens, table, 512, 0,
-                                             0.088f, 64, dev(6), ws, out, &o, nullptr) == FP4KV_OK);
-        }
-    const fp4kv_decode_options bad_kernel{9, 0}, bad_merge{0, 9};
+        for (int32_t m : {0, 1})
+            for (int32_t min_len : {0, 32768}) {
+                const fp4kv_decode_options o{k, m, min_len};
+                EXPECT(fp4kv_decode_with_options(&L, dev(1), nullptr, nullptr, dev(2), 32, 1, 64, lens, table, 512, 0,
+                                                 0.088f, 64, dev(6), ws, out, &o, nullptr) == FP4KV_OK);
+            }
+    {
+        // the split kernel alone: one launch, no output pointer needed
+        const fp4kv_decode_options o{0, 2, 32768};
+        const int before_split = fp4kv::g_stub_calls;
+        EXPECT(fp4kv_decode_with_options(&L, dev(1), nullptr, nullptr, dev(2), 32, 1, 64, lens, table, 512, 0,
+                                         0.088f, 64, dev(6), ws, nullptr, &o, nullptr) == FP4KV_OK);
+        EXPECT(fp4kv::g_stub_calls == before_split + 1);
+    }
+    const fp4kv_decode_options bad_kernel{9, 0, 0}, bad_merge{0, 9, 0}, bad_min{0, 0, -1};
+    EXPECT(fp4kv_decode_with_options(&L, dev(1), nullptr, nullptr, dev(2), 32, 1, 64, lens, table, 512, 0, 0.088f,
+                                     64, dev(6), ws, out, &bad_min, nullptr) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_with_options(&L, dev(1), nullptr, nullptr, dev(2), 32, 1, 64, lens, table, 512, 0, 0.088f,
                                      64, dev(6), ws, out, &bad_kernel, nullptr) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_with_options(&L, dev(1), nullptr, nullptr, dev(2), 32, 1, 64, lens, table, 512, 0, 0.088f,

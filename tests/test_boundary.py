@@ -171,8 +171,49 @@ def test_chunks():
             fk.decode_chunks(L, *args)
         assert e.value.status == code
     lc = ctypes.c_int32()
-    assert fk.library().fp4kv_decode_chunks(ctypes.byref(L), 4, 1, 32, 16, 0, 0, ctypes.byref(lc), None,
+    assert fk.library().fp4kv_decode_chunks(ctypes.byref(L), 4, 1, 32, 16, 0, 0, 0, ctypes.byref(lc), None,
                                             ctypes.byref(lc)) == fk.ERR_INVALID_ARGUMENT
+
+
+def test_chunks_with_a_shortest_length():
+    """min_seq_len: when every sequence covers at least 7/8 of the span, the
+    last 3/4 of the partials take chunks of 1/8 of the even size (at least a
+    page); a smaller bound, or none, keeps the default cut."""
+    L = fk.cache_layout(8, 128, 32 * 512)
+    # the 32 x 32K batch at 64 chunks: 48 one-page chunks, 16 of 29 pages
+    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=32768)) == (16, 29, 1)
+    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8)) == (16, 29, 1)
+    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8 - 64)) == (32, 13, 3)
+    # the paged batch's shortest sequence (1,024 tokens) keeps the default cut
+    assert tuple(fk.decode_chunks(L, 64, 32, 258, 0, min_seq_len=1024)) == (16, 14, 3)
+    # fewer than 1536 workgroups: even chunks whatever the bound
+    assert tuple(fk.decode_chunks(L, 1, 32, 8192, 256, min_seq_len=8192 * 64)) == (256, 32, 32)
+    for B, Hq, maxp, S, qt, win in [(32, 64, 512, 64, 1, 0), (64, 32, 258, 0, 1, 0), (48, 32, 48, 16, 1, 0),
+                                    (64, 32, 48, 16, 1, 0), (96, 32, 32, 7, 2, 700), (96, 32, 32, 0, 2, 700),
+                                    (200, 8, 100, 3, 1, 0), (512, 64, 40, 40, 1, 0), (33, 16, 77, 29, 4, 300),
+                                    (1024, 8, 2, 0, 1, 0), (64, 32, 400, 32, 1, 0), (128, 64, 300, 64, 1, 0)]:
+        span = maxp if win == 0 else min(maxp, -(-(win + qt - 1) // 64) + 1)
+        plan = (fk.decode_plan(L, B, Hq, maxp, S) if win == 0 and qt == 1
+                else fk.decode_window_plan(L, B, qt, Hq, maxp, win, S))
+        pps = -(-span // plan.splits)
+        chunks = 4 * plan.partials
+        for min_len in (span * 64, maxp * 64, -(-7 * span // 8) * 64):
+            ch = fk.decode_chunks(L, B, Hq, maxp, S, q_tokens=qt, window=win, min_seq_len=min_len)
+            assert ch.first_page(chunks) >= span                      # the chunks tile the span
+            if ch.lead_chunks == chunks:
+                assert ch.lead_pages == ch.tail_pages == pps
+            else:
+                assert 8 * B * plan.partials >= 1536
+                assert ch.lead_chunks == 4 * (plan.partials - 3 * plan.partials // 4)
+                assert ch.tail_pages == max(1, pps // 8) < pps <= ch.lead_pages
+                assert ch.lead_chunks * (ch.lead_pages - 1) + (chunks - ch.lead_chunks) * ch.tail_pages < span
+        # a bound under 7/8 of the span: the default cut
+        assert fk.decode_chunks(L, B, Hq, maxp, S, q_tokens=qt, window=win,
+                                min_seq_len=(7 * span // 8 - 1) * 64) == fk.decode_chunks(L, B, Hq, maxp, S,
+                                                                                         q_tokens=qt, window=win)
+    with pytest.raises(fk.Fp4KVError) as e:
+        fk.decode_chunks(L, 4, 32, 16, 0, min_seq_len=-1)
+    assert e.value.status == fk.ERR_INVALID_ARGUMENT
 
 
 def _lib():
@@ -380,15 +421,20 @@ def test_decode_with_options_host_checks():
     ok = 0x10000
     ws = fk.decode_window_plan(L, 2, 2, 8, 8, 0).workspace_bytes
 
-    def call(layout=L, kn=None, vn=None, qt=1, window=0, kernel=0, merge=0, opts=True):
-        o = fk.DecodeOptions(kernel, merge)
+    def call(layout=L, kn=None, vn=None, qt=1, window=0, kernel=0, merge=0, opts=True, min_len=0, out=ok):
+        o = fk.DecodeOptions(kernel, merge, min_len)
         return lib.fp4kv_decode_with_options(ctypes.byref(layout), ok, kn, vn, ok, 2, qt, 8, ok, ok, 8, window,
-                                             ctypes.c_float(0.1), 0, ok, ws, ok,
+                                             ctypes.c_float(0.1), 0, ok, ws, out,
                                              ctypes.byref(o) if opts else None, None)
 
     assert call(kernel=99) == fk.ERR_INVALID_ARGUMENT
     assert call(kernel=-1) == fk.ERR_INVALID_ARGUMENT
     assert call(merge=7) == fk.ERR_INVALID_ARGUMENT
+    assert call(merge=3) == fk.ERR_INVALID_ARGUMENT
+    assert call(min_len=-1) == fk.ERR_INVALID_ARGUMENT
+    assert call(out=None) == fk.ERR_INVALID_ARGUMENT              # out is needed unless the merge is none
+    assert call(merge=2, out=None, kernel=99) == fk.ERR_INVALID_ARGUMENT
+    assert call(out=ok + 4) == fk.ERR_MISALIGNED
     assert call(kn=ok) == fk.ERR_INVALID_ARGUMENT                 # v_new missing
     assert call(kn=ok, vn=ok, qt=2) == fk.ERR_UNSUPPORTED
     assert call(kn=ok, vn=ok, window=64) == fk.ERR_UNSUPPORTED

@@ -6,7 +6,10 @@ a lead chunk, at the lead/tail seam, inside a tail chunk, at the table's
 end -- occurs; every split kernel and cache format, the step that appends
 its own token, and a sliding window with two query tokens are checked
 against the oracle (1e-3 per output row) or, for the appended step,
-against quantize_append followed by decode_attention (bit for bit)."""
+against quantize_append followed by decode_attention (bit for bit).  The
+cut for uniform batches (a shortest length given through
+fp4kv_decode_with_options) is checked the same way, and so is a shortest
+length the batch does not keep (the results must not depend on it)."""
 import numpy as np
 import pytest
 import torch
@@ -175,3 +178,68 @@ def test_window_two_query_tokens_against_oracle():
             worst = max(worst, float(hx.row_rel_error(out[b, i][None], r).max()))
     _say(f"  worst per-row relative error {worst:.3e}")
     assert worst <= TOL
+
+
+def _hinted_lengths(ch, n_chunks, maxp, batch, lo, seed):
+    """Lengths one token before, at and after every chunk start at or past
+    page `lo`, and the table's end; seeded fill in [lo * 64, maxp * 64]."""
+    cuts = sorted({ch.first_page(k) for k in range(1, n_chunks)} | {maxp})
+    lens = {lo * 64, lo * 64 + 1, maxp * 64}
+    for c in cuts:
+        lens |= {c * 64 - 1, c * 64, c * 64 + 1}
+    lens = sorted(x for x in lens if lo * 64 <= x <= maxp * 64)
+    assert len(lens) <= batch, len(lens)
+    rng = np.random.default_rng(seed)
+    lens += [int(x) for x in rng.integers(lo * 64, maxp * 64 + 1, batch - len(lens))]
+    rng.shuffle(lens)
+    return lens
+
+
+@pytest.mark.parametrize("fmt,kernel", [("fp4", "auto"), ("fp4", "mfma_direct"), ("fp8", "auto"), ("fp8t", "auto")])
+def test_shortest_length_cut_against_oracle(fmt, kernel):
+    """Every sequence at least 7/8 of the table: with the shortest length
+    given, the last 3/4 of the partials take one-page chunks."""
+    plan = _chunks(fmt)[0]
+    L0 = kf.layout(fmt, HKV, D, 64)
+    lo = -(-7 * MAXP // 8)
+    ch = fk.decode_chunks(L0, BATCH, HKV * G, MAXP, SPLITS, min_seq_len=lo * 64)
+    assert ch.tail_pages == 1 < ch.lead_pages and ch.lead_chunks == 4 * (plan.partials - 3 * plan.partials // 4)
+    lens = _hinted_lengths(ch, 4 * plan.partials, MAXP, BATCH, lo, seed=15)
+    _say(f"shortest-length cut {tuple(ch)}: {fmt} kernel {kernel}, lengths {sorted(lens)[:8]}..")
+    L, cache, table, kv, g = _setup(lens, fmt, seed=17, maxp=MAXP)
+    q = torch.randn(BATCH, HKV * G, D, generator=g).to(torch.bfloat16)
+    out = fk.decode_with_options(L, cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), table.cuda(),
+                                 num_splits=SPLITS, kernel=kernel, min_seq_len=min(lens))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref = _oracle(fmt, L, kv, lens, q)
+    err = float(hx.row_rel_error(out, ref).max())
+    _say(f"  worst per-row relative error {err:.3e}")
+    assert np.isfinite(out).all() and err <= TOL
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_shortest_length_not_kept_is_still_correct(fmt):
+    """A shortest length the batch does not keep (ragged lengths from 0,
+    promised the whole table) changes only the cut: the rows still match the
+    oracle, and the split kernel alone (merge none) followed by the combine
+    gives the same bits as the whole call."""
+    plan, ch = _chunks(fmt)
+    lens = _boundary_lengths(ch, 4 * plan.partials, MAXP, BATCH, seed=19)
+    L, cache, table, kv, g = _setup(lens, fmt, seed=21, maxp=MAXP)
+    q = torch.randn(BATCH, HKV * G, D, generator=g).to(torch.bfloat16).cuda()
+    lens_d = torch.tensor(lens, dtype=torch.int32).cuda()
+    wrong = MAXP * 64
+    _say(f"{fmt}: ragged lengths, shortest length given as {wrong}")
+    out = fk.decode_with_options(L, cache, q, lens_d, table.cuda(), num_splits=SPLITS, min_seq_len=wrong)
+    ws, p = fk.decode_with_options(L, cache, q, lens_d, table.cuda(), num_splits=SPLITS, min_seq_len=wrong,
+                                   merge="none")
+    again = fk.decode_combine(ws, BATCH, HKV * G, D, p.partials)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    out = out.cpu().numpy()
+    ref = _oracle(fmt, L, kv, lens, q.cpu())
+    err = float(hx.row_rel_error(out, ref).max())
+    _say(f"  worst per-row relative error {err:.3e}")
+    assert np.isfinite(out).all() and err <= TOL
+    assert not out[[b for b, n in enumerate(lens) if n == 0]].any()

@@ -1,6 +1,8 @@
 """Parity at the full sizes the benchmark times, in its launch configurations.
 
-- the 32-sequence, 32K-context batch at 64 chunks: every sequence;
+- the 32-sequence, 32K-context batch at 64 chunks: every sequence, through
+  fp4kv_decode_attention and through fp4kv_decode_with_options given the
+  batch's shortest length (the chunk cut of uniform batches);
 - the 512K-token sequence at 256 chunks: every KV head;
 - the paged 64-sequence batch (lengths 1024..16384, random page table,
   automatic split count): three consecutive steps through
@@ -57,24 +59,34 @@ def test_gqa8_ctx32k_every_sequence():
     _say(f"full size: {w.name}, {w.splits} splits, all {w.batch} sequences")
     gc = hx.build_cache(w, seed=SEED)
     q = wl.queries(w, SEED)
-    out = fk.decode_attention(gc.layout, gc.cache, q.cuda(), gc.seq_lens, gc.page_table, num_splits=w.splits)
+    maxp = gc.page_table.shape[1]
+    cut = fk.decode_chunks(gc.layout, w.batch, w.q_heads, maxp, w.splits, min_seq_len=w.context)
+    _say(f"  chunks with the shortest length given: {tuple(cut)}")
+    assert cut.tail_pages < cut.lead_pages and cut != fk.decode_chunks(gc.layout, w.batch, w.q_heads, maxp, w.splits)
+    outs = {}
+    outs["plain"] = fk.decode_attention(gc.layout, gc.cache, q.cuda(), gc.seq_lens, gc.page_table,
+                                        num_splits=w.splits)
+    outs["hinted"] = fk.decode_with_options(gc.layout, gc.cache, q.cuda(), gc.seq_lens, gc.page_table,
+                                            num_splits=w.splits, min_seq_len=w.context)
     torch.cuda.synchronize()
-    out = out.cpu().numpy()
-    assert np.isfinite(out).all()
+    outs = {k: o.cpu().numpy() for k, o in outs.items()}
+    for o in outs.values():
+        assert np.isfinite(o).all()
     del gc
     torch.cuda.empty_cache()
     fk_, fv_ = wl.channel_factors(w, SEED, "k"), wl.channel_factors(w, SEED, "v")
     lens = [w.context] * w.batch
     rows_of = lambda b: (wl.kv_tokens(w, SEED, b, "k", 0, w.context, fk_),
                          wl.kv_tokens(w, SEED, b, "v", 0, w.context, fv_))
-    worst = 0.0
+    worst = {k: 0.0 for k in outs}
     for b0 in range(0, w.batch, 4):
         seqs = list(range(b0, b0 + 4))
         ref = _oracle_rows(w, q, rows_of, lens, seqs)
-        err = float(hx.row_rel_error(out[seqs], ref[seqs]).max())
-        worst = max(worst, err)
-        _say(f"  sequences {seqs[0]}..{seqs[-1]}: worst per-row relative error {err:.3e}")
-    assert worst <= TOL
+        for k, o in outs.items():
+            worst[k] = max(worst[k], float(hx.row_rel_error(o[seqs], ref[seqs]).max()))
+        _say(f"  sequences {seqs[0]}..{seqs[-1]}: worst per-row relative error so far " +
+             ", ".join(f"{k} {e:.3e}" for k, e in worst.items()))
+    assert max(worst.values()) <= TOL
 
 
 def test_ctx512k_every_kv_head():
