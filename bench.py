@@ -372,12 +372,23 @@ class DecodeRun:
                                num_splits=self.splits_req, workspace=self.ws, out=self.out, kernel=self.kernel,
                                min_seq_len=self.min_len, **kv)
 
+    def plain_call(self):
+        if self.kernel != "auto":
+            return "fp4kv_decode_with_options (min_seq_len 0)"
+        return "fp4kv_decode_append_attention" if self.fused else "fp4kv_decode_attention"
+
     def step_plain(self, s):
-        """The same step through the entry point that knows no lengths."""
+        """The same step through the entry point that knows no lengths (with
+        an explicit kernel: the options call without a length)."""
         fk, gc, L = self.fk, self.gc, self.gc.layout
         if self.paged and not self.fused:
             fk.quantize_append(L, self.news[s][0], self.news[s][1], self.slots[s], gc.cache)
-        if self.fused:
+        if self.kernel != "auto":
+            kv = dict(k_new=self.news[s][0], v_new=self.news[s][1]) if self.fused else {}
+            fk.decode_with_options(L, gc.cache, self.q(s), self.lens(s), gc.page_table, softmax_scale=self.scale,
+                                   num_splits=self.splits_req, workspace=self.ws, out=self.out, kernel=self.kernel,
+                                   **kv)
+        elif self.fused:
             fk.decode_append_attention(L, gc.cache, self.news[s][0], self.news[s][1], self.q(s), self.lens(s),
                                        gc.page_table, softmax_scale=self.scale, num_splits=self.splits_req,
                                        workspace=self.ws, out=self.out)
@@ -498,7 +509,7 @@ def decode_record(torch, run, stream, steps, warmup):
     split_bytes_b2b = run.split_bytes(ctx_last)
     split_gbs = split_bytes_b2b / (t_split_b2b * 1e-3) / 1e9
     plain_gbs = step_bytes / (t_plain * 1e-3) / 1e9
-    plain_call = "fp4kv_decode_append_attention" if run.fused else "fp4kv_decode_attention"
+    plain_call = run.plain_call()
     return {
         "workload": w.name, "ms_per_step": round(ms_per_step, 5), "gbs": round(gbs, 2),
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2), "decode_steps_per_s": round(1e3 / ms_per_step, 2),

@@ -195,7 +195,8 @@ def _hinted_lengths(ch, n_chunks, maxp, batch, lo, seed):
     return lens
 
 
-@pytest.mark.parametrize("fmt,kernel", [("fp4", "auto"), ("fp4", "mfma_direct"), ("fp8", "auto"), ("fp8t", "auto")])
+@pytest.mark.parametrize("fmt,kernel", [("fp4", "auto"), ("fp4", "mfma_direct"), ("fp4", "valu"), ("fp8", "auto"),
+                                        ("fp8t", "auto")])
 def test_shortest_length_cut_against_oracle(fmt, kernel):
     """Every sequence at least 7/8 of the table: with the shortest length
     given, the last 3/4 of the partials take one-page chunks."""
