@@ -532,8 +532,8 @@ def decode_record(torch, run, stream, steps, warmup):
 
 
 def cold_warm(torch, run, stream, reps=20):
-    """For a cache smaller than the last-level cache: the step (one
-    fp4kv_decode_attention call) cold (1 GiB of unrelated data read and
+    """For a cache smaller than the last-level cache: the step (one decode
+    call, as DecodeRun.step makes it) cold (1 GiB of unrelated data read and
     written between calls, outside the timed events, so every call reads the
     cache from HBM; median of `reps`) and warm (back to back: the cache stays
     in the last-level cache), and the split kernel alone cold for the
