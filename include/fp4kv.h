@@ -203,10 +203,13 @@ FP4KV_API int fp4kv_quantize_append(const fp4kv_cache_layout_t *layout,
  * max_pages_per_seq); 0 lets the library choose S, about 16384 chunks in
  * total over batch x H_kv, so that the GPU stays full even when sequence
  * lengths differ, but no more than max_pages_per_seq / 2 (chunks of at
- * least two pages) when that still gives batch x H_kv x S >= 1024.  Each chunk pays a fixed start (its first page's
- * latency, the merge): when every sequence is long and about equally so,
- * chunks of about 32 pages (S = max_pages_per_seq / 32) stream faster than
- * the automatic choice.  *splits_out gets S, *partials_out P and
+ * least two pages) when that still gives batch x H_kv x S >= 1024.  Each
+ * chunk pays a fixed start (its first page's latency, the merge): when every
+ * sequence is long and about equally so, chunks of about 32 pages
+ * (S = max_pages_per_seq / 32) stream faster than the automatic choice, and
+ * for any S a decode call given the shortest length
+ * (fp4kv_decode_options.min_seq_len) sizes its chunks for such a batch.
+ * *splits_out gets S, *partials_out P and
  * *workspace_bytes_out the workspace fp4kv_decode_attention needs, for the
  * same arguments.
  * Errors: INVALID_ARGUMENT (null pointer, batch < 0, num_q_heads < 1,
