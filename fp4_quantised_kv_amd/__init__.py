@@ -28,6 +28,7 @@ LIBRARY_PATH = os.path.join(HERE, "libfp4kv.so")
 PAGE_SIZE = 64
 MAX_GROUP = 16
 NOALLOC_WORKSPACE_BYTES = 32 << 20   # the static workspace of decode_attention_noalloc
+VERSION = 200                        # FP4KV_VERSION of the header these bindings follow
 INT_PER_TOKEN = 0
 INT_PER_CHANNEL = 1
 INT_FP8_E4M3 = 0x108          # the `bits` value of FP8 E4M3 codes with fp16 scales
@@ -116,6 +117,11 @@ def library():
             raise RuntimeError(f"{LIBRARY_PATH} is missing: build it with "
                                "`python -m fp4_quantised_kv_amd.build` (hipcc, gfx950)")
         L = ctypes.CDLL(LIBRARY_PATH)
+        L.fp4kv_version.argtypes = []
+        L.fp4kv_version.restype = ctypes.c_int
+        if L.fp4kv_version() != VERSION:
+            raise RuntimeError(f"{LIBRARY_PATH} is version {L.fp4kv_version()}, these bindings follow {VERSION}: "
+                               "rebuild it with `python -m fp4_quantised_kv_amd.build`")
         L.fp4kv_cache_layout.argtypes = [ctypes.POINTER(CacheParams), ctypes.POINTER(CacheLayout)]
         L.fp4kv_cache_layout.restype = ctypes.c_int
         L.fp4kv_quantize_append.argtypes = [ctypes.POINTER(CacheLayout), _P, _P, ctypes.c_int64,
@@ -196,8 +202,6 @@ def library():
         L.fp4kv_int_decode_attention.restype = ctypes.c_int
         L.fp4kv_status_string.argtypes = [ctypes.c_int]
         L.fp4kv_status_string.restype = ctypes.c_char_p
-        L.fp4kv_version.argtypes = []
-        L.fp4kv_version.restype = ctypes.c_int
         _LIB = L
     return _LIB
 

@@ -735,6 +735,6 @@ int fp4kv_stream_probe(const void *src, void *dst, int64_t units, int32_t read_b
     return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 }
 
-int fp4kv_version(void) { return 100; }
+int fp4kv_version(void) { return FP4KV_VERSION; }
 
 }  // extern "C"

@@ -530,7 +530,11 @@ FP4KV_API int fp4kv_stream_probe(const void *src, void *dst, int64_t units, int3
 /* Static text for a status code (never NULL). */
 FP4KV_API const char *fp4kv_status_string(int status);
 
-/* Library version: major * 10000 + minor * 100 + patch. */
+/* Library version: major * 10000 + minor * 100 + patch.  0.2.0 added
+ * min_seq_len to fp4kv_decode_options (and to fp4kv_decode_chunks' arguments)
+ * and FP4KV_DECODE_MERGE_NONE; a caller built against another version's
+ * header must not call this library. */
+#define FP4KV_VERSION 200
 FP4KV_API int fp4kv_version(void);
 
 #ifdef __cplusplus

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fk.library().fp4kv_version() >= 100
+    assert fk.library().fp4kv_version() == fk.VERSION == 200
     for code in (0, -1, -2, -3, -4, -5):
         assert fk.status_string(code) not in ("", "unknown status")
     assert fk.status_string(-99) == "unknown status"
