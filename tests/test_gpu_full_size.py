@@ -7,7 +7,8 @@
 - the paged 64-sequence batch (lengths 1024..16384, random page table,
   automatic split count): three consecutive steps through
   fp4kv_decode_append_attention, each appending one token per sequence from
-  inside the split kernel.  Every appended slot's bytes must equal the
+  inside the split kernel, and the last step again through the options call
+  given the shortest length, as the benchmark makes it (same bits).  Every appended slot's bytes must equal the
   oracle's codes of that token; after the first step 8 sequences (the
   shortest and the longest among them), after the last step all 64, must be
   within 1e-3 per row of the oracle's attention.
@@ -142,6 +143,20 @@ def test_paged_fused_steps_at_full_size():
         assert np.array_equal(gkc[rows], oracle.pack_nibbles(kc)) and np.array_equal(gks[rows], ks), s
         assert np.array_equal(gvc[rows], oracle.pack_nibbles(vc)) and np.array_equal(gvs[rows], vs), s
         _say(f"  step {s}: the {B} appended slots (K and V codes and scales) equal the oracle's")
+    # the last step again as the benchmark makes it: the options call given the
+    # shortest length (the same chunks here, so the same bits), appending the
+    # same token again (the same bytes)
+    cache_before = gc.cache.clone()
+    kn, vn = news[-1]
+    again = fk.decode_with_options(L, gc.cache, qs[-1].cuda(), lens.cuda(), gc.page_table, k_new=kn.cuda(),
+                                   v_new=vn.cuda(), workspace=ws, min_seq_len=int(lens.min()))
+    torch.cuda.synchronize()
+    assert fk.decode_chunks(L, B, w.q_heads, table.shape[1], 0, min_seq_len=int(lens.min())) == \
+        fk.decode_chunks(L, B, w.q_heads, table.shape[1], 0)
+    assert torch.equal(gc.cache, cache_before)
+    assert np.array_equal(again.cpu().numpy(), outs[-1])
+    del cache_before
+    _say("  the last step through the options call with the shortest length: the same cache bytes and output bits")
 
     factors = wl.channel_factors(w, SEED, "k"), wl.channel_factors(w, SEED, "v")
 
