@@ -244,3 +244,43 @@ def test_shortest_length_not_kept_is_still_correct(fmt):
     _say(f"  worst per-row relative error {err:.3e}")
     assert np.isfinite(out).all() and err <= TOL
     assert not out[[b for b, n in enumerate(lens) if n == 0]].any()
+
+
+def test_window_with_shortest_length_against_oracle():
+    """A 2,000-token window over 96 sequences whose plan differs when every
+    sequence is promised the whole table (most are shorter): both cuts of the
+    window's span, against the oracle's windowed attention."""
+    B, window, maxp, splits = 96, 2000, 48, 16
+    L0 = kf.layout("fp4", HKV, D, 64)
+    plan = fk.decode_window_plan(L0, B, 1, HKV * G, maxp, window, splits)
+    ch = fk.decode_chunks(L0, B, HKV * G, maxp, splits, window=window)
+    ch_h = fk.decode_chunks(L0, B, HKV * G, maxp, splits, window=window, min_seq_len=maxp * 64)
+    span = fk_span(maxp, 1, window)
+    assert ch != ch_h and ch_h.tail_pages < ch_h.lead_pages, (tuple(ch), tuple(ch_h))
+    cuts = sorted({c.first_page(k) for c in (ch, ch_h) for k in range(1, 4 * plan.partials)} | {span})
+    lens = sorted({0, 1, 64, 1999, 2000, 2001, maxp * 64} |
+                  {c * 64 + d for c in cuts for d in (-1, 0, 1)} |
+                  {c * 64 + window + d for c in (1, 5, 9) for d in (-1, 0, 1)})
+    lens = [n for n in lens if 0 <= n <= maxp * 64]
+    rng = np.random.default_rng(23)
+    lens += [int(x) for x in rng.integers(0, maxp * 64 + 1, B - len(lens))]
+    L, cache, table, kv, g = _setup(lens, "fp4", seed=25, maxp=maxp)
+    q = torch.randn(B, HKV * G, D, generator=g).to(torch.bfloat16)
+    lens_d = torch.tensor(lens, dtype=torch.int32).cuda()
+    _say(f"window {window}: chunks {tuple(ch)}, promised the whole table {tuple(ch_h)}")
+    outs = [fk.decode_with_options(L, cache, q.cuda(), lens_d, table.cuda(), window=window, num_splits=splits,
+                                   min_seq_len=m).cpu().numpy() for m in (0, maxp * 64)]
+    worst = 0.0
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert not outs[0][b].any() and not outs[1][b].any()
+            continue
+        lo = max(0, n - window)
+        kq = oracle.quantize(wl.bf16_bits(kv[b][0][lo:n]), want_xhat=False)
+        vq = oracle.quantize(wl.bf16_bits(kv[b][1][lo:n]), want_xhat=False)
+        r = oracle.decode_attention(wl.bf16_bits(q[b:b + 1]), [kq[0]], [kq[1]], [vq[0]], [vq[1]], [n - lo],
+                                    D ** -0.5)
+        for o in outs:
+            worst = max(worst, float(hx.row_rel_error(o[b][None], r).max()))
+    _say(f"  worst per-row relative error (both cuts) {worst:.3e}")
+    assert worst <= TOL
