@@ -165,12 +165,14 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
 //     even size;
 //   - when the caller promises that every sequence covers at least 7/8 of
 //     the span (min_span: pages each sequence is known to cover, 0 when
-//     nothing is known), the last 3/4 of the partials take chunks of 1/8 of
-//     the even size (at least one page).
+//     nothing is known), only as many lead partials are kept as fill the
+//     GPU's resident workgroups once (at least one), and every later
+//     partial takes chunks of 1/8 of the even size (at least one page).
 // (Measured on the 32 x 32K batch at 64 chunks and the paged 64-sequence
-// batch: the second cut gains 4.5 % on the first, but on the second it packs
-// a short sequence's pages into one long lead chunk whose workgroup's other
-// waves idle, and it holds the long sequences in few long workgroups.)
+// batch: the second cut gains 5.7 % on the first -- fewer or more lead
+// partials than one generation's worth are slower -- but on the second it
+// packs a short sequence's pages into one long lead chunk whose workgroup's
+// other waves idle, and it holds the long sequences in few long workgroups.)
 struct ChunkSizes {
     int32_t lead_chunks, lead_pages, tail_pages;
 };
@@ -180,13 +182,16 @@ ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan 
 {
     const int64_t chunks = static_cast<int64_t>(plan.partials) * kChunksPerGroup;
     ChunkSizes cs{static_cast<int32_t>(chunks), plan.pages_per_split, plan.pages_per_split};
-    const int64_t groups = static_cast<int64_t>(L.params.num_kv_heads) * batch * plan.partials;
+    const int64_t units = static_cast<int64_t>(L.params.num_kv_heads) * batch;     // workgroups per partial
+    const int64_t groups = units * plan.partials;
     const bool uniform = min_span > 0 && 8 * min_span >= 7 * span;
-    const int64_t tail_parts = uniform ? plan.partials * 3 / 4 : plan.partials / 2;
+    const int64_t lead_parts = uniform ? std::max<int64_t>(1, kResidentGroups / std::max<int64_t>(1, units))
+                                       : plan.partials - plan.partials / 2;
+    const int64_t tail_parts = plan.partials - lead_parts;
     if (groups < 2 * kResidentGroups || tail_parts < 1)
         return cs;
     const int64_t tail = std::max<int64_t>(1, plan.pages_per_split * (uniform ? 1 : 3) / 8);
-    const int64_t lead_chunks = chunks - tail_parts * kChunksPerGroup;
+    const int64_t lead_chunks = lead_parts * kChunksPerGroup;
     const int64_t lead = (span - tail_parts * kChunksPerGroup * tail + lead_chunks - 1) / lead_chunks;
     if (tail < plan.pages_per_split && lead >= plan.pages_per_split) {
         cs.lead_chunks = static_cast<int32_t>(lead_chunks);

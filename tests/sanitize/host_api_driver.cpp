@@ -89,8 +89,8 @@ static void plans()
     EXPECT(fp4kv_decode_plan(&L, 32, 64, 512, 64, &s, &p, &ws) == FP4KV_OK && s == 64 && p == 16);
     EXPECT(fp4kv_decode_chunks(&L, 32, 1, 64, 512, 0, 64, 0, &lc, &lp, &tp) == FP4KV_OK && lc == 32 && lp == 13 &&
            tp == 3);
-    EXPECT(fp4kv_decode_chunks(&L, 32, 1, 64, 512, 0, 64, 32768, &lc, &lp, &tp) == FP4KV_OK && lc == 16 &&
-           lp == 29 && tp == 1);
+    EXPECT(fp4kv_decode_chunks(&L, 32, 1, 64, 512, 0, 64, 32768, &lc, &lp, &tp) == FP4KV_OK && lc == 12 &&
+           lp == 39 && tp == 1);
     EXPECT(fp4kv_decode_plan(&L, -1, 64, 512, 64, &s, &p, &ws) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_plan(&L, 1, 65, 512, 64, &s, &p, &ws) == FP4KV_ERR_INVALID_ARGUMENT);
     EXPECT(fp4kv_decode_plan(&L, 1, 64, 512, 64, nullptr, &p, &ws) == FP4KV_ERR_INVALID_ARGUMENT);

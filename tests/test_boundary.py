@@ -177,12 +177,14 @@ def test_chunks():
 
 def test_chunks_with_a_shortest_length():
     """min_seq_len: when every sequence covers at least 7/8 of the span, the
-    last 3/4 of the partials take chunks of 1/8 of the even size (at least a
-    page); a smaller bound, or none, keeps the default cut."""
+    lead partials are as many as fill 768 resident workgroups once (at least
+    one) and every later partial takes chunks of 1/8 of the even size (at
+    least a page); a smaller bound, or none, keeps the default cut."""
     L = fk.cache_layout(8, 128, 32 * 512)
-    # the 32 x 32K batch at 64 chunks: 48 one-page chunks, 16 of 29 pages
-    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=32768)) == (16, 29, 1)
-    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8)) == (16, 29, 1)
+    # the 32 x 32K batch at 64 chunks: 3 lead partials (3 x 256 = 768 workgroups)
+    # of 39-page chunks, then 52 one-page chunks
+    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=32768)) == (12, 39, 1)
+    assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8)) == (12, 39, 1)
     assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8 - 64)) == (32, 13, 3)
     # the paged batch's shortest sequence (1,024 tokens) keeps the default cut
     assert tuple(fk.decode_chunks(L, 64, 32, 258, 0, min_seq_len=1024)) == (16, 14, 3)
@@ -204,7 +206,7 @@ def test_chunks_with_a_shortest_length():
                 assert ch.lead_pages == ch.tail_pages == pps
             else:
                 assert 8 * B * plan.partials >= 1536
-                assert ch.lead_chunks == 4 * (plan.partials - 3 * plan.partials // 4)
+                assert ch.lead_chunks == 4 * max(1, 768 // (8 * B))
                 assert ch.tail_pages == max(1, pps // 8) < pps <= ch.lead_pages
                 assert ch.lead_chunks * (ch.lead_pages - 1) + (chunks - ch.lead_chunks) * ch.tail_pages < span
         # a bound under 7/8 of the span: the default cut
