@@ -165,14 +165,17 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
 //     even size;
 //   - when the caller promises that every sequence covers at least 7/8 of
 //     the span (min_span: pages each sequence is known to cover, 0 when
-//     nothing is known), only as many lead partials are kept as fill the
-//     GPU's resident workgroups once (at least one), and every later
-//     partial takes chunks of 1/8 of the even size (at least one page).
+//     nothing is known), every partial after the lead ones takes chunks of
+//     1/8 of the even size (at least one page).  The lead partials are, for
+//     the FP4 cache, as many as fill the GPU's resident workgroups once (at
+//     least one); for the FP8 caches a quarter of the partials.
 // (Measured on the 32 x 32K batch at 64 chunks and the paged 64-sequence
-// batch: the second cut gains 5.7 % on the first -- fewer or more lead
-// partials than one generation's worth are slower -- but on the second it
-// packs a short sequence's pages into one long lead chunk whose workgroup's
-// other waves idle, and it holds the long sequences in few long workgroups.)
+// batch: the second cut gains about 6 % on the first -- with FP4 pages,
+// lead partials beyond one generation's worth are 1.6 % slower, with the
+// FP8 caches' 16 KB pages fewer than a quarter are 1-4 % slower -- but on
+// the second it packs a short sequence's pages into one long lead chunk
+// whose workgroup's other waves idle, and it holds the long sequences in
+// few long workgroups.)
 struct ChunkSizes {
     int32_t lead_chunks, lead_pages, tail_pages;
 };
@@ -185,8 +188,10 @@ ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan 
     const int64_t units = static_cast<int64_t>(L.params.num_kv_heads) * batch;     // workgroups per partial
     const int64_t groups = units * plan.partials;
     const bool uniform = min_span > 0 && 8 * min_span >= 7 * span;
-    const int64_t lead_parts = uniform ? std::max<int64_t>(1, kResidentGroups / std::max<int64_t>(1, units))
-                                       : plan.partials - plan.partials / 2;
+    const bool fp4 = L.params.format == FP4KV_FORMAT_FP4_E2M1;
+    const int64_t lead_parts = !uniform ? plan.partials - plan.partials / 2
+                               : fp4    ? std::max<int64_t>(1, kResidentGroups / std::max<int64_t>(1, units))
+                                        : plan.partials - plan.partials * 3 / 4;
     const int64_t tail_parts = plan.partials - lead_parts;
     if (groups < 2 * kResidentGroups || tail_parts < 1)
         return cs;
