@@ -167,11 +167,12 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
 //     the span (min_span: pages each sequence is known to cover, 0 when
 //     nothing is known), every partial after the lead ones takes chunks of
 //     1/8 of the even size (at least one page).  The lead partials are, for
-//     the FP4 cache, as many as fill the GPU's resident workgroups once (at
-//     least one); for the FP8 caches a quarter of the partials.
+//     the FP4 cache, the fewest whose workgroups fill the GPU's resident
+//     slots at least once; for the FP8 caches a quarter of the partials.
 // (Measured on the 32 x 32K batch at 64 chunks and the paged 64-sequence
 // batch: the second cut gains about 6 % on the first -- with FP4 pages,
-// lead partials beyond one generation's worth are 1.6 % slower, with the
+// lead partials beyond one generation's worth are 1.6 % slower, fewer than
+// one generation's worth (64 sequences, one partial of 512) 7 % slower, with the
 // FP8 caches' 16 KB pages fewer than a quarter are 1-4 % slower -- but on
 // the second it packs a short sequence's pages into one long lead chunk
 // whose workgroup's other waves idle, and it holds the long sequences in
@@ -190,7 +191,7 @@ ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan 
     const bool uniform = min_span > 0 && 8 * min_span >= 7 * span;
     const bool fp4 = L.params.format == FP4KV_FORMAT_FP4_E2M1;
     const int64_t lead_parts = !uniform ? plan.partials - plan.partials / 2
-                               : fp4    ? std::max<int64_t>(1, kResidentGroups / std::max<int64_t>(1, units))
+                               : fp4    ? (kResidentGroups + units - 1) / std::max<int64_t>(1, units)
                                         : plan.partials - plan.partials * 3 / 4;
     const int64_t tail_parts = plan.partials - lead_parts;
     if (groups < 2 * kResidentGroups || tail_parts < 1)

@@ -237,9 +237,9 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  * options) says that every sequence covers at least 7/8 of the span
  * (ceil(min_seq_len / 64) >= 7/8 of it), every partial after the lead
  * ones takes TP = max(1, E / 8) pages; the lead partials are the first
- * max(1, floor(768 / (H_kv x batch))) for the FP4 cache (as many workgroups
- * as the GPU holds at once) and the first P - floor(3P / 4) for the FP8
- * caches.  Either cut is used only where it leaves
+ * ceil(768 / (H_kv x batch)) for the FP4 cache (the fewest whose
+ * workgroups fill the 768 the GPU holds at once) and the first
+ * P - floor(3P / 4) for the FP8 caches.  Either cut is used only where it leaves
  * TP < E <= LP.  Arguments as for fp4kv_decode_plan, plus q_tokens >= 1 and
  * window >= 0 as for fp4kv_decode_window_attention (batch x q_tokens x
  * num_q_heads query rows) and min_seq_len >= 0.

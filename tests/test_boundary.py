@@ -178,15 +178,17 @@ def test_chunks():
 def test_chunks_with_a_shortest_length():
     """min_seq_len: when every sequence covers at least 7/8 of the span,
     every partial after the lead ones takes chunks of 1/8 of the even size
-    (at least a page); the lead partials fill 768 resident workgroups once
-    (at least one) for the FP4 cache, a quarter of the partials for the FP8
-    caches.  A smaller bound, or none, keeps the default cut."""
+    (at least a page); the lead partials are the fewest whose workgroups
+    fill 768 resident slots for the FP4 cache, a quarter of the partials for
+    the FP8 caches.  A smaller bound, or none, keeps the default cut."""
     L = fk.cache_layout(8, 128, 32 * 512)
     # the 32 x 32K batch at 64 chunks: 3 lead partials (3 x 256 = 768 workgroups)
     # of 39-page chunks, then 52 one-page chunks
     assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=32768)) == (12, 39, 1)
     assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8)) == (12, 39, 1)
     assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8 - 64)) == (32, 13, 3)
+    # 64 sequences: one partial is 512 workgroups, so two lead partials
+    assert tuple(fk.decode_chunks(L, 64, 64, 512, 64, min_seq_len=32768)) == (8, 57, 1)
     # the FP8 caches keep a quarter of the partials as lead ones: 16 chunks of 29 pages, 48 of one
     for kw in (dict(format=fk.FORMAT_FP8_E4M3, k_scale=1.0, v_scale=1.0), dict(format=fk.FORMAT_FP8_E4M3_TOKEN)):
         L8 = fk.cache_layout(8, 128, 32 * 512, **kw)
@@ -212,7 +214,7 @@ def test_chunks_with_a_shortest_length():
                 assert ch.lead_pages == ch.tail_pages == pps
             else:
                 assert 8 * B * plan.partials >= 1536
-                assert ch.lead_chunks == 4 * max(1, 768 // (8 * B))
+                assert ch.lead_chunks == 4 * -(-768 // (8 * B))
                 assert ch.tail_pages == max(1, pps // 8) < pps <= ch.lead_pages
                 assert ch.lead_chunks * (ch.lead_pages - 1) + (chunks - ch.lead_chunks) * ch.tail_pages < span
         # a bound under 7/8 of the span: the default cut

@@ -205,7 +205,7 @@ def test_shortest_length_cut_against_oracle(fmt, kernel):
     L0 = kf.layout(fmt, HKV, D, 64)
     lo = -(-7 * MAXP // 8)
     ch = fk.decode_chunks(L0, BATCH, HKV * G, MAXP, SPLITS, min_seq_len=lo * 64)
-    lead_parts = max(1, 768 // (HKV * BATCH)) if fmt == "fp4" else plan.partials - 3 * plan.partials // 4
+    lead_parts = -(-768 // (HKV * BATCH)) if fmt == "fp4" else plan.partials - 3 * plan.partials // 4
     assert ch.tail_pages == 1 < ch.lead_pages and ch.lead_chunks == 4 * lead_parts
     lens = _hinted_lengths(ch, 4 * plan.partials, MAXP, BATCH, lo, seed=15)
     _say(f"shortest-length cut {tuple(ch)}: {fmt} kernel {kernel}, lengths {sorted(lens)[:8]}..")
