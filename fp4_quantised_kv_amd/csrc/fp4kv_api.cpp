@@ -168,7 +168,8 @@ int make_plan(const fp4kv_cache_layout_t &L, int32_t batch, int32_t num_q_heads,
 //     nothing is known), every partial after the lead ones takes chunks of
 //     1/8 of the even size (at least one page).  The lead partials are, for
 //     the FP4 cache, the fewest whose workgroups fill the GPU's resident
-//     slots at least once; for the FP8 caches a quarter of the partials.
+//     slots at least once; for the FP8 caches a quarter of the partials, or
+//     that many if a quarter does not fill the slots.
 // (Measured on the 32 x 32K batch at 64 chunks and the paged 64-sequence
 // batch: the second cut gains about 6 % on the first -- with FP4 pages,
 // lead partials beyond one generation's worth are 1.6 % slower, fewer than
@@ -190,9 +191,10 @@ ChunkSizes chunk_sizes(const fp4kv_cache_layout_t &L, int32_t batch, const Plan 
     const int64_t groups = units * plan.partials;
     const bool uniform = min_span > 0 && 8 * min_span >= 7 * span;
     const bool fp4 = L.params.format == FP4KV_FORMAT_FP4_E2M1;
+    const int64_t fill = (kResidentGroups + units - 1) / std::max<int64_t>(1, units);   // lead partials to fill the GPU
     const int64_t lead_parts = !uniform ? plan.partials - plan.partials / 2
-                               : fp4    ? (kResidentGroups + units - 1) / std::max<int64_t>(1, units)
-                                        : plan.partials - plan.partials * 3 / 4;
+                               : fp4    ? fill
+                                        : std::max<int64_t>(fill, plan.partials - plan.partials * 3 / 4);
     const int64_t tail_parts = plan.partials - lead_parts;
     if (groups < 2 * kResidentGroups || tail_parts < 1)
         return cs;

@@ -238,8 +238,8 @@ FP4KV_API int fp4kv_decode_plan(const fp4kv_cache_layout_t *layout, int32_t batc
  * (ceil(min_seq_len / 64) >= 7/8 of it), every partial after the lead
  * ones takes TP = max(1, E / 8) pages; the lead partials are the first
  * ceil(768 / (H_kv x batch)) for the FP4 cache (the fewest whose
- * workgroups fill the 768 the GPU holds at once) and the first
- * P - floor(3P / 4) for the FP8 caches.  Either cut is used only where it leaves
+ * workgroups fill the 768 the GPU holds at once) and, for the FP8 caches,
+ * the first max(P - floor(3P / 4), ceil(768 / (H_kv x batch))).  Either cut is used only where it leaves
  * TP < E <= LP.  Arguments as for fp4kv_decode_plan, plus q_tokens >= 1 and
  * window >= 0 as for fp4kv_decode_window_attention (batch x q_tokens x
  * num_q_heads query rows) and min_seq_len >= 0.

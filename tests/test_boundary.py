@@ -179,8 +179,9 @@ def test_chunks_with_a_shortest_length():
     """min_seq_len: when every sequence covers at least 7/8 of the span,
     every partial after the lead ones takes chunks of 1/8 of the even size
     (at least a page); the lead partials are the fewest whose workgroups
-    fill 768 resident slots for the FP4 cache, a quarter of the partials for
-    the FP8 caches.  A smaller bound, or none, keeps the default cut."""
+    fill 768 resident slots for the FP4 cache, a quarter of the partials (or
+    that many) for the FP8 caches.  A smaller bound, or none, keeps the
+    default cut."""
     L = fk.cache_layout(8, 128, 32 * 512)
     # the 32 x 32K batch at 64 chunks: 3 lead partials (3 x 256 = 768 workgroups)
     # of 39-page chunks, then 52 one-page chunks
@@ -189,10 +190,12 @@ def test_chunks_with_a_shortest_length():
     assert tuple(fk.decode_chunks(L, 32, 64, 512, 64, min_seq_len=7 * 512 * 64 // 8 - 64)) == (32, 13, 3)
     # 64 sequences: one partial is 512 workgroups, so two lead partials
     assert tuple(fk.decode_chunks(L, 64, 64, 512, 64, min_seq_len=32768)) == (8, 57, 1)
-    # the FP8 caches keep a quarter of the partials as lead ones: 16 chunks of 29 pages, 48 of one
+    # the FP8 caches keep a quarter of the partials as lead ones (16 chunks of 29 pages, 48 of
+    # one), or more where a quarter would not fill the GPU (16 sequences: 6 partials of 128)
     for kw in (dict(format=fk.FORMAT_FP8_E4M3, k_scale=1.0, v_scale=1.0), dict(format=fk.FORMAT_FP8_E4M3_TOKEN)):
         L8 = fk.cache_layout(8, 128, 32 * 512, **kw)
         assert tuple(fk.decode_chunks(L8, 32, 64, 512, 64, min_seq_len=32768)) == (16, 29, 1)
+        assert tuple(fk.decode_chunks(L8, 16, 64, 512, 64, min_seq_len=32768)) == (24, 20, 1)
         assert tuple(fk.decode_chunks(L8, 32, 64, 512, 64)) == (32, 13, 3)
     # the paged batch's shortest sequence (1,024 tokens) keeps the default cut
     assert tuple(fk.decode_chunks(L, 64, 32, 258, 0, min_seq_len=1024)) == (16, 14, 3)

@@ -200,12 +200,13 @@ def _hinted_lengths(ch, n_chunks, maxp, batch, lo, seed):
 def test_shortest_length_cut_against_oracle(fmt, kernel):
     """Every sequence at least 7/8 of the table: with the shortest length
     given, the partials after the lead ones (the first generation's worth
-    for FP4, a quarter for FP8) take one-page chunks."""
+    for FP4, a quarter or that for FP8) take one-page chunks."""
     plan = _chunks(fmt)[0]
     L0 = kf.layout(fmt, HKV, D, 64)
     lo = -(-7 * MAXP // 8)
     ch = fk.decode_chunks(L0, BATCH, HKV * G, MAXP, SPLITS, min_seq_len=lo * 64)
-    lead_parts = -(-768 // (HKV * BATCH)) if fmt == "fp4" else plan.partials - 3 * plan.partials // 4
+    fill = -(-768 // (HKV * BATCH))
+    lead_parts = fill if fmt == "fp4" else max(fill, plan.partials - 3 * plan.partials // 4)
     assert ch.tail_pages == 1 < ch.lead_pages and ch.lead_chunks == 4 * lead_parts
     lens = _hinted_lengths(ch, 4 * plan.partials, MAXP, BATCH, lo, seed=15)
     _say(f"shortest-length cut {tuple(ch)}: {fmt} kernel {kernel}, lengths {sorted(lens)[:8]}..")
